@@ -1,0 +1,15 @@
+"""Oracle for block-diffusion attention: TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the build entry point's smoke check and the benchmark's
+CPU-baseline leg may import this package. The GPU library does not import,
+link or call it, and it imports nothing from the GPU library.
+
+Every function here is pinned by a CPU test against something other than
+itself (a hand-drawn mask fixture, closed forms at Q = 0, a library attention
+routine, scalar brute force, finite differences, invariants of the method).
+"""
+from .bdattn_oracle import (CLEAN, CORRUPTED, Layout, Oracle, key_tokens, layout,
+                            query_tokens, visible)
+
+__all__ = ["CLEAN", "CORRUPTED", "Layout", "Oracle", "key_tokens", "layout",
+           "query_tokens", "visible"]

@@ -1,0 +1,298 @@
+"""CPU float64 oracle for clean-plus-corrupted block-diffusion attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check of the build
+entry point and the benchmark's CPU-baseline leg may import this module. The
+GPU library never calls it and shares no code with it.
+
+What it computes follows "Block Parallelism for Efficient Distributed
+Long-Context Diffusion Language Model Training":
+
+* §3.2 (Block diffusion language models): a clean copy and a corrupted copy of
+  the sequence, split into blocks. A clean token of block b sees the clean
+  tokens of blocks <= b (the whole own block: the block-causal reading, see
+  ``visible``); a corrupted token of target block b sees its own corrupted
+  block bidirectionally and the clean prefix of blocks < b, and never the
+  corrupted tokens of other blocks.
+* §4.4 (Proposition 1): the distributed schemes reproduce exactly the plain
+  masked computation, so the oracle is the plain definition of masked softmax
+  attention over the visible keys, with its textbook analytic backward. No
+  tiling, no online softmax, no skipping beyond restricting each row chunk to
+  the columns its own mask marks visible.
+* §4.3 (Backward pass): gradients of clean K/V sum the contributions of every
+  query (clean, or corrupted of a later block) that sees them.
+
+Conventions (readings where the pages are silent): blocks are 0-indexed with
+block(p) = floor(p / B) on global clean positions; the scale defaults to
+1/sqrt(d); LSE is the natural log of the softmax normaliser, including the
+scale; q head h reads KV head floor(h / (H/Hkv)); no position encoding,
+dropout or bias; LSE is not differentiated.
+
+Every array is float64 numpy. Queries are indexed clean-local first, then
+corrupted-local; keys are the clean buffer first, then the corrupted keys.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+CLEAN = 0
+CORRUPTED = 1
+
+__all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens",
+           "Oracle", "CLEAN", "CORRUPTED"]
+
+
+@dataclass(frozen=True)
+class Layout:
+    B: int
+    H: int
+    Hkv: int
+    d: int
+    scale: float
+    n_clean_q: int
+    clean_q_start: int
+    n_clean_kv: int
+    clean_kv_start: int
+    corr_ids: tuple  # global ids of the local corrupted blocks, increasing
+
+    @property
+    def G(self) -> int:
+        return self.H // self.Hkv
+
+    @property
+    def n_corr(self) -> int:
+        return len(self.corr_ids) * self.B
+
+    @property
+    def nq(self) -> int:
+        return self.n_clean_q + self.n_corr
+
+    @property
+    def nk(self) -> int:
+        return self.n_clean_kv + self.n_corr
+
+
+def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int = 0,
+           n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
+           n_corr_blocks: Optional[int] = None,
+           corr_block_ids: Optional[Sequence[int]] = None,
+           scale: Optional[float] = None, require_coverage: bool = True) -> Layout:
+    """Describe one problem. Without ids, the corrupted blocks are 0..n-1
+    (n defaults to the number of clean blocks of the query shard).
+
+    With ``require_coverage`` (the default) the clean K/V buffer must hold
+    every clean key some local query sees; otherwise the problem would only
+    be a partial attention and a ValueError is raised."""
+    if n_clean_kv is None:
+        n_clean_kv = n_clean_q
+    if corr_block_ids is None:
+        if n_corr_blocks is None:
+            n_corr_blocks = n_clean_q // B
+        corr_block_ids = range(n_corr_blocks)
+    ids = tuple(int(i) for i in corr_block_ids)
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(d)
+    if require_coverage:
+        need = 0  # one past the last clean position some query sees
+        if n_clean_q:
+            need = ((clean_q_start + n_clean_q - 1) // B + 1) * B
+        if ids:
+            need = max(need, max(ids) * B)
+        if need and (clean_kv_start > 0 or clean_kv_start + n_clean_kv < need):
+            raise ValueError("clean K/V buffer does not cover every visible clean key")
+    return Layout(B, H, Hkv, d, float(scale), n_clean_q, clean_q_start, n_clean_kv,
+                  clean_kv_start, ids)
+
+
+def query_tokens(lay: Layout):
+    """(stream, block) of every query: clean-local rows, then corrupted."""
+    pos = lay.clean_q_start + np.arange(lay.n_clean_q, dtype=np.int64)
+    stream = np.concatenate([np.full(lay.n_clean_q, CLEAN, np.int8),
+                             np.full(lay.n_corr, CORRUPTED, np.int8)])
+    block = np.concatenate([pos // lay.B,
+                            np.repeat(np.asarray(lay.corr_ids, np.int64), lay.B)])
+    return stream, block
+
+
+def key_tokens(lay: Layout):
+    """(stream, block) of every key: the clean buffer, then corrupted."""
+    pos = lay.clean_kv_start + np.arange(lay.n_clean_kv, dtype=np.int64)
+    stream = np.concatenate([np.full(lay.n_clean_kv, CLEAN, np.int8),
+                             np.full(lay.n_corr, CORRUPTED, np.int8)])
+    block = np.concatenate([pos // lay.B,
+                            np.repeat(np.asarray(lay.corr_ids, np.int64), lay.B)])
+    return stream, block
+
+
+def visible(q_stream, q_block, k_stream, k_block):
+    """The four visibility rules of §3.2, broadcast over their arguments.
+
+    clean query, block qb     -> clean key of block kb  iff kb <= qb
+    clean query               -> corrupted key          never
+    corrupted query, block qb -> clean key of block kb  iff kb <  qb
+    corrupted query, block qb -> corrupted key, block kb iff kb == qb
+    """
+    qc = q_stream == CLEAN
+    kc = k_stream == CLEAN
+    clean_clean = qc & kc & (k_block <= q_block)
+    corr_clean = ~qc & kc & (k_block < q_block)
+    corr_corr = ~qc & ~kc & (k_block == q_block)
+    return clean_clean | corr_clean | corr_corr
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+class Oracle:
+    """Plain masked softmax attention and its analytic backward, in float64.
+
+    Construct with the layout and the inputs (Q/dO ``[n, H, d]``, K/V
+    ``[n, Hkv, d]``) exactly as the GPU receives them (upcast, never rounded).
+    """
+
+    # rows x columns of one chunk's dense score matrix (bounded memory only)
+    CHUNK_ELEMS = 1 << 23
+
+    def __init__(self, lay: Layout, q_c, k_c, v_c, q_x, k_x, v_x, do_c=None, do_x=None):
+        self.lay = lay
+        self.Q = np.concatenate([_f64(q_c), _f64(q_x)]).reshape(lay.nq, lay.H, lay.d)
+        self.K = np.concatenate([_f64(k_c), _f64(k_x)]).reshape(lay.nk, lay.Hkv, lay.d)
+        self.V = np.concatenate([_f64(v_c), _f64(v_x)]).reshape(lay.nk, lay.Hkv, lay.d)
+        if do_c is not None:
+            self.dO = np.concatenate([_f64(do_c), _f64(do_x)]).reshape(lay.nq, lay.H, lay.d)
+        else:
+            self.dO = None
+        self.qs, self.qb = query_tokens(lay)
+        self.ks, self.kb = key_tokens(lay)
+
+    # ---------------------------------------------------------------- helpers
+    def _mask(self, qidx, kidx=None):
+        if kidx is None:
+            return visible(self.qs[qidx, None], self.qb[qidx, None],
+                           self.ks[None, :], self.kb[None, :])
+        return visible(self.qs[qidx, None], self.qb[qidx, None],
+                       self.ks[None, kidx], self.kb[None, kidx])
+
+    def _chunks(self, qidx):
+        qidx = np.asarray(qidx, dtype=np.int64)
+        step = max(1, min(2048, self.CHUNK_ELEMS // max(1, self.lay.nk)))
+        for s in range(0, len(qidx), step):
+            yield s, qidx[s:s + step]
+
+    def _scores(self, rows, cols, Mc, h):
+        """Masked scores S = scale * q k^T, -inf where not visible."""
+        g = h // self.lay.G
+        S = self.lay.scale * (self.Q[rows, h] @ self.K[cols, g].T)
+        S[~Mc] = -np.inf
+        return S
+
+    # ---------------------------------------------------------------- forward
+    def rows_forward(self, qidx):
+        """O ``[n, H, d]`` and LSE ``[H, n]`` of the given query rows."""
+        qidx = np.asarray(qidx, dtype=np.int64)
+        lay = self.lay
+        O = np.zeros((len(qidx), lay.H, lay.d))
+        LSE = np.zeros((lay.H, len(qidx)))
+        for s, rows in self._chunks(qidx):
+            M = self._mask(rows)
+            if not M.any(axis=1).all():
+                raise ValueError("a query row sees no key")
+            cols = np.flatnonzero(M.any(axis=0))
+            Mc = M[:, cols]
+            for h in range(lay.H):
+                g = h // lay.G
+                S = self._scores(rows, cols, Mc, h)
+                m = S.max(axis=1)
+                E = np.exp(S - m[:, None])
+                l = E.sum(axis=1)
+                LSE[h, s:s + len(rows)] = m + np.log(l)
+                O[s:s + len(rows), h] = (E / l[:, None]) @ self.V[cols, g]
+        return O, LSE
+
+    def forward(self):
+        """Full forward: (O_c, O_x, LSE_c, LSE_x)."""
+        O, LSE = self.rows_forward(np.arange(self.lay.nq))
+        nc = self.lay.n_clean_q
+        return O[:nc], O[nc:], LSE[:, :nc], LSE[:, nc:]
+
+    # --------------------------------------------------------------- backward
+    def _row_stats(self, qidx, O=None, LSE=None):
+        if O is None or LSE is None:
+            O, LSE = self.rows_forward(qidx)
+        D = np.einsum("nhd,nhd->nh", self.dO[qidx], O)  # D_i = <dO_i, O_i>
+        return O, LSE, D
+
+    def rows_backward(self, qidx, kidx=None, O=None, LSE=None):
+        """Gradients contributed by the given query rows.
+
+        Returns dQ of those rows ``[n, H, d]`` and the dK, dV ``[nk, Hkv, d]``
+        those rows contribute (summed over the rows and the q heads of each KV
+        group). ``kidx`` restricts the key columns considered (all columns a
+        row sees must be included for dQ to be complete).
+        """
+        if self.dO is None:
+            raise ValueError("no upstream gradient given")
+        lay = self.lay
+        qidx = np.asarray(qidx, dtype=np.int64)
+        O, LSE, D = self._row_stats(qidx, O, LSE)
+        dQ = np.zeros((len(qidx), lay.H, lay.d))
+        dK = np.zeros((lay.nk, lay.Hkv, lay.d))
+        dV = np.zeros((lay.nk, lay.Hkv, lay.d))
+        for s, rows in self._chunks(qidx):
+            sl = slice(s, s + len(rows))
+            M = self._mask(rows)
+            if kidx is not None:
+                keep = np.zeros(lay.nk, bool)
+                keep[kidx] = True
+                M = M & keep[None, :]
+            cols = np.flatnonzero(M.any(axis=0))
+            if len(cols) == 0:
+                continue
+            Mc = M[:, cols]
+            for h in range(lay.H):
+                g = h // lay.G
+                S = self._scores(rows, cols, Mc, h)
+                P = np.exp(S - LSE[h, sl][:, None])  # exp(-inf) = 0 off the mask
+                dP = self.dO[rows, h] @ self.V[cols, g].T
+                dS = P * (dP - D[sl, h][:, None])
+                dQ[sl, h] = lay.scale * (dS @ self.K[cols, g])
+                dK[cols, g] += lay.scale * (dS.T @ self.Q[rows, h])
+                dV[cols, g] += P.T @ self.dO[rows, h]
+        return dQ, dK, dV
+
+    def backward(self, O=None, LSE=None):
+        """Full backward: (dQ_c, dQ_x, dK_c, dV_c, dK_x, dV_x)."""
+        lay = self.lay
+        dQ, dK, dV = self.rows_backward(np.arange(lay.nq), O=O, LSE=LSE)
+        nc, nkc = lay.n_clean_q, lay.n_clean_kv
+        return dQ[:nc], dQ[nc:], dK[:nkc], dV[:nkc], dK[nkc:], dV[nkc:]
+
+    def keys_backward(self, kidx):
+        """dK, dV ``[len(kidx), Hkv, d]`` of the given key columns: every
+        query that sees one of them contributes (its full row is used for its
+        LSE and D)."""
+        kidx = np.asarray(kidx, dtype=np.int64)
+        seen = np.zeros(self.lay.nq, bool)
+        for s, rows in self._chunks(np.arange(self.lay.nq)):
+            seen[rows] = self._mask(rows, kidx).any(axis=1)
+        qidx = np.flatnonzero(seen)
+        if len(qidx) == 0:
+            z = np.zeros((len(kidx), self.lay.Hkv, self.lay.d))
+            return z, z.copy()
+        _, dK, dV = self.rows_backward(qidx, kidx=kidx)
+        return dK[kidx], dV[kidx]
+
+    def query_index(self, stream, local_rows):
+        """Global query index of local rows of a stream."""
+        local_rows = np.asarray(local_rows, dtype=np.int64)
+        return local_rows if stream == CLEAN else self.lay.n_clean_q + local_rows
+
+    def key_index(self, stream, local_rows):
+        local_rows = np.asarray(local_rows, dtype=np.int64)
+        return local_rows if stream == CLEAN else self.lay.n_clean_kv + local_rows

@@ -1,0 +1,427 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test names what fixes the expected value: a hand-drawn mask, a closed
+form, a library attention routine, scalar brute force, numerical derivatives,
+or an invariant the method states ("Block Parallelism for Efficient
+Distributed Long-Context Diffusion Language Model Training", §3.2 separability,
+§4.3 clean-gradient accumulation, §4.4 Proposition 1 exactness).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import CLEAN, CORRUPTED, Oracle, key_tokens, layout, query_tokens, visible
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def make(lay, seed=0, scale=1.0):
+    n_c, n_kv, n_x = lay.n_clean_q, lay.n_clean_kv, lay.n_corr
+    H, Hkv, d = lay.H, lay.Hkv, lay.d
+    return dict(
+        q_c=rnd((n_c, H, d), seed + 1, scale), k_c=rnd((n_kv, Hkv, d), seed + 2, scale),
+        v_c=rnd((n_kv, Hkv, d), seed + 3, scale), q_x=rnd((n_x, H, d), seed + 4, scale),
+        k_x=rnd((n_x, Hkv, d), seed + 5, scale), v_x=rnd((n_x, Hkv, d), seed + 6, scale),
+        do_c=rnd((n_c, H, d), seed + 7), do_x=rnd((n_x, H, d), seed + 8))
+
+
+def oracle_of(lay, t):
+    return Oracle(lay, t["q_c"], t["k_c"], t["v_c"], t["q_x"], t["k_x"], t["v_x"],
+                  t.get("do_c"), t.get("do_x"))
+
+
+def full_mask(lay):
+    qs, qb = query_tokens(lay)
+    ks, kb = key_tokens(lay)
+    return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :])
+
+
+# --------------------------------------------------------------------- mask
+def read_golden(name):
+    rows, params = [], {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("params"):
+                for kv in line.split()[1:]:
+                    k, v = kv.split("=")
+                    params[k] = [int(x) for x in v.split(",")] if k == "ids" else int(v)
+                continue
+            bits = line.split()[1].replace("|", "")
+            rows.append([c == "1" for c in bits])
+    return params, np.array(rows, dtype=bool)
+
+
+@pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt"])
+def test_mask_matches_hand_drawn_fixture(name):
+    p, want = read_golden(name)
+    lay = layout(p["B"], 1, 1, 4, p["n_clean_q"], p["clean_q_start"], p["n_clean_kv"],
+                 corr_block_ids=p["ids"])
+    got = full_mask(lay)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("L,B", [(4, 1), (8, 2), (12, 3), (16, 4), (32, 8), (24, 24)])
+def test_visible_counts_closed_form(L, B):
+    """Both streams see (qb+1)*B keys: clean sees blocks 0..qb; corrupted sees
+    blocks 0..qb-1 clean plus its own corrupted block (§3.2)."""
+    lay = layout(B, 1, 1, 4, L)
+    M = full_mask(lay)
+    qs, qb = query_tokens(lay)
+    assert np.array_equal(M.sum(1), (qb + 1) * B)
+    # clean queries never see corrupted keys; each corrupted query sees
+    # exactly its own block's B corrupted keys
+    assert not M[:L, L:].any()
+    assert np.array_equal(M[L:, L:].sum(1), np.full(L, B))
+
+
+# ------------------------------------------------------------- closed forms
+def _prefix_sets(lay):
+    """Visible key index sets written as ranges (clean prefix length, own
+    corrupted block), a formulation independent of the pairwise rules."""
+    out = []
+    nkc = lay.n_clean_kv
+    for i in range(lay.n_clean_q):
+        b = (lay.clean_q_start + i) // lay.B
+        out.append(list(range(0, (b + 1) * lay.B)))
+    for j, bid in enumerate(lay.corr_ids):
+        own = list(range(nkc + j * lay.B, nkc + (j + 1) * lay.B))
+        for _ in range(lay.B):
+            out.append(list(range(0, bid * lay.B)) + own)
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=4, n_clean_q=32), dict(B=1, n_clean_q=9), dict(B=8, n_clean_q=24),
+    dict(B=2, n_clean_q=6, clean_q_start=10, n_clean_kv=16, corr_block_ids=[0, 3, 7]),
+])
+def test_q_zero_uniform_weights(case):
+    """Q = 0 makes every visible score 0: O_i is the mean of v over V(i) and
+    LSE_i = ln |V(i)|; dV_j = sum over rows i seeing j of dO_i / |V(i)|."""
+    lay = layout(H=4, Hkv=2, d=3, **case)
+    t = make(lay, seed=3)
+    t["q_c"][:] = 0
+    t["q_x"][:] = 0
+    orc = oracle_of(lay, t)
+    O_c, O_x, L_c, L_x = orc.forward()
+    O = np.concatenate([O_c, O_x])
+    LSE = np.concatenate([L_c, L_x], axis=1)
+    V = np.concatenate([t["v_c"], t["v_x"]])
+    dO = np.concatenate([t["do_c"], t["do_x"]])
+    sets = _prefix_sets(lay)
+    dV_want = np.zeros_like(V)
+    for i, s in enumerate(sets):
+        for h in range(lay.H):
+            g = h // lay.G
+            np.testing.assert_allclose(O[i, h], V[s, g].mean(0), rtol=0, atol=1e-13)
+            assert abs(LSE[h, i] - math.log(len(s))) < 1e-13
+            dV_want[s, g] += dO[i, h] / len(s)
+    _, _, _, dV_c, _, dV_x = orc.backward()
+    np.testing.assert_allclose(np.concatenate([dV_c, dV_x]), dV_want, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------- brute force
+def test_scalar_brute_force_forward():
+    """Per-query scalar loop, math.fsum softmax, over the range formulation."""
+    for B, L, d in [(1, 6, 3), (2, 8, 5), (4, 12, 8)]:
+        lay = layout(B, 2, 1, d, L)
+        t = make(lay, seed=11)
+        orc = oracle_of(lay, t)
+        O_c, O_x, L_c, L_x = orc.forward()
+        O = np.concatenate([O_c, O_x])
+        LSE = np.concatenate([L_c, L_x], axis=1)
+        Q = np.concatenate([t["q_c"], t["q_x"]])
+        K = np.concatenate([t["k_c"], t["k_x"]])
+        V = np.concatenate([t["v_c"], t["v_x"]])
+        for i, s in enumerate(_prefix_sets(lay)):
+            for h in range(lay.H):
+                sc = [math.fsum(Q[i, h, e] * K[j, 0, e] for e in range(d)) / math.sqrt(d)
+                      for j in s]
+                m = max(sc)
+                w = [math.exp(x - m) for x in sc]
+                z = math.fsum(w)
+                assert abs(LSE[h, i] - (m + math.log(z))) < 1e-12
+                for e in range(d):
+                    o = math.fsum(w[k] * V[j, 0, e] for k, j in enumerate(s)) / z
+                    assert abs(O[i, h, e] - o) < 1e-12
+
+
+# ------------------------------------------------------- library attention
+def _sdpa_reference(lay, t, mask):
+    """torch's scaled_dot_product_attention (float64, CPU) with an explicit
+    boolean mask, K/V repeated over each group, and autograd gradients."""
+    nc, nkc = lay.n_clean_q, lay.n_clean_kv
+    T = lambda a: torch.tensor(a, dtype=torch.float64)
+    Q = T(np.concatenate([t["q_c"], t["q_x"]])).requires_grad_()
+    K = T(np.concatenate([t["k_c"], t["k_x"]])).requires_grad_()
+    V = T(np.concatenate([t["v_c"], t["v_x"]])).requires_grad_()
+    dO = T(np.concatenate([t["do_c"], t["do_x"]]))
+    Kh = K.repeat_interleave(lay.G, dim=1)
+    Vh = V.repeat_interleave(lay.G, dim=1)
+    O = torch.nn.functional.scaled_dot_product_attention(
+        Q.transpose(0, 1)[None], Kh.transpose(0, 1)[None], Vh.transpose(0, 1)[None],
+        attn_mask=torch.tensor(mask), scale=lay.scale)[0].transpose(0, 1)
+    (O * dO).sum().backward()
+    S = lay.scale * torch.einsum("qhd,khd->hqk", Q.detach(), Kh.detach())
+    S = S.masked_fill(~torch.tensor(mask)[None], -math.inf)
+    LSE = torch.logsumexp(S, dim=-1)
+    n = lambda x: x.detach().numpy()
+    return (n(O[:nc]), n(O[nc:]), n(LSE[:, :nc]), n(LSE[:, nc:]),
+            n(Q.grad[:nc]), n(Q.grad[nc:]), n(K.grad[:nkc]), n(V.grad[:nkc]),
+            n(K.grad[nkc:]), n(V.grad[nkc:]))
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=4, H=4, Hkv=2, d=8, n_clean_q=32),
+    dict(B=3, H=3, Hkv=1, d=5, n_clean_q=21),
+    dict(B=2, H=2, Hkv=2, d=4, n_clean_q=8, clean_q_start=8, n_clean_kv=16,
+         corr_block_ids=[1, 4, 6]),
+])
+def test_matches_library_attention(case):
+    lay = layout(**case)
+    t = make(lay, seed=5)
+    orc = oracle_of(lay, t)
+    got = orc.forward() + orc.backward()
+    want = _sdpa_reference(lay, t, full_mask(lay))
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-11)
+
+
+def test_block_size_one_is_causal_attention():
+    """B = 1: the clean stream is causal attention; corrupted row i is row i
+    of causal attention over the clean keys with key/value i replaced by the
+    corrupted token's own."""
+    L, H, d = 12, 2, 6
+    lay = layout(1, H, H, d, L)
+    t = make(lay, seed=9)
+    O_c, O_x, L_c, L_x = oracle_of(lay, t).forward()
+    T = lambda a: torch.tensor(a, dtype=torch.float64).transpose(0, 1)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        T(t["q_c"]), T(t["k_c"]), T(t["v_c"]), is_causal=True)[0].transpose(0, 1)
+    np.testing.assert_allclose(O_c, ref.numpy(), rtol=1e-12, atol=1e-13)
+    for i in range(L):
+        k2 = t["k_c"].copy()
+        v2 = t["v_c"].copy()
+        k2[i] = t["k_x"][i]
+        v2[i] = t["v_x"][i]
+        q = t["q_c"].copy()
+        q[i] = t["q_x"][i]
+        r = torch.nn.functional.scaled_dot_product_attention(
+            T(q), T(k2), T(v2), is_causal=True)[0].transpose(0, 1)
+        np.testing.assert_allclose(O_x[i], r[i].numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------ numerical gradients
+def test_finite_difference_gradients():
+    lay = layout(4, 2, 1, 4, 16)
+    t = make(lay, seed=21)
+    orc = oracle_of(lay, t)
+    grads = dict(zip(["q_c", "q_x", "k_c", "v_c", "k_x", "v_x"], orc.backward()))
+    dO = np.concatenate([t["do_c"], t["do_x"]])
+
+    def f(tt):
+        o = oracle_of(lay, tt).forward()
+        return float(np.sum(np.concatenate([o[0], o[1]]) * dO))
+
+    h = 1e-6
+    for name in ["q_c", "q_x", "k_c", "v_c", "k_x", "v_x"]:
+        num = np.zeros_like(t[name])
+        for idx in np.ndindex(t[name].shape):
+            tp = {k: v.copy() for k, v in t.items()}
+            tm = {k: v.copy() for k, v in t.items()}
+            tp[name][idx] += h
+            tm[name][idx] -= h
+            num[idx] = (f(tp) - f(tm)) / (2 * h)
+        err = np.max(np.abs(num - grads[name])) / np.max(np.abs(num))
+        assert err < 1e-6, (name, err)
+
+
+# ------------------------------------------------------------- invariants
+def test_identical_streams_give_identical_outputs():
+    """With the corrupted copy equal to the clean copy, corrupted block b sees
+    {own block} + clean blocks < b, which is the clean query's set: outputs
+    and query gradients match (block-causal reading of §3.2)."""
+    lay = layout(4, 4, 2, 8, 32)
+    t = make(lay, seed=4)
+    for a, b in [("q_x", "q_c"), ("k_x", "k_c"), ("v_x", "v_c"), ("do_x", "do_c")]:
+        t[a] = t[b].copy()
+    orc = oracle_of(lay, t)
+    O_c, O_x, L_c, L_x = orc.forward()
+    dq_c, dq_x, *_ = orc.backward()
+    np.testing.assert_allclose(O_x, O_c, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L_x, L_c, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dq_x, dq_c, rtol=1e-11, atol=1e-12)
+
+
+def test_corrupted_block_separability():
+    """§3.2 / §4.2: corrupted activations of block b' affect only block b'.
+    Perturbing block b' leaves every other corrupted block's outputs and
+    gradients and all clean outputs and dQ bitwise unchanged; clean dK/dV
+    change by exactly block b''s contribution."""
+    lay = layout(4, 4, 2, 8, 32)
+    B, nb = 4, 8
+    t = make(lay, seed=8)
+    base = oracle_of(lay, t)
+    f0, g0 = base.forward(), base.backward()
+    bp = 5
+    rows = slice(bp * B, (bp + 1) * B)
+    t2 = {k: v.copy() for k, v in t.items()}
+    for name in ["q_x", "k_x", "v_x"]:
+        t2[name][rows] += rnd(t2[name][rows].shape, 99)
+    pert = oracle_of(lay, t2)
+    f1, g1 = pert.forward(), pert.backward()
+    other = np.ones(32, bool)
+    other[rows] = False
+    assert np.array_equal(f1[0], f0[0]) and np.array_equal(f1[2], f0[2])  # clean O, LSE
+    assert np.array_equal(f1[1][other], f0[1][other])
+    assert np.array_equal(f1[3][:, other], f0[3][:, other])
+    assert np.array_equal(g1[0], g0[0])  # dQ_c
+    for k in (1, 4, 5):  # dQ_x, dK_x, dV_x
+        assert np.array_equal(g1[k][other], g0[k][other])
+    # clean dK/dV change by block b''s own contribution
+    qrow = pert.query_index(CORRUPTED, np.arange(bp * B, (bp + 1) * B))
+    _, dk1, dv1 = pert.rows_backward(qrow)
+    qrow0 = base.query_index(CORRUPTED, np.arange(bp * B, (bp + 1) * B))
+    _, dk0, dv0 = base.rows_backward(qrow0)
+    np.testing.assert_allclose(g1[2] - g0[2], dk1[:32] - dk0[:32], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g1[3] - g0[3], dv1[:32] - dv0[:32], rtol=0, atol=1e-12)
+
+
+def test_clean_gradients_are_sums_of_per_block_contributions():
+    """§4.1 / §4.3: clean dK/dV accumulate the contributions of every query
+    block that sees them. Zeroing dO outside one query block yields that
+    block's contribution; the sum over all clean and corrupted blocks equals
+    the full gradient."""
+    lay = layout(4, 4, 2, 8, 32)
+    B, nb = 4, 8
+    t = make(lay, seed=12)
+    full = oracle_of(lay, t).backward()
+    acc_k = np.zeros_like(full[2])
+    acc_v = np.zeros_like(full[3])
+    for stream in ("c", "x"):
+        for b in range(nb):
+            tt = {k: v.copy() for k, v in t.items()}
+            keep = np.zeros(32, bool)
+            keep[b * B:(b + 1) * B] = True
+            tt["do_c"][:] = 0
+            tt["do_x"][:] = 0
+            tt["do_" + stream][keep] = t["do_" + stream][keep]
+            g = oracle_of(lay, tt).backward()
+            acc_k += g[2]
+            acc_v += g[3]
+    np.testing.assert_allclose(acc_k, full[2], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(acc_v, full[3], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("assign", ["dual_end", "strided"])
+def test_simulated_context_sharded_ranks_equal_full(assign):
+    """§4.3-§4.4 (Proposition 1): P ranks, each with one clean-query shard,
+    the clean K/V before its shard end, and a subset of corrupted blocks;
+    summing the clean dK/dV over ranks and concatenating the rest reproduces
+    the single full computation."""
+    L, B, P = 32, 2, 4  # 16 blocks, 4 per rank
+    nb = L // B
+    lay = layout(B, 4, 2, 4, L)
+    t = make(lay, seed=31)
+    full_f = oracle_of(lay, t).forward()
+    full_g = oracle_of(lay, t).backward()
+    if assign == "dual_end":
+        owner = {}
+        for r in range(P):
+            for k in range(nb // (2 * P)):
+                i = r + k * P
+                owner[i] = r
+                owner[nb - 1 - i] = r
+    else:
+        owner = {b: b % P for b in range(nb)}
+    shard = L // P
+    O_c = np.zeros_like(full_f[0])
+    O_x = np.zeros_like(full_f[1])
+    dk_c = np.zeros_like(full_g[2])
+    dv_c = np.zeros_like(full_g[3])
+    dq_x = np.zeros_like(full_g[1])
+    dk_x = np.zeros_like(full_g[4])
+    for r in range(P):
+        ids = sorted(b for b, o in owner.items() if o == r)
+        lo, hi = r * shard, (r + 1) * shard
+        # the clean K/V buffer is every clean position before the last one
+        # a local query sees (as after the forward all-gather)
+        kv_end = max(hi, max(ids) * B)
+        rl = layout(B, 4, 2, 4, shard, lo, kv_end, corr_block_ids=ids)
+        xr = np.concatenate([np.arange(b * B, (b + 1) * B) for b in ids])
+        tr = dict(q_c=t["q_c"][lo:hi], k_c=t["k_c"][:kv_end], v_c=t["v_c"][:kv_end],
+                  q_x=t["q_x"][xr], k_x=t["k_x"][xr], v_x=t["v_x"][xr],
+                  do_c=t["do_c"][lo:hi], do_x=t["do_x"][xr])
+        orc = oracle_of(rl, tr)
+        f = orc.forward()
+        g = orc.backward()
+        O_c[lo:hi] = f[0]
+        O_x[xr] = f[1]
+        dk_c[:kv_end] += g[2]
+        dv_c[:kv_end] += g[3]
+        dq_x[xr] = g[1]
+        dk_x[xr] = g[4]
+    np.testing.assert_allclose(O_c, full_f[0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(O_x, full_f[1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk_c, full_g[2], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv_c, full_g[3], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq_x, full_g[1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk_x, full_g[4], rtol=0, atol=1e-12)
+
+
+def test_sampled_rows_and_keys_match_full():
+    """The row-sampled forward/dQ and key-sampled dK/dV used at large sizes
+    agree with the full computation."""
+    lay = layout(4, 4, 2, 8, 48, 16, 64, corr_block_ids=[1, 5, 9, 14])
+    t = make(lay, seed=17)
+    orc = oracle_of(lay, t)
+    f, g = orc.forward(), orc.backward()
+    rows = np.array([0, 7, 30, 47])
+    O, LSE = orc.rows_forward(orc.query_index(CLEAN, rows))
+    np.testing.assert_allclose(O, f[0][rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(LSE, f[2][:, rows], rtol=0, atol=1e-14)
+    xr = np.array([1, 5, 15])
+    dq, _, _ = orc.rows_backward(orc.query_index(CORRUPTED, xr))
+    np.testing.assert_allclose(dq, g[1][xr], rtol=0, atol=1e-13)
+    keys = np.array([0, 3, 33, 63])
+    dk, dv = orc.keys_backward(orc.key_index(CLEAN, keys))
+    np.testing.assert_allclose(dk, g[2][keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, g[3][keys], rtol=0, atol=1e-12)
+    xk = np.array([2, 9, 15])
+    dk, dv = orc.keys_backward(orc.key_index(CORRUPTED, xk))
+    np.testing.assert_allclose(dk, g[4][xk], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, g[5][xk], rtol=0, atol=1e-12)
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    """A plausible slip in the oracle's rules (strict vs non-strict block
+    comparison) must break the hand-drawn fixture."""
+    import oracle.bdattn_oracle as ob
+
+    def wrong(q_stream, q_block, k_stream, k_block):
+        qc, kc = q_stream == CLEAN, k_stream == CLEAN
+        return (qc & kc & (k_block < q_block)) | (~qc & kc & (k_block < q_block)) | \
+            (~qc & ~kc & (k_block == q_block))
+
+    p, want = read_golden("mask_L8_B2.txt")
+    lay = layout(p["B"], 1, 1, 4, p["n_clean_q"])
+    qs, qb = query_tokens(lay)
+    ks, kb = key_tokens(lay)
+    assert not np.array_equal(wrong(qs[:, None], qb[:, None], ks[None], kb[None]), want)
+
+
+def test_missing_clean_coverage_is_rejected():
+    with pytest.raises(ValueError):
+        layout(2, 1, 1, 4, 4, 4, 6)  # queries at 4..7 need clean keys up to 8
+    with pytest.raises(ValueError):
+        layout(2, 1, 1, 4, 4, 0, 8, corr_block_ids=[5])  # block 5 needs keys < 10
