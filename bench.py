@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of bdattn: block-diffusion attention forward + backward on one GPU.
+
+One step = bdattn_fwd then bdattn_bwd over the whole workload (every row of
+both streams, every head), inputs resident in device memory. Prints one JSON
+line: whole-step useful TFLOP/s (12*d*H*pairs flops per step: QK^T and PV in
+the forward, dV, dP, dQ and dK in the backward; masked pairs and the
+backward's QK^T recompute are not counted), the roofline position of the
+dominant kernel (timed live with HIP events on its launch stream), and the
+float64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 256k]
+"""
+import argparse
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "bdattn fwd+bwd useful TFLOP/s at 256K ctx; % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bwd_256k.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "bdattn_mask.h", "launch.h"):
+        with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the backward key-tile kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    and this workload; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m = {k: v for k, v in re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M)}
+    if m.get("kernel_source") != kernel_source_hash() or m.get("workload") != workload:
+        return None
+    try:
+        return float(m["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(spec, t, seconds: float):
+    """The float64 oracle, as it stands, on whole query blocks of the
+    workload (one KV head group each, blocks spread over both streams and
+    the whole sequence) until about `seconds` of work; returns useful
+    TFLOP/s over the sample."""
+    import numpy as np
+
+    from oracle import Oracle, layout
+
+    f64 = lambda x: x.float().cpu().numpy().astype(np.float64)
+    B, G, d = spec.B, spec.H // spec.Hkv, spec.d
+    ids = list(spec.corr_block_ids) if spec.corr_block_ids is not None else \
+        list(range(spec.n_corr_blocks))
+    cb0 = spec.clean_q_start // B
+    ncb = spec.n_clean_q // B
+    order = []
+    for i in range(max(ncb, len(ids))):  # spread: stride through both streams
+        frac = ((i * 0.6180339887) % 1.0)
+        if ncb:
+            order.append(("c", cb0 + int(frac * ncb)))
+        if ids:
+            order.append(("x", int(frac * len(ids))))
+    flops = 0.0
+    spent = 0.0
+    n_blocks = 0
+    rows = 0
+    for k, (stream, b) in enumerate(order):
+        g = k % spec.Hkv
+        hq, hk = slice(g * G, (g + 1) * G), slice(g, g + 1)
+        if stream == "c":
+            r0 = b * B - spec.clean_q_start
+            lay = layout(B, G, 1, d, B, b * B, (b + 1) * B, 0, corr_block_ids=[])
+            e, ek = np.zeros((0, G, d)), np.zeros((0, 1, d))
+            args = (f64(t["q_c"][r0:r0 + B, hq]), f64(t["k_c"][:(b + 1) * B, hk]),
+                    f64(t["v_c"][:(b + 1) * B, hk]), e, ek, ek,
+                    f64(t["do_c"][r0:r0 + B, hq]), e)
+            pairs = B * (b + 1) * B
+        else:
+            bid = ids[b]
+            rr = slice(b * B, (b + 1) * B)
+            lay = layout(B, G, 1, d, 0, 0, bid * B, 0, corr_block_ids=[bid])
+            e = np.zeros((0, G, d))
+            args = (e, f64(t["k_c"][:bid * B, hk]), f64(t["v_c"][:bid * B, hk]),
+                    f64(t["q_x"][rr, hq]), f64(t["k_x"][rr, hk]), f64(t["v_x"][rr, hk]),
+                    e, f64(t["do_x"][rr, hq]))
+            pairs = B * (bid + 1) * B
+        t0 = time.perf_counter()
+        orc = Oracle(lay, *args)
+        orc.forward()
+        orc.backward()
+        spent += time.perf_counter() - t0
+        flops += 12.0 * d * G * pairs
+        n_blocks += 1
+        rows += B * G
+        if spent >= seconds:
+            break
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    if not threads:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_blocks} whole query blocks x {G} q heads ({rows} query rows, "
+                      f"full visible prefixes), float64 numpy fwd+bwd, {spent:.1f} s",
+            "seconds": round(spent, 2), "cpu": platform.processor() or platform.machine(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="256k",
+                    help="workload name (tiny, 8k, 64k, 256k, 512k_rank15)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_masked_attention_amd as bd
+    from workloads import GRAD_NAMES, INPUT_NAMES, config, make_inputs
+
+    spec = config(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p = bd.from_spec(spec)
+    pairs = bd.visible_pairs(p)
+    useful_step = 12.0 * spec.d * spec.H * pairs
+    log(f"[bench] workload {spec.name}: {spec.description}; visible pairs/head {pairs}; "
+        f"useful flops/step {useful_step:.4e}")
+    t = make_inputs(spec, device=dev)
+    tin = [t[k] for k in INPUT_NAMES]
+    dt = t["q_c"].dtype
+    H, Hkv, d = spec.H, spec.Hkv, spec.d
+    nc, nkv, nx = spec.n_clean_q, spec.n_clean_kv, spec.n_corr
+    e = lambda *s, dtype=dt: torch.empty(s, dtype=dtype, device=dev)
+    fout = [e(nc, H, d), e(nx, H, d), e(H, nc, dtype=torch.float32), e(H, nx, dtype=torch.float32)]
+    bout = [e(nc, H, d), e(nx, H, d), e(nkv, Hkv, d), e(nkv, Hkv, d), e(nx, Hkv, d), e(nx, Hkv, d)]
+    ws_f = e(bd.workspace_size(p, 0), dtype=torch.uint8)
+    ws_b = e(bd.workspace_size(p, 1), dtype=torch.uint8)
+
+    def step():
+        bd.fwd(p, *tin, workspace=ws_f, out=fout)
+        bd.bwd(p, *tin, *fout, t["do_c"], t["do_x"], workspace=ws_b, out=bout)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] ran one plain device copy of 1 GiB (counter calibration)")
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    bd.profile_read()  # drop anything recorded before
+    bd.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        log(f"[bench] step {i + 1}/{args.steps} enqueued")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    bd.profile_enable(False)
+    prof = bd.profile_read()
+    ms_step = (t1 - t0) * 1e3 / max(1, args.steps)
+    value = useful_step / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
+    fwd_ms = prof["fwd_ms"] / max(1, prof["fwd_launches"])
+    bwd_ms = prof["bwd_ms"] / max(1, prof["bwd_launches"])
+    fwd_flops = 4.0 * d * H * pairs
+    bwd_flops = 8.0 * d * H * pairs
+    dom = "bwd" if bwd_ms >= fwd_ms else "fwd"
+    dom_ms = bwd_ms if dom == "bwd" else fwd_ms
+    achieved = (bwd_flops if dom == "bwd" else fwd_flops) / (dom_ms * 1e-3) / 1e12
+    traffic = read_traffic(spec.name) if dom == "bwd" else None
+    log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
+        f"({100 * value / peak:.1f}% of {peak} peak); fwd kernel {fwd_ms:.2f} ms "
+        f"({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s), bwd key-tile kernel {bwd_ms:.2f} ms "
+        f"({bwd_flops / bwd_ms / 1e9:.1f} TFLOP/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the float64 oracle on a sample (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(spec, t, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "description": spec.description,
+                   "clean_q": nc, "clean_kv": nkv, "corrupted": nx, "B": spec.B, "H": H,
+                   "Hkv": Hkv, "d": d, "visible_pairs_per_head": pairs,
+                   "useful_flops_per_step": useful_step, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "kernels": {"fwd_ms": round(fwd_ms, 3), "bwd_keytile_ms": round(bwd_ms, 3),
+                    "fwd_tflops": round(fwd_flops / fwd_ms / 1e9, 1),
+                    "bwd_keytile_tflops": round(bwd_flops / bwd_ms / 1e9, 1),
+                    "other_ms": round(ms_step - fwd_ms - bwd_ms, 3)},
+        "roofline": {"kernel": "bwd_kernel (key-tile backward)" if dom == "bwd" else "fwd_kernel",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

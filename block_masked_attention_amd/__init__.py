@@ -1,0 +1,311 @@
+"""Python binding of libbdattn (block-diffusion attention on MI355X).
+
+Argument marshalling only: every step of the forward and backward runs in the
+library's HIP kernels. Torch supplies device memory (outputs, workspace) and
+the current HIP stream. The binding fails loudly when the library is missing:
+there is no fallback implementation.
+
+The entry points mirror the C ABI in include/bdattn.h: ``fwd``, ``bwd``,
+``validate``, ``workspace_size``, ``mask_render``, ``visible_pairs``,
+``plan_stats``, ``version``, ``status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbdattn.so")
+
+F32 = 0
+BF16 = 1
+STATUS = {0: "BDATTN_OK", -1: "BDATTN_ERR_INVALID_ARG", -2: "BDATTN_ERR_SHAPE",
+          -3: "BDATTN_ERR_UNSUPPORTED", -4: "BDATTN_ERR_COVERAGE",
+          -5: "BDATTN_ERR_WORKSPACE", -6: "BDATTN_ERR_HIP"}
+
+__all__ = ["Problem", "problem", "BdattnError", "lib", "fwd", "bwd", "validate",
+           "workspace_size", "mask_render", "visible_pairs", "plan_stats", "version",
+           "status_string", "profile_enable", "profile_read", "from_spec", "F32", "BF16",
+           "LIB_PATH"]
+
+
+class BdattnError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({message})")
+
+
+class Problem(ctypes.Structure):
+    """ctypes mirror of ``bdattn_problem``. Build it with ``problem(...)``,
+    which also keeps the host id array alive."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("n_clean_q", ctypes.c_int64), ("clean_q_start", ctypes.c_int64),
+        ("n_clean_kv", ctypes.c_int64), ("clean_kv_start", ctypes.c_int64),
+        ("n_corr_blocks", ctypes.c_int64),
+        ("corr_block_ids", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+    @property
+    def n_corr(self) -> int:
+        return int(self.n_corr_blocks) * int(self.B)
+
+
+def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_start: int = 0,
+            n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
+            n_corr_blocks: Optional[int] = None, corr_block_ids: Optional[Sequence[int]] = None,
+            scale: float = 0.0) -> Problem:
+    """Problem descriptor. ``dtype`` is F32/BF16, "f32"/"bf16" or a torch dtype.
+    Without ids the corrupted blocks are 0..n_corr_blocks-1 (default: as many
+    as the clean query shard has blocks)."""
+    dt = _dtype_code(dtype)
+    if n_clean_kv is None:
+        n_clean_kv = n_clean_q
+    p = Problem()
+    p.B, p.H, p.Hkv, p.d, p.dtype, p.scale = B, H, Hkv, d, dt, float(scale)
+    p.n_clean_q, p.clean_q_start = n_clean_q, clean_q_start
+    p.n_clean_kv, p.clean_kv_start = n_clean_kv, clean_kv_start
+    if corr_block_ids is not None:
+        ids = np.ascontiguousarray(np.asarray(corr_block_ids, dtype=np.int32))
+        p._ids = ids  # keep alive
+        p.n_corr_blocks = len(ids)
+        p.corr_block_ids = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        if n_corr_blocks is None:
+            n_corr_blocks = n_clean_q // B if B > 0 else 0
+        p.n_corr_blocks = n_corr_blocks
+        p.corr_block_ids = None
+    return p
+
+
+def from_spec(spec) -> Problem:
+    """Descriptor of a workload spec (any object with the descriptor's fields)."""
+    return problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
+                   spec.clean_q_start, spec.n_clean_kv, spec.clean_kv_start,
+                   spec.n_corr_blocks, spec.corr_block_ids)
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in (F32, "f32", "float32"):
+        return F32
+    if dtype in (BF16, "bf16", "bfloat16"):
+        return BF16
+    import torch
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbdattn.so (built in-tree); raise if it is not there."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_masked_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    L.bdattn_version.restype = ctypes.c_int
+    L.bdattn_status_string.restype = ctypes.c_char_p
+    L.bdattn_status_string.argtypes = [ctypes.c_int]
+    L.bdattn_last_error.restype = ctypes.c_char_p
+    L.bdattn_validate.argtypes = [P]
+    L.bdattn_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.bdattn_mask_render.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t]
+    L.bdattn_visible_pairs.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    L.bdattn_plan_stats.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    L.bdattn_fwd.argtypes = [P] + [vp] * 6 + [vp, vp, fp, fp] + [vp, ctypes.c_size_t, vp]
+    L.bdattn_bwd.argtypes = ([P] + [vp] * 6 + [vp, vp, fp, fp, vp, vp] + [vp] * 6 +
+                             [vp, ctypes.c_size_t, vp])
+    L.bdattn_profile_enable.argtypes = [ctypes.c_int]
+    L.bdattn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]
+    for name in ("bdattn_validate", "bdattn_workspace_size", "bdattn_mask_render",
+                 "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_bwd",
+                 "bdattn_profile_enable", "bdattn_profile_read"):
+        getattr(L, name).restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise BdattnError(status, where, lib().bdattn_last_error().decode())
+
+
+def version() -> int:
+    return lib().bdattn_version()
+
+
+def status_string(status: int) -> str:
+    return lib().bdattn_status_string(status).decode()
+
+
+def validate(p: Problem) -> int:
+    """Status of the descriptor (0 = valid); never raises."""
+    return lib().bdattn_validate(ctypes.byref(p))
+
+
+def workspace_size(p: Problem, pass_: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bdattn_workspace_size(ctypes.byref(p), pass_, ctypes.byref(n)), "workspace_size")
+    return n.value
+
+
+def mask_render(p: Problem) -> np.ndarray:
+    nq = int(p.n_clean_q) + p.n_corr
+    nk = int(p.n_clean_kv) + p.n_corr
+    out = np.zeros((nq, nk), dtype=np.uint8)
+    _check(lib().bdattn_mask_render(ctypes.byref(p), out.ctypes.data, out.nbytes), "mask_render")
+    return out.astype(bool)
+
+
+def visible_pairs(p: Problem) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().bdattn_visible_pairs(ctypes.byref(p), ctypes.byref(n)), "visible_pairs")
+    return n.value
+
+
+def plan_stats(p: Problem) -> dict:
+    out = (ctypes.c_int64 * 8)()
+    _check(lib().bdattn_plan_stats(ctypes.byref(p), out), "plan_stats")
+    keys = ("fwd_items", "fwd_tiles", "fwd_masked_tiles", "bwd_items", "bwd_qtiles",
+            "bwd_masked_qtiles", "fwd_rows_per_item", "bwd_keys_per_item")
+    return dict(zip(keys, list(out)))
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record HIP events around the main forward / backward kernels."""
+    _check(lib().bdattn_profile_enable(1 if on else 0), "profile_enable")
+
+
+def profile_read() -> dict:
+    """Wait for the recorded events; milliseconds and launch counts of the
+    forward kernel and the backward key-tile kernel since the last read."""
+    fm, fn = ctypes.c_double(0), ctypes.c_int64(0)
+    bm, bn = ctypes.c_double(0), ctypes.c_int64(0)
+    _check(lib().bdattn_profile_read(ctypes.byref(fm), ctypes.byref(fn), ctypes.byref(bm),
+                                     ctypes.byref(bn)), "profile_read")
+    return dict(fwd_ms=fm.value, fwd_launches=fn.value, bwd_ms=bm.value, bwd_launches=bn.value)
+
+
+# ------------------------------------------------------------------ torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _tdtype(p: Problem):
+    torch = _torch()
+    return torch.float32 if p.dtype == F32 else torch.bfloat16
+
+
+def _expect(t, shape, dtype, name, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(p: Problem, pass_: int, device, workspace):
+    torch = _torch()
+    need = workspace_size(p, pass_)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
+    return workspace
+
+
+def fwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, *, workspace=None, stream=None, out=None):
+    """Forward on the GPU. Returns (o_c, o_x, lse_c, lse_x)."""
+    torch = _torch()
+    dev = q_c.device if q_c.numel() else q_x.device
+    if dev.type != "cuda":
+        raise ValueError("bdattn runs on a GPU: inputs must be on a cuda (HIP) device")
+    dt = _tdtype(p)
+    H, Hkv, d = int(p.H), int(p.Hkv), int(p.d)
+    nc, nkv, nx = int(p.n_clean_q), int(p.n_clean_kv), p.n_corr
+    for t, shp, nm in ((q_c, (nc, H, d), "q_c"), (k_c, (nkv, Hkv, d), "k_c"),
+                       (v_c, (nkv, Hkv, d), "v_c"), (q_x, (nx, H, d), "q_x"),
+                       (k_x, (nx, Hkv, d), "k_x"), (v_x, (nx, Hkv, d), "v_x")):
+        _expect(t, shp, dt, nm, dev)
+    if out is None:
+        o_c = torch.empty((nc, H, d), dtype=dt, device=dev)
+        o_x = torch.empty((nx, H, d), dtype=dt, device=dev)
+        lse_c = torch.empty((H, nc), dtype=torch.float32, device=dev)
+        lse_x = torch.empty((H, nx), dtype=torch.float32, device=dev)
+    else:
+        o_c, o_x, lse_c, lse_x = out
+    ws = _workspace(p, 0, dev, workspace)
+    st = lib().bdattn_fwd(ctypes.byref(p), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(q_x),
+                          _ptr(k_x), _ptr(v_x), _ptr(o_c), _ptr(o_x), _ptr(lse_c), _ptr(lse_x),
+                          _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev, stream))
+    _check(st, "bdattn_fwd")
+    return o_c, o_x, lse_c, lse_x
+
+
+def bwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, do_c, do_x, *,
+        workspace=None, stream=None, out=None):
+    """Backward on the GPU. Returns (dq_c, dq_x, dk_c, dv_c, dk_x, dv_x)."""
+    torch = _torch()
+    dev = q_c.device if q_c.numel() else q_x.device
+    if dev.type != "cuda":
+        raise ValueError("bdattn runs on a GPU: inputs must be on a cuda (HIP) device")
+    dt = _tdtype(p)
+    H, Hkv, d = int(p.H), int(p.Hkv), int(p.d)
+    nc, nkv, nx = int(p.n_clean_q), int(p.n_clean_kv), p.n_corr
+    for t, shp, tdt, nm in ((q_c, (nc, H, d), dt, "q_c"), (k_c, (nkv, Hkv, d), dt, "k_c"),
+                            (v_c, (nkv, Hkv, d), dt, "v_c"), (q_x, (nx, H, d), dt, "q_x"),
+                            (k_x, (nx, Hkv, d), dt, "k_x"), (v_x, (nx, Hkv, d), dt, "v_x"),
+                            (o_c, (nc, H, d), dt, "o_c"), (o_x, (nx, H, d), dt, "o_x"),
+                            (lse_c, (H, nc), torch.float32, "lse_c"),
+                            (lse_x, (H, nx), torch.float32, "lse_x"),
+                            (do_c, (nc, H, d), dt, "do_c"), (do_x, (nx, H, d), dt, "do_x")):
+        _expect(t, shp, tdt, nm, dev)
+    if out is None:
+        dq_c = torch.empty((nc, H, d), dtype=dt, device=dev)
+        dq_x = torch.empty((nx, H, d), dtype=dt, device=dev)
+        dk_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
+        dv_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
+        dk_x = torch.empty((nx, Hkv, d), dtype=dt, device=dev)
+        dv_x = torch.empty((nx, Hkv, d), dtype=dt, device=dev)
+    else:
+        dq_c, dq_x, dk_c, dv_c, dk_x, dv_x = out
+    ws = _workspace(p, 1, dev, workspace)
+    st = lib().bdattn_bwd(ctypes.byref(p), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(q_x),
+                          _ptr(k_x), _ptr(v_x), _ptr(o_c), _ptr(o_x), _ptr(lse_c), _ptr(lse_x),
+                          _ptr(do_c), _ptr(do_x), _ptr(dq_c), _ptr(dq_x), _ptr(dk_c), _ptr(dv_c),
+                          _ptr(dk_x), _ptr(dv_x), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                          _stream(dev, stream))
+    _check(st, "bdattn_bwd")
+    return dq_c, dq_x, dk_c, dv_c, dk_x, dv_x

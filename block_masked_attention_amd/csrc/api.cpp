@@ -1,0 +1,330 @@
+// C ABI of bdattn (include/bdattn.h): validation, plan cache, workspace upload
+// and kernel launches.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/bdattn.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+// One cached plan per distinct problem (ids included), kept for the life of
+// the process: the work list and the ids are staged once into pinned host
+// memory, from which every call copies them asynchronously into the caller's
+// workspace. Entries are never freed, so a copy still in flight always reads
+// live memory.
+struct Entry {
+  bdattn::Plan plan;
+  std::mutex mu;
+  void* staged[2] = {nullptr, nullptr};
+  size_t staged_bytes[2] = {0, 0};
+};
+
+struct PlanCache {
+  std::mutex mu;
+  std::map<std::string, Entry*> entries;
+};
+
+PlanCache& cache() {
+  static PlanCache* c = new PlanCache;  // never destroyed (outlives the HIP runtime)
+  return *c;
+}
+
+std::string plan_key(const bdattn::Problem& P) {
+  std::string k;
+  const int32_t head[] = {P.B, P.H, P.Hkv, P.d, P.dtype, P.n_clean_q, P.clean_q_start,
+                          P.n_clean_kv, P.n_corr_blocks};
+  k.append((const char*)head, sizeof(head));
+  k.append((const char*)P.ids.data(), P.ids.size() * sizeof(int32_t));
+  return k;
+}
+
+Entry* get_entry(const bdattn::Problem& P) {
+  PlanCache& c = cache();
+  const std::string key = plan_key(P);
+  std::lock_guard<std::mutex> lock(c.mu);
+  auto it = c.entries.find(key);
+  if (it != c.entries.end()) return it->second;
+  Entry* e = new Entry;
+  bdattn::build_plan(P, &e->plan);
+  c.entries[key] = e;
+  return e;
+}
+
+int load(const bdattn_problem* p, bdattn::Problem* P) {
+  std::string msg;
+  int st = bdattn::load_problem(p, P, &msg);
+  if (st != BDATTN_OK) return fail(st, msg);
+  return BDATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Every tensor of nonzero size needs a non-null 16-byte aligned pointer.
+int check_ptr(const void* p, int64_t elems, const char* name) {
+  if (elems == 0) return BDATTN_OK;
+  if (!p) return fail(BDATTN_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned16(p)) return fail(BDATTN_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return BDATTN_OK;
+}
+
+// Copy the corrupted block ids and the work list (staged once in pinned host
+// memory) into the workspace head, asynchronously on the caller's stream.
+int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t s) {
+  const size_t bytes = w.items + w.items_bytes;
+  void* src = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(e->mu);
+    if (!e->staged[pass]) {
+      void* h = nullptr;
+      hipError_t er = hipHostMalloc(&h, bytes, hipHostMallocDefault);
+      if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("hipHostMalloc: ") + hipGetErrorString(er));
+      memset(h, 0, bytes);
+      const bdattn::Plan& plan = e->plan;
+      memcpy((char*)h + w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t));
+      if (pass == 0)
+        memcpy((char*)h + w.items, plan.fwd.data(), w.items_bytes);
+      else
+        memcpy((char*)h + w.items, plan.bwd.data(), w.items_bytes);
+      e->staged[pass] = h;
+      e->staged_bytes[pass] = bytes;
+    }
+    src = e->staged[pass];
+  }
+  hipError_t er = hipMemcpyAsync(ws, src, bytes, hipMemcpyHostToDevice, s);
+  if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(er));
+  return BDATTN_OK;
+}
+
+// Benchmark instrumentation: per-thread list of (pass, events) recorded by
+// the launches while profiling is on.
+struct Prof {
+  bool on = false;
+  std::vector<std::pair<int, bdattn::KernelEvents>> recs;
+};
+thread_local Prof g_prof;
+
+bdattn::KernelEvents prof_events(int pass) {
+  bdattn::KernelEvents ev;
+  if (!g_prof.on) return ev;
+  if (hipEventCreate(&ev.start) != hipSuccess) return bdattn::KernelEvents();
+  if (hipEventCreate(&ev.stop) != hipSuccess) {
+    hipEventDestroy(ev.start);
+    return bdattn::KernelEvents();
+  }
+  g_prof.recs.push_back({pass, ev});
+  return ev;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdattn_profile_enable(int on) {
+  g_prof.on = on != 0;
+  return BDATTN_OK;
+}
+
+int bdattn_profile_read(double* fwd_ms, int64_t* fwd_launches, double* bwd_ms,
+                        int64_t* bwd_launches) {
+  double ms[2] = {0, 0};
+  int64_t n[2] = {0, 0};
+  int st = BDATTN_OK;
+  for (auto& r : g_prof.recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.second.stop) == hipSuccess &&
+        hipEventElapsedTime(&t, r.second.start, r.second.stop) == hipSuccess) {
+      ms[r.first] += t;
+      n[r.first] += 1;
+    } else {
+      st = fail(BDATTN_ERR_HIP, "profile event wait failed");
+    }
+    hipEventDestroy(r.second.start);
+    hipEventDestroy(r.second.stop);
+  }
+  g_prof.recs.clear();
+  if (fwd_ms) *fwd_ms = ms[0];
+  if (fwd_launches) *fwd_launches = n[0];
+  if (bwd_ms) *bwd_ms = ms[1];
+  if (bwd_launches) *bwd_launches = n[1];
+  return st;
+}
+
+int bdattn_version(void) { return BDATTN_VERSION; }
+
+const char* bdattn_status_string(int status) {
+  switch (status) {
+    case BDATTN_OK: return "ok";
+    case BDATTN_ERR_INVALID_ARG: return "invalid argument";
+    case BDATTN_ERR_SHAPE: return "invalid shape";
+    case BDATTN_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
+    case BDATTN_ERR_COVERAGE: return "clean K/V buffer does not cover the visible keys";
+    case BDATTN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case BDATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bdattn_last_error(void) { return g_last_error.c_str(); }
+
+int bdattn_validate(const bdattn_problem* p) {
+  bdattn::Problem P;
+  int st = load(p, &P);
+  if (st != BDATTN_OK) return st;
+  if (!bdattn::have_kernels(P.dtype, P.d))
+    return fail(BDATTN_ERR_UNSUPPORTED, "no kernel for this dtype and head dim (fp32 needs d = 32)");
+  return BDATTN_OK;
+}
+
+int bdattn_workspace_size(const bdattn_problem* p, int pass, size_t* bytes) {
+  if (!bytes) return fail(BDATTN_ERR_INVALID_ARG, "bytes is NULL");
+  if (pass != 0 && pass != 1) return fail(BDATTN_ERR_INVALID_ARG, "pass must be 0 or 1");
+  bdattn::Problem P;
+  int st = load(p, &P);
+  if (st != BDATTN_OK) return st;
+  *bytes = bdattn::workspace_layout(P, pass, bdattn::n_items(P, pass)).total;
+  return BDATTN_OK;
+}
+
+int bdattn_mask_render(const bdattn_problem* p, uint8_t* host_out, size_t cap) {
+  bdattn::Problem P;
+  int st = load(p, &P);
+  if (st != BDATTN_OK) return st;
+  const size_t nq = size_t(P.n_clean_q) + P.n_corr();
+  const size_t nk = size_t(P.n_clean_kv) + P.n_corr();
+  if (!host_out || cap < nq * nk) return fail(BDATTN_ERR_INVALID_ARG, "output buffer too small");
+  bdattn::mask_render(P, host_out);
+  return BDATTN_OK;
+}
+
+int bdattn_visible_pairs(const bdattn_problem* p, int64_t* pairs) {
+  if (!pairs) return fail(BDATTN_ERR_INVALID_ARG, "pairs is NULL");
+  bdattn::Problem P;
+  int st = load(p, &P);
+  if (st != BDATTN_OK) return st;
+  *pairs = bdattn::visible_pairs(P);
+  return BDATTN_OK;
+}
+
+int bdattn_plan_stats(const bdattn_problem* p, int64_t out[8]) {
+  if (!out) return fail(BDATTN_ERR_INVALID_ARG, "out is NULL");
+  bdattn::Problem P;
+  int st = load(p, &P);
+  if (st != BDATTN_OK) return st;
+  const bdattn::Plan* plan = &get_entry(P)->plan;
+  out[0] = int64_t(plan->fwd.size());
+  out[1] = plan->fwd_tiles;
+  out[2] = plan->fwd_masked_tiles;
+  out[3] = int64_t(plan->bwd.size());
+  out[4] = plan->bwd_qtiles;
+  out[5] = plan->bwd_masked_qtiles;
+  out[6] = plan->fwd_rows;
+  out[7] = bdattn::BWD_TK;
+  return BDATTN_OK;
+}
+
+int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const void* v_c,
+               const void* q_x, const void* k_x, const void* v_x, void* o_c, void* o_x,
+               float* lse_c, float* lse_x, void* workspace, size_t ws_bytes, void* hip_stream) {
+  bdattn::Problem P;
+  int st = bdattn_validate(p);
+  if (st != BDATTN_OK) return st;
+  load(p, &P);
+  const int64_t nqc = int64_t(P.n_clean_q) * P.H * P.d, nqx = int64_t(P.n_corr()) * P.H * P.d;
+  const int64_t nkc = int64_t(P.n_clean_kv) * P.Hkv * P.d, nkx = int64_t(P.n_corr()) * P.Hkv * P.d;
+  if ((st = check_ptr(q_c, nqc, "q_c")) || (st = check_ptr(k_c, nkc, "k_c")) ||
+      (st = check_ptr(v_c, nkc, "v_c")) || (st = check_ptr(q_x, nqx, "q_x")) ||
+      (st = check_ptr(k_x, nkx, "k_x")) || (st = check_ptr(v_x, nkx, "v_x")) ||
+      (st = check_ptr(o_c, nqc, "o_c")) || (st = check_ptr(o_x, nqx, "o_x")) ||
+      (st = check_ptr(lse_c, nqc, "lse_c")) || (st = check_ptr(lse_x, nqx, "lse_x")))
+    return st;
+  Entry* entry = get_entry(P);
+  const bdattn::Plan* plan = &entry->plan;
+  const bdattn::WsLayout w = bdattn::workspace_layout(P, 0, plan->fwd.size());
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
+    return fail(BDATTN_ERR_WORKSPACE, "forward workspace missing, misaligned or smaller than " +
+                                          std::to_string(w.total) + " bytes");
+  hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  if ((st = upload(entry, 0, w, ws, s))) return st;
+  bdattn::FwdArgs a;
+  a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
+  a.o_c = o_c; a.o_x = o_x; a.lse_c = lse_c; a.lse_x = lse_x;
+  a.ids = (const int32_t*)(ws + w.ids);
+  a.items = (const bdattn::FwdItem*)(ws + w.items);
+  a.n_items = int32_t(plan->fwd.size());
+  a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
+  a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
+  a.n_corr = P.n_corr();
+  a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
+  hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, prof_events(0));
+  if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("forward launch: ") + hipGetErrorString(e));
+  return BDATTN_OK;
+}
+
+int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const void* v_c,
+               const void* q_x, const void* k_x, const void* v_x, const void* o_c, const void* o_x,
+               const float* lse_c, const float* lse_x, const void* do_c, const void* do_x, void* dq_c,
+               void* dq_x, void* dk_c, void* dv_c, void* dk_x, void* dv_x, void* workspace,
+               size_t ws_bytes, void* hip_stream) {
+  bdattn::Problem P;
+  int st = bdattn_validate(p);
+  if (st != BDATTN_OK) return st;
+  load(p, &P);
+  const int64_t nqc = int64_t(P.n_clean_q) * P.H * P.d, nqx = int64_t(P.n_corr()) * P.H * P.d;
+  const int64_t nkc = int64_t(P.n_clean_kv) * P.Hkv * P.d, nkx = int64_t(P.n_corr()) * P.Hkv * P.d;
+  if ((st = check_ptr(q_c, nqc, "q_c")) || (st = check_ptr(k_c, nkc, "k_c")) ||
+      (st = check_ptr(v_c, nkc, "v_c")) || (st = check_ptr(q_x, nqx, "q_x")) ||
+      (st = check_ptr(k_x, nkx, "k_x")) || (st = check_ptr(v_x, nkx, "v_x")) ||
+      (st = check_ptr(o_c, nqc, "o_c")) || (st = check_ptr(o_x, nqx, "o_x")) ||
+      (st = check_ptr(lse_c, nqc, "lse_c")) || (st = check_ptr(lse_x, nqx, "lse_x")) ||
+      (st = check_ptr(do_c, nqc, "do_c")) || (st = check_ptr(do_x, nqx, "do_x")) ||
+      (st = check_ptr(dq_c, nqc, "dq_c")) || (st = check_ptr(dq_x, nqx, "dq_x")) ||
+      (st = check_ptr(dk_c, nkc, "dk_c")) || (st = check_ptr(dv_c, nkc, "dv_c")) ||
+      (st = check_ptr(dk_x, nkx, "dk_x")) || (st = check_ptr(dv_x, nkx, "dv_x")))
+    return st;
+  Entry* entry = get_entry(P);
+  const bdattn::Plan* plan = &entry->plan;
+  const bdattn::WsLayout w = bdattn::workspace_layout(P, 1, plan->bwd.size());
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
+    return fail(BDATTN_ERR_WORKSPACE, "backward workspace missing, misaligned or smaller than " +
+                                          std::to_string(w.total) + " bytes");
+  hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  if ((st = upload(entry, 1, w, ws, s))) return st;
+  bdattn::BwdArgs a;
+  a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
+  a.o_c = o_c; a.o_x = o_x; a.do_c = do_c; a.do_x = do_x; a.lse_c = lse_c; a.lse_x = lse_x;
+  a.dq_c = dq_c; a.dq_x = dq_x; a.dk_c = dk_c; a.dv_c = dv_c; a.dk_x = dk_x; a.dv_x = dv_x;
+  a.ids = (const int32_t*)(ws + w.ids);
+  a.items = (const bdattn::BwdItem*)(ws + w.items);
+  a.n_items = int32_t(plan->bwd.size());
+  a.d_c = (float*)(ws + w.d_c);
+  a.d_x = (float*)(ws + w.d_x);
+  a.dqa_c = (float*)(ws + w.dqa_c);
+  a.dqa_x = (float*)(ws + w.dqa_x);
+  a.B = P.B; a.H = P.H; a.Hkv = P.Hkv;
+  a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
+  a.n_corr = P.n_corr();
+  a.scale = P.scale;
+  a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
+  hipError_t e = bdattn::launch_bwd(a, P.dtype, P.d, s, prof_events(1));
+  if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+  return BDATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Visibility rule of block-diffusion attention, compiled for host and device.
+//
+// "Block Parallelism for Efficient Distributed Long-Context Diffusion Language
+// Model Training", §3.2 (Block diffusion language models):
+//   clean query of block qb      sees clean keys of blocks kb <= qb,
+//                                never corrupted keys;
+//   corrupted query of block qb  sees clean keys of blocks kb < qb and the
+//                                corrupted keys of its own block.
+// Blocks are 0-indexed on global clean positions: block(p) = p / B.
+//
+// Every row's visible keys are two intervals: a clean prefix [0, cb) of the
+// clean K/V buffer (which starts at global position 0) and an interval
+// [xlo, xhi) of the local corrupted keys. This O(n) bound form is what the
+// planner, the kernels and the host mask render all evaluate.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIP__)
+#define BD_HD __attribute__((host, device, always_inline)) inline
+#else
+#define BD_HD inline
+#endif
+
+// Visible key intervals of one query row.
+struct BdRowBounds {
+  int32_t cb;   // clean keys [0, cb) are visible
+  int32_t xlo;  // corrupted keys [xlo, xhi) are visible (empty for clean rows)
+  int32_t xhi;
+};
+
+// Clean query at global position gpos: clean keys of blocks 0..block(gpos).
+BD_HD BdRowBounds bd_clean_row(int32_t gpos, int32_t B) {
+  BdRowBounds r;
+  r.cb = (gpos / B + 1) * B;
+  r.xlo = 0;
+  r.xhi = 0;
+  return r;
+}
+
+// Corrupted query at local corrupted row `row`, whose block has global id
+// `block_id`: clean keys of blocks < block_id, corrupted keys of its own block
+// (local block index row / B, packed contiguously).
+BD_HD BdRowBounds bd_corr_row(int32_t row, int32_t block_id, int32_t B) {
+  BdRowBounds r;
+  r.cb = block_id * B;
+  r.xlo = (row / B) * B;
+  r.xhi = r.xlo + B;
+  return r;
+}
+
+// Is clean key `k` (buffer index = global position) visible to the row?
+BD_HD bool bd_sees_clean(const BdRowBounds& r, int32_t k) { return k < r.cb; }
+
+// Is local corrupted key `k` visible to the row?
+BD_HD bool bd_sees_corr(const BdRowBounds& r, int32_t k) { return k >= r.xlo && k < r.xhi; }

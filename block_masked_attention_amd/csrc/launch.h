@@ -1,0 +1,50 @@
+// Kernel launchers shared by the C ABI (api.cpp) and the kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace bdattn {
+
+struct FwdArgs {
+  const void *q_c, *k_c, *v_c, *q_x, *k_x, *v_x;
+  void *o_c, *o_x;
+  float *lse_c, *lse_x;
+  const int32_t* ids;      // device: global id of each local corrupted block
+  const FwdItem* items;    // device work list
+  int32_t n_items;
+  int32_t B, H, Hkv, Gw, rows_per_item;
+  int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+struct BwdArgs {
+  const void *q_c, *k_c, *v_c, *q_x, *k_x, *v_x;
+  const void *o_c, *o_x, *do_c, *do_x;
+  const float *lse_c, *lse_x;
+  void *dq_c, *dq_x, *dk_c, *dv_c, *dk_x, *dv_x;
+  const int32_t* ids;
+  const BwdItem* items;
+  int32_t n_items;
+  float *d_c, *d_x;        // workspace: D = rowsum(dO * O)  [H][n]
+  float *dqa_c, *dqa_x;    // workspace: float dQ accumulators [n][H][d]
+  int32_t B, H, Hkv;
+  int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
+  float scale, scale_log2;
+};
+
+// True if this build has kernels for (dtype, d).
+bool have_kernels(int dtype, int d);
+
+// Optional events recorded around the main kernel (null = none).
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t stream,
+                      const KernelEvents& ev);
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t stream,
+                      const KernelEvents& ev);
+
+}  // namespace bdattn

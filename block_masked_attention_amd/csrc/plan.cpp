@@ -1,0 +1,266 @@
+// Host planner for block-diffusion attention: validation, pair counts, mask
+// render and the longest-first work lists of the forward and backward kernels.
+#include "plan.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <numeric>
+
+namespace bdattn {
+
+namespace {
+
+constexpr int64_t kMax32 = (int64_t(1) << 31) - 1;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
+
+BdRowBounds row_bounds(const Problem& P, int stream, int32_t row) {
+  if (stream == 0) return bd_clean_row(P.clean_q_start + row, P.B);
+  return bd_corr_row(row, P.ids[row / P.B], P.B);
+}
+
+}  // namespace
+
+int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
+  if (!p) {
+    *msg = "problem descriptor is NULL";
+    return BDATTN_ERR_INVALID_ARG;
+  }
+  if (p->dtype != BDATTN_F32 && p->dtype != BDATTN_BF16) {
+    *msg = "unknown dtype";
+    return BDATTN_ERR_INVALID_ARG;
+  }
+  if (p->B < 1 || p->H < 1 || p->Hkv < 1) {
+    *msg = "B, H and Hkv must be >= 1";
+    return BDATTN_ERR_SHAPE;
+  }
+  if (p->H % p->Hkv) {
+    *msg = "H must be a multiple of Hkv";
+    return BDATTN_ERR_SHAPE;
+  }
+  if (p->d != 32 && p->d != 128) {
+    *msg = "head dim must be 32 or 128";
+    return BDATTN_ERR_UNSUPPORTED;
+  }
+  if (p->n_clean_q < 0 || p->clean_q_start < 0 || p->n_clean_kv < 0 || p->clean_kv_start < 0 ||
+      p->n_corr_blocks < 0) {
+    *msg = "negative size or offset";
+    return BDATTN_ERR_SHAPE;
+  }
+  const int64_t B = p->B;
+  if (p->n_clean_q % B || p->clean_q_start % B || p->n_clean_kv % B) {
+    *msg = "n_clean_q, clean_q_start and n_clean_kv must be multiples of B";
+    return BDATTN_ERR_SHAPE;
+  }
+  if (p->clean_q_start + p->n_clean_q > kMax32 || p->n_clean_kv > kMax32 ||
+      p->n_corr_blocks * B > kMax32 || p->clean_kv_start > kMax32) {
+    *msg = "sizes must stay below 2^31 rows";
+    return BDATTN_ERR_SHAPE;
+  }
+  Problem P;
+  P.B = p->B;
+  P.H = p->H;
+  P.Hkv = p->Hkv;
+  P.d = p->d;
+  P.dtype = p->dtype;
+  P.scale = p->scale > 0.f ? p->scale : float(1.0 / sqrt(double(p->d)));
+  P.n_clean_q = int32_t(p->n_clean_q);
+  P.clean_q_start = int32_t(p->clean_q_start);
+  P.n_clean_kv = int32_t(p->n_clean_kv);
+  P.n_corr_blocks = int32_t(p->n_corr_blocks);
+  P.ids.resize(P.n_corr_blocks);
+  if (p->corr_block_ids) {
+    for (int32_t i = 0; i < P.n_corr_blocks; ++i) {
+      int32_t v = p->corr_block_ids[i];
+      if (v < 0 || (i > 0 && v <= P.ids[i - 1])) {
+        *msg = "corr_block_ids must be >= 0 and strictly increasing";
+        return BDATTN_ERR_INVALID_ARG;
+      }
+      if (int64_t(v) * B > kMax32) {
+        *msg = "corrupted block id beyond 2^31 positions";
+        return BDATTN_ERR_SHAPE;
+      }
+      P.ids[i] = v;
+    }
+  } else {
+    std::iota(P.ids.begin(), P.ids.end(), 0);
+  }
+  // Coverage: the buffer starts at position 0 and holds every clean key a
+  // local query sees: the whole last block of the query shard, and the
+  // prefix before the last local corrupted block.
+  int64_t need = 0;
+  if (P.n_clean_q > 0) need = int64_t(P.clean_q_start) + P.n_clean_q;
+  if (P.n_corr_blocks > 0) need = std::max<int64_t>(need, int64_t(P.ids.back()) * B);
+  if (p->clean_kv_start != 0 && (need > 0 || p->n_clean_kv > 0)) {
+    *msg = "the clean K/V buffer must start at global position 0";
+    return BDATTN_ERR_COVERAGE;
+  }
+  if (P.n_clean_kv < need) {
+    *msg = "the clean K/V buffer misses clean keys a local query sees";
+    return BDATTN_ERR_COVERAGE;
+  }
+  *out = std::move(P);
+  return BDATTN_OK;
+}
+
+int fwd_heads_per_group(const Problem& P) {
+  int G = P.G();
+  if (G % 4 == 0) return 4;
+  if (G % 2 == 0) return 2;
+  return 1;
+}
+
+int fwd_rows_per_item(const Problem& P) {
+  return FWD_WAVES * FWD_ROWS_PER_WAVE / fwd_heads_per_group(P);
+}
+
+size_t n_items(const Problem& P, int pass) {
+  if (pass == 0) {
+    const int Gw = fwd_heads_per_group(P), R = fwd_rows_per_item(P);
+    size_t tiles = size_t(ceil_div(P.n_clean_q, R)) + size_t(ceil_div(P.n_corr(), R));
+    return tiles * size_t(P.H / Gw);
+  }
+  size_t tiles = size_t(ceil_div(P.n_clean_kv, BWD_TK)) + size_t(ceil_div(P.n_corr(), BWD_TK));
+  return tiles * size_t(P.Hkv);
+}
+
+WsLayout workspace_layout(const Problem& P, int pass, size_t items) {
+  WsLayout w;
+  size_t off = 0;
+  w.ids = off;
+  off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, P.ids.size()), WS_ALIGN);
+  w.items = off;
+  w.items_bytes = items * (pass == 0 ? sizeof(FwdItem) : sizeof(BwdItem));
+  off = align_up(off + std::max<size_t>(1, w.items_bytes), WS_ALIGN);
+  if (pass == 1) {
+    w.d_c = off;
+    off = align_up(off + sizeof(float) * size_t(P.H) * P.n_clean_q, WS_ALIGN);
+    w.d_x = off;
+    off = align_up(off + sizeof(float) * size_t(P.H) * P.n_corr(), WS_ALIGN);
+    w.dqa_c = off;
+    off = align_up(off + sizeof(float) * size_t(P.n_clean_q) * P.H * P.d, WS_ALIGN);
+    w.dqa_x = off;
+    off = align_up(off + sizeof(float) * size_t(P.n_corr()) * P.H * P.d, WS_ALIGN);
+  }
+  w.total = off;
+  return w;
+}
+
+void build_plan(const Problem& P, Plan* plan) {
+  plan->P = P;
+  plan->Gw = fwd_heads_per_group(P);
+  plan->fwd_rows = fwd_rows_per_item(P);
+  plan->fwd.clear();
+  plan->bwd.clear();
+  plan->fwd_tiles = plan->fwd_masked_tiles = plan->bwd_qtiles = plan->bwd_masked_qtiles = 0;
+
+  // ---------------- forward: (stream, row tile) sorted by key tiles, longest first
+  {
+    const int R = plan->fwd_rows;
+    const int NHG = P.H / plan->Gw;
+    struct T { int32_t tile, stream; int64_t cost, masked; };
+    std::vector<T> tiles;
+    for (int s = 0; s < 2; ++s) {
+      const int32_t n = s == 0 ? P.n_clean_q : P.n_corr();
+      for (int32_t t = 0; t * int64_t(R) < n; ++t) {
+        const int32_t r0 = t * R, r1 = std::min<int32_t>(n, r0 + R);
+        BdRowBounds first = row_bounds(P, s, r0), last = row_bounds(P, s, r1 - 1);
+        const int32_t full_end = first.cb / FWD_TK * FWD_TK;  // tiles below are unmasked
+        const int32_t nct = ceil_div(last.cb, FWD_TK);
+        int64_t cost = nct, masked = nct - full_end / FWD_TK;
+        if (s == 1) {
+          const int32_t nxt = ceil_div(last.xhi - first.xlo, FWD_TK);
+          cost += nxt;
+          masked += nxt;
+        }
+        tiles.push_back({t, s, cost, masked});
+      }
+    }
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const T& a, const T& b) { return a.cost > b.cost; });
+    plan->fwd.reserve(tiles.size() * NHG);
+    // consecutive workgroup ids land on different XCDs; keep one head group
+    // per id residue so an XCD's L2 sees one KV head's prefix
+    for (const T& t : tiles) {
+      for (int hg = 0; hg < NHG; ++hg) plan->fwd.push_back({t.tile, (hg << 1) | t.stream});
+      plan->fwd_tiles += t.cost * NHG;
+      plan->fwd_masked_tiles += t.masked * NHG;
+    }
+  }
+
+  // ---------------- backward: key tiles sorted by query rows swept, longest first
+  {
+    const int G = P.G();
+    const int32_t nx = P.n_corr();
+    struct T { int32_t ktile, stream; BwdItem rows; int64_t cost, qt, masked; };
+    std::vector<T> tiles;
+    auto qtiles = [](int32_t r0, int32_t r1) -> int64_t {
+      if (r1 <= r0) return 0;
+      return (r1 - 1) / BWD_TQ - r0 / BWD_TQ + 1;
+    };
+    for (int32_t kt = 0; kt * int64_t(BWD_TK) < P.n_clean_kv; ++kt) {
+      const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(P.n_clean_kv, k0 + BWD_TK);
+      const int32_t kb = k0 / P.B;
+      // clean rows of blocks >= kb; corrupted rows of blocks with id > kb
+      int32_t c0 = std::min<int32_t>(P.n_clean_q, std::max<int32_t>(0, kb * P.B - P.clean_q_start));
+      int32_t j = int32_t(std::upper_bound(P.ids.begin(), P.ids.end(), kb) - P.ids.begin());
+      int32_t x0 = j * P.B;
+      BwdItem it{kt, 0, c0, P.n_clean_q, x0, nx};
+      // a q tile needs the mask unless its first row sees the whole key tile
+      int64_t qt = qtiles(c0, P.n_clean_q) + qtiles(x0, nx), masked = 0;
+      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r < P.n_clean_q; r += BWD_TQ)
+        if (r < c0 || row_bounds(P, 0, r).cb < k1 || k1 - k0 < BWD_TK) ++masked; else break;
+      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r < nx; r += BWD_TQ)
+        if (r < x0 || row_bounds(P, 1, r).cb < k1 || k1 - k0 < BWD_TK) ++masked; else break;
+      tiles.push_back({kt, 0, it, (P.n_clean_q - c0) + int64_t(nx - x0), qt, masked});
+    }
+    for (int32_t kt = 0; kt * int64_t(BWD_TK) < nx; ++kt) {
+      const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(nx, k0 + BWD_TK);
+      const int32_t x0 = k0 / P.B * P.B, x1 = std::min<int32_t>(nx, ceil_div(k1, P.B) * P.B);
+      BwdItem it{kt, 1, 0, 0, x0, x1};
+      const int64_t qt = qtiles(x0, x1);
+      tiles.push_back({kt, 1, it, x1 - x0, qt, qt});
+    }
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const T& a, const T& b) { return a.cost > b.cost; });
+    plan->bwd.reserve(tiles.size() * P.Hkv);
+    for (const T& t : tiles) {
+      for (int g = 0; g < P.Hkv; ++g) {
+        BwdItem it = t.rows;
+        it.hs = (g << 1) | t.stream;
+        plan->bwd.push_back(it);
+      }
+      plan->bwd_qtiles += t.qt * G * P.Hkv;
+      plan->bwd_masked_qtiles += t.masked * G * P.Hkv;
+    }
+  }
+}
+
+int64_t visible_pairs(const Problem& P) {
+  int64_t pairs = 0;
+  for (int32_t r = 0; r < P.n_clean_q; ++r) pairs += row_bounds(P, 0, r).cb;
+  for (int32_t r = 0; r < P.n_corr(); ++r) {
+    BdRowBounds b = row_bounds(P, 1, r);
+    pairs += int64_t(b.cb) + (b.xhi - b.xlo);
+  }
+  return pairs;
+}
+
+void mask_render(const Problem& P, uint8_t* out) {
+  const int64_t nq = int64_t(P.n_clean_q) + P.n_corr();
+  const int64_t nk = int64_t(P.n_clean_kv) + P.n_corr();
+  for (int64_t q = 0; q < nq; ++q) {
+    const int stream = q < P.n_clean_q ? 0 : 1;
+    const int32_t row = int32_t(stream == 0 ? q : q - P.n_clean_q);
+    BdRowBounds b = row_bounds(P, stream, row);
+    uint8_t* o = out + q * nk;
+    for (int32_t k = 0; k < P.n_clean_kv; ++k) o[k] = bd_sees_clean(b, k) ? 1 : 0;
+    for (int32_t k = 0; k < P.n_corr(); ++k) o[P.n_clean_kv + k] = bd_sees_corr(b, k) ? 1 : 0;
+  }
+}
+
+}  // namespace bdattn

@@ -1,0 +1,86 @@
+// Host planner: problem validation, exact pair counts, and the work lists the
+// kernels consume. No HIP calls here, so it builds with any host compiler.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/bdattn.h"
+#include "bdattn_mask.h"
+
+namespace bdattn {
+
+// Forward: a workgroup of 4 waves covers FWD_ROWS_PER_WAVE query rows per wave
+// and sweeps the visible keys in tiles of FWD_TK.
+constexpr int FWD_WAVES = 4;
+constexpr int FWD_ROWS_PER_WAVE = 32;
+constexpr int FWD_TK = 64;
+// Backward: a workgroup of 4 waves owns BWD_TK keys of one KV head (32 per
+// wave) and sweeps the query rows that see them in tiles of BWD_TQ.
+constexpr int BWD_WAVES = 4;
+constexpr int BWD_TK = 128;
+constexpr int BWD_TQ = 64;
+
+constexpr size_t WS_ALIGN = 256;
+
+// One forward work item: `tile` of `rows` query rows (stream bit 0 of hs),
+// head group hs >> 1 (Gw consecutive q heads).
+struct FwdItem {
+  int32_t tile;
+  int32_t hs;
+};
+
+// One backward work item: key tile `ktile` of the key stream (bit 0 of hs) of
+// KV head hs >> 1; sweeps clean query rows [c0, c1) and corrupted rows
+// [x0, x1).
+struct BwdItem {
+  int32_t ktile;
+  int32_t hs;
+  int32_t c0, c1, x0, x1;
+};
+
+struct Problem {
+  int32_t B, H, Hkv, d, dtype;
+  float scale;  // resolved (> 0)
+  int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks;
+  std::vector<int32_t> ids;  // always materialised (0..n-1 when NULL)
+  int32_t n_corr() const { return n_corr_blocks * B; }
+  int32_t G() const { return H / Hkv; }
+};
+
+// Validate and copy a descriptor. Returns a bdattn_status; `msg` explains.
+int load_problem(const bdattn_problem* p, Problem* out, std::string* msg);
+
+// Heads per forward workgroup: the largest of 4, 2, 1 dividing H/Hkv.
+int fwd_heads_per_group(const Problem& P);
+int fwd_rows_per_item(const Problem& P);
+
+struct Plan {
+  Problem P;
+  int Gw = 1;        // q heads per forward workgroup
+  int fwd_rows = 0;  // query rows per forward workgroup
+  std::vector<FwdItem> fwd;
+  std::vector<BwdItem> bwd;
+  // statistics
+  int64_t fwd_tiles = 0, fwd_masked_tiles = 0, bwd_qtiles = 0, bwd_masked_qtiles = 0;
+};
+
+void build_plan(const Problem& P, Plan* plan);
+
+// Workspace layout (byte offsets from the workspace start).
+struct WsLayout {
+  size_t ids = 0, items = 0, items_bytes = 0;
+  size_t d_c = 0, d_x = 0;      // bwd: D = rowsum(dO * O), float [H][n]
+  size_t dqa_c = 0, dqa_x = 0;  // bwd: float dQ accumulators [n][H][d]
+  size_t total = 0;
+};
+WsLayout workspace_layout(const Problem& P, int pass, size_t n_items);
+size_t n_items(const Problem& P, int pass);
+
+int64_t visible_pairs(const Problem& P);
+void mask_render(const Problem& P, uint8_t* out);
+
+}  // namespace bdattn

@@ -1,0 +1,175 @@
+/*
+ * bdattn — clean-plus-corrupted block-diffusion attention on one MI355X (gfx950).
+ *
+ * The operation is the attention of block-diffusion language-model training
+ * described in "Block Parallelism for Efficient Distributed Long-Context
+ * Diffusion Language Model Training":
+ *
+ *  - §3.2 (Block diffusion language models): a clean copy and a corrupted copy
+ *    of the sequence, cut into blocks of B tokens. A clean query of block b sees
+ *    the clean keys of blocks 0..b (its whole own block: block-causal). A
+ *    corrupted query of target block b sees its own block's corrupted keys
+ *    (bidirectionally) and the clean keys of blocks < b, never another block's
+ *    corrupted keys.
+ *  - §4.3 (Context-sharded block parallelism): one rank holds a shard of clean
+ *    queries, the clean K/V of the positions its queries need (gathered into
+ *    one buffer in original position order), and a set of whole corrupted
+ *    blocks. The problem descriptor below expresses exactly that share; the
+ *    whole single-GPU problem is the share with one rank.
+ *  - Appendix, "Efficient fused operator" (Implementations 1 and 2): the
+ *    forward saves the output and the log-sum-exp; the backward reuses them
+ *    and returns the query gradients together with the gradients of the local
+ *    corrupted K/V and of the clean K/V buffer, the latter summed over every
+ *    local query that sees each clean key (§4.3, Backward pass).
+ *
+ * Softmax attention per query row i and q head h (KV head g = h / (H/Hkv)):
+ *   s_ij = scale <q_i, k_j>,  LSE_i = ln sum_{j visible} exp(s_ij),
+ *   O_i = sum_j exp(s_ij - LSE_i) v_j.
+ * Blocks are 0-indexed on global clean positions: block(p) = p / B.
+ *
+ * Layouts (all tensors contiguous, token-major, one dtype):
+ *   Q, O, dO, dQ : [n, H, d]        K, V, dK, dV : [n, Hkv, d]
+ *   LSE          : [H, n] float32, natural log, scale included.
+ * Clean query tensors have n = n_clean_q; clean K/V tensors n = n_clean_kv;
+ * corrupted tensors n = n_corr_blocks * B, blocks packed in increasing id order.
+ *
+ * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
+ * the caller. bdattn_fwd / bdattn_bwd enqueue work on `hip_stream` (a
+ * hipStream_t; NULL = the default stream) and return without waiting; they
+ * never allocate device memory. Scratch space is the caller's `workspace`
+ * (device memory of at least bdattn_workspace_size bytes, 256-byte aligned),
+ * which must not be used by anything else until the enqueued work is done.
+ * Outputs are overwritten, never accumulated into. Tensor pointers must be
+ * 16-byte aligned. Calls on different streams may run concurrently if they
+ * use distinct workspaces and outputs.
+ *
+ * Errors: every function returns a bdattn_status. Arguments are validated on
+ * the host before any GPU work; on failure nothing is enqueued. After the
+ * launches a HIP launch error is reported as BDATTN_ERR_HIP. Nothing aborts or
+ * throws across this interface. bdattn_last_error() gives a message for the
+ * most recent failure on the calling thread.
+ */
+#ifndef BDATTN_H
+#define BDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BDATTN_VERSION 1
+
+typedef enum {
+  BDATTN_OK = 0,
+  BDATTN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad enum, bad ids */
+  BDATTN_ERR_SHAPE = -2,       /* sizes not multiples of B, H % Hkv != 0, ... */
+  BDATTN_ERR_UNSUPPORTED = -3, /* head dim or dtype this build has no kernel for */
+  BDATTN_ERR_COVERAGE = -4,    /* clean K/V buffer misses keys a local query sees */
+  BDATTN_ERR_WORKSPACE = -5,   /* workspace missing, too small or misaligned */
+  BDATTN_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+} bdattn_status;
+
+typedef enum { BDATTN_F32 = 0, BDATTN_BF16 = 1 } bdattn_dtype;
+
+/* One rank's share of the block-diffusion attention (§4.3), or the whole
+ * problem on one GPU. */
+typedef struct {
+  int32_t B;       /* block size in tokens, >= 1 */
+  int32_t H;       /* query heads */
+  int32_t Hkv;     /* key/value heads; H % Hkv == 0 (q head h reads KV head h/(H/Hkv)) */
+  int32_t d;       /* head dim: 32 or 128 */
+  int32_t dtype;   /* bdattn_dtype of every Q/K/V/O/dO/dQ/dK/dV tensor */
+  float scale;     /* softmax scale; <= 0 selects 1/sqrt(d) */
+  int64_t n_clean_q;      /* local clean queries ...                         */
+  int64_t clean_q_start;  /* ... at global clean positions [start, start+n)  */
+  int64_t n_clean_kv;     /* clean K/V buffer ...                            */
+  int64_t clean_kv_start; /* ... at global positions [start, start+n); must be 0 */
+  int64_t n_corr_blocks;  /* local corrupted blocks (each B tokens)          */
+  /* HOST array of n_corr_blocks global block ids, strictly increasing, or
+   * NULL for ids 0..n_corr_blocks-1. Read during the call only. */
+  const int32_t* corr_block_ids;
+} bdattn_problem;
+
+/* BDATTN_VERSION of the loaded library. */
+int bdattn_version(void);
+
+/* Static description of a status code. */
+const char* bdattn_status_string(int status);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* bdattn_last_error(void);
+
+/* Host-only check of a problem descriptor (no HIP calls). Rules: B >= 1;
+ * H, Hkv >= 1 and H % Hkv == 0; d in {32, 128}; dtype known;
+ * n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks >= 0; clean_q_start,
+ * n_clean_q and n_clean_kv multiples of B (BDATTN_ERR_SHAPE); ids strictly
+ * increasing and >= 0 (BDATTN_ERR_INVALID_ARG); every row count and global
+ * position below 2^31; coverage: clean_kv_start == 0 and n_clean_kv reaches
+ * the end of the last block of the query shard and the start of the last
+ * local corrupted block (BDATTN_ERR_COVERAGE). */
+int bdattn_validate(const bdattn_problem* p);
+
+/* Bytes of workspace needed by bdattn_fwd (pass 0) or bdattn_bwd (pass 1).
+ * Host-only. */
+int bdattn_workspace_size(const bdattn_problem* p, int pass, size_t* bytes);
+
+/* Dense visibility matrix of the problem, written to HOST memory as uint8
+ * (1 = visible), row-major [nq][nk] with queries = clean-local rows then
+ * corrupted rows, keys = clean buffer then corrupted keys. `cap` is the size
+ * of host_out in bytes; BDATTN_ERR_INVALID_ARG if it is smaller than nq*nk.
+ * Computed from the same predicate the GPU kernels compile. Host-only. */
+int bdattn_mask_render(const bdattn_problem* p, uint8_t* host_out, size_t cap);
+
+/* Exact number of visible (query, key) pairs of one q head (host-only). The
+ * useful work of fwd+bwd is 12*d*H*pairs flops (QK^T, PV forward; dV, dP,
+ * dQ, dK backward). */
+int bdattn_visible_pairs(const bdattn_problem* p, int64_t* pairs);
+
+/* Planner statistics (host-only), for tests and logs. out[0..7] =
+ * {fwd work items, fwd key tiles visited, fwd key tiles needing a mask,
+ *  bwd work items, bwd q tiles visited, bwd q tiles needing a mask,
+ *  fwd rows per work item, bwd keys per work item}. */
+int bdattn_plan_stats(const bdattn_problem* p, int64_t out[8]);
+
+/* Forward (Implementation 1 of the appendix, fused into one launch): writes
+ * o_c [n_clean_q,H,d], o_x [n_corr,H,d], lse_c [H,n_clean_q],
+ * lse_x [H,n_corr]. Inputs q_c [n_clean_q,H,d], k_c/v_c [n_clean_kv,Hkv,d],
+ * q_x [n_corr,H,d], k_x/v_x [n_corr,Hkv,d]. Pointers of empty tensors may be
+ * NULL. */
+int bdattn_fwd(const bdattn_problem* p,
+               const void* q_c, const void* k_c, const void* v_c,
+               const void* q_x, const void* k_x, const void* v_x,
+               void* o_c, void* o_x, float* lse_c, float* lse_x,
+               void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Backward (Implementation 2 of the appendix): from the forward's saved
+ * o_c/o_x and lse_c/lse_x and the upstream do_c/do_x, writes dq_c, dq_x,
+ * dk_c/dv_c [n_clean_kv,Hkv,d] (clean keys no local query sees get zeros)
+ * and dk_x/dv_x [n_corr,Hkv,d]. LSE is not differentiated. */
+int bdattn_bwd(const bdattn_problem* p,
+               const void* q_c, const void* k_c, const void* v_c,
+               const void* q_x, const void* k_x, const void* v_x,
+               const void* o_c, const void* o_x,
+               const float* lse_c, const float* lse_x,
+               const void* do_c, const void* do_x,
+               void* dq_c, void* dq_x, void* dk_c, void* dv_c, void* dk_x, void* dv_x,
+               void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Optional instrumentation for benchmarks. With profiling on (per calling
+ * thread), bdattn_fwd and bdattn_bwd record a pair of HIP events on the
+ * call's stream around their main kernel (the forward kernel; the backward's
+ * key-tile kernel, without its D and dQ-conversion kernels). bdattn_profile_read
+ * waits for the recorded events, returns the summed milliseconds and the
+ * number of launches of each since the last read, and releases the events.
+ * Off by default; costs nothing when off. */
+int bdattn_profile_enable(int on);
+int bdattn_profile_read(double* fwd_ms, int64_t* fwd_launches, double* bwd_ms,
+                        int64_t* bwd_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDATTN_H */

@@ -9,7 +9,7 @@ itself (a hand-drawn mask fixture, closed forms at Q = 0, a library attention
 routine, scalar brute force, finite differences, invariants of the method).
 """
 from .bdattn_oracle import (CLEAN, CORRUPTED, Layout, Oracle, key_tokens, layout,
-                            query_tokens, visible)
+                            query_tokens, round_bf16, visible)
 
 __all__ = ["CLEAN", "CORRUPTED", "Layout", "Oracle", "key_tokens", "layout",
-           "query_tokens", "visible"]
+           "query_tokens", "round_bf16", "visible"]

@@ -42,7 +42,7 @@ CLEAN = 0
 CORRUPTED = 1
 
 __all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens",
-           "Oracle", "CLEAN", "CORRUPTED"]
+           "Oracle", "CLEAN", "CORRUPTED", "round_bf16"]
 
 
 @dataclass(frozen=True)
@@ -149,18 +149,45 @@ def _f64(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 
+def round_bf16(x):
+    """Round to the nearest bfloat16 value (ties to even), through float32
+    (as a kernel that rounds its fp32 results does). bfloat16 keeps the top
+    16 bits of a float32: add half of the dropped part, with the tie going
+    to the even kept value, then truncate."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _ident(x):
+    return x
+
+
 class Oracle:
     """Plain masked softmax attention and its analytic backward, in float64.
 
     Construct with the layout and the inputs (Q/dO ``[n, H, d]``, K/V
     ``[n, Hkv, d]``) exactly as the GPU receives them (upcast, never rounded).
+
+    ``operand_rounding="bf16"`` gives the same definition evaluated with the
+    roundings a bf16 matrix-core implementation cannot avoid, and nothing
+    else: the softmax weights are rounded to bf16 before they multiply V (and
+    dO), dS is rounded to bf16 before it multiplies K (and Q), the saved O
+    that D = <dO, O> reads is the bf16 output, and every output is stored in
+    bf16. Products are still exact sums in float64. It measures what bf16
+    arithmetic at those points costs; the default (None) is the exact oracle.
     """
 
     # rows x columns of one chunk's dense score matrix (bounded memory only)
     CHUNK_ELEMS = 1 << 23
 
-    def __init__(self, lay: Layout, q_c, k_c, v_c, q_x, k_x, v_x, do_c=None, do_x=None):
+    def __init__(self, lay: Layout, q_c, k_c, v_c, q_x, k_x, v_x, do_c=None, do_x=None,
+                 operand_rounding=None):
         self.lay = lay
+        if operand_rounding not in (None, "bf16"):
+            raise ValueError("operand_rounding must be None or 'bf16'")
+        self.rd = round_bf16 if operand_rounding == "bf16" else _ident
         self.Q = np.concatenate([_f64(q_c), _f64(q_x)]).reshape(lay.nq, lay.H, lay.d)
         self.K = np.concatenate([_f64(k_c), _f64(k_x)]).reshape(lay.nk, lay.Hkv, lay.d)
         self.V = np.concatenate([_f64(v_c), _f64(v_x)]).reshape(lay.nk, lay.Hkv, lay.d)
@@ -212,8 +239,8 @@ class Oracle:
                 E = np.exp(S - m[:, None])
                 l = E.sum(axis=1)
                 LSE[h, s:s + len(rows)] = m + np.log(l)
-                O[s:s + len(rows), h] = (E / l[:, None]) @ self.V[cols, g]
-        return O, LSE
+                O[s:s + len(rows), h] = (self.rd(E) @ self.V[cols, g]) / l[:, None]
+        return self.rd(O), LSE
 
     def forward(self):
         """Full forward: (O_c, O_x, LSE_c, LSE_x)."""
@@ -225,7 +252,7 @@ class Oracle:
     def _row_stats(self, qidx, O=None, LSE=None):
         if O is None or LSE is None:
             O, LSE = self.rows_forward(qidx)
-        D = np.einsum("nhd,nhd->nh", self.dO[qidx], O)  # D_i = <dO_i, O_i>
+        D = np.einsum("nhd,nhd->nh", self.dO[qidx], self.rd(O))  # D_i = <dO_i, O_i>
         return O, LSE, D
 
     def rows_backward(self, qidx, kidx=None, O=None, LSE=None):
@@ -260,11 +287,11 @@ class Oracle:
                 S = self._scores(rows, cols, Mc, h)
                 P = np.exp(S - LSE[h, sl][:, None])  # exp(-inf) = 0 off the mask
                 dP = self.dO[rows, h] @ self.V[cols, g].T
-                dS = P * (dP - D[sl, h][:, None])
+                dS = self.rd(P * (dP - D[sl, h][:, None]))
                 dQ[sl, h] = lay.scale * (dS @ self.K[cols, g])
                 dK[cols, g] += lay.scale * (dS.T @ self.Q[rows, h])
-                dV[cols, g] += P.T @ self.dO[rows, h]
-        return dQ, dK, dV
+                dV[cols, g] += self.rd(P).T @ self.dO[rows, h]
+        return self.rd(dQ), self.rd(dK), self.rd(dV)
 
     def backward(self, O=None, LSE=None):
         """Full backward: (dQ_c, dQ_x, dK_c, dV_c, dK_x, dV_x)."""

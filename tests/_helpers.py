@@ -38,3 +38,37 @@ def rel_err(x, y):
         return 0.0
     den = float(np.max(np.abs(y)))
     return float(np.max(np.abs(x - y)) / (den if den > 0 else 1.0))
+
+
+def bf16_round(y):
+    """Round float64 values to the nearest bfloat16 (ties to even)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(y, dtype=np.float64)).float() \
+        .bfloat16().double().numpy()
+
+
+def bf16_ulp(y):
+    """Spacing of bfloat16 numbers at |y| (8 significant bits)."""
+    a = np.abs(np.asarray(y, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 7), 0.0)
+
+
+def bf16_metrics(x, y):
+    """Error measures of a bf16 result x against the float64 oracle y:
+    raw    = max|x-y| / rms(y)
+    floor  = max|bf16(y)-y| / rms(y)   (storing the exact result in bf16)
+    excess = max(|x-y| - ulp(y), 0) / rms(y)  (error beyond one bf16 ulp)
+    row    = max over output vectors of max|x-y| / rms(vector)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    r = rms(y) or 1.0
+    ex = np.maximum(np.abs(x - y) - bf16_ulp(y), 0.0)
+    yr = y.reshape(-1, y.shape[-1]) if y.ndim > 1 else y.reshape(1, -1)
+    xr = x.reshape(yr.shape)
+    rr = np.sqrt(np.mean(yr * yr, axis=1, keepdims=True))
+    rr = np.where(rr > 0, rr, 1.0)
+    return dict(raw=float(np.max(np.abs(x - y)) / r),
+                floor=float(np.max(np.abs(bf16_round(y) - y)) / r),
+                excess=float(np.max(ex)) / r,
+                row=float(np.max(np.abs(xr - yr) / rr)))

@@ -1,0 +1,168 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI, and
+build oracle sub-problems for sampled checks at full size.
+
+A sampled check uses the context-sharded share semantics ("Block Parallelism
+for Efficient Distributed Long-Context Diffusion Language Model Training",
+§4.3; pinned in the oracle tests by the simulated-ranks test): the outputs of
+the query rows of one block depend only on the keys those rows see, so a
+sub-problem holding that block's queries and exactly its visible clean prefix
+reproduces them; the dK/dV of a clean key come from every query that sees it,
+so a sub-problem holding all those queries reproduces them.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import torch
+
+import block_masked_attention_amd as bd
+from oracle import Oracle, layout
+from tests._helpers import bf16_metrics, f64, rel_err, rms_err
+from workloads import GRAD_NAMES, INPUT_NAMES
+
+OUT_NAMES = ("o_c", "o_x", "lse_c", "lse_x", "dq_c", "dq_x", "dk_c", "dv_c", "dk_x", "dv_x")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_gpu(spec, t):
+    """fwd then bwd through the C ABI on the tensors' device."""
+    p = bd.from_spec(spec)
+    o_c, o_x, lse_c, lse_x = bd.fwd(p, *[t[k] for k in INPUT_NAMES])
+    grads = bd.bwd(p, *[t[k] for k in INPUT_NAMES], o_c, o_x, lse_c, lse_x, t["do_c"], t["do_x"])
+    torch.cuda.synchronize()
+    return dict(zip(OUT_NAMES, (o_c, o_x, lse_c, lse_x) + tuple(grads)))
+
+
+def _rounding(spec):
+    return "bf16" if spec.dtype == "bf16" else None
+
+
+def oracle_full(spec, t, rounding=None):
+    lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start,
+                 spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks, spec.corr_block_ids)
+    orc = Oracle(lay, *[f64(t[k]) for k in INPUT_NAMES], *[f64(t[k]) for k in GRAD_NAMES],
+                 operand_rounding=rounding)
+    f = orc.forward()
+    g = orc.backward(O=np.concatenate([f[0], f[1]]), LSE=np.concatenate([f[2], f[3]], axis=1))
+    return dict(zip(OUT_NAMES, f + g))
+
+
+def metric(spec):
+    return rel_err if spec.dtype == "f32" else rms_err
+
+
+# fp32: max|x-y| / max|y| <= 1e-4 per output tensor.
+# bf16: max|x-y| / rms(y) per output tensor may exceed, by at most 2e-2, the
+# same measure of the oracle evaluated with bf16 operands and bf16 outputs
+# (Oracle(..., operand_rounding="bf16")): storing the exact result in bf16
+# alone already scores 0.02-0.15 on these heavy-tailed outputs.
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def compare(spec, got: dict, want: dict, names=OUT_NAMES, label="", ideal=None):
+    """Per output tensor: (error of the GPU result, error of the bf16-operand
+    oracle or 0) with the dtype's metric against the exact oracle."""
+    m = metric(spec)
+    errs = {}
+    for k in names:
+        if k not in want:
+            continue
+        g = got[k]
+        g = f64(g) if torch.is_tensor(g) else np.asarray(g, np.float64)
+        w = np.asarray(want[k], np.float64)
+        assert g.shape == w.shape, (k, g.shape, w.shape)
+        if w.size == 0:
+            continue
+        assert np.isfinite(g).all(), f"{label} {k}: non-finite values"
+        base = m(np.asarray(ideal[k], np.float64), w) if ideal is not None else 0.0
+        errs[k] = (m(g, w), base)
+        if spec.dtype == "bf16" and os.environ.get("BDATTN_METRICS_LOG"):
+            with open(os.environ["BDATTN_METRICS_LOG"], "a") as f:
+                f.write(json.dumps(dict(label=label, out=k, ideal=base, **bf16_metrics(g, w)))
+                        + "\n")
+    say(f"  {label} errors (gpu, bf16-operand oracle):",
+        {k: f"{v[0]:.2e},{v[1]:.2e}" for k, v in errs.items()})
+    return errs
+
+
+def assert_parity(spec, errs, label=""):
+    tol = TOL[spec.dtype]
+    bad = {k: v for k, v in errs.items() if not v[0] <= tol + v[1]}
+    assert not bad, f"{label}: errors above {tol} (+ bf16-operand oracle error): {bad}"
+
+
+# ------------------------------------------------------------ sub-problems
+def _sl(t, rows, heads=None):
+    x = t[rows[0]:rows[1]]
+    if heads is not None:
+        x = x[:, heads[0]:heads[1]]
+    return f64(x)
+
+
+def sub_clean_block(spec, t, b, g, rounding=None):
+    """Oracle for the clean query block with global id b, q heads of KV head g."""
+    B, G = spec.B, spec.H // spec.Hkv
+    r0 = b * B - spec.clean_q_start
+    hq = (g * G, (g + 1) * G)
+    hk = (g, g + 1)
+    lay = layout(B, G, 1, spec.d, B, b * B, (b + 1) * B, 0, corr_block_ids=[])
+    e = np.zeros((0, G, spec.d))
+    ek = np.zeros((0, 1, spec.d))
+    orc = Oracle(lay, _sl(t["q_c"], (r0, r0 + B), hq), _sl(t["k_c"], (0, (b + 1) * B), hk),
+                 _sl(t["v_c"], (0, (b + 1) * B), hk), e, ek, ek,
+                 _sl(t["do_c"], (r0, r0 + B), hq), e, operand_rounding=rounding)
+    O_c, _, L_c, _ = orc.forward()
+    dq_c, *_ = orc.backward()
+    return dict(rows=(r0, r0 + B), heads=hq, o_c=O_c, lse_c=L_c, dq_c=dq_c)
+
+
+def sub_corr_block(spec, t, j, g, rounding=None):
+    """Oracle for local corrupted block j (global id ids[j]), KV head g: its
+    O, LSE, dQ and its own dK/dV (seen by no other block)."""
+    B, G = spec.B, spec.H // spec.Hkv
+    bid = spec.corr_block_ids[j] if spec.corr_block_ids is not None else j
+    hq = (g * G, (g + 1) * G)
+    hk = (g, g + 1)
+    rows = (j * B, (j + 1) * B)
+    lay = layout(B, G, 1, spec.d, 0, 0, bid * B, 0, corr_block_ids=[bid])
+    e = np.zeros((0, G, spec.d))
+    orc = Oracle(lay, e, _sl(t["k_c"], (0, bid * B), hk), _sl(t["v_c"], (0, bid * B), hk),
+                 _sl(t["q_x"], rows, hq), _sl(t["k_x"], rows, hk), _sl(t["v_x"], rows, hk),
+                 e, _sl(t["do_x"], rows, hq), operand_rounding=rounding)
+    _, O_x, _, L_x = orc.forward()
+    _, dq_x, _, _, dk_x, dv_x = orc.backward()
+    return dict(rows=rows, heads=hq, kv=hk, o_x=O_x, lse_x=L_x, dq_x=dq_x, dk_x=dk_x, dv_x=dv_x)
+
+
+def sub_clean_keys(spec, t, kb, g, rounding=None):
+    """dK/dV of the clean keys of block kb (KV head g) from every query that
+    sees them: clean rows of blocks >= kb, corrupted blocks with id > kb."""
+    B, G = spec.B, spec.H // spec.Hkv
+    ids = list(spec.corr_block_ids) if spec.corr_block_ids is not None else \
+        list(range(spec.n_corr_blocks))
+    c0 = max(0, kb * B - spec.clean_q_start)
+    jx = [j for j, bid in enumerate(ids) if bid > kb]
+    hq = (g * G, (g + 1) * G)
+    hk = (g, g + 1)
+    nq = spec.n_clean_q - c0
+    lay = layout(B, G, 1, spec.d, nq, spec.clean_q_start + c0, spec.n_clean_kv, 0,
+                 corr_block_ids=[ids[j] for j in jx])
+    xr = np.concatenate([np.arange(j * B, (j + 1) * B) for j in jx]) if jx else \
+        np.zeros(0, np.int64)
+
+    def xs(name, heads):
+        x = t[name][torch.as_tensor(xr, device=t[name].device, dtype=torch.long)]
+        return f64(x[:, heads[0]:heads[1]])
+
+    orc = Oracle(lay, _sl(t["q_c"], (c0, spec.n_clean_q), hq),
+                 _sl(t["k_c"], (0, spec.n_clean_kv), hk), _sl(t["v_c"], (0, spec.n_clean_kv), hk),
+                 xs("q_x", hq), xs("k_x", hk), xs("v_x", hk),
+                 _sl(t["do_c"], (c0, spec.n_clean_q), hq), xs("do_x", hq),
+                 operand_rounding=rounding)
+    keys = orc.key_index(0, np.arange(kb * B, (kb + 1) * B))
+    dk, dv = orc.keys_backward(keys)
+    return dict(keys=(kb * B, (kb + 1) * B), kv=hk, dk_c=dk, dv_c=dv)

@@ -1,0 +1,193 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+declared symbol, host validation returns the documented codes, and the
+library's mask render and pair count agree with the independent oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_masked_attention_amd as bd
+from oracle import key_tokens, layout, query_tokens, visible
+from tests.test_oracle import read_golden
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "bdattn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(bdattn_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"bdattn_fwd", "bdattn_bwd", "bdattn_validate", "bdattn_workspace_size",
+            "bdattn_mask_render"} <= set(names)
+    L = ctypes.CDLL(bd.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert bd.version() == 1
+
+
+def test_status_strings():
+    for code in range(0, -7, -1):
+        assert bd.status_string(code) != "unknown status"
+    assert bd.status_string(-99) == "unknown status"
+
+
+def oracle_mask(p):
+    ids = None
+    if p.corr_block_ids:
+        ids = [p.corr_block_ids[i] for i in range(p.n_corr_blocks)]
+    lay = layout(p.B, p.H, p.Hkv, p.d, p.n_clean_q, p.clean_q_start, p.n_clean_kv,
+                 p.clean_kv_start, p.n_corr_blocks, ids)
+    qs, qb = query_tokens(lay)
+    ks, kb = key_tokens(lay)
+    return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :])
+
+
+CASES = [
+    dict(B=2, n_clean_q=8),
+    dict(B=1, n_clean_q=7),
+    dict(B=16, n_clean_q=256),
+    dict(B=32, n_clean_q=1056),
+    dict(B=7, n_clean_q=63),
+    dict(B=128, n_clean_q=384),
+    dict(B=4, n_clean_q=16, clean_q_start=32, n_clean_kv=64, corr_block_ids=[2, 5, 11, 15]),
+    dict(B=32, n_clean_q=0, n_clean_kv=2048, corr_block_ids=[0, 9, 33, 63]),
+    dict(B=8, n_clean_q=64, n_corr_blocks=0),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_mask_render_matches_oracle(case):
+    p = bd.problem(H=2, Hkv=1, d=32, dtype="bf16", **case)
+    assert bd.validate(p) == 0
+    got = bd.mask_render(p)
+    want = oracle_mask(p)
+    assert got.shape == want.shape and np.array_equal(got, want)
+    assert bd.visible_pairs(p) == int(want.sum())
+
+
+@pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt"])
+def test_mask_render_matches_hand_drawn_fixture(name):
+    prm, want = read_golden(name)
+    p = bd.problem(prm["B"], 1, 1, 32, "f32", prm["n_clean_q"], prm["clean_q_start"],
+                   prm["n_clean_kv"], corr_block_ids=prm["ids"])
+    assert np.array_equal(bd.mask_render(p), want)
+
+
+def test_visible_pairs_closed_forms_at_full_size():
+    """Pairs per head: L(L+B) for a full sequence (each stream L(L+B)/2);
+    the rank-15 share is the sum of B^2 (b+1) over its clean and corrupted
+    blocks."""
+    for spec in CONFIGS[:4]:
+        p = bd.from_spec(spec)
+        L, B = spec.n_clean_q, spec.B
+        assert bd.visible_pairs(p) == L * (L + B)
+    spec = CONFIGS[4]
+    p = bd.from_spec(spec)
+    B = spec.B
+    want = sum(B * B * (b + 1) for b in range(spec.clean_q_start // B,
+                                              (spec.clean_q_start + spec.n_clean_q) // B))
+    want += sum(B * B * (b + 1) for b in spec.corr_block_ids)
+    assert bd.visible_pairs(p) == want
+
+
+def _p(**kw):
+    base = dict(B=4, H=4, Hkv=2, d=32, dtype="bf16", n_clean_q=16)
+    base.update(kw)
+    return bd.problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=3, Hkv=2), -2),
+    (dict(B=0), -2),
+    (dict(d=64), -3),
+    (dict(dtype=bd.F32, d=128), -3),
+    (dict(n_clean_q=18), -2),
+    (dict(clean_q_start=2, n_clean_kv=20), -2),
+    (dict(n_clean_kv=12), -4),
+    (dict(clean_q_start=16, n_clean_kv=16), -4),
+    (dict(clean_kv_start=4, n_clean_kv=32), -4),
+    (dict(corr_block_ids=[3, 2]), -1),
+    (dict(corr_block_ids=[1, 1]), -1),
+    (dict(corr_block_ids=[-1, 2]), -1),
+    (dict(corr_block_ids=[0, 9]), -4),  # block 9 needs clean keys < 36
+    (dict(n_clean_q=-4), -2),
+])
+def test_validation_error_codes(kw, code):
+    p = _p(**kw)
+    assert bd.validate(p) == code
+    assert bd.lib().bdattn_last_error().decode() != ""
+
+
+def test_unknown_dtype_and_null_problem():
+    p = _p()
+    p.dtype = 7
+    assert bd.validate(p) == -1
+    assert bd.lib().bdattn_validate(None) == -1
+
+
+def test_workspace_size_and_launch_errors_without_gpu_work():
+    """Errors found on the host come back before anything is enqueued, so
+    they are testable without a GPU: bad pass, missing workspace, NULL or
+    misaligned tensor pointers."""
+    p = _p()
+    L = bd.lib()
+    n = ctypes.c_size_t(0)
+    assert L.bdattn_workspace_size(ctypes.byref(p), 2, ctypes.byref(n)) == -1
+    assert L.bdattn_workspace_size(ctypes.byref(p), 0, None) == -1
+    assert bd.workspace_size(p, 0) > 0 and bd.workspace_size(p, 1) > bd.workspace_size(p, 0)
+    vp = ctypes.c_void_p
+    good = vp(1 << 20)  # never dereferenced: every call below fails validation first
+    bad = vp((1 << 20) + 8)
+    args = [good] * 6 + [good, good, good, good]
+    # NULL q_c
+    assert L.bdattn_fwd(ctypes.byref(p), None, *args[1:], good, 1 << 30, None) == -1
+    # misaligned v_x
+    a2 = list(args)
+    a2[5] = bad
+    assert L.bdattn_fwd(ctypes.byref(p), *a2, good, 1 << 30, None) == -1
+    # workspace too small / missing / misaligned
+    assert L.bdattn_fwd(ctypes.byref(p), *args, good, 16, None) == -5
+    assert L.bdattn_fwd(ctypes.byref(p), *args, None, 1 << 30, None) == -5
+    assert L.bdattn_fwd(ctypes.byref(p), *args, vp((1 << 20) + 16), 1 << 30, None) == -5
+    bargs = [good] * 6 + [good] * 6 + [good] * 6
+    assert L.bdattn_bwd(ctypes.byref(p), *bargs, good, 16, None) == -5
+    bargs[13] = None  # dq_x
+    assert L.bdattn_bwd(ctypes.byref(p), *bargs, good, 1 << 40, None) == -1
+
+
+def test_plan_covers_every_visible_tile():
+    """The forward work list visits, for every query row tile, exactly the key
+    tiles holding a visible key; the backward list has one item per key tile
+    and KV head (so every dK/dV row is written)."""
+    for case in CASES:
+        p = bd.problem(H=4, Hkv=2, d=32, dtype="bf16", **case)
+        st = bd.plan_stats(p)
+        M = bd.mask_render(p)
+        nc, nkv, nx = int(p.n_clean_q), int(p.n_clean_kv), p.n_corr
+        R = st["fwd_rows_per_item"]
+        Gw = 4 * 32 // R
+        want_items, want_tiles = 0, 0
+        for s, (r0, n) in enumerate(((0, nc), (nc, nx))):
+            for t in range(0, n, R):
+                rows = M[r0 + t:r0 + min(n, t + R)]
+                vis = rows.any(0)
+                cl = np.flatnonzero(vis[:nkv])
+                ntiles = 0
+                if len(cl):
+                    ntiles += (cl.max() // 64) + 1  # clean keys swept from 0
+                xk = np.flatnonzero(vis[nkv:])
+                if len(xk):
+                    ntiles += (xk.max() - xk.min()) // 64 + 1
+                want_items += 1
+                want_tiles += ntiles
+        heads_groups = int(p.H) // Gw
+        assert st["fwd_items"] == want_items * heads_groups
+        assert st["fwd_tiles"] == want_tiles * heads_groups
+        kt = -(-nkv // 128) + -(-nx // 128)
+        assert st["bwd_items"] == kt * int(p.Hkv)

@@ -1,0 +1,223 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Tolerances: fp32 problems max|x-y|/max|y| <= 1e-4 per output tensor. bf16
+problems: max|x-y|/rms(y) per output tensor (O, LSE, dQ, dK, dV of each
+stream) at most 2e-2 above the same measure of the oracle evaluated with bf16
+operands and bf16 outputs (storing even the exact result in bf16 scores
+0.02-0.15 on these outputs, whose magnitudes vary by orders between rows).
+
+Small problems are compared element by element on every output. The five
+full-size workloads are compared on sampled query blocks, sampled corrupted
+blocks and the clean keys of late blocks (oracle sub-problems, see
+gpu_util), and every output element is checked against identities that hold
+at any size.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from tests._helpers import f64
+from tests.gpu_util import (OUT_NAMES, _rounding, assert_parity, compare, oracle_full,
+                            run_gpu, say, sub_clean_block, sub_clean_keys, sub_corr_block)
+from workloads import CONFIGS, Spec, make_inputs, small_spec
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def full_parity(spec, label):
+    _need_gpu()
+    say(f"[gpu] {label}: {spec}")
+    t = make_inputs(spec, device="cuda")
+    got = run_gpu(spec, t)
+    want = oracle_full(spec, t)
+    ideal = oracle_full(spec, t, "bf16") if spec.dtype == "bf16" else None
+    errs = compare(spec, got, want, label=label, ideal=ideal)
+    assert_parity(spec, errs, label)
+    return got, want
+
+
+SMALL = [
+    # fp32: the kernels' full logic at fp32 precision (1e-4)
+    ("f32_L256_B16", dict(L=256, B=16, H=2, Hkv=2, d=32, dtype="f32")),
+    ("f32_ragged_B8_G2", dict(L=200, B=8, H=4, Hkv=2, d=32, dtype="f32")),
+    ("f32_B1", dict(L=70, B=1, H=2, Hkv=1, d=32, dtype="f32")),
+    ("f32_B96", dict(L=288, B=96, H=4, Hkv=4, d=32, dtype="f32")),
+    ("f32_G3", dict(L=160, B=16, H=6, Hkv=2, d=32, dtype="f32")),
+    ("f32_share", dict(L=128, B=16, H=4, Hkv=1, d=32, dtype="f32", n_clean_q=64,
+                        clean_q_start=64, n_clean_kv=128, corr_block_ids=[1, 3, 5, 7])),
+    # bf16, head dim 128
+    ("bf16_L1056_B32_G4", dict(L=1056, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5)),
+    ("bf16_L512_B16_G1", dict(L=512, B=16, H=4, Hkv=4, d=128, dtype="bf16", std=0.5)),
+    ("bf16_L640_B128_G8", dict(L=640, B=128, H=8, Hkv=1, d=128, dtype="bf16", std=0.5)),
+    ("bf16_L300_B5_G2", dict(L=300, B=5, H=4, Hkv=2, d=128, dtype="bf16", std=0.5)),
+    ("bf16_B1", dict(L=96, B=1, H=2, Hkv=2, d=128, dtype="bf16", std=0.5)),
+    ("bf16_L768_B256", dict(L=768, B=256, H=4, Hkv=1, d=128, dtype="bf16", std=0.5)),
+    ("bf16_d32_G3", dict(L=384, B=32, H=6, Hkv=2, d=32, dtype="bf16", std=0.5)),
+    ("bf16_outliers", dict(L=1024, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                           outlier_frac=0.01, outlier_mult=8.0)),
+    # one rank's share: offset clean queries, long clean buffer, strided blocks
+    ("bf16_share_strided", dict(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                n_clean_q=128, clean_q_start=384, n_clean_kv=512,
+                                corr_block_ids=list(range(3, 16, 4)))),
+    # dual-end pairing of blocks b and nb-1-b
+    ("bf16_share_dualend", dict(L=256, B=16, H=4, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                n_clean_q=64, clean_q_start=64, n_clean_kv=256,
+                                corr_block_ids=[1, 5, 10, 14])),
+    # a rank holding no clean queries, and one holding no corrupted blocks
+    ("bf16_no_clean_q", dict(L=0, B=32, H=4, Hkv=2, d=128, dtype="bf16", std=0.5,
+                             n_clean_q=0, n_clean_kv=640, corr_block_ids=[0, 7, 20])),
+    ("bf16_no_corrupted", dict(L=320, B=32, H=4, Hkv=2, d=128, dtype="bf16", std=0.5,
+                               corr_block_ids=[])),
+]
+
+
+@pytest.mark.parametrize("label,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_full_parity(label, kw):
+    full_parity(small_spec(name=label, seed=zlib.crc32(label.encode()) % 10000, **kw), label)
+
+
+def test_tiny_workload_full_parity():
+    """The tiny fp32 workload (clean 256 + corrupted 256, B=16, H=Hkv=2, d=32)."""
+    full_parity(CONFIGS[0], CONFIGS[0].name)
+
+
+def test_repeat_calls_and_determinism():
+    """Forward is bitwise repeatable; the backward's dK/dV are written once
+    per key (bitwise repeatable); dQ uses atomics (within tolerance)."""
+    _need_gpu()
+    spec = small_spec(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=3)
+    t = make_inputs(spec, device="cuda")
+    a = run_gpu(spec, t)
+    b = run_gpu(spec, t)
+    for k in ("o_c", "o_x", "lse_c", "lse_x", "dk_c", "dv_c", "dk_x", "dv_x"):
+        assert torch.equal(a[k], b[k]), k
+    for k in ("dq_c", "dq_x"):
+        d = (a[k].float() - b[k].float()).abs().max().item()
+        assert d <= 2e-2 * a[k].float().pow(2).mean().sqrt().item()
+
+
+def test_outputs_fully_overwritten():
+    """NaN-poisoned output buffers are overwritten everywhere (including
+    clean keys no local query sees, which get zero gradients)."""
+    _need_gpu()
+    import block_masked_attention_amd as bd
+    spec = small_spec(L=256, B=32, H=4, Hkv=2, d=128, dtype="bf16", std=0.5, n_clean_q=64,
+                      clean_q_start=64, n_clean_kv=256, corr_block_ids=[2, 3], seed=5)
+    t = make_inputs(spec, device="cuda")
+    p = bd.from_spec(spec)
+    nan = lambda x: torch.full_like(x, float("nan"))
+    o = [nan(t["q_c"]), nan(t["q_x"]),
+         torch.full((spec.H, spec.n_clean_q), float("nan"), device="cuda"),
+         torch.full((spec.H, spec.n_corr), float("nan"), device="cuda")]
+    o_c, o_x, lse_c, lse_x = bd.fwd(p, *[t[k] for k in ("q_c", "k_c", "v_c", "q_x", "k_x", "v_x")],
+                                    out=o)
+    g = [nan(t["q_c"]), nan(t["q_x"]), nan(t["k_c"]), nan(t["v_c"]), nan(t["k_x"]), nan(t["v_x"])]
+    dq_c, dq_x, dk_c, dv_c, dk_x, dv_x = bd.bwd(
+        p, *[t[k] for k in ("q_c", "k_c", "v_c", "q_x", "k_x", "v_x")], o_c, o_x, lse_c, lse_x,
+        t["do_c"], t["do_x"], out=g)
+    torch.cuda.synchronize()
+    for x in (o_c, o_x, lse_c, lse_x, dq_c, dq_x, dk_c, dv_c, dk_x, dv_x):
+        assert torch.isfinite(x).all()
+    # clean keys past every local query's prefix (positions >= 128) are unseen
+    assert (dk_c[128:] == 0).all() and (dv_c[128:] == 0).all()
+
+
+# ------------------------------------------------------------- full size
+def _identities(spec, t, got):
+    """Identities of softmax attention that hold at any size, per KV head:
+    sum_j dV_j = sum_i,h dO_i;  sum_j <dV_j, v_j> = sum_i <dO_i, O_i>;
+    sum_i <dQ_i, q_i> = sum_j <dK_j, k_j>."""
+    G = spec.H // spec.Hkv
+    d = lambda x: x.double()
+    for g in range(spec.Hkv):
+        hq = slice(g * G, (g + 1) * G)
+        dv = torch.cat([d(got["dv_c"][:, g]), d(got["dv_x"][:, g])])
+        do = torch.cat([d(t["do_c"][:, hq]), d(t["do_x"][:, hq])]).reshape(-1, spec.d)
+        lhs, rhs = dv.sum(0), do.sum(0)
+        tol = 2e-2 * dv.pow(2).sum(0).sqrt() + 1e-3 * do.abs().sum(0).sqrt()
+        assert ((lhs - rhs).abs() <= tol).all(), f"sum dV identity, kv head {g}"
+        v = torch.cat([d(t["v_c"][:, g]), d(t["v_x"][:, g])])
+        o = torch.cat([d(got["o_c"][:, hq]), d(got["o_x"][:, hq])]).reshape(-1, spec.d)
+        a1, b1 = (dv * v).sum(), (do * o).sum()
+        assert abs(a1 - b1) <= 2e-2 * (dv * v).abs().sum() ** 0.5 * 10 + 1e-2 * abs(b1), \
+            f"<dV,v> identity, kv head {g}: {a1.item()} vs {b1.item()}"
+        q = torch.cat([d(t["q_c"][:, hq]), d(t["q_x"][:, hq])]).reshape(-1, spec.d)
+        dq = torch.cat([d(got["dq_c"][:, hq]), d(got["dq_x"][:, hq])]).reshape(-1, spec.d)
+        k = torch.cat([d(t["k_c"][:, g]), d(t["k_x"][:, g])])
+        dk = torch.cat([d(got["dk_c"][:, g]), d(got["dk_x"][:, g])])
+        a2, b2 = (dq * q).sum(), (dk * k).sum()
+        scale = max((dq * q).abs().sum().item(), (dk * k).abs().sum().item())
+        assert abs(a2 - b2) <= 2e-2 * scale ** 0.5 * 10 + 1e-2 * max(abs(a2), abs(b2)), \
+            f"<dQ,q> = <dK,k> identity, kv head {g}: {a2.item()} vs {b2.item()}"
+
+
+def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
+    B = spec.B
+    rng = np.random.default_rng(spec.seed)
+    cb0, cb1 = spec.clean_q_start // B, (spec.clean_q_start + spec.n_clean_q) // B
+    clean_blocks = sorted({cb0, cb1 - 1} | set(rng.integers(cb0, cb1, n_blocks).tolist()))
+    corr = sorted({0, spec.n_corr_blocks - 1} |
+                  set(rng.integers(0, spec.n_corr_blocks, n_blocks).tolist()))
+    key_blocks = [cb1 - 1, cb1 - 3]
+    want = {k: [] for k in OUT_NAMES}
+    have = {k: [] for k in OUT_NAMES}
+    for g in kv_groups:
+        for b in clean_blocks:
+            say(f"  oracle clean block {b}, kv head {g}")
+            r = sub_clean_block(spec, t, b, g, rounding)
+            (r0, r1), (h0, h1) = r["rows"], r["heads"]
+            for k in ("o_c", "dq_c"):
+                want[k].append(r[k].ravel())
+                have[k].append(f64(got[k][r0:r1, h0:h1]).ravel())
+            want["lse_c"].append(r["lse_c"].ravel())
+            have["lse_c"].append(f64(got["lse_c"][h0:h1, r0:r1]).ravel())
+        for j in corr:
+            say(f"  oracle corrupted block {j}, kv head {g}")
+            r = sub_corr_block(spec, t, j, g, rounding)
+            (r0, r1), (h0, h1), (k0, k1) = r["rows"], r["heads"], r["kv"]
+            for k in ("o_x", "dq_x"):
+                want[k].append(r[k].ravel())
+                have[k].append(f64(got[k][r0:r1, h0:h1]).ravel())
+            want["lse_x"].append(r["lse_x"].ravel())
+            have["lse_x"].append(f64(got["lse_x"][h0:h1, r0:r1]).ravel())
+            for k in ("dk_x", "dv_x"):
+                want[k].append(r[k].ravel())
+                have[k].append(f64(got[k][r0:r1, k0:k1]).ravel())
+        for kb in key_blocks:
+            say(f"  oracle clean keys of block {kb}, kv head {g}")
+            r = sub_clean_keys(spec, t, kb, g, rounding)
+            (a0, a1), (k0, k1) = r["keys"], r["kv"]
+            for k in ("dk_c", "dv_c"):
+                want[k].append(r[k].ravel())
+                have[k].append(f64(got[k][a0:a1, k0:k1]).ravel())
+    want = {k: np.concatenate(v) for k, v in want.items() if v}
+    have = {k: np.concatenate(v) for k, v in have.items() if v}
+    return have, want
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4], ids=[c.name for c in CONFIGS])
+def test_workload_sampled_parity(idx):
+    """Each of the five workloads at full size, launched as the benchmark
+    launches it."""
+    _need_gpu()
+    spec = CONFIGS[idx]
+    say(f"[gpu] workload {spec.name}: {spec.description}")
+    t = make_inputs(spec, device="cuda")
+    got = run_gpu(spec, t)
+    for k, v in got.items():
+        assert torch.isfinite(v).all(), f"{k} has non-finite values"
+    _identities(spec, t, got)
+    groups = (0,) if spec.Hkv == 1 else (0, spec.Hkv - 1)
+    have, want = _sampled(spec, t, got, kv_groups=groups)
+    ideal = None
+    if spec.dtype == "bf16":
+        _, ideal = _sampled(spec, t, got, kv_groups=groups, rounding="bf16")
+    errs = compare(spec, have, want, names=list(want), label=spec.name, ideal=ideal)
+    assert_parity(spec, errs, spec.name)

@@ -425,3 +425,39 @@ def test_missing_clean_coverage_is_rejected():
         layout(2, 1, 1, 4, 4, 4, 6)  # queries at 4..7 need clean keys up to 8
     with pytest.raises(ValueError):
         layout(2, 1, 1, 4, 4, 0, 8, corr_block_ids=[5])  # block 5 needs keys < 10
+
+
+# -------------------------------------------------- bf16 operand rounding mode
+def test_round_bf16_matches_library_cast():
+    from oracle import round_bf16
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(10000) * 10.0 ** rng.integers(-6, 6, 10000),
+                        [0.0, -0.0, 1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8),
+                         65504.0, 1e-30, 3.0e38]])
+    want = torch.tensor(x, dtype=torch.float32).bfloat16().double().numpy()
+    assert np.array_equal(round_bf16(x), want)
+
+
+def test_operand_rounding_mode_is_the_exact_oracle_plus_roundings():
+    """Exact mode is unchanged; bf16 mode stays within bf16 rounding of the
+    exact result and its outputs are bf16 values."""
+    from oracle import round_bf16
+    lay = layout(4, 4, 2, 8, 32)
+    t = make(lay, seed=41, scale=0.5)
+    for k in t:  # inputs as a bf16 kernel receives them
+        t[k] = round_bf16(t[k])
+    ex = oracle_of(lay, t)
+    bf = Oracle(lay, t["q_c"], t["k_c"], t["v_c"], t["q_x"], t["k_x"], t["v_x"], t["do_c"],
+                t["do_x"], operand_rounding="bf16")
+    e = ex.forward() + ex.backward()
+    b = bf.forward() + bf.backward()
+    for i, (x, y) in enumerate(zip(b, e)):
+        if i in (2, 3):  # LSE is not rounded
+            np.testing.assert_allclose(x, y, rtol=1e-14)
+            continue
+        assert np.array_equal(round_bf16(x), x)
+        err = np.max(np.abs(x - y)) / np.max(np.abs(y))
+        assert 0 < err < 2e-2, (i, err)
+    with pytest.raises(ValueError):
+        Oracle(lay, t["q_c"], t["k_c"], t["v_c"], t["q_x"], t["k_x"], t["v_x"],
+               operand_rounding="fp8")
