@@ -180,7 +180,7 @@ class Oracle:
     """
 
     # rows x columns of one chunk's dense score matrix (bounded memory only)
-    CHUNK_ELEMS = 1 << 23
+    CHUNK_ELEMS = 1 << 24
 
     def __init__(self, lay: Layout, q_c, k_c, v_c, q_x, k_x, v_x, do_c=None, do_x=None,
                  operand_rounding=None):
@@ -189,8 +189,12 @@ class Oracle:
             raise ValueError("operand_rounding must be None or 'bf16'")
         self.rd = round_bf16 if operand_rounding == "bf16" else _ident
         self.Q = np.concatenate([_f64(q_c), _f64(q_x)]).reshape(lay.nq, lay.H, lay.d)
-        self.K = np.concatenate([_f64(k_c), _f64(k_x)]).reshape(lay.nk, lay.Hkv, lay.d)
-        self.V = np.concatenate([_f64(v_c), _f64(v_x)]).reshape(lay.nk, lay.Hkv, lay.d)
+        K = np.concatenate([_f64(k_c), _f64(k_x)]).reshape(lay.nk, lay.Hkv, lay.d)
+        V = np.concatenate([_f64(v_c), _f64(v_x)]).reshape(lay.nk, lay.Hkv, lay.d)
+        # keys of each KV head as one contiguous [nk, d] array
+        self.Kh = [np.ascontiguousarray(K[:, g]) for g in range(lay.Hkv)]
+        self.Vh = [np.ascontiguousarray(V[:, g]) for g in range(lay.Hkv)]
+        del K, V
         if do_c is not None:
             self.dO = np.concatenate([_f64(do_c), _f64(do_x)]).reshape(lay.nq, lay.H, lay.d)
         else:
@@ -206,16 +210,24 @@ class Oracle:
         return visible(self.qs[qidx, None], self.qb[qidx, None],
                        self.ks[None, kidx], self.kb[None, kidx])
 
+    @staticmethod
+    def _columns(cols):
+        """Index of the visible key columns: a slice when they are one
+        contiguous run (a view, no copy), else the index array."""
+        if len(cols) and cols[-1] - cols[0] + 1 == len(cols):
+            return slice(int(cols[0]), int(cols[-1]) + 1)
+        return cols
+
     def _chunks(self, qidx):
         qidx = np.asarray(qidx, dtype=np.int64)
         step = max(1, min(2048, self.CHUNK_ELEMS // max(1, self.lay.nk)))
         for s in range(0, len(qidx), step):
             yield s, qidx[s:s + step]
 
-    def _scores(self, rows, cols, Mc, h):
-        """Masked scores S = scale * q k^T, -inf where not visible."""
-        g = h // self.lay.G
-        S = self.lay.scale * (self.Q[rows, h] @ self.K[cols, g].T)
+    def _scores(self, rows, Kg, Mc, h):
+        """Masked scores S = scale * q k^T over the gathered keys Kg of the
+        row's KV head, -inf where not visible."""
+        S = self.lay.scale * (self.Q[rows, h] @ Kg.T)
         S[~Mc] = -np.inf
         return S
 
@@ -232,14 +244,16 @@ class Oracle:
                 raise ValueError("a query row sees no key")
             cols = np.flatnonzero(M.any(axis=0))
             Mc = M[:, cols]
-            for h in range(lay.H):
-                g = h // lay.G
-                S = self._scores(rows, cols, Mc, h)
-                m = S.max(axis=1)
-                E = np.exp(S - m[:, None])
-                l = E.sum(axis=1)
-                LSE[h, s:s + len(rows)] = m + np.log(l)
-                O[s:s + len(rows), h] = (self.rd(E) @ self.V[cols, g]) / l[:, None]
+            cs = self._columns(cols)
+            for g in range(lay.Hkv):
+                Kg, Vg = self.Kh[g][cs], self.Vh[g][cs]  # visible keys of KV head g
+                for h in range(g * lay.G, (g + 1) * lay.G):
+                    S = self._scores(rows, Kg, Mc, h)
+                    m = S.max(axis=1)
+                    E = np.exp(S - m[:, None])
+                    l = E.sum(axis=1)
+                    LSE[h, s:s + len(rows)] = m + np.log(l)
+                    O[s:s + len(rows), h] = (self.rd(E) @ Vg) / l[:, None]
         return self.rd(O), LSE
 
     def forward(self):
@@ -282,15 +296,21 @@ class Oracle:
             if len(cols) == 0:
                 continue
             Mc = M[:, cols]
-            for h in range(lay.H):
-                g = h // lay.G
-                S = self._scores(rows, cols, Mc, h)
-                P = np.exp(S - LSE[h, sl][:, None])  # exp(-inf) = 0 off the mask
-                dP = self.dO[rows, h] @ self.V[cols, g].T
-                dS = self.rd(P * (dP - D[sl, h][:, None]))
-                dQ[sl, h] = lay.scale * (dS @ self.K[cols, g])
-                dK[cols, g] += lay.scale * (dS.T @ self.Q[rows, h])
-                dV[cols, g] += self.rd(P).T @ self.dO[rows, h]
+            cs = self._columns(cols)
+            for g in range(lay.Hkv):
+                Kg, Vg = self.Kh[g][cs], self.Vh[g][cs]  # visible keys of KV head g
+                dKg = np.zeros_like(Kg)
+                dVg = np.zeros_like(Vg)
+                for h in range(g * lay.G, (g + 1) * lay.G):
+                    S = self._scores(rows, Kg, Mc, h)
+                    P = np.exp(S - LSE[h, sl][:, None])  # exp(-inf) = 0 off the mask
+                    dP = self.dO[rows, h] @ Vg.T
+                    dS = self.rd(P * (dP - D[sl, h][:, None]))
+                    dQ[sl, h] = lay.scale * (dS @ Kg)
+                    dKg += lay.scale * (dS.T @ self.Q[rows, h])
+                    dVg += self.rd(P).T @ self.dO[rows, h]
+                dK[cs, g] += dKg
+                dV[cs, g] += dVg
         return self.rd(dQ), self.rd(dK), self.rd(dV)
 
     def backward(self, O=None, LSE=None):

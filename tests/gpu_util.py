@@ -103,6 +103,22 @@ def _sl(t, rows, heads=None):
     return f64(x)
 
 
+# float64 host copies of whole clean K/V heads, shared by the sub-problems of
+# one sampled check (each of them reads a long prefix of the same keys)
+_KV_HOST = {}
+
+
+def _kv(t, name, rows, g):
+    key = (name, id(t[name]), g)
+    if key not in _KV_HOST:
+        _KV_HOST[key] = f64(t[name][:, g:g + 1])
+    return _KV_HOST[key][rows[0]:rows[1]]
+
+
+def clear_host_cache():
+    _KV_HOST.clear()
+
+
 def sub_clean_block(spec, t, b, g, rounding=None):
     """Oracle for the clean query block with global id b, q heads of KV head g."""
     B, G = spec.B, spec.H // spec.Hkv
@@ -112,11 +128,11 @@ def sub_clean_block(spec, t, b, g, rounding=None):
     lay = layout(B, G, 1, spec.d, B, b * B, (b + 1) * B, 0, corr_block_ids=[])
     e = np.zeros((0, G, spec.d))
     ek = np.zeros((0, 1, spec.d))
-    orc = Oracle(lay, _sl(t["q_c"], (r0, r0 + B), hq), _sl(t["k_c"], (0, (b + 1) * B), hk),
-                 _sl(t["v_c"], (0, (b + 1) * B), hk), e, ek, ek,
+    orc = Oracle(lay, _sl(t["q_c"], (r0, r0 + B), hq), _kv(t, "k_c", (0, (b + 1) * B), g),
+                 _kv(t, "v_c", (0, (b + 1) * B), g), e, ek, ek,
                  _sl(t["do_c"], (r0, r0 + B), hq), e, operand_rounding=rounding)
-    O_c, _, L_c, _ = orc.forward()
-    dq_c, *_ = orc.backward()
+    O_c, O_x, L_c, L_x = orc.forward()
+    dq_c, *_ = orc.backward(O=np.concatenate([O_c, O_x]), LSE=np.concatenate([L_c, L_x], axis=1))
     return dict(rows=(r0, r0 + B), heads=hq, o_c=O_c, lse_c=L_c, dq_c=dq_c)
 
 
@@ -130,11 +146,12 @@ def sub_corr_block(spec, t, j, g, rounding=None):
     rows = (j * B, (j + 1) * B)
     lay = layout(B, G, 1, spec.d, 0, 0, bid * B, 0, corr_block_ids=[bid])
     e = np.zeros((0, G, spec.d))
-    orc = Oracle(lay, e, _sl(t["k_c"], (0, bid * B), hk), _sl(t["v_c"], (0, bid * B), hk),
+    orc = Oracle(lay, e, _kv(t, "k_c", (0, bid * B), g), _kv(t, "v_c", (0, bid * B), g),
                  _sl(t["q_x"], rows, hq), _sl(t["k_x"], rows, hk), _sl(t["v_x"], rows, hk),
                  e, _sl(t["do_x"], rows, hq), operand_rounding=rounding)
-    _, O_x, _, L_x = orc.forward()
-    _, dq_x, _, _, dk_x, dv_x = orc.backward()
+    O_c, O_x, L_c, L_x = orc.forward()
+    _, dq_x, _, _, dk_x, dv_x = orc.backward(O=np.concatenate([O_c, O_x]),
+                                             LSE=np.concatenate([L_c, L_x], axis=1))
     return dict(rows=rows, heads=hq, kv=hk, o_x=O_x, lse_x=L_x, dq_x=dq_x, dk_x=dk_x, dv_x=dv_x)
 
 
@@ -159,7 +176,7 @@ def sub_clean_keys(spec, t, kb, g, rounding=None):
         return f64(x[:, heads[0]:heads[1]])
 
     orc = Oracle(lay, _sl(t["q_c"], (c0, spec.n_clean_q), hq),
-                 _sl(t["k_c"], (0, spec.n_clean_kv), hk), _sl(t["v_c"], (0, spec.n_clean_kv), hk),
+                 _kv(t, "k_c", (0, spec.n_clean_kv), g), _kv(t, "v_c", (0, spec.n_clean_kv), g),
                  xs("q_x", hq), xs("k_x", hk), xs("v_x", hk),
                  _sl(t["do_c"], (c0, spec.n_clean_q), hq), xs("do_x", hq),
                  operand_rounding=rounding)

@@ -12,6 +12,7 @@ blocks and the clean keys of late blocks (oracle sub-problems, see
 gpu_util), and every output element is checked against identities that hold
 at any size.
 """
+import time
 import zlib
 
 import numpy as np
@@ -19,7 +20,8 @@ import pytest
 import torch
 
 from tests._helpers import f64
-from tests.gpu_util import (OUT_NAMES, _rounding, assert_parity, compare, oracle_full,
+from tests.gpu_util import (OUT_NAMES, _rounding, assert_parity, clear_host_cache, compare,
+                            oracle_full,
                             run_gpu, say, sub_clean_block, sub_clean_keys, sub_corr_block)
 from workloads import CONFIGS, Spec, make_inputs, small_spec
 
@@ -160,6 +162,8 @@ def _identities(spec, t, got):
 
 def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
     B = spec.B
+    if spec.n_clean_kv > 100_000:
+        n_blocks = 1  # each sampled block carries a prefix of 10^5+ keys
     rng = np.random.default_rng(spec.seed)
     cb0, cb1 = spec.clean_q_start // B, (spec.clean_q_start + spec.n_clean_q) // B
     clean_blocks = sorted({cb0, cb1 - 1} | set(rng.integers(cb0, cb1, n_blocks).tolist()))
@@ -197,6 +201,7 @@ def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
             for k in ("dk_c", "dv_c"):
                 want[k].append(r[k].ravel())
                 have[k].append(f64(got[k][a0:a1, k0:k1]).ravel())
+    clear_host_cache()
     want = {k: np.concatenate(v) for k, v in want.items() if v}
     have = {k: np.concatenate(v) for k, v in have.items() if v}
     return have, want
@@ -209,15 +214,20 @@ def test_workload_sampled_parity(idx):
     _need_gpu()
     spec = CONFIGS[idx]
     say(f"[gpu] workload {spec.name}: {spec.description}")
+    t0 = time.perf_counter()
     t = make_inputs(spec, device="cuda")
     got = run_gpu(spec, t)
+    say(f"  inputs + fwd + bwd on the GPU: {time.perf_counter() - t0:.1f} s")
     for k, v in got.items():
         assert torch.isfinite(v).all(), f"{k} has non-finite values"
     _identities(spec, t, got)
+    say(f"  identities checked: {time.perf_counter() - t0:.1f} s")
     groups = (0,) if spec.Hkv == 1 else (0, spec.Hkv - 1)
     have, want = _sampled(spec, t, got, kv_groups=groups)
+    say(f"  exact oracle samples: {time.perf_counter() - t0:.1f} s")
     ideal = None
     if spec.dtype == "bf16":
         _, ideal = _sampled(spec, t, got, kv_groups=groups, rounding="bf16")
+        say(f"  bf16-operand oracle samples: {time.perf_counter() - t0:.1f} s")
     errs = compare(spec, have, want, names=list(want), label=spec.name, ideal=ideal)
     assert_parity(spec, errs, spec.name)
