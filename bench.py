@@ -26,7 +26,7 @@ if ROOT not in sys.path:
 METRIC = "bdattn fwd+bwd useful TFLOP/s at 256K ctx; % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_bwd_256k.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bdattn_256k_hbm_traffic.md")
 
 
 def log(*a):
@@ -42,15 +42,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch of the backward key-tile kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source
-    and this workload; else None."""
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source and this workload;
+    else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     txt = open(TRAFFIC_FILE).read()
     m = {k: v for k, v in re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M)}
-    if m.get("kernel_source") != kernel_source_hash() or m.get("workload") != workload:
+    if (m.get("kernel_source") != kernel_source_hash() or m.get("workload") != workload
+            or m.get("kernel") != kernel):
         return None
     try:
         return float(m["hbm_bytes_per_launch"])
@@ -205,18 +206,24 @@ def main():
     ms_step = (t1 - t0) * 1e3 / max(1, args.steps)
     value = useful_step / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
-    fwd_ms = prof["fwd_ms"] / max(1, prof["fwd_launches"])
-    bwd_ms = prof["bwd_ms"] / max(1, prof["bwd_launches"])
-    fwd_flops = 4.0 * d * H * pairs
-    bwd_flops = 8.0 * d * H * pairs
-    dom = "bwd" if bwd_ms >= fwd_ms else "fwd"
-    dom_ms = bwd_ms if dom == "bwd" else fwd_ms
-    achieved = (bwd_flops if dom == "bwd" else fwd_flops) / (dom_ms * 1e-3) / 1e12
-    traffic = read_traffic(spec.name) if dom == "bwd" else None
+    # useful flops per visible pair and q head of each kernel (12d in total:
+    # QK^T, PV forward; dP, dV, dK in the dK/dV kernel; dQ in the dQ kernel)
+    # and the MFMA flops it executes (recomputed QK^T and dP included)
+    useful_d = {"fwd": 4, "bwd_dq": 2, "bwd_dkdv": 6}
+    executed_d = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+    kern = {}
+    for k, r in prof.items():
+        ms = r["ms"] / max(1, r["launches"])
+        kern[k] = dict(ms=round(ms, 3),
+                       useful_tflops=round(useful_d[k] * d * H * pairs / (ms * 1e-3) / 1e12, 1),
+                       executed_tflops=round(executed_d[k] * d * H * pairs / (ms * 1e-3) / 1e12, 1))
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    achieved = kern[dom]["useful_tflops"]
+    traffic = read_traffic(spec.name, dom)
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
-        f"({100 * value / peak:.1f}% of {peak} peak); fwd kernel {fwd_ms:.2f} ms "
-        f"({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s), bwd key-tile kernel {bwd_ms:.2f} ms "
-        f"({bwd_flops / bwd_ms / 1e9:.1f} TFLOP/s)")
+        f"({100 * value / peak:.1f}% of {peak} peak); " +
+        ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
+                  f"executed TFLOP/s)" for k, v in kern.items()))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -242,14 +249,11 @@ def main():
                    "Hkv": Hkv, "d": d, "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful_step, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),
-        "kernels": {"fwd_ms": round(fwd_ms, 3), "bwd_keytile_ms": round(bwd_ms, 3),
-                    "fwd_tflops": round(fwd_flops / fwd_ms / 1e9, 1),
-                    "bwd_keytile_tflops": round(bwd_flops / bwd_ms / 1e9, 1),
-                    "other_ms": round(ms_step - fwd_ms - bwd_ms, 3)},
-        "roofline": {"kernel": "bwd_kernel (key-tile backward)" if dom == "bwd" else "fwd_kernel",
-                     "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic},
+        "kernels": dict(kern, other_ms=round(ms_step - sum(v["ms"] for v in kern.values()), 3)),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "flops_per_pair_head": f"{useful_d[dom]}*d useful "
+                                            f"({executed_d[dom]}*d executed)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -130,8 +130,6 @@ def lib() -> ctypes.CDLL:
                              [vp, ctypes.c_size_t, vp])
     L.bdattn_profile_enable.argtypes = [ctypes.c_int]
     L.bdattn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
-                                      ctypes.POINTER(ctypes.c_int64),
-                                      ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("bdattn_validate", "bdattn_workspace_size", "bdattn_mask_render",
                  "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_bwd",
@@ -187,19 +185,22 @@ def plan_stats(p: Problem) -> dict:
     return dict(zip(keys, list(out)))
 
 
+PROFILED_KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")
+
+
 def profile_enable(on: bool = True) -> None:
-    """Record HIP events around the main forward / backward kernels."""
+    """Record HIP events around the forward kernel and the backward's dQ and
+    dK/dV kernels, on the stream each call is enqueued on."""
     _check(lib().bdattn_profile_enable(1 if on else 0), "profile_enable")
 
 
 def profile_read() -> dict:
-    """Wait for the recorded events; milliseconds and launch counts of the
-    forward kernel and the backward key-tile kernel since the last read."""
-    fm, fn = ctypes.c_double(0), ctypes.c_int64(0)
-    bm, bn = ctypes.c_double(0), ctypes.c_int64(0)
-    _check(lib().bdattn_profile_read(ctypes.byref(fm), ctypes.byref(fn), ctypes.byref(bm),
-                                     ctypes.byref(bn)), "profile_read")
-    return dict(fwd_ms=fm.value, fwd_launches=fn.value, bwd_ms=bm.value, bwd_launches=bn.value)
+    """Wait for the recorded events; per kernel ("fwd", "bwd_dq", "bwd_dkdv")
+    the summed milliseconds and the number of launches since the last read."""
+    ms = (ctypes.c_double * 3)()
+    n = (ctypes.c_int64 * 3)()
+    _check(lib().bdattn_profile_read(ms, n), "profile_read")
+    return {k: dict(ms=ms[i], launches=n[i]) for i, k in enumerate(PROFILED_KERNELS)}
 
 
 # ------------------------------------------------------------------ torch side

@@ -82,10 +82,10 @@ int check_ptr(const void* p, int64_t elems, const char* name) {
   return BDATTN_OK;
 }
 
-// Copy the corrupted block ids and the work list (staged once in pinned host
+// Copy the corrupted block ids and the work lists (staged once in pinned host
 // memory) into the workspace head, asynchronously on the caller's stream.
 int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t s) {
-  const size_t bytes = w.items + w.items_bytes;
+  const size_t bytes = w.staged;
   void* src = nullptr;
   {
     std::lock_guard<std::mutex> lock(e->mu);
@@ -96,10 +96,8 @@ int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t 
       memset(h, 0, bytes);
       const bdattn::Plan& plan = e->plan;
       memcpy((char*)h + w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t));
-      if (pass == 0)
-        memcpy((char*)h + w.items, plan.fwd.data(), w.items_bytes);
-      else
-        memcpy((char*)h + w.items, plan.bwd.data(), w.items_bytes);
+      memcpy((char*)h + w.q_items, plan.fwd.data(), w.q_items_bytes);
+      if (pass == 1) memcpy((char*)h + w.kv_items, plan.bwd.data(), w.kv_items_bytes);
       e->staged[pass] = h;
       e->staged_bytes[pass] = bytes;
     }
@@ -110,23 +108,35 @@ int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t 
   return BDATTN_OK;
 }
 
-// Benchmark instrumentation: per-thread list of (pass, events) recorded by
-// the launches while profiling is on.
+// Benchmark instrumentation: per-thread list of (kernel index, events)
+// recorded by the launches while profiling is on. Kernel 0 = forward,
+// 1 = backward dQ, 2 = backward dK/dV.
+constexpr int kProfKernels = 3;
 struct Prof {
   bool on = false;
   std::vector<std::pair<int, bdattn::KernelEvents>> recs;
 };
 thread_local Prof g_prof;
 
-bdattn::KernelEvents prof_events(int pass) {
-  bdattn::KernelEvents ev;
-  if (!g_prof.on) return ev;
-  if (hipEventCreate(&ev.start) != hipSuccess) return bdattn::KernelEvents();
-  if (hipEventCreate(&ev.stop) != hipSuccess) {
-    hipEventDestroy(ev.start);
-    return bdattn::KernelEvents();
+// Fills ev[0..n-1] with fresh events for kernels first..first+n-1; returns
+// ev, or nullptr when profiling is off or an event cannot be created.
+const bdattn::KernelEvents* prof_events(int first, int n, bdattn::KernelEvents* ev) {
+  if (!g_prof.on) return nullptr;
+  for (int i = 0; i < n; ++i) {
+    bool ok = hipEventCreate(&ev[i].start) == hipSuccess;
+    if (ok && hipEventCreate(&ev[i].stop) != hipSuccess) {
+      (void)hipEventDestroy(ev[i].start);
+      ok = false;
+    }
+    if (!ok) {
+      for (int k = 0; k < i; ++k) {
+        (void)hipEventDestroy(ev[k].start);
+        (void)hipEventDestroy(ev[k].stop);
+      }
+      return nullptr;
+    }
   }
-  g_prof.recs.push_back({pass, ev});
+  for (int i = 0; i < n; ++i) g_prof.recs.push_back({first + i, ev[i]});
   return ev;
 }
 
@@ -139,28 +149,27 @@ int bdattn_profile_enable(int on) {
   return BDATTN_OK;
 }
 
-int bdattn_profile_read(double* fwd_ms, int64_t* fwd_launches, double* bwd_ms,
-                        int64_t* bwd_launches) {
-  double ms[2] = {0, 0};
-  int64_t n[2] = {0, 0};
+int bdattn_profile_read(double* ms, int64_t* launches) {
+  double t[kProfKernels] = {0, 0, 0};
+  int64_t n[kProfKernels] = {0, 0, 0};
   int st = BDATTN_OK;
   for (auto& r : g_prof.recs) {
-    float t = 0.f;
+    float x = 0.f;
     if (hipEventSynchronize(r.second.stop) == hipSuccess &&
-        hipEventElapsedTime(&t, r.second.start, r.second.stop) == hipSuccess) {
-      ms[r.first] += t;
+        hipEventElapsedTime(&x, r.second.start, r.second.stop) == hipSuccess) {
+      t[r.first] += x;
       n[r.first] += 1;
     } else {
       st = fail(BDATTN_ERR_HIP, "profile event wait failed");
     }
-    hipEventDestroy(r.second.start);
-    hipEventDestroy(r.second.stop);
+    (void)hipEventDestroy(r.second.start);
+    (void)hipEventDestroy(r.second.stop);
   }
   g_prof.recs.clear();
-  if (fwd_ms) *fwd_ms = ms[0];
-  if (fwd_launches) *fwd_launches = n[0];
-  if (bwd_ms) *bwd_ms = ms[1];
-  if (bwd_launches) *bwd_launches = n[1];
+  for (int k = 0; k < kProfKernels; ++k) {
+    if (ms) ms[k] = t[k];
+    if (launches) launches[k] = n[k];
+  }
   return st;
 }
 
@@ -196,7 +205,7 @@ int bdattn_workspace_size(const bdattn_problem* p, int pass, size_t* bytes) {
   bdattn::Problem P;
   int st = load(p, &P);
   if (st != BDATTN_OK) return st;
-  *bytes = bdattn::workspace_layout(P, pass, bdattn::n_items(P, pass)).total;
+  *bytes = bdattn::workspace_layout(P, pass).total;
   return BDATTN_OK;
 }
 
@@ -254,7 +263,7 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
     return st;
   Entry* entry = get_entry(P);
   const bdattn::Plan* plan = &entry->plan;
-  const bdattn::WsLayout w = bdattn::workspace_layout(P, 0, plan->fwd.size());
+  const bdattn::WsLayout w = bdattn::workspace_layout(P, 0);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
     return fail(BDATTN_ERR_WORKSPACE, "forward workspace missing, misaligned or smaller than " +
                                           std::to_string(w.total) + " bytes");
@@ -265,13 +274,14 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
   a.o_c = o_c; a.o_x = o_x; a.lse_c = lse_c; a.lse_x = lse_x;
   a.ids = (const int32_t*)(ws + w.ids);
-  a.items = (const bdattn::FwdItem*)(ws + w.items);
+  a.items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_items = int32_t(plan->fwd.size());
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
-  hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, prof_events(0));
+  bdattn::KernelEvents ev[1];
+  hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, prof_events(0, 1, ev));
   if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("forward launch: ") + hipGetErrorString(e));
   return BDATTN_OK;
 }
@@ -299,7 +309,7 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
     return st;
   Entry* entry = get_entry(P);
   const bdattn::Plan* plan = &entry->plan;
-  const bdattn::WsLayout w = bdattn::workspace_layout(P, 1, plan->bwd.size());
+  const bdattn::WsLayout w = bdattn::workspace_layout(P, 1);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
     return fail(BDATTN_ERR_WORKSPACE, "backward workspace missing, misaligned or smaller than " +
                                           std::to_string(w.total) + " bytes");
@@ -311,18 +321,19 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.o_c = o_c; a.o_x = o_x; a.do_c = do_c; a.do_x = do_x; a.lse_c = lse_c; a.lse_x = lse_x;
   a.dq_c = dq_c; a.dq_x = dq_x; a.dk_c = dk_c; a.dv_c = dv_c; a.dk_x = dk_x; a.dv_x = dv_x;
   a.ids = (const int32_t*)(ws + w.ids);
-  a.items = (const bdattn::BwdItem*)(ws + w.items);
-  a.n_items = int32_t(plan->bwd.size());
+  a.q_items = (const bdattn::FwdItem*)(ws + w.q_items);
+  a.n_q_items = int32_t(plan->fwd.size());
+  a.kv_items = (const bdattn::BwdItem*)(ws + w.kv_items);
+  a.n_kv_items = int32_t(plan->bwd.size());
   a.d_c = (float*)(ws + w.d_c);
   a.d_x = (float*)(ws + w.d_x);
-  a.dqa_c = (float*)(ws + w.dqa_c);
-  a.dqa_x = (float*)(ws + w.dqa_x);
-  a.B = P.B; a.H = P.H; a.Hkv = P.Hkv;
+  a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
   a.scale = P.scale;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
-  hipError_t e = bdattn::launch_bwd(a, P.dtype, P.d, s, prof_events(1));
+  bdattn::KernelEvents ev[2];
+  hipError_t e = bdattn::launch_bwd(a, P.dtype, P.d, s, prof_events(1, 2, ev));
   if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
   return BDATTN_OK;
 }

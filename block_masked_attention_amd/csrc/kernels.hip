@@ -2,11 +2,21 @@
 //
 // Forward and backward of the attention described in "Block Parallelism for
 // Efficient Distributed Long-Context Diffusion Language Model Training":
-// §3.2 gives the visibility (bdattn_mask.h), the appendix's "Efficient fused
-// operator" paragraph gives the shape of the fused forward (one launch covers
-// the clean-K/V part and the block-diagonal corrupted part) and of the fused
-// backward (reuses saved O and LSE; returns dQ, the local corrupted dK/dV and
-// the clean dK/dV summed over every local query that sees each clean key).
+// §3.2 gives the visibility (bdattn_mask.h); the appendix's "Efficient fused
+// operator" paragraph gives the shape of the operator: the forward covers the
+// clean-K/V part and the block-diagonal corrupted part and saves O and the
+// log-sum-exp; the backward reuses them and returns dQ, the local corrupted
+// dK/dV and the clean dK/dV summed over every local query that sees each
+// clean key (§4.3, Backward pass).
+//
+// Kernels:
+//   fwd_kernel       query-tile parallel: online softmax over the visible keys
+//   bwd_prep_kernel  D = rowsum(dO * O)
+//   bwd_dq_kernel    query-tile parallel: dQ = scale * dS K, written once
+//   bwd_dkdv_kernel  key-tile parallel: dV = P^T dO, dK = scale * dS^T Q over
+//                    every query tile (and q head of the KV group) that sees
+//                    the keys, written once
+// No kernel uses atomics, so every output is bitwise reproducible.
 //
 // Matrix products use the CDNA4 32x32x16 bf16 MFMA (fp32 accumulate), or, for
 // fp32 problems, eight 32x32x2 fp32 MFMAs per 16-deep step. The softmax is the
@@ -16,15 +26,24 @@
 // MFMA 32x32 operand and result layout (lane l of a 64-lane wave):
 //   A (32 x 16): row l%32, 8 contraction slots; B (16 x 32): column l%32,
 //   8 slots. The hardware pairs slot j of A with slot j of B for the same
-//   lane half (l/32); which contraction index a slot stands for is the
-//   caller's choice as long as A and B agree. Here slot j of lane half h in
-//   step t stands for index 16t + 8h + j ("natural"), or, when an operand is
-//   built from a result tile, for 16t + 8(j/4) + 4h + j%4 ("result order").
-//   C (32 x 32, 16 floats): column l%32, element i is row 8(i/4) + 4(l/32) + i%4.
-// An LDS copy stored in "result order" (index bits 2 and 3 swapped within each
-// 16) lets one 16-byte read supply a lane's 8 slots in either case.
+//   lane half h = l/32; which contraction index a slot stands for is the
+//   caller's choice as long as A and B agree. Here slot j of half h in the
+//   16-deep step starting at k0 stands for k0 + 8h + j ("natural"), or, when an
+//   operand is built from a result tile, for k0 + 8(j/4) + 4h + j%4 ("result
+//   order").
+//   C (32 x 32, 16 floats): column l%32, element i is row 8(i/4) + 4h + i%4.
+//
+// LDS tiles are row-major with no padding; the 16-byte chunk c of row r sits
+// at chunk position c ^ swz(r), swz(r) = 2(r%4) + (r/4)%2. A row-slice operand
+// (8 consecutive rows, same chunk) and a transposed operand (4 consecutive
+// rows x 32 bytes, read with ds_read_b64_tr_b16) both hit 32 distinct banks.
+// The transposed read gives lane i of each 16-lane group column i of four
+// consecutive rows, i.e. the operand of a matrix whose contraction index runs
+// down the tile's rows, so no transposed copy is ever stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "bdattn_mask.h"
 #include "launch.h"
@@ -36,21 +55,31 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float floatx2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short shortx4;
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-constexpr int PAD = 8;  // elements of padding after every LDS row (bank spread)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int swap23(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
+// 2^x with one v_exp_f32 (results below 2^-126 flush to zero, which is
+// harmless for softmax weights; exp2(-inf) = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
+}
+
+// Element offset of (row r, column col) in a swizzled tile of D-element rows
+// with EPC elements per 16-byte chunk.
+template <int D, int EPC>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  constexpr int NCH = D / EPC;
+  const int s = (((r & 3) << 1) | ((r >> 2) & 1)) & (NCH - 1);
+  return r * D + (((col / EPC) ^ s) * EPC) + (col % EPC);
 }
 
 // ----------------------------------------------------------------- elements
@@ -60,13 +89,13 @@ struct Elem;
 template <>
 struct Elem<true> {
   using T = uint16_t;  // bf16 bits
+  static constexpr int EPC = 8;
   struct Frag {
     uint4 v;
   };
-  static constexpr int kBytes = 2;
   static __device__ __forceinline__ Frag zero() { return Frag{make_uint4(0, 0, 0, 0)}; }
+  // 8 consecutive elements from global memory
   static __device__ __forceinline__ Frag load(const T* p) { return Frag{*(const uint4*)p}; }
-  static __device__ __forceinline__ void store(T* p, const Frag& f) { *(uint4*)p = f.v; }
   static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
                                                 __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
@@ -82,44 +111,44 @@ struct Elem<true> {
   }
   static __device__ __forceinline__ float to_f(T v) { return __uint_as_float(uint32_t(v) << 16); }
   static __device__ __forceinline__ T from_f(float x) { return T(pack2(x, 0.f) & 0xffffu); }
-  // element e (0..7) of each of 4 fragments, as 4 consecutive elements at p
-  static __device__ __forceinline__ void store_col4(T* p, const Frag* f, int e) {
-    const uint32_t* w0 = (const uint32_t*)&f[0].v;
-    const uint32_t* w1 = (const uint32_t*)&f[1].v;
-    const uint32_t* w2 = (const uint32_t*)&f[2].v;
-    const uint32_t* w3 = (const uint32_t*)&f[3].v;
-    const int wi = e >> 1;
-    uint32_t lo, hi;
-    if (e & 1) {
-      lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-      hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-    } else {
-      lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-      hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-    }
-    *(uint2*)p = make_uint2(lo, hi);
-  }
   static __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
     *(uint2*)p = make_uint2(pack2(a, b), pack2(c, d));
+  }
+  // Row slice of an LDS tile: 8 consecutive elements of row r from column col.
+  template <int D>
+  static __device__ __forceinline__ Frag lds_row(const T* tile, int r, int col) {
+    return Frag{*(const uint4*)(tile + tile_off<D, EPC>(r, col))};
+  }
+  // Operand whose contraction index runs down the tile's rows: lane l takes
+  // column n0 + l%32, slot j of half h takes row k0 + (natural or result
+  // order). Two transposed reads of four rows each.
+  template <int D, bool RESULT>
+  static __device__ __forceinline__ Frag lds_tr(const T* tile, int k0, int n0, int lane) {
+    const int r = lane & 15, c = (lane >> 4) & 1, h = lane >> 5;
+    const int col = n0 + 16 * c + 4 * (r & 3);
+    const int row0 = k0 + (RESULT ? 4 * h : 8 * h) + (r >> 2);
+    const int dt = RESULT ? 8 : 4;
+    const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4*)(tile + tile_off<D, EPC>(row0, col)));
+    const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4*)(tile + tile_off<D, EPC>(row0 + dt, col)));
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    return Frag{make_uint4(ux.x, ux.y, uy.x, uy.y)};
   }
 };
 
 template <>
 struct Elem<false> {
   using T = float;
+  static constexpr int EPC = 4;
   struct Frag {
     float4 a, b;
   };
-  static constexpr int kBytes = 4;
   static __device__ __forceinline__ Frag zero() {
     return Frag{make_float4(0, 0, 0, 0), make_float4(0, 0, 0, 0)};
   }
   static __device__ __forceinline__ Frag load(const T* p) {
     return Frag{*(const float4*)p, *(const float4*)(p + 4)};
-  }
-  static __device__ __forceinline__ void store(T* p, const Frag& f) {
-    *(float4*)p = f.a;
-    *(float4*)(p + 4) = f.b;
   }
   static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a.x, b.a.x, c, 0, 0, 0);
@@ -136,23 +165,24 @@ struct Elem<false> {
   }
   static __device__ __forceinline__ float to_f(T v) { return v; }
   static __device__ __forceinline__ T from_f(float x) { return x; }
-  static __device__ __forceinline__ float el(const Frag& f, int e) {
-    switch (e) {
-      case 0: return f.a.x;
-      case 1: return f.a.y;
-      case 2: return f.a.z;
-      case 3: return f.a.w;
-      case 4: return f.b.x;
-      case 5: return f.b.y;
-      case 6: return f.b.z;
-      default: return f.b.w;
-    }
-  }
-  static __device__ __forceinline__ void store_col4(T* p, const Frag* f, int e) {
-    *(float4*)p = make_float4(el(f[0], e), el(f[1], e), el(f[2], e), el(f[3], e));
-  }
   static __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
     *(float4*)p = make_float4(a, b, c, d);
+  }
+  template <int D>
+  static __device__ __forceinline__ Frag lds_row(const T* tile, int r, int col) {
+    return Frag{*(const float4*)(tile + tile_off<D, EPC>(r, col)),
+                *(const float4*)(tile + tile_off<D, EPC>(r, col + 4))};
+  }
+  template <int D, bool RESULT>
+  static __device__ __forceinline__ Frag lds_tr(const T* tile, int k0, int n0, int lane) {
+    const int n = n0 + (lane & 31), h = lane >> 5;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = k0 + (RESULT ? 8 * (j >> 2) + 4 * h : 8 * h + 4 * (j >> 2)) + (j & 3);
+      x[j] = tile[tile_off<D, EPC>(row, n)];
+    }
+    return pack(x);
   }
 };
 
@@ -163,13 +193,94 @@ __device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, int32
   return bd_corr_row(row, ids[row / B], B);
 }
 
+// ------------------------------------------------------------ tile staging
+// Tiles are copied from global memory straight into LDS (global_load_lds,
+// 16 bytes per lane: lane l of the wave writes LDS bytes [base + 16 l, +16)).
+// The copy is issued from inline assembly so that the compiler neither holds
+// registers for it nor waits for it before unrelated LDS reads; callers wait
+// with lds_dma_wait() before the barrier that publishes the tile. M0 (the LDS
+// base of the copy) is saved and restored around it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base));
+}
+
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Stage rows [row0, row0 + R) of a token-major tensor (row stride `stride`
+// elements) into the swizzled R x D tile at `tile`. Rows past nrows - 1 repeat
+// row nrows - 1 (callers mask them). All 4 waves take part.
+template <typename T, int R, int D>
+__device__ __forceinline__ void tile_dma(T* tile, const T* src, int64_t stride, int row0, int nrows,
+                                         int wave, int lane) {
+  constexpr int EPC = 16 / int(sizeof(T));
+  constexpr int NCH = D / EPC;
+  constexpr int CPW = R * NCH / 256;  // copies per lane
+  static_assert(R * NCH % 256 == 0, "tile size must be a multiple of 256 chunks");
+  const uint32_t base = lds_addr(tile);
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int pos = u * 256 + wave * 64 + lane;  // chunk position in the tile
+    const int r = pos / NCH, p = pos % NCH;
+    const int c = p ^ ((((r & 3) << 1) | ((r >> 2) & 1)) & (NCH - 1));  // source chunk
+    const int row = min(row0 + r, nrows - 1);
+    lds_dma16(src + (int64_t)row * stride + c * EPC,
+              __builtin_amdgcn_readfirstlane(base + uint32_t(u * 256 + wave * 64) * 16u));
+  }
+}
+
 // ======================================================================
-// Forward. One workgroup = 4 waves; wave w covers 32 query rows of one q head
-// (head group: Gw heads x R rows, Gw * R / 32 = 4). It sweeps the clean keys
-// [0, max cb) and then, for corrupted rows, the local corrupted keys of its
-// blocks, in tiles of 64 keys staged through LDS (K as is, V transposed), double
-// buffered. Per tile: S^T = K Q^T (keys x queries) so each lane owns one query
-// row; mask only on tiles that need it; online softmax; O^T += V^T P^T.
+// Query-tile work item shared by the forward and the dQ kernel: `rows`
+// consecutive rows of one stream for Gw q heads of one KV group; wave w covers
+// 32 rows of one head. The keys are swept in tiles of TK staged through LDS
+// (K and V, row-major, double buffered): the clean prefix [0, last cb), then,
+// for corrupted rows, the local corrupted keys of their blocks.
+// ======================================================================
+struct QTile {
+  int stream, head, kvh, n_rows, row0, my_row, crow, n_ct, n_xt, xlo, full_end;
+  bool row_ok;
+  BdRowBounds rb;
+};
+
+template <int TK>
+__device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, int Gw, int H,
+                                        int Hkv, int n_clean_q, int n_corr, int clean_q_start,
+                                        const int32_t* ids, int B, int wave, int lq) {
+  QTile q;
+  q.stream = it.hs & 1;
+  const int hg = it.hs >> 1;
+  q.head = hg * Gw + (wave % Gw);
+  q.kvh = q.head / (H / Hkv);
+  q.n_rows = q.stream ? n_corr : n_clean_q;
+  q.row0 = it.tile * rows_per_item;
+  const int row_end = min(q.n_rows, q.row0 + rows_per_item);
+  q.my_row = q.row0 + (wave / Gw) * 32 + lq;
+  q.row_ok = q.my_row < q.n_rows;
+  q.crow = min(q.my_row, q.n_rows - 1);
+  q.rb = row_bounds(q.stream, q.crow, clean_q_start, ids, B);
+  const BdRowBounds first = row_bounds(q.stream, q.row0, clean_q_start, ids, B);
+  const BdRowBounds last = row_bounds(q.stream, row_end - 1, clean_q_start, ids, B);
+  q.full_end = first.cb / TK * TK;  // clean tiles below need no mask
+  q.n_ct = (last.cb + TK - 1) / TK;
+  q.xlo = q.stream ? first.xlo : 0;
+  q.n_xt = q.stream ? (last.xhi - first.xlo + TK - 1) / TK : 0;
+  return q;
+}
+
+// ======================================================================
+// Forward. Per key tile: S^T = K Q^T (keys x queries, so each lane owns one
+// query row); mask only on tiles that need it; online softmax; O^T += V^T P^T.
 // ======================================================================
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -178,82 +289,36 @@ void fwd_kernel(FwdArgs a) {
   using T = typename E::T;
   using Frag = typename E::Frag;
   constexpr int TK = FWD_TK;
-  constexpr int KP = D + PAD;   // K tile row pitch (elements)
-  constexpr int VP = TK + PAD;  // V^T tile row pitch
-  constexpr int KSZ = TK * KP, VSZ = D * VP;
-  constexpr int NCH = D / 8;                 // 8-element chunks per row
-  constexpr int LOADERS = (TK / 4) * NCH;    // threads that stage a tile
-  static_assert(LOADERS <= 256, "tile loader needs more than 256 threads");
-  static_assert(2 * (KSZ + VSZ) * E::kBytes <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(16))) T smem[2 * (KSZ + VSZ)];
+  constexpr int TSZ = TK * D;
+  static_assert(4 * TSZ * sizeof(T) <= 80 * 1024, "LDS (two workgroups per CU)");
+  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][K, V]
 
-  const FwdItem it = a.items[blockIdx.x];
-  const int stream = it.hs & 1, hg = it.hs >> 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
-  const int head = hg * a.Gw + (wave % a.Gw);
-  const int kvh = head / (a.H / a.Hkv);
-  const int n_rows = stream ? a.n_corr : a.n_clean_q;
-  const int row0 = it.tile * a.rows_per_item;
-  const int row_end = min(n_rows, row0 + a.rows_per_item);
-  const int my_row = row0 + (wave / a.Gw) * 32 + lq;
-  const bool row_ok = my_row < n_rows;
-  const int crow = min(my_row, n_rows - 1);
-  const BdRowBounds rb = row_bounds(stream, crow, a.clean_q_start, a.ids, a.B);
-  const BdRowBounds first = row_bounds(stream, row0, a.clean_q_start, a.ids, a.B);
-  const BdRowBounds last = row_bounds(stream, row_end - 1, a.clean_q_start, a.ids, a.B);
-  const int full_end = first.cb / TK * TK;  // clean tiles below need no mask
-  const int n_ct = (last.cb + TK - 1) / TK;
-  const int xlo = stream ? first.xlo : 0;
-  const int n_xt = stream ? (last.xhi - first.xlo + TK - 1) / TK : 0;
-  const int n_tiles = n_ct + n_xt;
+  const QTile q = q_tile<TK>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
+                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B, wave, lq);
+  const int n_tiles = q.n_ct + q.n_xt;
+  const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
 
-  const T* qsrc = (const T*)(stream ? a.q_x : a.q_c);
-  const T* kc = (const T*)a.k_c;
-  const T* vc = (const T*)a.v_c;
-  const T* kx = (const T*)a.k_x;
-  const T* vx = (const T*)a.v_x;
-
-  // Q as the B operand of S^T = K Q^T: lane (row lq, half hf), slot j = d 16ks+8hf+j
+  // Q as the B operand of S^T = K Q^T: column = this lane's row, natural over d
   Frag qf[D / 16];
   {
-    const T* qrow = qsrc + ((int64_t)crow * a.H + head) * D;
+    const T* qrow = qsrc + ((int64_t)q.crow * a.H + q.head) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = row_ok ? E::load(qrow + 16 * ks + 8 * hf) : E::zero();
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[ks] = q.row_ok ? E::load(qrow + 16 * ks + 8 * hf) : E::zero();
   }
 
-  // tile staging: thread -> (key group of 4, 8-element chunk)
-  const int ld_c = tid % NCH, ld_g = tid / NCH;
-  Frag kr[4], vr[4];
-  auto fetch = [&](int j) {
-    if (tid >= LOADERS) return;
-    const bool cl = j < n_ct;
-    const int k0 = cl ? j * TK : xlo + (j - n_ct) * TK;
+  // stage key tile j (K then V) into LDS buffer `buf`
+  auto fetch = [&](int j, int buf) {
+    const bool cl = j < q.n_ct;
+    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
     const int nk = cl ? a.n_clean_kv : a.n_corr;
-    const T* ks = cl ? kc : kx;
-    const T* vs = cl ? vc : vx;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + 4 * ld_g + r;
-      if (key < nk) {
-        const int64_t off = ((int64_t)key * a.Hkv + kvh) * D + 8 * ld_c;
-        kr[r] = E::load(ks + off);
-        vr[r] = E::load(vs + off);
-      } else {
-        kr[r] = E::zero();
-        vr[r] = E::zero();
-      }
-    }
-  };
-  auto stage = [&](int buf) {
-    if (tid >= LOADERS) return;
-    T* Ks = smem + buf * (KSZ + VSZ);
-    T* Vt = Ks + KSZ;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) E::store(Ks + (4 * ld_g + r) * KP + 8 * ld_c, kr[r]);
-    const int pcol = swap23(4 * ld_g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) E::store_col4(Vt + (8 * ld_c + e) * VP + pcol, vr, e);
+    const T* ks = (const T*)(cl ? a.k_c : a.k_x) + (int64_t)q.kvh * D;
+    const T* vs = (const T*)(cl ? a.v_c : a.v_x) + (int64_t)q.kvh * D;
+    T* dst = smem + buf * 2 * TSZ;
+    tile_dma<T, TK, D>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    tile_dma<T, TK, D>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
   };
 
   f32x16 o[D / 32];
@@ -261,106 +326,113 @@ void fwd_kernel(FwdArgs a) {
   for (int i = 0; i < D / 32; ++i) o[i] = zero16();
   float m = kNegInf, l = 0.f;
 
-  if (n_tiles > 0) {
-    fetch(0);
-    stage(0);
-  }
-  __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j + 1 < n_tiles) fetch(j + 1);
-    const T* Ks = smem + (j & 1) * (KSZ + VSZ);
-    const T* Vt = Ks + KSZ;
-    const bool cl = j < n_ct;
-    const int k0 = cl ? j * TK : xlo + (j - n_ct) * TK;
-    const bool need_mask = !cl || (k0 + TK > full_end);
+  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
+  const int j_full = min(q.n_ct, q.full_end / TK);
+  auto sweep = [&](auto mask_tag, int j0, int j1) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int j = j0; j < j1; ++j) {
+      if (j + 1 < n_tiles) fetch(j + 1, (j + 1) & 1);
+      const T* Ks = smem + (j & 1) * 2 * TSZ;
+      const T* Vs = Ks + TSZ;
+      const bool cl = j < q.n_ct;
+      const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
 
     f32x16 s[TK / 32];
 #pragma unroll
     for (int mb = 0; mb < TK / 32; ++mb) {
       s[mb] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        Frag ka = E::load(Ks + (32 * mb + lq) * KP + 16 * ks + 8 * hf);
-        E::mma(s[mb], ka, qf[ks]);
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        E::mma(s[mb], E::template lds_row<D>(Ks, 32 * mb + lq, 16 * ks + 8 * hf), qf[ks]);
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[mb][i] * a.scale_log2;
-        if (need_mask) {
-          const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool vis = cl ? bd_sees_clean(rb, key) : bd_sees_corr(rb, key);
-          v = vis ? v : kNegInf;
-        }
-        s[mb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-    float rs = 0.f;
-    Frag pf[TK / 32][2];
-#pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = exp2f(s[mb][i] - m_use);
-        rs += p[i];
-      }
-      pf[mb][0] = E::pack(p);
-      pf[mb][1] = E::pack(p + 8);
-    }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    // online softmax; the row max is taken on raw scores (the scale is > 0)
+    // and the scale folded into the exponent's multiply-add
+    {
+      float mx = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < TK / 32; ++mb) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          Frag va = E::load(Vt + (32 * db + lq) * VP + 32 * mb + 16 * t + 8 * hf);
-          E::mma(o[db], va, pf[mb][t]);
+        for (int i = 0; i < 16; ++i) {
+          if (MASK) {
+            const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
+            s[mb][i] = vis ? s[mb][i] : kNegInf;
+          }
+          mx = fmaxf(mx, s[mb][i]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const bool grew = __any(m_new > m);  // some row's max moved: rescale
+      const float alpha = fast_exp2(m - m_use);
+      float rs = 0.f;
+      Frag pf[TK / 32][2];
+#pragma unroll
+      for (int mb = 0; mb < TK / 32; ++mb) {
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, -m_use));
+          rs += p[i];
+        }
+        pf[mb][0] = E::pack(p);
+        pf[mb][1] = E::pack(p + 8);
+      }
+      l = l * alpha + rs;
+      m = m_new;
+      if (grew) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int mb = 0; mb < TK / 32; ++mb) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            E::mma(o[db], E::template lds_tr<D, true>(Vs, 32 * mb + 16 * t, 32 * db, lane),
+                   pf[mb][t]);
         }
       }
     }
-    if (j + 1 < n_tiles) stage((j + 1) & 1);
-    __syncthreads();
-  }
+      lds_dma_wait();
+      __syncthreads();
+    }
+  };
+  if (n_tiles > 0) fetch(0, 0);
+  lds_dma_wait();
+  __syncthreads();
+  sweep(std::false_type{}, 0, j_full);
+  sweep(std::true_type{}, j_full, n_tiles);
 
   const float lt = l + __shfl_xor(l, 32);
-  if (row_ok) {
+  if (q.row_ok) {
     const float inv = 1.f / lt;
-    T* orow = (T*)(stream ? a.o_x : a.o_c) + ((int64_t)my_row * a.H + head) * D;
+    T* orow = (T*)(q.stream ? a.o_x : a.o_c) + ((int64_t)q.my_row * a.H + q.head) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g)
         E::store4(orow + 32 * db + 8 * g + 4 * hf, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
                   o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-      }
     }
     if (hf == 0) {
-      float* lse = stream ? a.lse_x : a.lse_c;
-      lse[(int64_t)head * n_rows + my_row] = (m + log2f(lt)) * kLn2;
+      float* lse = q.stream ? a.lse_x : a.lse_c;
+      lse[(int64_t)q.head * q.n_rows + q.my_row] = (m + log2f(lt)) * kLn2;
     }
   }
 }
 
 // ======================================================================
-// Backward preprocess: D = rowsum(dO * O) per (row, head), and zero the fp32
-// dQ accumulator. D/8 lanes per (row, head).
+// Backward preprocess: D = rowsum(dO * O) per (row, head), D/8 lanes each.
 // ======================================================================
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const void* do_, float* Dout,
-                                                       float* dqa, int32_t n_rows, int32_t H) {
+                                                       int32_t n_rows, int32_t H) {
   using E = Elem<BF16>;
   using T = typename E::T;
   constexpr int LPR = D / 8;
@@ -370,16 +442,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
   const int64_t npairs = (int64_t)n_rows * H;
   float acc = 0.f;
   if (pair < npairs) {
-    const T* o = (const T*)o_ + pair * D + 8 * sub;
-    const T* g = (const T*)do_ + pair * D + 8 * sub;
-    typename E::Frag fo = E::load(o), fg = E::load(g);
+    typename E::Frag fo = E::load((const T*)o_ + pair * D + 8 * sub);
+    typename E::Frag fg = E::load((const T*)do_ + pair * D + 8 * sub);
     const T* po = (const T*)&fo;
     const T* pg = (const T*)&fg;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += E::to_f(po[e]) * E::to_f(pg[e]);
-    float* q = dqa + pair * D + 8 * sub;
-    *(float4*)q = make_float4(0, 0, 0, 0);
-    *(float4*)(q + 4) = make_float4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
@@ -389,89 +457,177 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
   }
 }
 
-// fp32 dQ accumulator -> output dtype, times the softmax scale.
-template <bool BF16>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* acc, void* out_, int64_t n,
-                                                         float scale) {
+// ======================================================================
+// Backward, dQ. Same query tiles and key sweep as the forward. Per key tile:
+// S^T = K Q^T and dP^T = V dO^T (each lane owns one query row, so its LSE and
+// D are scalars); P^T = exp2(S^T c - LSE2); dS^T = P^T (dP^T - D);
+// dQ^T += K^T dS^T with K^T read transposed from the K tile.
+// ======================================================================
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
-  T* out = (T*)out_;
-  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
-  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
-    float4 v = *(const float4*)(acc + i);
-    E::store4(out + i, v.x * scale, v.y * scale, v.z * scale, v.w * scale);
+  using Frag = typename E::Frag;
+  constexpr int TK = FWD_TK;
+  constexpr int TSZ = TK * D;
+  static_assert(4 * TSZ * sizeof(T) <= 80 * 1024, "LDS (two workgroups per CU)");
+  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][K, V]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, hf = lane >> 5;
+  const QTile q = q_tile<TK>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
+                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B, wave, lq);
+  const int n_tiles = q.n_ct + q.n_xt;
+  const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
+  const T* gsrc = (const T*)(q.stream ? a.do_x : a.do_c);
+
+  Frag qf[D / 16], gf[D / 16];
+  {
+    const int64_t off = ((int64_t)q.crow * a.H + q.head) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = q.row_ok ? E::load(qsrc + off + 16 * ks + 8 * hf) : E::zero();
+      gf[ks] = q.row_ok ? E::load(gsrc + off + 16 * ks + 8 * hf) : E::zero();
+    }
+  }
+  const float* lse = q.stream ? a.lse_x : a.lse_c;
+  const float* dd = q.stream ? a.d_x : a.d_c;
+  const float lse2 = q.row_ok ? lse[(int64_t)q.head * q.n_rows + q.crow] * kLog2e
+                              : __builtin_inff();
+  const float drow = q.row_ok ? dd[(int64_t)q.head * q.n_rows + q.crow] : 0.f;
+
+  // stage key tile j (K then V) into LDS buffer `buf`
+  auto fetch = [&](int j, int buf) {
+    const bool cl = j < q.n_ct;
+    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+    const int nk = cl ? a.n_clean_kv : a.n_corr;
+    const T* ks = (const T*)(cl ? a.k_c : a.k_x) + (int64_t)q.kvh * D;
+    const T* vs = (const T*)(cl ? a.v_c : a.v_x) + (int64_t)q.kvh * D;
+    T* dst = smem + buf * 2 * TSZ;
+    tile_dma<T, TK, D>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    tile_dma<T, TK, D>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+  };
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
+
+  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
+  const int j_full = min(q.n_ct, q.full_end / TK);
+  auto sweep = [&](auto mask_tag, int j0, int j1) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int j = j0; j < j1; ++j) {
+      if (j + 1 < n_tiles) fetch(j + 1, (j + 1) & 1);
+      const T* Ks = smem + (j & 1) * 2 * TSZ;
+      const T* Vs = Ks + TSZ;
+      const bool cl = j < q.n_ct;
+      const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+      Frag sf[TK / 32][2];
+#pragma unroll
+      for (int mb = 0; mb < TK / 32; ++mb) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          E::mma(s, E::template lds_row<D>(Ks, 32 * mb + lq, 16 * ks + 8 * hf), qf[ks]);
+          E::mma(dp, E::template lds_row<D>(Vs, 32 * mb + lq, 16 * ks + 8 * hf), gf[ks]);
+        }
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
+          if (MASK) {
+            const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
+            p = vis ? p : 0.f;
+          }
+          ds[i] = p * (dp[i] - drow);
+        }
+        sf[mb][0] = E::pack(ds);
+        sf[mb][1] = E::pack(ds + 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int mb = 0; mb < TK / 32; ++mb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            E::mma(dq[db], E::template lds_tr<D, true>(Ks, 32 * mb + 16 * t, 32 * db, lane),
+                   sf[mb][t]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      lds_dma_wait();
+      __syncthreads();
+    }
+  };
+  if (n_tiles > 0) fetch(0, 0);
+  lds_dma_wait();
+  __syncthreads();
+  sweep(std::false_type{}, 0, j_full);
+  sweep(std::true_type{}, j_full, n_tiles);
+
+  if (q.row_ok) {
+    T* out = (T*)(q.stream ? a.dq_x : a.dq_c) + ((int64_t)q.my_row * a.H + q.head) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        E::store4(out + 32 * db + 8 * g + 4 * hf, dq[db][4 * g] * a.scale,
+                  dq[db][4 * g + 1] * a.scale, dq[db][4 * g + 2] * a.scale,
+                  dq[db][4 * g + 3] * a.scale);
+    }
   }
 }
 
 // ======================================================================
-// Backward main. One workgroup = 4 waves owning 128 keys of one KV head (32
-// per wave, kept in registers as the B operand of S = Q K^T and dP = dO V^T).
-// It sweeps every query tile (64 rows) that sees its keys, for each q head of
-// the group: recompute S, P = exp2(S*c - LSE2), dP, dS = P (dP - D);
-// dV += P^T dO and dK += dS^T Q accumulate in registers; dQ += dS K is
-// contracted over the workgroup's 128 keys through LDS and added into the
-// fp32 accumulator with atomics.
+// Backward, dK/dV. One workgroup = 4 waves owning BWD_TK keys of one KV head
+// (32 per wave, kept in registers as the B operand of S = Q K^T and
+// dP = dO V^T). It sweeps every query tile (BWD_TQ rows) that sees its keys,
+// for each q head of the group, with the next tile's Q, dO and row data
+// prefetched into registers and stored to the other LDS buffer while the
+// current one is in use: S, dP; P = exp2(S c - LSE2); dS = P (dP - D);
+// dV += P^T dO and dK += dS^T Q, with dO and Q read transposed from their
+// row-major tiles.
 // ======================================================================
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_kernel(BwdArgs a) {
+void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
   using Frag = typename E::Frag;
   constexpr int TK = BWD_TK, TQ = BWD_TQ;
-  constexpr int NCH = D / 8;
-  constexpr int KTP = TK + PAD;  // K^T rows (d) x keys
-  constexpr int QP = D + PAD;    // Q, dO rows (q) x d
-  constexpr int QTP = TQ + PAD;  // Q^T, dO^T rows (d) x q (result order)
-  constexpr int SP = TK + PAD;   // dS rows (q) x keys
-  constexpr int KT_SZ = D * KTP, Q_SZ = TQ * QP, QT_SZ = D * QTP, S_SZ = TQ * SP;
-  constexpr int LDS_ELEMS = KT_SZ + 2 * Q_SZ + 2 * QT_SZ + S_SZ;
-  static_assert(LDS_ELEMS * E::kBytes + TQ * 16 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(16))) T smem[LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) float r_lse2[TQ];
-  __shared__ __attribute__((aligned(16))) float r_d[TQ];
-  __shared__ __attribute__((aligned(16))) int32_t r_lo[TQ];
-  __shared__ __attribute__((aligned(16))) int32_t r_hi[TQ];
-  T* Kt = smem;
-  T* Qs = Kt + KT_SZ;
-  T* dOs = Qs + Q_SZ;
-  T* Qt = dOs + Q_SZ;
-  T* dOt = Qt + QT_SZ;
-  T* dSs = dOt + QT_SZ;
+  constexpr int TSZ = TQ * D;
+  static_assert(4 * TSZ * sizeof(T) + 8 * TQ * 4 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float r_lse2[2][TQ];
+  __shared__ __attribute__((aligned(16))) float r_d[2][TQ];
+  __shared__ __attribute__((aligned(16))) int32_t r_lo[2][TQ];
+  __shared__ __attribute__((aligned(16))) int32_t r_hi[2][TQ];
 
-  const BwdItem it = a.items[blockIdx.x];
-  const int kstream = it.hs & 1, kvh = it.hs >> 1;
+  const BwdItem item = a.kv_items[blockIdx.x];
+  const int it_x0 = item.x0, it_x1 = item.x1, it_c0 = item.c0, it_c1 = item.c1;
+  const int kstream = item.hs & 1, kvh = item.hs >> 1;
   const int G = a.H / a.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lk = lane & 31, hf = lane >> 5;
-  const int key0 = it.ktile * TK;
+  const int key0 = item.ktile * TK;
   const int n_keys = kstream ? a.n_corr : a.n_clean_kv;
   const int my_key = key0 + 32 * wave + lk;
   const bool key_ok = my_key < n_keys;
-  const T* ksrc = (const T*)(kstream ? a.k_x : a.k_c);
-  const T* vsrc = (const T*)(kstream ? a.v_x : a.v_c);
 
   // this lane's key and value as B operands (natural order over d)
   Frag kf[D / 16], vf[D / 16];
   {
+    const T* ksrc = (const T*)(kstream ? a.k_x : a.k_c);
+    const T* vsrc = (const T*)(kstream ? a.v_x : a.v_c);
     const int64_t off = ((int64_t)min(my_key, n_keys - 1) * a.Hkv + kvh) * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       kf[ks] = key_ok ? E::load(ksrc + off + 16 * ks + 8 * hf) : E::zero();
       vf[ks] = key_ok ? E::load(vsrc + off + 16 * ks + 8 * hf) : E::zero();
     }
-  }
-  // K^T of the workgroup's 128 keys (natural key order) for dQ = dS K
-  for (int u = tid; u < (TK / 4) * NCH; u += 256) {
-    const int c = u % NCH, g = u / NCH;
-    Frag kr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + 4 * g + r;
-      kr[r] = key < n_keys ? E::load(ksrc + ((int64_t)key * a.Hkv + kvh) * D + 8 * c) : E::zero();
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) E::store_col4(Kt + (8 * c + e) * KTP + 4 * g, kr, e);
   }
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -481,159 +637,156 @@ void bwd_kernel(BwdArgs a) {
     dv[i] = zero16();
   }
 
-  const int ld_c = tid % NCH, ld_g = tid / NCH;
-  constexpr int LOADERS = (TQ / 4) * NCH;
-  static_assert(LOADERS <= 256, "q tile loader");
+  // iteration -> (query stream, tile, head). The query tiles that see every
+  // key of the workgroup (those starting at or after xf / cf) come first, then
+  // the ones that need the mask; within each, corrupted tiles then clean ones,
+  // each from the last tile down, every q head of the group per tile.
+  const int it_xf = item.xf, it_cf = item.cf;
+  auto ntiles = [](int r0, int r1) { return r1 > r0 ? (r1 - 1) / TQ - r0 / TQ + 1 : 0; };
+  const int top_x = (it_x1 - 1) / TQ, top_c = (it_c1 - 1) / TQ;
+  const int nf_x = it_xf < it_x1 ? top_x - it_xf / TQ + 1 : 0;
+  const int nf_c = it_cf < it_c1 ? top_c - it_cf / TQ + 1 : 0;
+  const int nm_x = ntiles(it_x0, it_x1) - nf_x, nm_c = ntiles(it_c0, it_c1) - nf_c;
+  const int n_full = (nf_x + nf_c) * G;
+  const int n_it = n_full + (nm_x + nm_c) * G;
+  struct Step {
+    int qs, q0, h;
+  };
+  auto step = [&](int i) {
+    Step s;
+    int t = i / G;
+    s.h = kvh * G + i % G;
+    if (t < nf_x) {
+      s.qs = 1;
+      s.q0 = (top_x - t) * TQ;
+    } else if ((t -= nf_x) < nf_c) {
+      s.qs = 0;
+      s.q0 = (top_c - t) * TQ;
+    } else if ((t -= nf_c) < nm_x) {
+      s.qs = 1;
+      s.q0 = (top_x - nf_x - t) * TQ;
+    } else {
+      t -= nm_x;
+      s.qs = 0;
+      s.q0 = (top_c - nf_c - t) * TQ;
+    }
+    return s;
+  };
 
-  for (int qs = 1; qs >= 0; --qs) {
-    const int r0 = qs ? it.x0 : it.c0;
-    const int r1 = qs ? it.x1 : it.c1;
-    if (r1 <= r0) continue;
-    const int n_rows = qs ? a.n_corr : a.n_clean_q;
-    const T* qsrc = (const T*)(qs ? a.q_x : a.q_c);
-    const T* gsrc = (const T*)(qs ? a.do_x : a.do_c);
-    const float* lse = qs ? a.lse_x : a.lse_c;
-    const float* dd = qs ? a.d_x : a.d_c;
-    float* dqa = qs ? a.dqa_x : a.dqa_c;
-    for (int qt = (r1 - 1) / TQ; qt >= r0 / TQ; --qt) {
-      const int q0 = qt * TQ;
-      bool full = false;
-      if (kstream == 0 && q0 >= r0 && key0 + TK <= n_keys) {
-        const BdRowBounds fb = row_bounds(qs, q0, a.clean_q_start, a.ids, a.B);
-        full = fb.cb >= key0 + TK;
+  // stage the Q and dO tiles of step s into LDS buffer `buf` (DMA) and fetch
+  // its row data into registers (threads 0..TQ-1), stored by stage_rows
+  float p_lse2 = 0.f, p_d = 0.f;
+  int p_lo = 0, p_hi = 0;
+  auto fetch = [&](const Step& s, int buf) {
+    const int n_rows = s.qs ? a.n_corr : a.n_clean_q;
+    const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
+    const T* gsrc = (const T*)(s.qs ? a.do_x : a.do_c) + (int64_t)s.h * D;
+    T* dst = smem + buf * 2 * TSZ;
+    tile_dma<T, TQ, D>(dst, qsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
+    tile_dma<T, TQ, D>(dst + TSZ, gsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
+    if (tid < TQ) {
+      const int row = s.q0 + tid;
+      if (row < n_rows) {
+        const float* lse = s.qs ? a.lse_x : a.lse_c;
+        const float* dd = s.qs ? a.d_x : a.d_c;
+        const BdRowBounds b = row_bounds(s.qs, row, a.clean_q_start, a.ids, a.B);
+        p_lse2 = lse[(int64_t)s.h * n_rows + row] * kLog2e;
+        p_d = dd[(int64_t)s.h * n_rows + row];
+        p_lo = kstream ? b.xlo : 0;
+        p_hi = kstream ? b.xhi : b.cb;
+      } else {
+        p_lse2 = __builtin_inff();
+        p_d = 0.f;
+        p_lo = 0;
+        p_hi = 0;
       }
-      for (int hh = 0; hh < G; ++hh) {
-        const int h = kvh * G + hh;
-        __syncthreads();  // previous users of the q-side LDS are done
-        if (tid < LOADERS) {
-          Frag qr[4], gr[4];
+    }
+  };
+  auto stage_rows = [&](int buf) {
+    if (tid < TQ) {
+      r_lse2[buf][tid] = p_lse2;
+      r_d[buf][tid] = p_d;
+      r_lo[buf][tid] = p_lo;
+      r_hi[buf][tid] = p_hi;
+    }
+  };
+
+  auto sweep = [&](auto mask_tag, int i0, int i1) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    for (int i = i0; i < i1; ++i) {
+      const int cur = i & 1;
+      if (i + 1 < n_it) fetch(step(i + 1), cur ^ 1);
+      const T* Qs = smem + cur * 2 * TSZ;
+      const T* Gs = Qs + TSZ;
+    {
+      Frag pa[TQ / 32][2], sa[TQ / 32][2];
+#pragma unroll
+      for (int mb = 0; mb < TQ / 32; ++mb) {
+        f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          E::mma(sacc, E::template lds_row<D>(Qs, 32 * mb + lk, 16 * ks + 8 * hf), kf[ks]);
+          E::mma(pacc, E::template lds_row<D>(Gs, 32 * mb + lk, 16 * ks + 8 * hf), vf[ks]);
+        }
+        float p[16], ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qr = 32 * mb + 8 * g + 4 * hf;
+          const float4 l4 = *(const float4*)(&r_lse2[cur][qr]);
+          const float4 d4 = *(const float4*)(&r_d[cur][qr]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+          int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
+          if (MASK) {
+            const int4 lo4 = *(const int4*)(&r_lo[cur][qr]);
+            const int4 hi4 = *(const int4*)(&r_hi[cur][qr]);
+            lo[0] = lo4.x; lo[1] = lo4.y; lo[2] = lo4.z; lo[3] = lo4.w;
+            hi[0] = hi4.x; hi[1] = hi4.y; hi[2] = hi4.z; hi[3] = hi4.w;
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = q0 + 4 * ld_g + r;
-            if (row < n_rows) {
-              const int64_t off = ((int64_t)row * a.H + h) * D + 8 * ld_c;
-              qr[r] = E::load(qsrc + off);
-              gr[r] = E::load(gsrc + off);
-            } else {
-              qr[r] = E::zero();
-              gr[r] = E::zero();
-            }
-            E::store(Qs + (4 * ld_g + r) * QP + 8 * ld_c, qr[r]);
-            E::store(dOs + (4 * ld_g + r) * QP + 8 * ld_c, gr[r]);
-          }
-          const int pcol = swap23(4 * ld_g);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            E::store_col4(Qt + (8 * ld_c + e) * QTP + pcol, qr, e);
-            E::store_col4(dOt + (8 * ld_c + e) * QTP + pcol, gr, e);
+            const int e = 4 * g + r;
+            float pv = fast_exp2(fmaf(sacc[e], a.scale_log2, -lv[r]));
+            if (MASK) pv = (key_ok && my_key >= lo[r] && my_key < hi[r]) ? pv : 0.f;
+            p[e] = pv;
+            ds[e] = pv * (pacc[e] - dv4[r]);
           }
         }
-        if (tid < TQ) {
-          const int row = q0 + tid;
-          if (row < n_rows) {
-            const BdRowBounds b = row_bounds(qs, row, a.clean_q_start, a.ids, a.B);
-            r_lse2[tid] = lse[(int64_t)h * n_rows + row] * kLog2e;
-            r_d[tid] = dd[(int64_t)h * n_rows + row];
-            r_lo[tid] = kstream ? b.xlo : 0;
-            r_hi[tid] = kstream ? b.xhi : b.cb;
-          } else {
-            r_lse2[tid] = __builtin_inff();
-            r_d[tid] = 0.f;
-            r_lo[tid] = 0;
-            r_hi[tid] = 0;
+        pa[mb][0] = E::pack(p);
+        pa[mb][1] = E::pack(p + 8);
+        sa[mb][0] = E::pack(ds);
+        sa[mb][1] = E::pack(ds + 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // dV += P^T dO, dK += dS^T Q (contraction over this tile's queries)
+#pragma unroll
+      for (int mb = 0; mb < TQ / 32; ++mb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            E::mma(dv[db], pa[mb][t],
+                   E::template lds_tr<D, true>(Gs, 32 * mb + 16 * t, 32 * db, lane));
+            E::mma(dk[db], sa[mb][t],
+                   E::template lds_tr<D, true>(Qs, 32 * mb + 16 * t, 32 * db, lane));
           }
-        }
-        __syncthreads();
-
-        // S = Q K^T and dP = dO V^T for this wave's 32 keys (rows = queries)
-        f32x16 sacc[TQ / 32], pacc[TQ / 32];
-#pragma unroll
-        for (int mb = 0; mb < TQ / 32; ++mb) {
-          sacc[mb] = zero16();
-          pacc[mb] = zero16();
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            Frag qa = E::load(Qs + (32 * mb + lk) * QP + 16 * ks + 8 * hf);
-            E::mma(sacc[mb], qa, kf[ks]);
-            Frag ga = E::load(dOs + (32 * mb + lk) * QP + 16 * ks + 8 * hf);
-            E::mma(pacc[mb], ga, vf[ks]);
-          }
-        }
-        Frag pa[TQ / 32][2], sa[TQ / 32][2];
-#pragma unroll
-        for (int mb = 0; mb < TQ / 32; ++mb) {
-          float p[16], ds[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int q = 32 * mb + 8 * g + 4 * hf;
-            const float4 l4 = *(const float4*)(r_lse2 + q);
-            const float4 d4 = *(const float4*)(r_d + q);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-            int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
-            if (!full) {
-              const int4 lo4 = *(const int4*)(r_lo + q);
-              const int4 hi4 = *(const int4*)(r_hi + q);
-              lo[0] = lo4.x; lo[1] = lo4.y; lo[2] = lo4.z; lo[3] = lo4.w;
-              hi[0] = hi4.x; hi[1] = hi4.y; hi[2] = hi4.z; hi[3] = hi4.w;
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * g + r;
-              float pv = exp2f(sacc[mb][i] * a.scale_log2 - lv[r]);
-              if (!full) pv = (key_ok && my_key >= lo[r] && my_key < hi[r]) ? pv : 0.f;
-              p[i] = pv;
-              ds[i] = pv * (pacc[mb][i] - dv4[r]);
-            }
-          }
-          pa[mb][0] = E::pack(p);
-          pa[mb][1] = E::pack(p + 8);
-          sa[mb][0] = E::pack(ds);
-          sa[mb][1] = E::pack(ds + 8);
-          // dS (rows = queries, natural key order) for the workgroup's dQ
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int q = 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            dSs[q * SP + 32 * wave + lk] = E::from_f(ds[i]);
-          }
-        }
-        // dV += P^T dO, dK += dS^T Q (contraction over this tile's queries)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-          for (int mb = 0; mb < TQ / 32; ++mb) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int col = 32 * mb + 16 * t + 8 * hf;
-              Frag gb = E::load(dOt + (32 * db + lk) * QTP + col);
-              E::mma(dv[db], pa[mb][t], gb);
-              Frag qb = E::load(Qt + (32 * db + lk) * QTP + col);
-              E::mma(dk[db], sa[mb][t], qb);
-            }
-          }
-        }
-        __syncthreads();  // dS complete
-        // dQ[q, d] += sum over the 128 keys of dS[q, k] K[k, d]
-        constexpr int NB = (TQ / 32) * (D / 32);
-        for (int blk = wave; blk < NB; blk += 4) {
-          const int mb = blk / (D / 32), db = blk % (D / 32);
-          f32x16 acc = zero16();
-#pragma unroll
-          for (int ks = 0; ks < TK / 16; ++ks) {
-            Frag sa2 = E::load(dSs + (32 * mb + lk) * SP + 16 * ks + 8 * hf);
-            Frag kb2 = E::load(Kt + (32 * db + lk) * KTP + 16 * ks + 8 * hf);
-            E::mma(acc, sa2, kb2);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = q0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (row < n_rows)
-              unsafeAtomicAdd(dqa + ((int64_t)row * a.H + h) * D + 32 * db + lk, acc[i]);
-          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
+      if (i + 1 < n_it) stage_rows(cur ^ 1);
+      lds_dma_wait();
+      __syncthreads();
+    }
+  };
+  if (n_it > 0) {
+    fetch(step(0), 0);
+    stage_rows(0);
   }
+  lds_dma_wait();
+  __syncthreads();
+  sweep(std::false_type{}, 0, n_full);
+  sweep(std::true_type{}, n_full, n_it);
 
   // write dK (times the scale) and dV for this wave's 32 keys
   T* dko = (T*)(kstream ? a.dk_x : a.dk_c);
@@ -653,17 +806,15 @@ void bwd_kernel(BwdArgs a) {
 }
 
 template <bool BF16, int D>
-hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents& ev) {
-  if (ev.start) hipEventRecord(ev.start, s);
-  if (a.n_items > 0) {
-    hipLaunchKernelGGL((fwd_kernel<BF16, D>), dim3(a.n_items), dim3(256), 0, s, a);
-  }
-  if (ev.stop) hipEventRecord(ev.stop, s);
+hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
+  if (ev) (void)hipEventRecord(ev[0].start, s);
+  if (a.n_items > 0) hipLaunchKernelGGL((fwd_kernel<BF16, D>), dim3(a.n_items), dim3(256), 0, s, a);
+  if (ev) (void)hipEventRecord(ev[0].stop, s);
   return hipGetLastError();
 }
 
 template <bool BF16, int D>
-hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents& ev) {
+hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   constexpr int LPR = D / 8;
   for (int st = 0; st < 2; ++st) {
     const int32_t n = st ? a.n_corr : a.n_clean_q;
@@ -671,22 +822,16 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents& ev) {
     const int64_t threads = (int64_t)n * a.H * LPR;
     const int blocks = int((threads + 255) / 256);
     hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3(blocks), dim3(256), 0, s,
-                       st ? a.o_x : a.o_c, st ? a.do_x : a.do_c, st ? a.d_x : a.d_c,
-                       st ? a.dqa_x : a.dqa_c, n, a.H);
+                       st ? a.o_x : a.o_c, st ? a.do_x : a.do_c, st ? a.d_x : a.d_c, n, a.H);
   }
-  if (ev.start) hipEventRecord(ev.start, s);
-  if (a.n_items > 0) {
-    hipLaunchKernelGGL((bwd_kernel<BF16, D>), dim3(a.n_items), dim3(256), 0, s, a);
-  }
-  if (ev.stop) hipEventRecord(ev.stop, s);
-  for (int st = 0; st < 2; ++st) {
-    const int32_t n = st ? a.n_corr : a.n_clean_q;
-    if (n == 0) continue;
-    const int64_t elems = (int64_t)n * a.H * D;
-    const int blocks = int(std::min<int64_t>((elems / 4 + 255) / 256, 16384));
-    hipLaunchKernelGGL((dq_convert_kernel<BF16>), dim3(blocks), dim3(256), 0, s,
-                       st ? a.dqa_x : a.dqa_c, st ? a.dq_x : a.dq_c, elems, a.scale);
-  }
+  if (ev) (void)hipEventRecord(ev[0].start, s);
+  if (a.n_q_items > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.n_q_items), dim3(256), 0, s, a);
+  if (ev) (void)hipEventRecord(ev[0].stop, s);
+  if (ev) (void)hipEventRecord(ev[1].start, s);
+  if (a.n_kv_items > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.n_kv_items), dim3(256), 0, s, a);
+  if (ev) (void)hipEventRecord(ev[1].stop, s);
   return hipGetLastError();
 }
 
@@ -698,14 +843,14 @@ bool have_kernels(int dtype, int d) {
   return false;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t s, const KernelEvents& ev) {
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t s, const KernelEvents* ev) {
   if (dtype == BDATTN_BF16 && d == 128) return run_fwd<true, 128>(a, s, ev);
   if (dtype == BDATTN_BF16 && d == 32) return run_fwd<true, 32>(a, s, ev);
   if (dtype == BDATTN_F32 && d == 32) return run_fwd<false, 32>(a, s, ev);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t s, const KernelEvents& ev) {
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t s, const KernelEvents* ev) {
   if (dtype == BDATTN_BF16 && d == 128) return run_bwd<true, 128>(a, s, ev);
   if (dtype == BDATTN_BF16 && d == 32) return run_bwd<true, 32>(a, s, ev);
   if (dtype == BDATTN_F32 && d == 32) return run_bwd<false, 32>(a, s, ev);

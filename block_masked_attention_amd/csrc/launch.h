@@ -25,11 +25,12 @@ struct BwdArgs {
   const float *lse_c, *lse_x;
   void *dq_c, *dq_x, *dk_c, *dv_c, *dk_x, *dv_x;
   const int32_t* ids;
-  const BwdItem* items;
-  int32_t n_items;
+  const FwdItem* q_items;  // dQ kernel: the forward's query-tile work list
+  int32_t n_q_items;
+  const BwdItem* kv_items;  // dK/dV kernel: key-tile work list
+  int32_t n_kv_items;
   float *d_c, *d_x;        // workspace: D = rowsum(dO * O)  [H][n]
-  float *dqa_c, *dqa_x;    // workspace: float dQ accumulators [n][H][d]
-  int32_t B, H, Hkv;
+  int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
   float scale, scale_log2;
 };
@@ -37,14 +38,16 @@ struct BwdArgs {
 // True if this build has kernels for (dtype, d).
 bool have_kernels(int dtype, int d);
 
-// Optional events recorded around the main kernel (null = none).
+// Events recorded around the main kernels (ev == nullptr: none). The forward
+// records ev[0] around its kernel; the backward records ev[0] around the dQ
+// kernel and ev[1] around the dK/dV kernel.
 struct KernelEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t stream,
-                      const KernelEvents& ev);
+                      const KernelEvents* ev);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t stream,
-                      const KernelEvents& ev);
+                      const KernelEvents* ev);
 
 }  // namespace bdattn

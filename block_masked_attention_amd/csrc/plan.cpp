@@ -118,33 +118,36 @@ int fwd_rows_per_item(const Problem& P) {
   return FWD_WAVES * FWD_ROWS_PER_WAVE / fwd_heads_per_group(P);
 }
 
-size_t n_items(const Problem& P, int pass) {
-  if (pass == 0) {
-    const int Gw = fwd_heads_per_group(P), R = fwd_rows_per_item(P);
-    size_t tiles = size_t(ceil_div(P.n_clean_q, R)) + size_t(ceil_div(P.n_corr(), R));
-    return tiles * size_t(P.H / Gw);
-  }
+size_t n_q_items(const Problem& P) {
+  const int Gw = fwd_heads_per_group(P), R = fwd_rows_per_item(P);
+  size_t tiles = size_t(ceil_div(P.n_clean_q, R)) + size_t(ceil_div(P.n_corr(), R));
+  return tiles * size_t(P.H / Gw);
+}
+
+size_t n_kv_items(const Problem& P) {
   size_t tiles = size_t(ceil_div(P.n_clean_kv, BWD_TK)) + size_t(ceil_div(P.n_corr(), BWD_TK));
   return tiles * size_t(P.Hkv);
 }
 
-WsLayout workspace_layout(const Problem& P, int pass, size_t items) {
+WsLayout workspace_layout(const Problem& P, int pass) {
   WsLayout w;
   size_t off = 0;
   w.ids = off;
   off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, P.ids.size()), WS_ALIGN);
-  w.items = off;
-  w.items_bytes = items * (pass == 0 ? sizeof(FwdItem) : sizeof(BwdItem));
-  off = align_up(off + std::max<size_t>(1, w.items_bytes), WS_ALIGN);
+  w.q_items = off;
+  w.q_items_bytes = n_q_items(P) * sizeof(FwdItem);
+  off = align_up(off + std::max<size_t>(1, w.q_items_bytes), WS_ALIGN);
+  if (pass == 1) {
+    w.kv_items = off;
+    w.kv_items_bytes = n_kv_items(P) * sizeof(BwdItem);
+    off = align_up(off + std::max<size_t>(1, w.kv_items_bytes), WS_ALIGN);
+  }
+  w.staged = off;
   if (pass == 1) {
     w.d_c = off;
     off = align_up(off + sizeof(float) * size_t(P.H) * P.n_clean_q, WS_ALIGN);
     w.d_x = off;
     off = align_up(off + sizeof(float) * size_t(P.H) * P.n_corr(), WS_ALIGN);
-    w.dqa_c = off;
-    off = align_up(off + sizeof(float) * size_t(P.n_clean_q) * P.H * P.d, WS_ALIGN);
-    w.dqa_x = off;
-    off = align_up(off + sizeof(float) * size_t(P.n_corr()) * P.H * P.d, WS_ALIGN);
   }
   w.total = off;
   return w;
@@ -209,19 +212,34 @@ void build_plan(const Problem& P, Plan* plan) {
       int32_t c0 = std::min<int32_t>(P.n_clean_q, std::max<int32_t>(0, kb * P.B - P.clean_q_start));
       int32_t j = int32_t(std::upper_bound(P.ids.begin(), P.ids.end(), kb) - P.ids.begin());
       int32_t x0 = j * P.B;
-      BwdItem it{kt, 0, c0, P.n_clean_q, x0, nx};
-      // a q tile needs the mask unless its first row sees the whole key tile
+      // a q tile needs the mask unless it lies inside the swept rows and its
+      // first row sees the whole key tile (row bounds are nondecreasing, so
+      // the unmasked tiles are the top ones of each stream)
       int64_t qt = qtiles(c0, P.n_clean_q) + qtiles(x0, nx), masked = 0;
-      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r < P.n_clean_q; r += BWD_TQ)
-        if (r < c0 || row_bounds(P, 0, r).cb < k1 || k1 - k0 < BWD_TK) ++masked; else break;
-      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r < nx; r += BWD_TQ)
-        if (r < x0 || row_bounds(P, 1, r).cb < k1 || k1 - k0 < BWD_TK) ++masked; else break;
+      int32_t cf = P.n_clean_q, xf = nx;
+      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r < P.n_clean_q; r += BWD_TQ) {
+        if (r < c0 || row_bounds(P, 0, r).cb < k1 || k1 - k0 < BWD_TK) {
+          ++masked;
+        } else {
+          cf = r;
+          break;
+        }
+      }
+      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r < nx; r += BWD_TQ) {
+        if (r < x0 || row_bounds(P, 1, r).cb < k1 || k1 - k0 < BWD_TK) {
+          ++masked;
+        } else {
+          xf = r;
+          break;
+        }
+      }
+      BwdItem it{kt, 0, c0, P.n_clean_q, x0, nx, cf, xf};
       tiles.push_back({kt, 0, it, (P.n_clean_q - c0) + int64_t(nx - x0), qt, masked});
     }
     for (int32_t kt = 0; kt * int64_t(BWD_TK) < nx; ++kt) {
       const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(nx, k0 + BWD_TK);
       const int32_t x0 = k0 / P.B * P.B, x1 = std::min<int32_t>(nx, ceil_div(k1, P.B) * P.B);
-      BwdItem it{kt, 1, 0, 0, x0, x1};
+      BwdItem it{kt, 1, 0, 0, x0, x1, 0, x1};
       const int64_t qt = qtiles(x0, x1);
       tiles.push_back({kt, 1, it, x1 - x0, qt, qt});
     }

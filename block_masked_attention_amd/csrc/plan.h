@@ -35,11 +35,14 @@ struct FwdItem {
 
 // One backward work item: key tile `ktile` of the key stream (bit 0 of hs) of
 // KV head hs >> 1; sweeps clean query rows [c0, c1) and corrupted rows
-// [x0, x1).
+// [x0, x1). Query tiles (BWD_TQ rows, aligned) starting at or after cf
+// (clean) / xf (corrupted) see every key of the tile and skip the mask; cf =
+// c1 / xf = x1 when no tile does.
 struct BwdItem {
   int32_t ktile;
   int32_t hs;
   int32_t c0, c1, x0, x1;
+  int32_t cf, xf;
 };
 
 struct Problem {
@@ -70,15 +73,19 @@ struct Plan {
 
 void build_plan(const Problem& P, Plan* plan);
 
-// Workspace layout (byte offsets from the workspace start).
+// Workspace layout (byte offsets from the workspace start). Forward: the
+// corrupted block ids and the query-tile work list. Backward: the ids, the
+// query-tile list (dQ kernel), the key-tile list (dK/dV kernel) and
+// D = rowsum(dO * O) of each stream.
 struct WsLayout {
-  size_t ids = 0, items = 0, items_bytes = 0;
-  size_t d_c = 0, d_x = 0;      // bwd: D = rowsum(dO * O), float [H][n]
-  size_t dqa_c = 0, dqa_x = 0;  // bwd: float dQ accumulators [n][H][d]
+  size_t ids = 0, q_items = 0, q_items_bytes = 0, kv_items = 0, kv_items_bytes = 0;
+  size_t d_c = 0, d_x = 0;  // bwd: float [H][n]
+  size_t staged = 0;        // bytes copied from the host (ids and work lists)
   size_t total = 0;
 };
-WsLayout workspace_layout(const Problem& P, int pass, size_t n_items);
-size_t n_items(const Problem& P, int pass);
+WsLayout workspace_layout(const Problem& P, int pass);
+size_t n_q_items(const Problem& P);
+size_t n_kv_items(const Problem& P);
 
 int64_t visible_pairs(const Problem& P);
 void mask_render(const Problem& P, uint8_t* out);

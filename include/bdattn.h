@@ -36,7 +36,8 @@
  * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
  * the caller. bdattn_fwd / bdattn_bwd enqueue work on `hip_stream` (a
  * hipStream_t; NULL = the default stream) and return without waiting; they
- * never allocate device memory. Scratch space is the caller's `workspace`
+ * never allocate device memory. They use no atomics: results are bitwise
+ * reproducible for a given problem and inputs. Scratch space is the caller's `workspace`
  * (device memory of at least bdattn_workspace_size bytes, 256-byte aligned),
  * which must not be used by anything else until the enqueued work is done.
  * Outputs are overwritten, never accumulated into. Tensor pointers must be
@@ -159,14 +160,14 @@ int bdattn_bwd(const bdattn_problem* p,
 
 /* Optional instrumentation for benchmarks. With profiling on (per calling
  * thread), bdattn_fwd and bdattn_bwd record a pair of HIP events on the
- * call's stream around their main kernel (the forward kernel; the backward's
- * key-tile kernel, without its D and dQ-conversion kernels). bdattn_profile_read
- * waits for the recorded events, returns the summed milliseconds and the
- * number of launches of each since the last read, and releases the events.
- * Off by default; costs nothing when off. */
+ * call's stream around each of their main kernels: index 0 = the forward
+ * kernel, 1 = the backward dQ kernel, 2 = the backward dK/dV kernel (the
+ * backward's D = rowsum(dO*O) kernel is not timed). bdattn_profile_read
+ * waits for the recorded events, writes ms[0..2] (summed milliseconds) and
+ * launches[0..2] (number of launches) since the last read, and releases the
+ * events; either pointer may be NULL. Off by default; costs nothing when off. */
 int bdattn_profile_enable(int on);
-int bdattn_profile_read(double* fwd_ms, int64_t* fwd_launches, double* bwd_ms,
-                        int64_t* bwd_launches);
+int bdattn_profile_read(double* ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

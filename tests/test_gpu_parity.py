@@ -91,18 +91,15 @@ def test_tiny_workload_full_parity():
 
 
 def test_repeat_calls_and_determinism():
-    """Forward is bitwise repeatable; the backward's dK/dV are written once
-    per key (bitwise repeatable); dQ uses atomics (within tolerance)."""
+    """No kernel uses atomics and every output element is written by one
+    thread, so repeated calls are bitwise identical."""
     _need_gpu()
     spec = small_spec(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=3)
     t = make_inputs(spec, device="cuda")
     a = run_gpu(spec, t)
     b = run_gpu(spec, t)
-    for k in ("o_c", "o_x", "lse_c", "lse_x", "dk_c", "dv_c", "dk_x", "dv_x"):
+    for k in OUT_NAMES:
         assert torch.equal(a[k], b[k]), k
-    for k in ("dq_c", "dq_x"):
-        d = (a[k].float() - b[k].float()).abs().max().item()
-        assert d <= 2e-2 * a[k].float().pow(2).mean().sqrt().item()
 
 
 def test_outputs_fully_overwritten():
