@@ -327,6 +327,8 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.n_kv_items = int32_t(plan->bwd.size());
   a.d_c = (float*)(ws + w.d_c);
   a.d_x = (float*)(ws + w.d_x);
+  a.l2_c = (float*)(ws + w.l2_c);
+  a.l2_x = (float*)(ws + w.l2_x);
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();

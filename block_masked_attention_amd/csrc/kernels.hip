@@ -11,7 +11,7 @@
 //
 // Kernels:
 //   fwd_kernel       query-tile parallel: online softmax over the visible keys
-//   bwd_prep_kernel  D = rowsum(dO * O)
+//   bwd_prep_kernel  D = rowsum(dO * O) and LSE * log2(e) per query row
 //   bwd_dq_kernel    query-tile parallel: dQ = scale * dS K, written once
 //   bwd_dkdv_kernel  key-tile parallel: dV = P^T dO, dK = scale * dS^T Q over
 //                    every query tile (and q head of the KV group) that sees
@@ -34,12 +34,14 @@
 //   C (32 x 32, 16 floats): column l%32, element i is row 8(i/4) + 4h + i%4.
 //
 // LDS tiles are row-major with no padding; the 16-byte chunk c of row r sits
-// at chunk position c ^ swz(r), swz(r) = 2(r%4) + (r/4)%2. A row-slice operand
-// (8 consecutive rows, same chunk) and a transposed operand (4 consecutive
-// rows x 32 bytes, read with ds_read_b64_tr_b16) both hit 32 distinct banks.
-// The transposed read gives lane i of each 16-lane group column i of four
-// consecutive rows, i.e. the operand of a matrix whose contraction index runs
-// down the tile's rows, so no transposed copy is ever stored.
+// at chunk position c ^ swz(r), swz(r) = 4(r%4) + (r/4)%4. The LDS has 64
+// banks: a row-slice operand read (ds_read_b128, 16 lanes per cycle = 16
+// consecutive rows, same chunk) and a transposed operand read
+// (ds_read_b64_tr_b16, 32 lanes per cycle = 4 consecutive rows x 64 bytes)
+// both hit 64 distinct banks. The transposed read gives lane i of each 16-lane
+// group column i of four consecutive rows, i.e. the operand of a matrix whose
+// contraction index runs down the tile's rows, so no transposed copy is ever
+// stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,13 +75,17 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Chunk swizzle of row r in a tile with NCH 16-byte chunks per row.
+template <int NCH>
+__device__ __forceinline__ int tile_swz(int r) {
+  return (((r & 3) << 2) | ((r >> 2) & 3)) & (NCH - 1);
+}
+
 // Element offset of (row r, column col) in a swizzled tile of D-element rows
 // with EPC elements per 16-byte chunk.
 template <int D, int EPC>
 __device__ __forceinline__ int tile_off(int r, int col) {
-  constexpr int NCH = D / EPC;
-  const int s = (((r & 3) << 1) | ((r >> 2) & 1)) & (NCH - 1);
-  return r * D + (((col / EPC) ^ s) * EPC) + (col % EPC);
+  return r * D + (((col / EPC) ^ tile_swz<D / EPC>(r)) * EPC) + (col % EPC);
 }
 
 // ----------------------------------------------------------------- elements
@@ -114,27 +120,6 @@ struct Elem<true> {
   static __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
     *(uint2*)p = make_uint2(pack2(a, b), pack2(c, d));
   }
-  // Row slice of an LDS tile: 8 consecutive elements of row r from column col.
-  template <int D>
-  static __device__ __forceinline__ Frag lds_row(const T* tile, int r, int col) {
-    return Frag{*(const uint4*)(tile + tile_off<D, EPC>(r, col))};
-  }
-  // Operand whose contraction index runs down the tile's rows: lane l takes
-  // column n0 + l%32, slot j of half h takes row k0 + (natural or result
-  // order). Two transposed reads of four rows each.
-  template <int D, bool RESULT>
-  static __device__ __forceinline__ Frag lds_tr(const T* tile, int k0, int n0, int lane) {
-    const int r = lane & 15, c = (lane >> 4) & 1, h = lane >> 5;
-    const int col = n0 + 16 * c + 4 * (r & 3);
-    const int row0 = k0 + (RESULT ? 4 * h : 8 * h) + (r >> 2);
-    const int dt = RESULT ? 8 : 4;
-    const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_shortx4*)(tile + tile_off<D, EPC>(row0, col)));
-    const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_shortx4*)(tile + tile_off<D, EPC>(row0 + dt, col)));
-    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
-    return Frag{make_uint4(ux.x, ux.y, uy.x, uy.y)};
-  }
 };
 
 template <>
@@ -168,21 +153,88 @@ struct Elem<false> {
   static __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
     *(float4*)p = make_float4(a, b, c, d);
   }
-  template <int D>
-  static __device__ __forceinline__ Frag lds_row(const T* tile, int r, int col) {
-    return Frag{*(const float4*)(tile + tile_off<D, EPC>(r, col)),
-                *(const float4*)(tile + tile_off<D, EPC>(r, col + 4))};
-  }
-  template <int D, bool RESULT>
-  static __device__ __forceinline__ Frag lds_tr(const T* tile, int k0, int n0, int lane) {
-    const int n = n0 + (lane & 31), h = lane >> 5;
-    float x[8];
+};
+
+// Per-lane byte offsets of the operand reads from swizzled LDS tiles. The
+// swizzle depends on a row's low 4 bits only, so 32-row blocks and 16-row
+// steps add compile-time constants to a few offsets fixed per lane. Offsets
+// are relative to the start of the kernel's LDS array (one constant base) and
+// include the current buffer of a double-buffered pair whose buffers are BUF
+// bytes apart (BUF a power of two); flip() switches to the other buffer.
+template <bool BF16, int D, uint32_t BUF>
+struct OperandReads {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  using Frag = typename E::Frag;
+  static constexpr int EPC = E::EPC;
+  static constexpr uint32_t ROW = D * sizeof(T);  // bytes per tile row
+  static constexpr int NCHF = BF16 ? 1 : 2;       // 16-byte chunks per fragment
+  static constexpr int NTR = BF16 ? 2 : 8;         // reads per transposed fragment
+  uint32_t row[D / 16][NCHF];  // row lane%32, column 16 ks + 8 (lane/32) (+4)
+  uint32_t tr[D / 32][NTR];    // transposed: see tr_frag
+
+  __device__ __forceinline__ void init(int lane) {
+    const int lq = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = k0 + (RESULT ? 8 * (j >> 2) + 4 * h : 8 * h + 4 * (j >> 2)) + (j & 3);
-      x[j] = tile[tile_off<D, EPC>(row, n)];
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int c = 0; c < NCHF; ++c)
+        row[ks][c] = sizeof(T) * tile_off<D, EPC>(lq, 16 * ks + 8 * h + 4 * c);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      if (BF16) {
+        // ds_read_b64_tr_b16: lanes r/4 = 0..3 of each 16-lane group address
+        // four consecutive rows, 4 r%4 columns apart (see the file header)
+        const int r = lane & 15, c = (lane >> 4) & 1;
+        const int col = 32 * db + 16 * c + 4 * (r & 3);
+#pragma unroll
+        for (int t = 0; t < NTR; ++t)
+          tr[db][t] = sizeof(T) * tile_off<D, EPC>(8 * t + 4 * h + (r >> 2), col);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NTR; ++j)
+          tr[db][j] = sizeof(T) * tile_off<D, EPC>(8 * (j >> 2) + 4 * h + (j & 3), 32 * db + lq);
+      }
     }
-    return pack(x);
+  }
+  __device__ __forceinline__ void flip() {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int c = 0; c < NCHF; ++c) row[ks][c] ^= BUF;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int t = 0; t < NTR; ++t) tr[db][t] ^= BUF;
+  }
+  // 8 consecutive elements of row 32 mb + lane%32, from column 16 ks + 8
+  // (lane/32), of the tile TILE bytes into the current buffer.
+  template <uint32_t TILE>
+  __device__ __forceinline__ Frag row_frag(const void* lds, int mb, int ks) const {
+    const char* b = (const char*)lds + TILE + mb * 32 * ROW;
+    if constexpr (BF16) {
+      return Frag{*(const uint4*)(b + row[ks][0])};
+    } else {
+      return Frag{*(const float4*)(b + row[ks][0]), *(const float4*)(b + row[ks][1])};
+    }
+  }
+  // Operand whose contraction index runs down the tile rows, in result order:
+  // lane l takes column 32 db + l%32; slot j of half h takes row
+  // k0 + 8 (j/4) + 4 h + j%4 (k0 a multiple of 16).
+  template <uint32_t TILE>
+  __device__ __forceinline__ Frag tr_frag(const void* lds, int k0, int db) const {
+    const char* b = (const char*)lds + TILE + k0 * ROW;
+    if constexpr (BF16) {
+      const shortx4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(b + tr[db][0]));
+      const shortx4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(b + tr[db][1]));
+      const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+      return Frag{make_uint4(ux.x, ux.y, uy.x, uy.y)};
+    } else {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = *(const float*)(b + tr[db][j]);
+      return E::pack(x);
+    }
   }
 };
 
@@ -233,7 +285,7 @@ __device__ __forceinline__ void tile_dma(T* tile, const T* src, int64_t stride, 
   for (int u = 0; u < CPW; ++u) {
     const int pos = u * 256 + wave * 64 + lane;  // chunk position in the tile
     const int r = pos / NCH, p = pos % NCH;
-    const int c = p ^ ((((r & 3) << 1) | ((r >> 2) & 1)) & (NCH - 1));  // source chunk
+    const int c = p ^ tile_swz<NCH>(r);  // source chunk
     const int row = min(row0 + r, nrows - 1);
     lds_dma16(src + (int64_t)row * stride + c * EPC,
               __builtin_amdgcn_readfirstlane(base + uint32_t(u * 256 + wave * 64) * 16u));
@@ -292,6 +344,7 @@ void fwd_kernel(FwdArgs a) {
   constexpr int TSZ = TK * D;
   static_assert(4 * TSZ * sizeof(T) <= 80 * 1024, "LDS (two workgroups per CU)");
   __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][K, V]
+  constexpr uint32_t VT = TSZ * sizeof(T);                   // V tile offset in a buffer
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
@@ -321,6 +374,9 @@ void fwd_kernel(FwdArgs a) {
     tile_dma<T, TK, D>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
   };
 
+  OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
+  rd.init(lane);
+
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = zero16();
@@ -332,8 +388,6 @@ void fwd_kernel(FwdArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     for (int j = j0; j < j1; ++j) {
       if (j + 1 < n_tiles) fetch(j + 1, (j + 1) & 1);
-      const T* Ks = smem + (j & 1) * 2 * TSZ;
-      const T* Vs = Ks + TSZ;
       const bool cl = j < q.n_ct;
       const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
 
@@ -343,7 +397,7 @@ void fwd_kernel(FwdArgs a) {
       s[mb] = zero16();
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        E::mma(s[mb], E::template lds_row<D>(Ks, 32 * mb + lq, 16 * ks + 8 * hf), qf[ks]);
+        E::mma(s[mb], rd.template row_frag<0>(smem, mb, ks), qf[ks]);
     }
     // online softmax; the row max is taken on raw scores (the scale is > 0)
     // and the scale folded into the exponent's multiply-add
@@ -394,11 +448,11 @@ void fwd_kernel(FwdArgs a) {
         for (int mb = 0; mb < TK / 32; ++mb) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            E::mma(o[db], E::template lds_tr<D, true>(Vs, 32 * mb + 16 * t, 32 * db, lane),
-                   pf[mb][t]);
+            E::mma(o[db], rd.template tr_frag<VT>(smem, 32 * mb + 16 * t, db), pf[mb][t]);
         }
       }
     }
+      rd.flip();
       lds_dma_wait();
       __syncthreads();
     }
@@ -428,20 +482,25 @@ void fwd_kernel(FwdArgs a) {
 }
 
 // ======================================================================
-// Backward preprocess: D = rowsum(dO * O) per (row, head), D/8 lanes each.
+// Backward preprocess: per (row, head) D = rowsum(dO * O) and LSE * log2(e),
+// D/8 lanes each, written [H][n_pad]; rows n..n_pad-1 get D = 0, LSE = +inf
+// (query tiles past the end of a stream then contribute nothing).
 // ======================================================================
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const void* do_, float* Dout,
-                                                       int32_t n_rows, int32_t H) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const void* do_,
+                                                       const float* lse, float* Dout, float* L2out,
+                                                       int32_t n_rows, int32_t n_pad, int32_t H) {
   using E = Elem<BF16>;
   using T = typename E::T;
   constexpr int LPR = D / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t pair = idx / LPR;
   const int sub = int(idx % LPR);
-  const int64_t npairs = (int64_t)n_rows * H;
+  const int64_t npairs = (int64_t)n_pad * H;
+  const int64_t row = pair / H, head = pair % H;
+  const bool real = pair < npairs && row < n_rows;
   float acc = 0.f;
-  if (pair < npairs) {
+  if (real) {
     typename E::Frag fo = E::load((const T*)o_ + pair * D + 8 * sub);
     typename E::Frag fg = E::load((const T*)do_ + pair * D + 8 * sub);
     const T* po = (const T*)&fo;
@@ -452,8 +511,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
   if (pair < npairs && sub == 0) {
-    const int64_t row = pair / H, head = pair % H;
-    Dout[head * n_rows + row] = acc;
+    Dout[head * n_pad + row] = real ? acc : 0.f;
+    L2out[head * n_pad + row] = real ? lse[head * n_rows + row] * kLog2e : __builtin_inff();
   }
 }
 
@@ -473,6 +532,7 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int TSZ = TK * D;
   static_assert(4 * TSZ * sizeof(T) <= 80 * 1024, "LDS (two workgroups per CU)");
   __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][K, V]
+  constexpr uint32_t VT = TSZ * sizeof(T);                   // V tile offset in a buffer
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, hf = lane >> 5;
@@ -491,11 +551,9 @@ void bwd_dq_kernel(BwdArgs a) {
       gf[ks] = q.row_ok ? E::load(gsrc + off + 16 * ks + 8 * hf) : E::zero();
     }
   }
-  const float* lse = q.stream ? a.lse_x : a.lse_c;
-  const float* dd = q.stream ? a.d_x : a.d_c;
-  const float lse2 = q.row_ok ? lse[(int64_t)q.head * q.n_rows + q.crow] * kLog2e
-                              : __builtin_inff();
-  const float drow = q.row_ok ? dd[(int64_t)q.head * q.n_rows + q.crow] : 0.f;
+  const int64_t ri = (int64_t)q.head * row_pad(q.n_rows) + q.crow;
+  const float lse2 = q.row_ok ? (q.stream ? a.l2_x : a.l2_c)[ri] : __builtin_inff();
+  const float drow = q.row_ok ? (q.stream ? a.d_x : a.d_c)[ri] : 0.f;
 
   // stage key tile j (K then V) into LDS buffer `buf`
   auto fetch = [&](int j, int buf) {
@@ -509,6 +567,9 @@ void bwd_dq_kernel(BwdArgs a) {
     tile_dma<T, TK, D>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
   };
 
+  OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
+  rd.init(lane);
+
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
@@ -519,8 +580,6 @@ void bwd_dq_kernel(BwdArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     for (int j = j0; j < j1; ++j) {
       if (j + 1 < n_tiles) fetch(j + 1, (j + 1) & 1);
-      const T* Ks = smem + (j & 1) * 2 * TSZ;
-      const T* Vs = Ks + TSZ;
       const bool cl = j < q.n_ct;
       const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
       Frag sf[TK / 32][2];
@@ -529,8 +588,8 @@ void bwd_dq_kernel(BwdArgs a) {
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          E::mma(s, E::template lds_row<D>(Ks, 32 * mb + lq, 16 * ks + 8 * hf), qf[ks]);
-          E::mma(dp, E::template lds_row<D>(Vs, 32 * mb + lq, 16 * ks + 8 * hf), gf[ks]);
+          E::mma(s, rd.template row_frag<0>(smem, mb, ks), qf[ks]);
+          E::mma(dp, rd.template row_frag<VT>(smem, mb, ks), gf[ks]);
         }
         float ds[16];
 #pragma unroll
@@ -553,11 +612,11 @@ void bwd_dq_kernel(BwdArgs a) {
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
-            E::mma(dq[db], E::template lds_tr<D, true>(Ks, 32 * mb + 16 * t, 32 * db, lane),
-                   sf[mb][t]);
+            E::mma(dq[db], rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db), sf[mb][t]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      rd.flip();
       lds_dma_wait();
       __syncthreads();
     }
@@ -585,11 +644,11 @@ void bwd_dq_kernel(BwdArgs a) {
 // Backward, dK/dV. One workgroup = 4 waves owning BWD_TK keys of one KV head
 // (32 per wave, kept in registers as the B operand of S = Q K^T and
 // dP = dO V^T). It sweeps every query tile (BWD_TQ rows) that sees its keys,
-// for each q head of the group, with the next tile's Q, dO and row data
-// prefetched into registers and stored to the other LDS buffer while the
-// current one is in use: S, dP; P = exp2(S c - LSE2); dS = P (dP - D);
+// for each q head of the group: S, dP; P = exp2(S c - LSE2); dS = P (dP - D);
 // dV += P^T dO and dK += dS^T Q, with dO and Q read transposed from their
-// row-major tiles.
+// row-major tiles. The next step's Q and dO tiles and its LSE2 / D values are
+// copied into the other LDS buffer while the current one is in use. Tiles
+// whose rows all see every key of the workgroup come first and skip the mask.
 // ======================================================================
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -599,15 +658,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
   using Frag = typename E::Frag;
   constexpr int TK = BWD_TK, TQ = BWD_TQ;
   constexpr int TSZ = TQ * D;
-  static_assert(4 * TSZ * sizeof(T) + 8 * TQ * 4 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float r_lse2[2][TQ];
-  __shared__ __attribute__((aligned(16))) float r_d[2][TQ];
-  __shared__ __attribute__((aligned(16))) int32_t r_lo[2][TQ];
-  __shared__ __attribute__((aligned(16))) int32_t r_hi[2][TQ];
+  static_assert(TQ == 64, "row data copy assumes 64-row query tiles");
+  static_assert(4 * TSZ * sizeof(T) + 4 * TQ * 4 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];            // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];      // [buffer][LSE2, D]
+  constexpr uint32_t GT = TSZ * sizeof(T);                             // dO tile offset in a buffer
 
   const BwdItem item = a.kv_items[blockIdx.x];
   const int it_x0 = item.x0, it_x1 = item.x1, it_c0 = item.c0, it_c1 = item.c1;
+  const int it_xf = item.xf, it_cf = item.cf;
   const int kstream = item.hs & 1, kvh = item.hs >> 1;
   const int G = a.H / a.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -616,6 +675,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int n_keys = kstream ? a.n_corr : a.n_clean_kv;
   const int my_key = key0 + 32 * wave + lk;
   const bool key_ok = my_key < n_keys;
+  const int key_blk = my_key / a.B;  // clean: global block; corrupted: local block
 
   // this lane's key and value as B operands (natural order over d)
   Frag kf[D / 16], vf[D / 16];
@@ -630,6 +690,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
+  rd.init(lane);
+
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
@@ -641,7 +704,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // key of the workgroup (those starting at or after xf / cf) come first, then
   // the ones that need the mask; within each, corrupted tiles then clean ones,
   // each from the last tile down, every q head of the group per tile.
-  const int it_xf = item.xf, it_cf = item.cf;
   auto ntiles = [](int r0, int r1) { return r1 > r0 ? (r1 - 1) / TQ - r0 / TQ + 1 : 0; };
   const int top_x = (it_x1 - 1) / TQ, top_c = (it_c1 - 1) / TQ;
   const int nf_x = it_xf < it_x1 ? top_x - it_xf / TQ + 1 : 0;
@@ -673,10 +735,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     return s;
   };
 
-  // stage the Q and dO tiles of step s into LDS buffer `buf` (DMA) and fetch
-  // its row data into registers (threads 0..TQ-1), stored by stage_rows
-  float p_lse2 = 0.f, p_d = 0.f;
-  int p_lo = 0, p_hi = 0;
+  // copy step s's Q and dO tiles and its LSE2 / D rows into LDS buffer `buf`
   auto fetch = [&](const Step& s, int buf) {
     const int n_rows = s.qs ? a.n_corr : a.n_clean_q;
     const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
@@ -684,30 +743,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
     T* dst = smem + buf * 2 * TSZ;
     tile_dma<T, TQ, D>(dst, qsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
     tile_dma<T, TQ, D>(dst + TSZ, gsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
-    if (tid < TQ) {
-      const int row = s.q0 + tid;
-      if (row < n_rows) {
-        const float* lse = s.qs ? a.lse_x : a.lse_c;
-        const float* dd = s.qs ? a.d_x : a.d_c;
-        const BdRowBounds b = row_bounds(s.qs, row, a.clean_q_start, a.ids, a.B);
-        p_lse2 = lse[(int64_t)s.h * n_rows + row] * kLog2e;
-        p_d = dd[(int64_t)s.h * n_rows + row];
-        p_lo = kstream ? b.xlo : 0;
-        p_hi = kstream ? b.xhi : b.cb;
-      } else {
-        p_lse2 = __builtin_inff();
-        p_d = 0.f;
-        p_lo = 0;
-        p_hi = 0;
-      }
-    }
-  };
-  auto stage_rows = [&](int buf) {
-    if (tid < TQ) {
-      r_lse2[buf][tid] = p_lse2;
-      r_d[buf][tid] = p_d;
-      r_lo[buf][tid] = p_lo;
-      r_hi[buf][tid] = p_hi;
+    if (wave == 0 && lane < 32) {  // lanes 0-15: 64 LSE2 values, 16-31: 64 D values
+      const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane & 15);
+      const float* src = (lane < 16 ? (s.qs ? a.l2_x : a.l2_c) : (s.qs ? a.d_x : a.d_c)) + r0;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(&r_row[buf][0][0])));
     }
   };
 
@@ -715,39 +754,38 @@ void bwd_dkdv_kernel(BwdArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     for (int i = i0; i < i1; ++i) {
       const int cur = i & 1;
+      const Step st = step(i);
       if (i + 1 < n_it) fetch(step(i + 1), cur ^ 1);
-      const T* Qs = smem + cur * 2 * TSZ;
-      const T* Gs = Qs + TSZ;
-    {
+      const int n_rows = st.qs ? a.n_corr : a.n_clean_q;
+      // visibility of (query row, this lane's key) on tiles that need the mask
+      auto sees = [&](int row) -> bool {
+        if (!key_ok || row >= n_rows) return false;
+        if (kstream) return row / a.B == key_blk;  // own corrupted block
+        if (st.qs == 0) return key_blk <= (a.clean_q_start + row) / a.B;
+        return key_blk < a.ids[row / a.B];
+      };
       Frag pa[TQ / 32][2], sa[TQ / 32][2];
 #pragma unroll
       for (int mb = 0; mb < TQ / 32; ++mb) {
         f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          E::mma(sacc, E::template lds_row<D>(Qs, 32 * mb + lk, 16 * ks + 8 * hf), kf[ks]);
-          E::mma(pacc, E::template lds_row<D>(Gs, 32 * mb + lk, 16 * ks + 8 * hf), vf[ks]);
+          E::mma(sacc, rd.template row_frag<0>(smem, mb, ks), kf[ks]);
+          E::mma(pacc, rd.template row_frag<GT>(smem, mb, ks), vf[ks]);
         }
         float p[16], ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qr = 32 * mb + 8 * g + 4 * hf;
-          const float4 l4 = *(const float4*)(&r_lse2[cur][qr]);
-          const float4 d4 = *(const float4*)(&r_d[cur][qr]);
+          const float4 l4 = *(const float4*)(&r_row[cur][0][qr]);
+          const float4 d4 = *(const float4*)(&r_row[cur][1][qr]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
           const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-          int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
-          if (MASK) {
-            const int4 lo4 = *(const int4*)(&r_lo[cur][qr]);
-            const int4 hi4 = *(const int4*)(&r_hi[cur][qr]);
-            lo[0] = lo4.x; lo[1] = lo4.y; lo[2] = lo4.z; lo[3] = lo4.w;
-            hi[0] = hi4.x; hi[1] = hi4.y; hi[2] = hi4.z; hi[3] = hi4.w;
-          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int e = 4 * g + r;
             float pv = fast_exp2(fmaf(sacc[e], a.scale_log2, -lv[r]));
-            if (MASK) pv = (key_ok && my_key >= lo[r] && my_key < hi[r]) ? pv : 0.f;
+            if (MASK) pv = sees(st.q0 + qr + r) ? pv : 0.f;
             p[e] = pv;
             ds[e] = pv * (pacc[e] - dv4[r]);
           }
@@ -765,24 +803,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            E::mma(dv[db], pa[mb][t],
-                   E::template lds_tr<D, true>(Gs, 32 * mb + 16 * t, 32 * db, lane));
-            E::mma(dk[db], sa[mb][t],
-                   E::template lds_tr<D, true>(Qs, 32 * mb + 16 * t, 32 * db, lane));
+            E::mma(dv[db], pa[mb][t], rd.template tr_frag<GT>(smem, 32 * mb + 16 * t, db));
+            E::mma(dk[db], sa[mb][t], rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
-      if (i + 1 < n_it) stage_rows(cur ^ 1);
+      rd.flip();
       lds_dma_wait();
       __syncthreads();
     }
   };
-  if (n_it > 0) {
-    fetch(step(0), 0);
-    stage_rows(0);
-  }
+  if (n_it > 0) fetch(step(0), 0);
   lds_dma_wait();
   __syncthreads();
   sweep(std::false_type{}, 0, n_full);
@@ -819,10 +851,12 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   for (int st = 0; st < 2; ++st) {
     const int32_t n = st ? a.n_corr : a.n_clean_q;
     if (n == 0) continue;
-    const int64_t threads = (int64_t)n * a.H * LPR;
+    const int32_t n_pad = row_pad(n);
+    const int64_t threads = (int64_t)n_pad * a.H * LPR;
     const int blocks = int((threads + 255) / 256);
     hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3(blocks), dim3(256), 0, s,
-                       st ? a.o_x : a.o_c, st ? a.do_x : a.do_c, st ? a.d_x : a.d_c, n, a.H);
+                       st ? a.o_x : a.o_c, st ? a.do_x : a.do_c, st ? a.lse_x : a.lse_c,
+                       st ? a.d_x : a.d_c, st ? a.l2_x : a.l2_c, n, n_pad, a.H);
   }
   if (ev) (void)hipEventRecord(ev[0].start, s);
   if (a.n_q_items > 0)

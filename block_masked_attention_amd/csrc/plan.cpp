@@ -144,10 +144,16 @@ WsLayout workspace_layout(const Problem& P, int pass) {
   }
   w.staged = off;
   if (pass == 1) {
+    const size_t rc = sizeof(float) * size_t(P.H) * row_pad(P.n_clean_q);
+    const size_t rx = sizeof(float) * size_t(P.H) * row_pad(P.n_corr());
     w.d_c = off;
-    off = align_up(off + sizeof(float) * size_t(P.H) * P.n_clean_q, WS_ALIGN);
+    off = align_up(off + rc, WS_ALIGN);
+    w.l2_c = off;
+    off = align_up(off + rc, WS_ALIGN);
     w.d_x = off;
-    off = align_up(off + sizeof(float) * size_t(P.H) * P.n_corr(), WS_ALIGN);
+    off = align_up(off + rx, WS_ALIGN);
+    w.l2_x = off;
+    off = align_up(off + rx, WS_ALIGN);
   }
   w.total = off;
   return w;

@@ -77,12 +77,16 @@ void build_plan(const Problem& P, Plan* plan);
 // corrupted block ids and the query-tile work list. Backward: the ids, the
 // query-tile list (dQ kernel), the key-tile list (dK/dV kernel) and
 // D = rowsum(dO * O) of each stream.
+// The backward's per-row data of each stream, D = rowsum(dO * O) and
+// LSE * log2(e), are float [H][round_up(n, BWD_TQ)]: every query tile's
+// values are one contiguous run, and rows past n hold D = 0, LSE = +inf.
 struct WsLayout {
   size_t ids = 0, q_items = 0, q_items_bytes = 0, kv_items = 0, kv_items_bytes = 0;
-  size_t d_c = 0, d_x = 0;  // bwd: float [H][n]
-  size_t staged = 0;        // bytes copied from the host (ids and work lists)
+  size_t d_c = 0, d_x = 0, l2_c = 0, l2_x = 0;  // bwd row data
+  size_t staged = 0;  // bytes copied from the host (ids and work lists)
   size_t total = 0;
 };
+BD_HD int32_t row_pad(int32_t n) { return (n + BWD_TQ - 1) / BWD_TQ * BWD_TQ; }
 WsLayout workspace_layout(const Problem& P, int pass);
 size_t n_q_items(const Problem& P);
 size_t n_kv_items(const Problem& P);
