@@ -19,7 +19,6 @@ HEADERS = ["bdattn_mask.h", "plan.h", "launch.h"]
 # form them from plain float code).
 HIP_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
-    "-munsafe-fp-atomics",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]

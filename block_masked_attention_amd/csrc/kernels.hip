@@ -272,23 +272,26 @@ __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0
 
 // Stage rows [row0, row0 + R) of a token-major tensor (row stride `stride`
 // elements) into the swizzled R x D tile at `tile`. Rows past nrows - 1 repeat
-// row nrows - 1 (callers mask them). All 4 waves take part.
-template <typename T, int R, int D>
+// row nrows - 1 (callers mask them). All NW waves of the workgroup take part.
+template <typename T, int R, int D, int NW>
 __device__ __forceinline__ void tile_dma(T* tile, const T* src, int64_t stride, int row0, int nrows,
                                          int wave, int lane) {
   constexpr int EPC = 16 / int(sizeof(T));
   constexpr int NCH = D / EPC;
-  constexpr int CPW = R * NCH / 256;  // copies per lane
-  static_assert(R * NCH % 256 == 0, "tile size must be a multiple of 256 chunks");
+  constexpr int NT = 64 * NW;
+  constexpr int NC = R * NCH;              // chunks in the tile
+  constexpr int CPW = (NC + NT - 1) / NT;  // copies per lane
+  static_assert(NC % 64 == 0 && (NC % NT == 0 || NC < NT), "tile chunks vs workgroup size");
   const uint32_t base = lds_addr(tile);
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
-    const int pos = u * 256 + wave * 64 + lane;  // chunk position in the tile
+    if (NC < NT && wave * 64 >= NC) break;  // small tile: whole waves idle
+    const int pos = u * NT + wave * 64 + lane;  // chunk position in the tile
     const int r = pos / NCH, p = pos % NCH;
     const int c = p ^ tile_swz<NCH>(r);  // source chunk
     const int row = min(row0 + r, nrows - 1);
     lds_dma16(src + (int64_t)row * stride + c * EPC,
-              __builtin_amdgcn_readfirstlane(base + uint32_t(u * 256 + wave * 64) * 16u));
+              __builtin_amdgcn_readfirstlane(base + uint32_t(u * NT + wave * 64) * 16u));
   }
 }
 
@@ -335,7 +338,7 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
 // query row); mask only on tiles that need it; online softmax; O^T += V^T P^T.
 // ======================================================================
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -370,8 +373,8 @@ void fwd_kernel(FwdArgs a) {
     const T* ks = (const T*)(cl ? a.k_c : a.k_x) + (int64_t)q.kvh * D;
     const T* vs = (const T*)(cl ? a.v_c : a.v_x) + (int64_t)q.kvh * D;
     T* dst = smem + buf * 2 * TSZ;
-    tile_dma<T, TK, D>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
-    tile_dma<T, TK, D>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    tile_dma<T, TK, D, FWD_WAVES>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    tile_dma<T, TK, D, FWD_WAVES>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
   };
 
   OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
 // dQ^T += K^T dS^T with K^T read transposed from the K tile.
 // ======================================================================
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -563,8 +566,8 @@ void bwd_dq_kernel(BwdArgs a) {
     const T* ks = (const T*)(cl ? a.k_c : a.k_x) + (int64_t)q.kvh * D;
     const T* vs = (const T*)(cl ? a.v_c : a.v_x) + (int64_t)q.kvh * D;
     T* dst = smem + buf * 2 * TSZ;
-    tile_dma<T, TK, D>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
-    tile_dma<T, TK, D>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    tile_dma<T, TK, D, FWD_WAVES>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    tile_dma<T, TK, D, FWD_WAVES>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
   };
 
   OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
@@ -604,7 +607,7 @@ void bwd_dq_kernel(BwdArgs a) {
         }
         sf[mb][0] = E::pack(ds);
         sf[mb][1] = E::pack(ds + 8);
-        __builtin_amdgcn_sched_barrier(0);
+
       }
 #pragma unroll
       for (int mb = 0; mb < TK / 32; ++mb) {
@@ -613,7 +616,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
             E::mma(dq[db], rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db), sf[mb][t]);
-          __builtin_amdgcn_sched_barrier(0);
+  
         }
       }
       rd.flip();
@@ -658,7 +661,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   using Frag = typename E::Frag;
   constexpr int TK = BWD_TK, TQ = BWD_TQ;
   constexpr int TSZ = TQ * D;
-  static_assert(TQ == 64, "row data copy assumes 64-row query tiles");
+  static_assert(TQ % 32 == 0 && TQ <= 128, "row data copy: one wave, 16 bytes per lane");
   static_assert(4 * TSZ * sizeof(T) + 4 * TQ * 4 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];            // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];      // [buffer][LSE2, D]
@@ -741,11 +744,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
     const T* gsrc = (const T*)(s.qs ? a.do_x : a.do_c) + (int64_t)s.h * D;
     T* dst = smem + buf * 2 * TSZ;
-    tile_dma<T, TQ, D>(dst, qsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
-    tile_dma<T, TQ, D>(dst + TSZ, gsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
-    if (wave == 0 && lane < 32) {  // lanes 0-15: 64 LSE2 values, 16-31: 64 D values
-      const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane & 15);
-      const float* src = (lane < 16 ? (s.qs ? a.l2_x : a.l2_c) : (s.qs ? a.d_x : a.d_c)) + r0;
+    tile_dma<T, TQ, D, 4>(dst, qsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
+    tile_dma<T, TQ, D, 4>(dst + TSZ, gsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
+    if (wave == 0 && lane < TQ / 2) {  // lanes [0, TQ/4): LSE2 of the TQ rows, then D
+      constexpr int L = TQ / 4;
+      const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane % L);
+      const float* src = (lane < L ? (s.qs ? a.l2_x : a.l2_c) : (s.qs ? a.d_x : a.d_c)) + r0;
       lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(&r_row[buf][0][0])));
     }
   };
@@ -794,7 +798,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         pa[mb][1] = E::pack(p + 8);
         sa[mb][0] = E::pack(ds);
         sa[mb][1] = E::pack(ds + 8);
-        __builtin_amdgcn_sched_barrier(0);
+
       }
       // dV += P^T dO, dK += dS^T Q (contraction over this tile's queries)
 #pragma unroll
@@ -806,7 +810,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
             E::mma(dv[db], pa[mb][t], rd.template tr_frag<GT>(smem, 32 * mb + 16 * t, db));
             E::mma(dk[db], sa[mb][t], rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db));
           }
-          __builtin_amdgcn_sched_barrier(0);
+  
         }
       }
       rd.flip();
@@ -840,7 +844,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 template <bool BF16, int D>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  if (a.n_items > 0) hipLaunchKernelGGL((fwd_kernel<BF16, D>), dim3(a.n_items), dim3(256), 0, s, a);
+  if (a.n_items > 0)
+    hipLaunchKernelGGL((fwd_kernel<BF16, D>), dim3(a.n_items), dim3(FWD_WAVES * 64), 0, s, a);
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   return hipGetLastError();
 }
@@ -860,7 +865,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   }
   if (ev) (void)hipEventRecord(ev[0].start, s);
   if (a.n_q_items > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.n_q_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.n_q_items), dim3(FWD_WAVES * 64), 0, s, a);
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   if (ev) (void)hipEventRecord(ev[1].start, s);
   if (a.n_kv_items > 0)

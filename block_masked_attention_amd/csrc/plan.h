@@ -13,16 +13,23 @@
 
 namespace bdattn {
 
-// Forward: a workgroup of 4 waves covers FWD_ROWS_PER_WAVE query rows per wave
-// and sweeps the visible keys in tiles of FWD_TK.
-constexpr int FWD_WAVES = 4;
+// Forward and backward dQ: a workgroup of FWD_WAVES waves covers
+// FWD_ROWS_PER_WAVE query rows per wave and sweeps the visible keys in tiles
+// of FWD_TK.
+#ifndef BDATTN_FWD_WAVES
+#define BDATTN_FWD_WAVES 4
+#endif
+constexpr int FWD_WAVES = BDATTN_FWD_WAVES;
 constexpr int FWD_ROWS_PER_WAVE = 32;
 constexpr int FWD_TK = 64;
-// Backward: a workgroup of 4 waves owns BWD_TK keys of one KV head (32 per
-// wave) and sweeps the query rows that see them in tiles of BWD_TQ.
+// Backward dK/dV: a workgroup of 4 waves owns BWD_TK keys of one KV head (32
+// per wave) and sweeps the query rows that see them in tiles of BWD_TQ.
+#ifndef BDATTN_BWD_TQ
+#define BDATTN_BWD_TQ 64
+#endif
 constexpr int BWD_WAVES = 4;
 constexpr int BWD_TK = 128;
-constexpr int BWD_TQ = 64;
+constexpr int BWD_TQ = BDATTN_BWD_TQ;
 
 constexpr size_t WS_ALIGN = 256;
 
