@@ -270,6 +270,13 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
 
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait for every outstanding vector-memory load, visibly to the compiler.
+// Register loads issued before a tile loop would otherwise stay "pending" in
+// the compiler's bookkeeping at the loop header, and it would place a full
+// vmcnt(0) inside the loop, where that wait also drains the (invisible)
+// prefetch copies of the next tile.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Stage rows [row0, row0 + R) of a token-major tensor (row stride `stride`
 // elements) into the swizzled R x D tile at `tile`. Rows past nrows - 1 repeat
 // row nrows - 1 (callers mask them). All NW waves of the workgroup take part.
@@ -461,7 +468,7 @@ void fwd_kernel(FwdArgs a) {
     }
   };
   if (n_tiles > 0) fetch(0, 0);
-  lds_dma_wait();
+  vm_drain();
   __syncthreads();
   sweep(std::false_type{}, 0, j_full);
   sweep(std::true_type{}, j_full, n_tiles);
@@ -625,7 +632,7 @@ void bwd_dq_kernel(BwdArgs a) {
     }
   };
   if (n_tiles > 0) fetch(0, 0);
-  lds_dma_wait();
+  vm_drain();
   __syncthreads();
   sweep(std::false_type{}, 0, j_full);
   sweep(std::true_type{}, j_full, n_tiles);
@@ -739,6 +746,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   // copy step s's Q and dO tiles and its LSE2 / D rows into LDS buffer `buf`
+  // per-lane source of the row-data copy: lanes [0, TQ/4) copy LSE2, the
+  // next TQ/4 lanes D (kept opaque so the per-step stream choice stays a
+  // register select rather than a load of the selected argument)
+  const float* rsrc_c = lane < TQ / 4 ? a.l2_c : a.d_c;
+  const float* rsrc_x = lane < TQ / 4 ? a.l2_x : a.d_x;
+  asm volatile("" : "+v"(rsrc_c), "+v"(rsrc_x));
   auto fetch = [&](const Step& s, int buf) {
     const int n_rows = s.qs ? a.n_corr : a.n_clean_q;
     const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
@@ -749,7 +762,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     if (wave == 0 && lane < TQ / 2) {  // lanes [0, TQ/4): LSE2 of the TQ rows, then D
       constexpr int L = TQ / 4;
       const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane % L);
-      const float* src = (lane < L ? (s.qs ? a.l2_x : a.l2_c) : (s.qs ? a.d_x : a.d_c)) + r0;
+      const float* src = (s.qs ? rsrc_x : rsrc_c) + r0;
       lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(&r_row[buf][0][0])));
     }
   };
@@ -768,15 +781,31 @@ void bwd_dkdv_kernel(BwdArgs a) {
         if (st.qs == 0) return key_blk <= (a.clean_q_start + row) / a.B;
         return key_blk < a.ids[row / a.B];
       };
-      Frag pa[TQ / 32][2], sa[TQ / 32][2];
 #pragma unroll
       for (int mb = 0; mb < TQ / 32; ++mb) {
+        Frag pa[2], sa[2];
         f32x16 sacc = zero16(), pacc = zero16();
+        // this block's Q and dO rows, read ahead of the products that use them
+        Frag qa[D / 16], ga[D / 16];
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-          E::mma(sacc, rd.template row_frag<0>(smem, mb, ks), kf[ks]);
-          E::mma(pacc, rd.template row_frag<GT>(smem, mb, ks), vf[ks]);
+          qa[ks] = rd.template row_frag<0>(smem, mb, ks);
+          ga[ks] = rd.template row_frag<GT>(smem, mb, ks);
         }
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          E::mma(sacc, qa[ks], kf[ks]);
+          E::mma(pacc, ga[ks], vf[ks]);
+        }
+        // scheduling hint: the first six operand reads, then one product per
+        // further read, so LDS latency hides behind the matrix products
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int u = 0; u < 2 * D / 16 - 6; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         float p[16], ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -794,23 +823,24 @@ void bwd_dkdv_kernel(BwdArgs a) {
             ds[e] = pv * (pacc[e] - dv4[r]);
           }
         }
-        pa[mb][0] = E::pack(p);
-        pa[mb][1] = E::pack(p + 8);
-        sa[mb][0] = E::pack(ds);
-        sa[mb][1] = E::pack(ds + 8);
-
-      }
-      // dV += P^T dO, dK += dS^T Q (contraction over this tile's queries)
-#pragma unroll
-      for (int mb = 0; mb < TQ / 32; ++mb) {
+        pa[0] = E::pack(p);
+        pa[1] = E::pack(p + 8);
+        sa[0] = E::pack(ds);
+        sa[1] = E::pack(ds + 8);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
+          // dV += P^T dO, dK += dS^T Q over these 16 queries
+          Frag ga_t[D / 32], qa_t[D / 32];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            E::mma(dv[db], pa[mb][t], rd.template tr_frag<GT>(smem, 32 * mb + 16 * t, db));
-            E::mma(dk[db], sa[mb][t], rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db));
+            ga_t[db] = rd.template tr_frag<GT>(smem, 32 * mb + 16 * t, db);
+            qa_t[db] = rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db);
           }
-  
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            E::mma(dv[db], pa[t], ga_t[db]);
+            E::mma(dk[db], sa[t], qa_t[db]);
+          }
         }
       }
       rd.flip();
@@ -819,7 +849,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   if (n_it > 0) fetch(step(0), 0);
-  lds_dma_wait();
+  vm_drain();
   __syncthreads();
   sweep(std::false_type{}, 0, n_full);
   sweep(std::true_type{}, n_full, n_it);
