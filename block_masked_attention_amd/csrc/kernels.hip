@@ -42,6 +42,10 @@
 // group column i of four consecutive rows, i.e. the operand of a matrix whose
 // contraction index runs down the tile's rows, so no transposed copy is ever
 // stored.
+//
+// Tile loops are double buffered with the buffer index a compile-time
+// constant of the loop body (two copies of each body), so every LDS operand
+// read carries its buffer in the instruction's immediate offset.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,9 +64,18 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short shortx4;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
+template <int N>
+using Int = std::integral_constant<int, N>;
+
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The forward moves its running row maximum (log2 units) as soon as a tile's
+// maximum exceeds it, so the largest softmax weight of a row is exactly 1
+// when it is rounded to bf16 for the P V product. (Letting the maximum lag by
+// a margin saves rescales but rounds the dominant weight, which the gradients
+// of strongly peaked rows amplify.)
+constexpr float kRescaleMargin = 0.f;
 
 // 2^x with one v_exp_f32 (results below 2^-126 flush to zero, which is
 // harmless for softmax weights; exp2(-inf) = 0).
@@ -158,10 +171,10 @@ struct Elem<false> {
 // Per-lane byte offsets of the operand reads from swizzled LDS tiles. The
 // swizzle depends on a row's low 4 bits only, so 32-row blocks and 16-row
 // steps add compile-time constants to a few offsets fixed per lane. Offsets
-// are relative to the start of the kernel's LDS array (one constant base) and
-// include the current buffer of a double-buffered pair whose buffers are BUF
-// bytes apart (BUF a power of two); flip() switches to the other buffer.
-template <bool BF16, int D, uint32_t BUF>
+// are relative to the start of the kernel's LDS array; the template argument
+// TILE of the reads adds the (compile-time) byte offset of the tile itself,
+// buffer included.
+template <bool BF16, int D>
 struct OperandReads {
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -197,18 +210,8 @@ struct OperandReads {
       }
     }
   }
-  __device__ __forceinline__ void flip() {
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int c = 0; c < NCHF; ++c) row[ks][c] ^= BUF;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int t = 0; t < NTR; ++t) tr[db][t] ^= BUF;
-  }
   // 8 consecutive elements of row 32 mb + lane%32, from column 16 ks + 8
-  // (lane/32), of the tile TILE bytes into the current buffer.
+  // (lane/32), of the tile TILE bytes into the LDS array `lds`.
   template <uint32_t TILE>
   __device__ __forceinline__ Frag row_frag(const void* lds, int mb, int ks) const {
     const char* b = (const char*)lds + TILE + mb * 32 * ROW;
@@ -245,6 +248,15 @@ __device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, int32
   return bd_corr_row(row, ids[row / B], B);
 }
 
+// floor(n / d) for 0 <= n < 2^24, d >= 1, with inv_d = 1.0f / d: a float
+// estimate that is off by at most one, then corrected with integer checks.
+__device__ __forceinline__ int div_small(int n, int d, float inv_d) {
+  int q = int(float(n) * inv_d);
+  q -= q * d > n ? 1 : 0;
+  q += (q + 1) * d <= n ? 1 : 0;
+  return q;
+}
+
 // ------------------------------------------------------------ tile staging
 // Tiles are copied from global memory straight into LDS (global_load_lds,
 // 16 bytes per lane: lane l of the wave writes LDS bytes [base + 16 l, +16)).
@@ -277,30 +289,54 @@ __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0
 // prefetch copies of the next tile.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Stage rows [row0, row0 + R) of a token-major tensor (row stride `stride`
-// elements) into the swizzled R x D tile at `tile`. Rows past nrows - 1 repeat
-// row nrows - 1 (callers mask them). All NW waves of the workgroup take part.
+// Copy plan of one lane for staging R rows x D elements of a token-major
+// tensor into a swizzled LDS tile with NW waves: the lane's 16-byte chunks
+// and their element offsets within the source rows, computed once. Rows past
+// nrows - 1 repeat row nrows - 1 (callers mask them).
 template <typename T, int R, int D, int NW>
-__device__ __forceinline__ void tile_dma(T* tile, const T* src, int64_t stride, int row0, int nrows,
-                                         int wave, int lane) {
-  constexpr int EPC = 16 / int(sizeof(T));
-  constexpr int NCH = D / EPC;
-  constexpr int NT = 64 * NW;
-  constexpr int NC = R * NCH;              // chunks in the tile
-  constexpr int CPW = (NC + NT - 1) / NT;  // copies per lane
+struct TileCopy {
+  static constexpr int EPC = 16 / int(sizeof(T));
+  static constexpr int NCH = D / EPC;
+  static constexpr int NT = 64 * NW;
+  static constexpr int NC = R * NCH;              // chunks in the tile
+  static constexpr int CPW = (NC + NT - 1) / NT;  // copies per lane
   static_assert(NC % 64 == 0 && (NC % NT == 0 || NC < NT), "tile chunks vs workgroup size");
-  const uint32_t base = lds_addr(tile);
+  uint32_t off[CPW];  // element offset of each copy's chunk: r * stride + c * EPC
+  int wave, lane;
+  int64_t stride;
+
+  __device__ __forceinline__ void init(int wave_, int lane_, int64_t stride_) {
+    wave = wave_;
+    lane = lane_;
+    stride = stride_;
 #pragma unroll
-  for (int u = 0; u < CPW; ++u) {
-    if (NC < NT && wave * 64 >= NC) break;  // small tile: whole waves idle
-    const int pos = u * NT + wave * 64 + lane;  // chunk position in the tile
-    const int r = pos / NCH, p = pos % NCH;
-    const int c = p ^ tile_swz<NCH>(r);  // source chunk
-    const int row = min(row0 + r, nrows - 1);
-    lds_dma16(src + (int64_t)row * stride + c * EPC,
-              __builtin_amdgcn_readfirstlane(base + uint32_t(u * NT + wave * 64) * 16u));
+    for (int u = 0; u < CPW; ++u) {
+      const int pos = u * NT + wave * 64 + lane;
+      const int r = pos / NCH, c = (pos % NCH) ^ tile_swz<NCH>(r);
+      off[u] = uint32_t(r * stride + c * EPC);
+    }
   }
-}
+  __device__ __forceinline__ bool active() const { return !(NC < NT && wave * 64 >= NC); }
+  __device__ __forceinline__ void issue(T* tile, const T* src, int row0, int nrows) const {
+    if (!active()) return;  // small tile: whole waves idle
+    const uint32_t base = lds_addr(tile) + uint32_t(wave * 64) * 16u;
+    if (row0 + R <= nrows) {
+      const T* s0 = src + (int64_t)row0 * stride;
+#pragma unroll
+      for (int u = 0; u < CPW; ++u)
+        lds_dma16(s0 + off[u], __builtin_amdgcn_readfirstlane(base + uint32_t(u * NT) * 16u));
+    } else {
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int pos = u * NT + wave * 64 + lane;
+        const int r = pos / NCH, c = (pos % NCH) ^ tile_swz<NCH>(r);
+        const int row = min(row0 + r, nrows - 1);
+        lds_dma16(src + (int64_t)row * stride + c * EPC,
+                  __builtin_amdgcn_readfirstlane(base + uint32_t(u * NT) * 16u));
+      }
+    }
+  }
+};
 
 // ======================================================================
 // Query-tile work item shared by the forward and the dQ kernel: `rows`
@@ -354,9 +390,10 @@ void fwd_kernel(FwdArgs a) {
   constexpr int TSZ = TK * D;
   static_assert(4 * TSZ * sizeof(T) <= 80 * 1024, "LDS (two workgroups per CU)");
   __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][K, V]
-  constexpr uint32_t VT = TSZ * sizeof(T);                   // V tile offset in a buffer
+  constexpr uint32_t TB = TSZ * sizeof(T);                   // bytes per tile
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const QTile q = q_tile<TK>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
                              a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B, wave, lq);
@@ -372,104 +409,114 @@ void fwd_kernel(FwdArgs a) {
       qf[ks] = q.row_ok ? E::load(qrow + 16 * ks + 8 * hf) : E::zero();
   }
 
+  TileCopy<T, TK, D, FWD_WAVES> cp;
+  cp.init(wave, lane, (int64_t)a.Hkv * D);
+  const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
+  const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
+  const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
+  const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
   // stage key tile j (K then V) into LDS buffer `buf`
-  auto fetch = [&](int j, int buf) {
+  auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
     const bool cl = j < q.n_ct;
     const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
     const int nk = cl ? a.n_clean_kv : a.n_corr;
-    const T* ks = (const T*)(cl ? a.k_c : a.k_x) + (int64_t)q.kvh * D;
-    const T* vs = (const T*)(cl ? a.v_c : a.v_x) + (int64_t)q.kvh * D;
     T* dst = smem + buf * 2 * TSZ;
-    tile_dma<T, TK, D, FWD_WAVES>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
-    tile_dma<T, TK, D, FWD_WAVES>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    cp.issue(dst, cl ? kc : kx, k0, nk);
+    cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
   };
 
-  OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
+  OperandReads<BF16, D> rd;
   rd.init(lane);
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = zero16();
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf, l = 0.f;  // running reference maximum (log2 units), row sum
 
-  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
-  const int j_full = min(q.n_ct, q.full_end / TK);
-  auto sweep = [&](auto mask_tag, int j0, int j1) {
+  // one key tile in LDS buffer BUF (the next one is copied into the other)
+  auto body = [&](auto mask_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    for (int j = j0; j < j1; ++j) {
-      if (j + 1 < n_tiles) fetch(j + 1, (j + 1) & 1);
-      const bool cl = j < q.n_ct;
-      const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr uint32_t KT = BUF * 2 * TB, VT = KT + TB;
+    if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
+    const bool cl = j < q.n_ct;
+    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
 
     f32x16 s[TK / 32];
 #pragma unroll
     for (int mb = 0; mb < TK / 32; ++mb) {
       s[mb] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        E::mma(s[mb], rd.template row_frag<0>(smem, mb, ks), qf[ks]);
+      for (int ks = 0; ks < D / 16; ++ks) E::mma(s[mb], rd.template row_frag<KT>(smem, mb, ks), qf[ks]);
     }
     // online softmax; the row max is taken on raw scores (the scale is > 0)
     // and the scale folded into the exponent's multiply-add
-    {
-      float mx = kNegInf;
+    float mx = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < TK / 32; ++mb) {
+    for (int mb = 0; mb < TK / 32; ++mb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (MASK) {
-            const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
-            s[mb][i] = vis ? s[mb][i] : kNegInf;
-          }
-          mx = fmaxf(mx, s[mb][i]);
+      for (int i = 0; i < 16; ++i) {
+        if (MASK) {
+          const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
+          s[mb][i] = vis ? s[mb][i] : kNegInf;
         }
+        mx = fmaxf(mx, s[mb][i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    if (__any(mx > m + kRescaleMargin)) {  // some row's maximum moved (wave-uniform)
       const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const bool grew = __any(m_new > m);  // some row's max moved: rescale
-      const float alpha = fast_exp2(m - m_use);
-      float rs = 0.f;
-      Frag pf[TK / 32][2];
-#pragma unroll
-      for (int mb = 0; mb < TK / 32; ++mb) {
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, -m_use));
-          rs += p[i];
-        }
-        pf[mb][0] = E::pack(p);
-        pf[mb][1] = E::pack(p + 8);
-      }
-      l = l * alpha + rs;
-      m = m_new;
-      if (grew) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        }
-      }
+      const float alpha = m == kNegInf ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int mb = 0; mb < TK / 32; ++mb) {
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      m = m_new;
+    }
+    const float m_use = m == kNegInf ? 0.f : m;
+    Frag pf[TK / 32][2];
+    float rs = 0.f;
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            E::mma(o[db], rd.template tr_frag<VT>(smem, 32 * mb + 16 * t, db), pf[mb][t]);
-        }
+    for (int mb = 0; mb < TK / 32; ++mb) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, -m_use));
+        rs += p[i];
+      }
+      pf[mb][0] = E::pack(p);
+      pf[mb][1] = E::pack(p + 8);
+    }
+    l += rs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int mb = 0; mb < TK / 32; ++mb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          E::mma(o[db], rd.template tr_frag<VT>(smem, 32 * mb + 16 * t, db), pf[mb][t]);
       }
     }
-      rd.flip();
-      lds_dma_wait();
-      __syncthreads();
+    lds_dma_wait();
+    __syncthreads();
+  };
+  auto sweep = [&](auto mask_tag, int j0, int j1) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) body(mask_tag, Int<1>{}, j++);
+    for (; j + 1 < j1; j += 2) {
+      body(mask_tag, Int<0>{}, j);
+      body(mask_tag, Int<1>{}, j + 1);
     }
+    if (j < j1) body(mask_tag, Int<0>{}, j);
   };
   if (n_tiles > 0) fetch(0, 0);
   vm_drain();
   __syncthreads();
+  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
+  const int j_full = min(q.n_ct, q.full_end / TK);
   sweep(std::false_type{}, 0, j_full);
   sweep(std::true_type{}, j_full, n_tiles);
 
@@ -542,9 +589,10 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int TSZ = TK * D;
   static_assert(4 * TSZ * sizeof(T) <= 80 * 1024, "LDS (two workgroups per CU)");
   __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];  // [buffer][K, V]
-  constexpr uint32_t VT = TSZ * sizeof(T);                   // V tile offset in a buffer
+  constexpr uint32_t TB = TSZ * sizeof(T);                   // bytes per tile
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const QTile q = q_tile<TK>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
                              a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B, wave, lq);
@@ -565,75 +613,85 @@ void bwd_dq_kernel(BwdArgs a) {
   const float lse2 = q.row_ok ? (q.stream ? a.l2_x : a.l2_c)[ri] : __builtin_inff();
   const float drow = q.row_ok ? (q.stream ? a.d_x : a.d_c)[ri] : 0.f;
 
+  TileCopy<T, TK, D, FWD_WAVES> cp;
+  cp.init(wave, lane, (int64_t)a.Hkv * D);
+  const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
+  const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
+  const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
+  const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
   // stage key tile j (K then V) into LDS buffer `buf`
-  auto fetch = [&](int j, int buf) {
+  auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
     const bool cl = j < q.n_ct;
     const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
     const int nk = cl ? a.n_clean_kv : a.n_corr;
-    const T* ks = (const T*)(cl ? a.k_c : a.k_x) + (int64_t)q.kvh * D;
-    const T* vs = (const T*)(cl ? a.v_c : a.v_x) + (int64_t)q.kvh * D;
     T* dst = smem + buf * 2 * TSZ;
-    tile_dma<T, TK, D, FWD_WAVES>(dst, ks, (int64_t)a.Hkv * D, k0, nk, wave, lane);
-    tile_dma<T, TK, D, FWD_WAVES>(dst + TSZ, vs, (int64_t)a.Hkv * D, k0, nk, wave, lane);
+    cp.issue(dst, cl ? kc : kx, k0, nk);
+    cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
   };
 
-  OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
+  OperandReads<BF16, D> rd;
   rd.init(lane);
 
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
 
-  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
-  const int j_full = min(q.n_ct, q.full_end / TK);
-  auto sweep = [&](auto mask_tag, int j0, int j1) {
+  auto body = [&](auto mask_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    for (int j = j0; j < j1; ++j) {
-      if (j + 1 < n_tiles) fetch(j + 1, (j + 1) & 1);
-      const bool cl = j < q.n_ct;
-      const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
-      Frag sf[TK / 32][2];
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr uint32_t KT = BUF * 2 * TB, VT = KT + TB;
+    if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
+    const bool cl = j < q.n_ct;
+    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+    Frag sf[TK / 32][2];
 #pragma unroll
-      for (int mb = 0; mb < TK / 32; ++mb) {
-        f32x16 s = zero16(), dp = zero16();
+    for (int mb = 0; mb < TK / 32; ++mb) {
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          E::mma(s, rd.template row_frag<0>(smem, mb, ks), qf[ks]);
-          E::mma(dp, rd.template row_frag<VT>(smem, mb, ks), gf[ks]);
-        }
-        float ds[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
-          if (MASK) {
-            const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
-            p = vis ? p : 0.f;
-          }
-          ds[i] = p * (dp[i] - drow);
-        }
-        sf[mb][0] = E::pack(ds);
-        sf[mb][1] = E::pack(ds + 8);
-
+      for (int ks = 0; ks < D / 16; ++ks) {
+        E::mma(s, rd.template row_frag<KT>(smem, mb, ks), qf[ks]);
+        E::mma(dp, rd.template row_frag<VT>(smem, mb, ks), gf[ks]);
       }
+      float ds[16];
 #pragma unroll
-      for (int mb = 0; mb < TK / 32; ++mb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            E::mma(dq[db], rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db), sf[mb][t]);
-  
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
+        if (MASK) {
+          const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+          const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
+          p = vis ? p : 0.f;
         }
+        ds[i] = p * (dp[i] - drow);
       }
-      rd.flip();
-      lds_dma_wait();
-      __syncthreads();
+      sf[mb][0] = E::pack(ds);
+      sf[mb][1] = E::pack(ds + 8);
     }
+#pragma unroll
+    for (int mb = 0; mb < TK / 32; ++mb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          E::mma(dq[db], rd.template tr_frag<KT>(smem, 32 * mb + 16 * t, db), sf[mb][t]);
+      }
+    }
+    lds_dma_wait();
+    __syncthreads();
+  };
+  auto sweep = [&](auto mask_tag, int j0, int j1) __attribute__((always_inline)) {
+    int j = j0;
+    if (j < j1 && (j & 1)) body(mask_tag, Int<1>{}, j++);
+    for (; j + 1 < j1; j += 2) {
+      body(mask_tag, Int<0>{}, j);
+      body(mask_tag, Int<1>{}, j + 1);
+    }
+    if (j < j1) body(mask_tag, Int<0>{}, j);
   };
   if (n_tiles > 0) fetch(0, 0);
   vm_drain();
   __syncthreads();
+  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
+  const int j_full = min(q.n_ct, q.full_end / TK);
   sweep(std::false_type{}, 0, j_full);
   sweep(std::true_type{}, j_full, n_tiles);
 
@@ -651,69 +709,75 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ======================================================================
-// Backward, dK/dV. One workgroup = 4 waves owning BWD_TK keys of one KV head
-// (32 per wave, kept in registers as the B operand of S = Q K^T and
-// dP = dO V^T). It sweeps every query tile (BWD_TQ rows) that sees its keys,
-// for each q head of the group: S, dP; P = exp2(S c - LSE2); dS = P (dP - D);
-// dV += P^T dO and dK += dS^T Q, with dO and Q read transposed from their
-// row-major tiles. The next step's Q and dO tiles and its LSE2 / D values are
-// copied into the other LDS buffer while the current one is in use. Tiles
-// whose rows all see every key of the workgroup come first and skip the mask.
+// Backward, dK/dV. One workgroup = 8 waves owning BWD_TK keys of one KV head.
+// Waves w and w + 4 (which share a SIMD) own the same 32 keys, in two roles:
+//   the P wave    S = Q K^T, P = exp2(S c - LSE2) (masked), dV += P^T dO;
+//   the dS wave   dP = dO V^T, dS = P (dP - D), dK += dS^T Q,
+// with P handed over through LDS in the exact register layout in which both
+// waves hold their 32 x 32 result tiles. Each step (BWD_TQ query rows of one
+// q head) has two phases separated by a barrier: {S, P | dP} then {dV | dS,
+// dK}, so in each phase one wave's vector work overlaps the other's matrix
+// products. Each wave keeps one accumulator (dV or dK) and one operand (K or
+// V) in registers, which lets two waves share a SIMD. The next step's Q and dO
+// tiles and its LSE2 / D values are copied into the other LDS buffer while the
+// current one is in use. Tiles whose rows all see every key of the workgroup
+// come first and skip the mask.
 // ======================================================================
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<BF16>;
   using T = typename E::T;
   using Frag = typename E::Frag;
-  constexpr int TK = BWD_TK, TQ = BWD_TQ;
+  constexpr int TK = BWD_TK, TQ = BWD_TQ, NW = 8, NMB = TQ / 32;
   constexpr int TSZ = TQ * D;
+  static_assert(TK == 32 * NW / 2, "two waves per 32 keys");
   static_assert(TQ % 32 == 0 && TQ <= 128, "row data copy: one wave, 16 bytes per lane");
-  static_assert(4 * TSZ * sizeof(T) + 4 * TQ * 4 <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];            // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];      // [buffer][LSE2, D]
-  constexpr uint32_t GT = TSZ * sizeof(T);                             // dO tile offset in a buffer
+  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];        // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];  // [buffer][LSE2, D]
+  __shared__ __attribute__((aligned(16))) float4 p_hand[NW / 2][NMB][4][64];  // P handoff
+  static_assert(sizeof(smem) + sizeof(r_row) + sizeof(p_hand) <= 160 * 1024, "LDS");
+  constexpr uint32_t TB = TSZ * sizeof(T);  // bytes per tile
 
   const BwdItem item = a.kv_items[blockIdx.x];
   const int it_x0 = item.x0, it_x1 = item.x1, it_c0 = item.c0, it_c1 = item.c1;
   const int it_xf = item.xf, it_cf = item.cf;
   const int kstream = item.hs & 1, kvh = item.hs >> 1;
   const int G = a.H / a.Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;            // key group: keys 32 kg .. 32 kg + 31 of the tile
+  const bool p_role = wave < NW / 2;  // P wave (dV) or dS wave (dK)
   const int lk = lane & 31, hf = lane >> 5;
   const int key0 = item.ktile * TK;
   const int n_keys = kstream ? a.n_corr : a.n_clean_kv;
-  const int my_key = key0 + 32 * wave + lk;
+  const int my_key = key0 + 32 * kg + lk;
   const bool key_ok = my_key < n_keys;
-  const int key_blk = my_key / a.B;  // clean: global block; corrupted: local block
+  const float inv_b = 1.f / float(a.B);
+  const int key_blk = div_small(my_key, a.B, inv_b);  // clean: global block; corrupted: local
 
-  // this lane's key and value as B operands (natural order over d)
-  Frag kf[D / 16], vf[D / 16];
+  // this lane's key (P wave) or value (dS wave) as B operand, natural over d
+  Frag kvf[D / 16];
   {
-    const T* ksrc = (const T*)(kstream ? a.k_x : a.k_c);
-    const T* vsrc = (const T*)(kstream ? a.v_x : a.v_c);
+    const T* src = (const T*)(p_role ? (kstream ? a.k_x : a.k_c) : (kstream ? a.v_x : a.v_c));
     const int64_t off = ((int64_t)min(my_key, n_keys - 1) * a.Hkv + kvh) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kf[ks] = key_ok ? E::load(ksrc + off + 16 * ks + 8 * hf) : E::zero();
-      vf[ks] = key_ok ? E::load(vsrc + off + 16 * ks + 8 * hf) : E::zero();
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      kvf[ks] = key_ok ? E::load(src + off + 16 * ks + 8 * hf) : E::zero();
   }
 
-  OperandReads<BF16, D, 2 * TSZ * sizeof(T)> rd;
+  OperandReads<BF16, D> rd;
   rd.init(lane);
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];  // dV (P wave) or dK / scale (dS wave)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dk[i] = zero16();
-    dv[i] = zero16();
-  }
+  for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
 
-  // iteration -> (query stream, tile, head). The query tiles that see every
-  // key of the workgroup (those starting at or after xf / cf) come first, then
-  // the ones that need the mask; within each, corrupted tiles then clean ones,
-  // each from the last tile down, every q head of the group per tile.
+  // Step order: the query tiles that see every key of the workgroup (those
+  // starting at or after xf / cf) come first, then the ones that need the
+  // mask; within each, corrupted tiles then clean ones, each from the last
+  // tile down, every q head of the group per tile. A step is (tile index t in
+  // that order, head offset hi), advanced without divisions.
   auto ntiles = [](int r0, int r1) { return r1 > r0 ? (r1 - 1) / TQ - r0 / TQ + 1 : 0; };
   const int top_x = (it_x1 - 1) / TQ, top_c = (it_c1 - 1) / TQ;
   const int nf_x = it_xf < it_x1 ? top_x - it_xf / TQ + 1 : 0;
@@ -724,10 +788,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
   struct Step {
     int qs, q0, h;
   };
-  auto step = [&](int i) {
+  struct Pos {
+    int t, hi;
+  };
+  auto decode = [&](Pos p) __attribute__((always_inline)) {
     Step s;
-    int t = i / G;
-    s.h = kvh * G + i % G;
+    s.h = kvh * G + p.hi;
+    int t = p.t;
     if (t < nf_x) {
       s.qs = 1;
       s.q0 = (top_x - t) * TQ;
@@ -744,21 +811,30 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
     return s;
   };
+  auto next_pos = [&](Pos p) __attribute__((always_inline)) {
+    if (++p.hi == G) {
+      p.hi = 0;
+      ++p.t;
+    }
+    return p;
+  };
 
-  // copy step s's Q and dO tiles and its LSE2 / D rows into LDS buffer `buf`
   // per-lane source of the row-data copy: lanes [0, TQ/4) copy LSE2, the
   // next TQ/4 lanes D (kept opaque so the per-step stream choice stays a
   // register select rather than a load of the selected argument)
   const float* rsrc_c = lane < TQ / 4 ? a.l2_c : a.d_c;
   const float* rsrc_x = lane < TQ / 4 ? a.l2_x : a.d_x;
   asm volatile("" : "+v"(rsrc_c), "+v"(rsrc_x));
-  auto fetch = [&](const Step& s, int buf) {
+  TileCopy<T, TQ, D, NW> cp;
+  cp.init(wave, lane, (int64_t)a.H * D);
+  // copy step s's Q and dO tiles and its LSE2 / D rows into LDS buffer `buf`
+  auto fetch = [&](const Step& s, int buf) __attribute__((always_inline)) {
     const int n_rows = s.qs ? a.n_corr : a.n_clean_q;
     const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
     const T* gsrc = (const T*)(s.qs ? a.do_x : a.do_c) + (int64_t)s.h * D;
     T* dst = smem + buf * 2 * TSZ;
-    tile_dma<T, TQ, D, 4>(dst, qsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
-    tile_dma<T, TQ, D, 4>(dst + TSZ, gsrc, (int64_t)a.H * D, s.q0, n_rows, wave, lane);
+    cp.issue(dst, qsrc, s.q0, n_rows);
+    cp.issue(dst + TSZ, gsrc, s.q0, n_rows);
     if (wave == 0 && lane < TQ / 2) {  // lanes [0, TQ/4): LSE2 of the TQ rows, then D
       constexpr int L = TQ / 4;
       const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane % L);
@@ -767,106 +843,144 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  auto sweep = [&](auto mask_tag, int i0, int i1) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    for (int i = i0; i < i1; ++i) {
-      const int cur = i & 1;
-      const Step st = step(i);
-      if (i + 1 < n_it) fetch(step(i + 1), cur ^ 1);
-      const int n_rows = st.qs ? a.n_corr : a.n_clean_q;
-      // visibility of (query row, this lane's key) on tiles that need the mask
-      auto sees = [&](int row) -> bool {
-        if (!key_ok || row >= n_rows) return false;
-        if (kstream) return row / a.B == key_blk;  // own corrupted block
-        if (st.qs == 0) return key_blk <= (a.clean_q_start + row) / a.B;
-        return key_blk < a.ids[row / a.B];
-      };
+  // 32 x 32 result tile of block mb of tile TILE: its rows against this
+  // wave's keys, contraction over d with the operand kept in registers
+  auto product = [&](auto tile_tag, int mb, f32x16& c) __attribute__((always_inline)) {
+    constexpr uint32_t TILE = decltype(tile_tag)::value;
+    Frag fr[D / 16];
 #pragma unroll
-      for (int mb = 0; mb < TQ / 32; ++mb) {
-        Frag pa[2], sa[2];
-        f32x16 sacc = zero16(), pacc = zero16();
-        // this block's Q and dO rows, read ahead of the products that use them
-        Frag qa[D / 16], ga[D / 16];
+    for (int ks = 0; ks < D / 16; ++ks) fr[ks] = rd.template row_frag<TILE>(smem, mb, ks);
+    c = zero16();
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          qa[ks] = rd.template row_frag<0>(smem, mb, ks);
-          ga[ks] = rd.template row_frag<GT>(smem, mb, ks);
-        }
+    for (int ks = 0; ks < D / 16; ++ks) E::mma(c, fr[ks], kvf[ks]);
+  };
+  // acc += X^T Y over the 32 rows of block mb, X given as packed result-order
+  // fragments, Y the rows of tile TILE read transposed
+  auto accumulate = [&](auto tile_tag, int mb, const Frag* x) __attribute__((always_inline)) {
+    constexpr uint32_t TILE = decltype(tile_tag)::value;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          E::mma(sacc, qa[ks], kf[ks]);
-          E::mma(pacc, ga[ks], vf[ks]);
-        }
-        // scheduling hint: the first six operand reads, then one product per
-        // further read, so LDS latency hides behind the matrix products
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    for (int t = 0; t < 2; ++t) {
+      Frag y[D / 32];
 #pragma unroll
-        for (int u = 0; u < 2 * D / 16 - 6; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-        float p[16], ds[16];
+      for (int db = 0; db < D / 32; ++db) y[db] = rd.template tr_frag<TILE>(smem, 32 * mb + 16 * t, db);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qr = 32 * mb + 8 * g + 4 * hf;
-          const float4 l4 = *(const float4*)(&r_row[cur][0][qr]);
-          const float4 d4 = *(const float4*)(&r_row[cur][1][qr]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * g + r;
-            float pv = fast_exp2(fmaf(sacc[e], a.scale_log2, -lv[r]));
-            if (MASK) pv = sees(st.q0 + qr + r) ? pv : 0.f;
-            p[e] = pv;
-            ds[e] = pv * (pacc[e] - dv4[r]);
-          }
-        }
-        pa[0] = E::pack(p);
-        pa[1] = E::pack(p + 8);
-        sa[0] = E::pack(ds);
-        sa[1] = E::pack(ds + 8);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // dV += P^T dO, dK += dS^T Q over these 16 queries
-          Frag ga_t[D / 32], qa_t[D / 32];
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            ga_t[db] = rd.template tr_frag<GT>(smem, 32 * mb + 16 * t, db);
-            qa_t[db] = rd.template tr_frag<0>(smem, 32 * mb + 16 * t, db);
-          }
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            E::mma(dv[db], pa[t], ga_t[db]);
-            E::mma(dk[db], sa[t], qa_t[db]);
-          }
-        }
-      }
-      rd.flip();
-      lds_dma_wait();
-      __syncthreads();
+      for (int db = 0; db < D / 32; ++db) E::mma(acc[db], x[t], y[db]);
     }
   };
-  if (n_it > 0) fetch(step(0), 0);
+
+  Pos pos = {0, 0};  // position of the current step
+  // P wave: S, P (masked on tiles that need it), hand P over, dV += P^T dO
+  auto body_p = [&](auto mask_tag, auto buf_tag, int i) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+    using QT = std::integral_constant<uint32_t, BUF * 2 * TB>;
+    using GT = std::integral_constant<uint32_t, BUF * 2 * TB + TB>;
+    const Pos nxt = next_pos(pos);
+    if (i + 1 < n_it) fetch(decode(nxt), BUF ^ 1);
+    const Step st = decode(pos);
+    const int n_rows = st.qs ? a.n_corr : a.n_clean_q;
+    // visibility of (query row, this lane's key) on tiles that need the mask
+    auto sees = [&](int row) -> bool __attribute__((always_inline)) {
+      if (!key_ok || row >= n_rows) return false;
+      const int rb = div_small(row, a.B, inv_b);
+      if (kstream) return rb == key_blk;  // own corrupted block
+      if (st.qs == 0) return key_blk <= div_small(a.clean_q_start + row, a.B, inv_b);
+      return key_blk < a.ids[rb];
+    };
+    Frag pa[NMB][2];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      f32x16 s;
+      product(QT{}, mb, s);
+      float p[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = 32 * mb + 8 * g + 4 * hf;
+        const float4 l4 = *(const float4*)(&r_row[BUF][0][qr]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pv = fast_exp2(fmaf(s[4 * g + r], a.scale_log2, -lv[r]));
+          if (MASK) pv = sees(st.q0 + qr + r) ? pv : 0.f;
+          p[4 * g + r] = pv;
+        }
+        p_hand[kg][mb][g][lane] = make_float4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
+      }
+      pa[mb][0] = E::pack(p);
+      pa[mb][1] = E::pack(p + 8);
+    }
+    __syncthreads();  // P handed over
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) accumulate(GT{}, mb, pa[mb]);
+    pos = nxt;
+    lds_dma_wait();
+    __syncthreads();
+  };
+  // dS wave: dP, then (once P is there) dS = P (dP - D), dK += dS^T Q
+  auto body_ds = [&](auto buf_tag, int i) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using QT = std::integral_constant<uint32_t, BUF * 2 * TB>;
+    using GT = std::integral_constant<uint32_t, BUF * 2 * TB + TB>;
+    const Pos nxt = next_pos(pos);
+    if (i + 1 < n_it) fetch(decode(nxt), BUF ^ 1);
+    f32x16 dp[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) product(GT{}, mb, dp[mb]);
+    __syncthreads();  // P handed over
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      float ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = 32 * mb + 8 * g + 4 * hf;
+        const float4 d4 = *(const float4*)(&r_row[BUF][1][qr]);
+        const float4 p4 = p_hand[kg][mb][g][lane];
+        ds[4 * g + 0] = p4.x * (dp[mb][4 * g + 0] - d4.x);
+        ds[4 * g + 1] = p4.y * (dp[mb][4 * g + 1] - d4.y);
+        ds[4 * g + 2] = p4.z * (dp[mb][4 * g + 2] - d4.z);
+        ds[4 * g + 3] = p4.w * (dp[mb][4 * g + 3] - d4.w);
+      }
+      const Frag sa[2] = {E::pack(ds), E::pack(ds + 8)};
+      accumulate(QT{}, mb, sa);
+    }
+    pos = nxt;
+    lds_dma_wait();
+    __syncthreads();
+  };
+  auto sweep_p = [&](auto mask_tag, int i0, int i1) __attribute__((always_inline)) {
+    int i = i0;
+    if (i < i1 && (i & 1)) body_p(mask_tag, Int<1>{}, i++);
+    for (; i + 1 < i1; i += 2) {
+      body_p(mask_tag, Int<0>{}, i);
+      body_p(mask_tag, Int<1>{}, i + 1);
+    }
+    if (i < i1) body_p(mask_tag, Int<0>{}, i);
+  };
+
+  if (n_it > 0) fetch(decode(pos), 0);
   vm_drain();
   __syncthreads();
-  sweep(std::false_type{}, 0, n_full);
-  sweep(std::true_type{}, n_full, n_it);
+  if (p_role) {
+    sweep_p(std::false_type{}, 0, n_full);
+    sweep_p(std::true_type{}, n_full, n_it);
+  } else {
+    int i = 0;
+    for (; i + 1 < n_it; i += 2) {
+      body_ds(Int<0>{}, i);
+      body_ds(Int<1>{}, i + 1);
+    }
+    if (i < n_it) body_ds(Int<0>{}, i);
+  }
 
-  // write dK (times the scale) and dV for this wave's 32 keys
-  T* dko = (T*)(kstream ? a.dk_x : a.dk_c);
-  T* dvo = (T*)(kstream ? a.dv_x : a.dv_c);
+  // write dV (P wave) or dK times the scale (dS wave) for this pair's 32 keys
+  T* out = (T*)(p_role ? (kstream ? a.dv_x : a.dv_c) : (kstream ? a.dk_x : a.dk_c));
+  const float osc = p_role ? 1.f : a.scale;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = key0 + 32 * wave + 8 * (i >> 2) + 4 * hf + (i & 3);
-      if (key < n_keys) {
-        const int64_t off = ((int64_t)key * a.Hkv + kvh) * D + 32 * db + lk;
-        dko[off] = E::from_f(dk[db][i] * a.scale);
-        dvo[off] = E::from_f(dv[db][i]);
-      }
+      const int key = key0 + 32 * kg + 8 * (i >> 2) + 4 * hf + (i & 3);
+      if (key < n_keys) out[((int64_t)key * a.Hkv + kvh) * D + 32 * db + lk] = E::from_f(acc[db][i] * osc);
     }
   }
 }
@@ -899,7 +1013,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   if (ev) (void)hipEventRecord(ev[1].start, s);
   if (a.n_kv_items > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.n_kv_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D>), dim3(a.n_kv_items), dim3(512), 0, s, a);
   if (ev) (void)hipEventRecord(ev[1].stop, s);
   return hipGetLastError();
 }
