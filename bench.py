@@ -36,7 +36,7 @@ def log(*a):
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "bdattn_mask.h", "launch.h"):
+    for f in ("kernels.hip", "kernels_dkdv.hip", "device.h", "bdattn_mask.h", "launch.h"):
         with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -8,20 +8,24 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip"]
-HEADERS = ["bdattn_mask.h", "plan.h", "launch.h"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dkdv.hip"]
+HEADERS = ["bdattn_mask.h", "plan.h", "launch.h", "device.h"]
 
 # Packed fp32 ops are disabled for all device code (hipcc -O3 would otherwise
 # form them from plain float code).
 HIP_FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
+# Per-file options: the key-tile backward is scheduled for instruction-level
+# parallelism (measured faster for that kernel, slower for the dQ kernel).
+FILE_FLAGS = {"kernels_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:
@@ -31,26 +35,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the bdattn library needs ROCm's hipcc")
 
 
+def _clean(out: str) -> str:
+    return "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into libbdattn.so next to this file; return its path."""
-    srcs = []
-    for s in SOURCES:
-        p = os.path.join(CSRC, s)
-        # hipcc treats .cpp as host C++ unless told otherwise; api.cpp and plan.cpp
-        # only launch kernels through launch.h, so compile them as HIP too.
-        srcs += ["-x", "hip", p] if s.endswith(".cpp") else [p]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIP_FLAGS + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
+    """Compile every source (in parallel) and link libbdattn.so next to this
+    file; return its path."""
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    with tempfile.TemporaryDirectory(prefix="bdattn_build_") as tmpdir:
+        jobs = []
+        for s in SOURCES:
+            src = os.path.join(CSRC, s)
+            obj = os.path.join(tmpdir, s + ".o")
+            # hipcc treats .cpp as host C++ unless told otherwise; api.cpp and
+            # plan.cpp only launch kernels through launch.h, so compile them as
+            # HIP too.
+            lang = ["-x", "hip"] if s.endswith(".cpp") else []
+            cmd = [hipcc()] + HIP_FLAGS + FILE_FLAGS.get(s, []) + inc + ["-c"] + lang + [src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            jobs.append((s, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                  stderr=subprocess.STDOUT, text=True)))
+        errors = []
+        for s, obj, proc in jobs:
+            out = _clean(proc.communicate()[0])
+            if proc.returncode != 0:
+                errors.append(f"{s}:\n{out}")
+            elif verbose and out.strip():
+                print(out)
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp = LIB + ".tmp"
+        link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for _, o, _ in jobs] + ["-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        res = subprocess.run(link, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + _clean(res.stdout + res.stderr))
+        os.replace(tmp, LIB)
     return LIB
 
 

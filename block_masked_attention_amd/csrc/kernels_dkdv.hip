@@ -1,0 +1,304 @@
+// gfx950 (CDNA4) key-tile backward kernel of block-diffusion attention: dK
+// and dV of the clean K/V buffer and of the local corrupted keys, each summed
+// over every local query that sees the key ("Block Parallelism for Efficient
+// Distributed Long-Context Diffusion Language Model Training", §4.3, Backward
+// pass; visibility of §3.2 in bdattn_mask.h). Operand layouts and the LDS tile
+// format are described in device.h. This file is compiled on its own so that
+// its scheduling options apply to this kernel only.
+#include "device.h"
+
+namespace bdattn {
+namespace {
+
+using namespace dev;
+
+// ======================================================================
+// Backward, dK/dV. One workgroup = 8 waves owning BWD_TK keys of one KV head.
+// Waves w and w + 4 (which share a SIMD) own the same 32 keys, in two roles:
+//   the P wave    S = Q K^T, P = exp2(S c - LSE2) (masked), dV += P^T dO;
+//   the dS wave   dP = dO V^T, dS = P (dP - D), dK += dS^T Q,
+// with P handed over through LDS in the exact register layout in which both
+// waves hold their 32 x 32 result tiles. Each step (BWD_TQ query rows of one
+// q head) has two phases separated by a barrier: {S, P | dP} then {dV | dS,
+// dK}, so in each phase one wave's vector work overlaps the other's matrix
+// products. Each wave keeps one accumulator (dV or dK) and one operand (K or
+// V) in registers, which lets two waves share a SIMD. The next step's Q and dO
+// tiles and its LSE2 / D values are copied into the other LDS buffer while the
+// current one is in use. Tiles whose rows all see every key of the workgroup
+// come first and skip the mask.
+// ======================================================================
+template <bool BF16, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  using Frag = typename E::Frag;
+  constexpr int TK = BWD_TK, TQ = BWD_TQ, NW = 8, NMB = TQ / 32;
+  constexpr int TSZ = TQ * D;
+  static_assert(TK == 32 * NW / 2, "two waves per 32 keys");
+  static_assert(TQ % 32 == 0 && TQ <= 128, "row data copy: one wave, 16 bytes per lane");
+  __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];        // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];  // [buffer][LSE2, D]
+  __shared__ __attribute__((aligned(16))) float4 p_hand[NW / 2][NMB][4][64];  // P handoff
+  static_assert(sizeof(smem) + sizeof(r_row) + sizeof(p_hand) <= 160 * 1024, "LDS");
+  constexpr uint32_t TB = TSZ * sizeof(T);  // bytes per tile
+
+  const BwdItem item = a.kv_items[blockIdx.x];
+  const int it_x0 = item.x0, it_x1 = item.x1, it_c0 = item.c0, it_c1 = item.c1;
+  const int it_xf = item.xf, it_cf = item.cf;
+  const int kstream = item.hs & 1, kvh = item.hs >> 1;
+  const int G = a.H / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3;            // key group: keys 32 kg .. 32 kg + 31 of the tile
+  const bool p_role = wave < NW / 2;  // P wave (dV) or dS wave (dK)
+  const int lk = lane & 31, hf = lane >> 5;
+  const int key0 = item.ktile * TK;
+  const int n_keys = kstream ? a.n_corr : a.n_clean_kv;
+  const int my_key = key0 + 32 * kg + lk;
+  const bool key_ok = my_key < n_keys;
+  const float inv_b = 1.f / float(a.B);
+  const int key_blk = div_small(my_key, a.B, inv_b);  // clean: global block; corrupted: local
+
+  // this lane's key (P wave) or value (dS wave) as B operand, natural over d
+  Frag kvf[D / 16];
+  {
+    const T* src = (const T*)(p_role ? (kstream ? a.k_x : a.k_c) : (kstream ? a.v_x : a.v_c));
+    const int64_t off = ((int64_t)min(my_key, n_keys - 1) * a.Hkv + kvh) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      kvf[ks] = key_ok ? E::load(src + off + 16 * ks + 8 * hf) : E::zero();
+  }
+
+  OperandReads<BF16, D> rd;
+  rd.init(lane);
+
+  f32x16 acc[D / 32];  // dV (P wave) or dK / scale (dS wave)
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
+
+  // Step order: the query tiles that see every key of the workgroup (those
+  // starting at or after xf / cf) come first, then the ones that need the
+  // mask; within each, corrupted tiles then clean ones, each from the last
+  // tile down, every q head of the group per tile. A step is (tile index t in
+  // that order, head offset hi), advanced without divisions.
+  auto ntiles = [](int r0, int r1) { return r1 > r0 ? (r1 - 1) / TQ - r0 / TQ + 1 : 0; };
+  const int top_x = (it_x1 - 1) / TQ, top_c = (it_c1 - 1) / TQ;
+  const int nf_x = it_xf < it_x1 ? top_x - it_xf / TQ + 1 : 0;
+  const int nf_c = it_cf < it_c1 ? top_c - it_cf / TQ + 1 : 0;
+  const int nm_x = ntiles(it_x0, it_x1) - nf_x, nm_c = ntiles(it_c0, it_c1) - nf_c;
+  const int n_full = (nf_x + nf_c) * G;
+  const int n_it = n_full + (nm_x + nm_c) * G;
+  struct Step {
+    int qs, q0, h;
+  };
+  struct Pos {
+    int t, hi;
+  };
+  auto decode = [&](Pos p) __attribute__((always_inline)) {
+    Step s;
+    s.h = kvh * G + p.hi;
+    int t = p.t;
+    if (t < nf_x) {
+      s.qs = 1;
+      s.q0 = (top_x - t) * TQ;
+    } else if ((t -= nf_x) < nf_c) {
+      s.qs = 0;
+      s.q0 = (top_c - t) * TQ;
+    } else if ((t -= nf_c) < nm_x) {
+      s.qs = 1;
+      s.q0 = (top_x - nf_x - t) * TQ;
+    } else {
+      t -= nm_x;
+      s.qs = 0;
+      s.q0 = (top_c - nf_c - t) * TQ;
+    }
+    return s;
+  };
+  auto next_pos = [&](Pos p) __attribute__((always_inline)) {
+    if (++p.hi == G) {
+      p.hi = 0;
+      ++p.t;
+    }
+    return p;
+  };
+
+  // per-lane source of the row-data copy: lanes [0, TQ/4) copy LSE2, the
+  // next TQ/4 lanes D (kept opaque so the per-step stream choice stays a
+  // register select rather than a load of the selected argument)
+  const float* rsrc_c = lane < TQ / 4 ? a.l2_c : a.d_c;
+  const float* rsrc_x = lane < TQ / 4 ? a.l2_x : a.d_x;
+  asm volatile("" : "+v"(rsrc_c), "+v"(rsrc_x));
+  TileCopy<T, TQ, D, NW> cp;
+  cp.init(wave, lane, (int64_t)a.H * D);
+  // copy step s's Q and dO tiles and its LSE2 / D rows into LDS buffer `buf`
+  auto fetch = [&](const Step& s, int buf) __attribute__((always_inline)) {
+    const int n_rows = s.qs ? a.n_corr : a.n_clean_q;
+    const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
+    const T* gsrc = (const T*)(s.qs ? a.do_x : a.do_c) + (int64_t)s.h * D;
+    T* dst = smem + buf * 2 * TSZ;
+    cp.issue(dst, qsrc, s.q0, n_rows);
+    cp.issue(dst + TSZ, gsrc, s.q0, n_rows);
+    if (wave == 0 && lane < TQ / 2) {  // lanes [0, TQ/4): LSE2 of the TQ rows, then D
+      constexpr int L = TQ / 4;
+      const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane % L);
+      const float* src = (s.qs ? rsrc_x : rsrc_c) + r0;
+      lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(&r_row[buf][0][0])));
+    }
+  };
+
+  // 32 x 32 result tile of block mb of tile TILE: its rows against this
+  // wave's keys, contraction over d with the operand kept in registers
+  auto product = [&](auto tile_tag, int mb, f32x16& c) __attribute__((always_inline)) {
+    constexpr uint32_t TILE = decltype(tile_tag)::value;
+    Frag fr[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) fr[ks] = rd.template row_frag<TILE>(smem, mb, ks);
+    c = zero16();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) E::mma(c, fr[ks], kvf[ks]);
+  };
+  // acc += X^T Y over the 32 rows of block mb, X given as packed result-order
+  // fragments, Y the rows of tile TILE read transposed
+  auto accumulate = [&](auto tile_tag, int mb, const Frag* x) __attribute__((always_inline)) {
+    constexpr uint32_t TILE = decltype(tile_tag)::value;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      Frag y[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) y[db] = rd.template tr_frag<TILE>(smem, 32 * mb + 16 * t, db);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) E::mma(acc[db], x[t], y[db]);
+    }
+  };
+
+  Pos pos = {0, 0};  // position of the current step
+  // P wave: S, P (masked on tiles that need it), hand P over, dV += P^T dO
+  auto body_p = [&](auto mask_tag, auto buf_tag, int i) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+    using QT = std::integral_constant<uint32_t, BUF * 2 * TB>;
+    using GT = std::integral_constant<uint32_t, BUF * 2 * TB + TB>;
+    const Pos nxt = next_pos(pos);
+    if (i + 1 < n_it) fetch(decode(nxt), BUF ^ 1);
+    const Step st = decode(pos);
+    const int n_rows = st.qs ? a.n_corr : a.n_clean_q;
+    // visibility of (query row, this lane's key) on tiles that need the mask
+    auto sees = [&](int row) -> bool __attribute__((always_inline)) {
+      if (!key_ok || row >= n_rows) return false;
+      const int rb = div_small(row, a.B, inv_b);
+      if (kstream) return rb == key_blk;  // own corrupted block
+      if (st.qs == 0) return key_blk <= div_small(a.clean_q_start + row, a.B, inv_b);
+      return key_blk < a.ids[rb];
+    };
+    Frag pa[NMB][2];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      f32x16 s;
+      product(QT{}, mb, s);
+      float p[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = 32 * mb + 8 * g + 4 * hf;
+        const float4 l4 = *(const float4*)(&r_row[BUF][0][qr]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float pv = fast_exp2(fmaf(s[4 * g + r], a.scale_log2, -lv[r]));
+          if (MASK) pv = sees(st.q0 + qr + r) ? pv : 0.f;
+          p[4 * g + r] = pv;
+        }
+        p_hand[kg][mb][g][lane] = make_float4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
+      }
+      pa[mb][0] = E::pack(p);
+      pa[mb][1] = E::pack(p + 8);
+    }
+    __syncthreads();  // P handed over
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) accumulate(GT{}, mb, pa[mb]);
+    pos = nxt;
+    lds_dma_wait();
+    __syncthreads();
+  };
+  // dS wave: dP, then (once P is there) dS = P (dP - D), dK += dS^T Q
+  auto body_ds = [&](auto buf_tag, int i) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using QT = std::integral_constant<uint32_t, BUF * 2 * TB>;
+    using GT = std::integral_constant<uint32_t, BUF * 2 * TB + TB>;
+    const Pos nxt = next_pos(pos);
+    if (i + 1 < n_it) fetch(decode(nxt), BUF ^ 1);
+    f32x16 dp[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) product(GT{}, mb, dp[mb]);
+    __syncthreads();  // P handed over
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      float ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qr = 32 * mb + 8 * g + 4 * hf;
+        const float4 d4 = *(const float4*)(&r_row[BUF][1][qr]);
+        const float4 p4 = p_hand[kg][mb][g][lane];
+        ds[4 * g + 0] = p4.x * (dp[mb][4 * g + 0] - d4.x);
+        ds[4 * g + 1] = p4.y * (dp[mb][4 * g + 1] - d4.y);
+        ds[4 * g + 2] = p4.z * (dp[mb][4 * g + 2] - d4.z);
+        ds[4 * g + 3] = p4.w * (dp[mb][4 * g + 3] - d4.w);
+      }
+      const Frag sa[2] = {E::pack(ds), E::pack(ds + 8)};
+      accumulate(QT{}, mb, sa);
+    }
+    pos = nxt;
+    lds_dma_wait();
+    __syncthreads();
+  };
+  auto sweep_p = [&](auto mask_tag, int i0, int i1) __attribute__((always_inline)) {
+    int i = i0;
+    if (i < i1 && (i & 1)) body_p(mask_tag, Int<1>{}, i++);
+    for (; i + 1 < i1; i += 2) {
+      body_p(mask_tag, Int<0>{}, i);
+      body_p(mask_tag, Int<1>{}, i + 1);
+    }
+    if (i < i1) body_p(mask_tag, Int<0>{}, i);
+  };
+
+  if (n_it > 0) fetch(decode(pos), 0);
+  vm_drain();
+  __syncthreads();
+  if (p_role) {
+    sweep_p(std::false_type{}, 0, n_full);
+    sweep_p(std::true_type{}, n_full, n_it);
+  } else {
+    int i = 0;
+    for (; i + 1 < n_it; i += 2) {
+      body_ds(Int<0>{}, i);
+      body_ds(Int<1>{}, i + 1);
+    }
+    if (i < n_it) body_ds(Int<0>{}, i);
+  }
+
+  // write dV (P wave) or dK times the scale (dS wave) for this pair's 32 keys
+  T* out = (T*)(p_role ? (kstream ? a.dv_x : a.dv_c) : (kstream ? a.dk_x : a.dk_c));
+  const float osc = p_role ? 1.f : a.scale;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + 32 * kg + 8 * (i >> 2) + 4 * hf + (i & 3);
+      if (key < n_keys) out[((int64_t)key * a.Hkv + kvh) * D + 32 * db + lk] = E::from_f(acc[db][i] * osc);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t s) {
+  if (a.n_kv_items <= 0) return hipSuccess;
+  const dim3 grid(a.n_kv_items), block(512);
+  if (dtype == BDATTN_BF16 && d == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_BF16 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_F32 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<false, 32>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace bdattn

@@ -50,5 +50,7 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t stream,
                       const KernelEvents* ev);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t stream,
                       const KernelEvents* ev);
+// The key-tile dK/dV kernel alone (called by launch_bwd after the dQ kernel).
+hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t stream);
 
 }  // namespace bdattn

@@ -17,7 +17,7 @@ namespace bdattn {
 // FWD_ROWS_PER_WAVE query rows per wave and sweeps the visible keys in tiles
 // of FWD_TK.
 #ifndef BDATTN_FWD_WAVES
-#define BDATTN_FWD_WAVES 4
+#define BDATTN_FWD_WAVES 8
 #endif
 constexpr int FWD_WAVES = BDATTN_FWD_WAVES;
 constexpr int FWD_ROWS_PER_WAVE = 32;

@@ -171,7 +171,8 @@ def test_plan_covers_every_visible_tile():
         M = bd.mask_render(p)
         nc, nkv, nx = int(p.n_clean_q), int(p.n_clean_kv), p.n_corr
         R = st["fwd_rows_per_item"]
-        Gw = 4 * 32 // R
+        G = int(p.H) // int(p.Hkv)  # q heads per KV head; a work item takes 4, 2 or 1 of them
+        Gw = 4 if G % 4 == 0 else (2 if G % 2 == 0 else 1)
         want_items, want_tiles = 0, 0
         for s, (r0, n) in enumerate(((0, nc), (nc, nx))):
             for t in range(0, n, R):
