@@ -249,6 +249,11 @@ def main():
                    "Hkv": Hkv, "d": d, "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful_step, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),
+        # the same step under the FlashAttention convention (14d per pair and q
+        # head: the backward's QK^T recompute counted as work)
+        "fa_convention_tflops": round(14.0 * d * H * pairs / (ms_step * 1e-3) / 1e12, 2),
+        "fwd_ms": kern["fwd"]["ms"],
+        "bwd_ms": round(kern["bwd_dq"]["ms"] + kern["bwd_dkdv"]["ms"], 3),
         "kernels": dict(kern, other_ms=round(ms_step - sum(v["ms"] for v in kern.values()), 3)),
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
