@@ -57,8 +57,32 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int n_keys = kstream ? a.n_corr : a.n_clean_kv;
   const int my_key = key0 + 32 * kg + lk;
   const bool key_ok = my_key < n_keys;
-  const float inv_b = 1.f / float(a.B);
-  const int key_blk = div_small(my_key, a.B, inv_b);  // clean: global block; corrupted: local
+  // Local query rows that see this lane's key form one interval per query
+  // stream (§3.2 rules with row-nondecreasing bounds): [lo_c, hi_c) of the
+  // clean rows and [lo_x, hi_x) of the corrupted rows.
+  //   clean key of block kb:  clean rows of blocks >= kb; corrupted rows of
+  //     blocks with id > kb, i.e. from the first local block whose id exceeds
+  //     kb. The item gives that block j0 for the tile's first key block k0/B;
+  //     ids increase strictly, so for kb = k0/B + delta it lies in
+  //     [j0, j0 + delta] and a short scan finds it;
+  //   corrupted key of local block kb: the corrupted rows of that block.
+  int lo_c = 0, hi_c = 0, lo_x = 0, hi_x = 0;
+  if (key_ok) {
+    const int key_blk = my_key / a.B;  // clean: global block; corrupted: local block
+    if (kstream) {
+      lo_x = key_blk * a.B;
+      hi_x = lo_x + a.B;
+    } else {
+      lo_c = max(0, key_blk * a.B - a.clean_q_start);
+      hi_c = a.n_clean_q;
+      const int n_blk = a.n_corr / a.B;
+      int j = it_x0 / a.B;  // j0: first local corrupted block with id > k0 / B
+      const int j_end = min(n_blk, j + (key_blk - key0 / a.B));
+      while (j < j_end && a.ids[j] <= key_blk) ++j;
+      lo_x = j * a.B;
+      hi_x = a.n_corr;
+    }
+  }
 
   // this lane's key (P wave) or value (dS wave) as B operand, natural over d
   Frag kvf[D / 16];
@@ -184,13 +208,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const Step st = decode(pos);
     const int n_rows = st.qs ? a.n_corr : a.n_clean_q;
     // visibility of (query row, this lane's key) on tiles that need the mask
-    auto sees = [&](int row) -> bool __attribute__((always_inline)) {
-      if (!key_ok || row >= n_rows) return false;
-      const int rb = div_small(row, a.B, inv_b);
-      if (kstream) return rb == key_blk;  // own corrupted block
-      if (st.qs == 0) return key_blk <= div_small(a.clean_q_start + row, a.B, inv_b);
-      return key_blk < a.ids[rb];
-    };
+    const int lo = st.qs ? lo_x : lo_c, hi = st.qs ? hi_x : hi_c;
+    auto sees = [&](int row) -> bool __attribute__((always_inline)) { return row >= lo && row < hi; };
     Frag pa[NMB][2];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
