@@ -282,8 +282,8 @@ struct TileCopy {
   static constexpr int NCH = D / EPC;
   static constexpr int NT = 64 * NW;
   static constexpr int NC = R * NCH;              // chunks in the tile
-  static constexpr int CPW = (NC + NT - 1) / NT;  // copies per lane
-  static_assert(NC % 64 == 0 && (NC % NT == 0 || NC < NT), "tile chunks vs workgroup size");
+  static constexpr int CPW = (NC + NT - 1) / NT;  // copies per lane (the last may be partial)
+  static_assert(NC % 64 == 0, "whole waves per copy");
   uint32_t off[CPW];  // element offset of each copy's chunk: r * stride + c * EPC
   int wave, lane;
   int64_t stride;
@@ -294,23 +294,27 @@ struct TileCopy {
     stride = stride_;
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
-      const int pos = u * NT + wave * 64 + lane;
+      const int pos = min(u * NT + wave * 64 + lane, NC - 1);
       const int r = pos / NCH, c = (pos % NCH) ^ tile_swz<NCH>(r);
       off[u] = uint32_t(r * stride + c * EPC);
     }
   }
-  __device__ __forceinline__ bool active() const { return !(NC < NT && wave * 64 >= NC); }
+  // copy u of this wave exists (whole waves: NC is a multiple of 64)
+  __device__ __forceinline__ bool has(int u) const {
+    if constexpr (NC % NT == 0) return true;
+    return u * NT + wave * 64 < NC;
+  }
   __device__ __forceinline__ void issue(T* tile, const T* src, int row0, int nrows) const {
-    if (!active()) return;  // small tile: whole waves idle
     const uint32_t base = lds_addr(tile) + uint32_t(wave * 64) * 16u;
     if (row0 + R <= nrows) {
       const T* s0 = src + (int64_t)row0 * stride;
 #pragma unroll
       for (int u = 0; u < CPW; ++u)
-        lds_dma16(s0 + off[u], __builtin_amdgcn_readfirstlane(base + uint32_t(u * NT) * 16u));
+        if (has(u)) lds_dma16(s0 + off[u], __builtin_amdgcn_readfirstlane(base + uint32_t(u * NT) * 16u));
     } else {
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
+        if (!has(u)) continue;
         const int pos = u * NT + wave * 64 + lane;
         const int r = pos / NCH, c = (pos % NCH) ^ tile_swz<NCH>(r);
         const int row = min(row0 + r, nrows - 1);
