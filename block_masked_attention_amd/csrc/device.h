@@ -325,5 +325,28 @@ struct TileCopy {
   }
 };
 
+// Operand reads kept in flight ahead of the matrix product that consumes them.
+constexpr int kReadAhead = 3;
+
+// A chain of N matrix products in which product k takes one operand fragment
+// read from LDS by read(k) and is issued by mma(k, fragment). The reads run
+// PF products ahead of the products, and scheduling fences keep that order.
+// Left to itself, the compiler sinks each read next to its product when
+// registers are scarce, and every product then waits for a full LDS round
+// trip.
+template <int N, int PF, class Frag, class Read, class Mma>
+__device__ __forceinline__ void product_chain(Read read, Mma mma) {
+  Frag buf[PF];
+#pragma unroll
+  for (int k = 0; k < PF && k < N; ++k) buf[k] = read(k);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma(k, buf[k % PF]);
+    if (k + PF < N) buf[k % PF] = read(k + PF);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace dev
 }  // namespace bdattn

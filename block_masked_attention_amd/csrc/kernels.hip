@@ -140,16 +140,13 @@ void fwd_kernel(FwdArgs a) {
     const bool cl = j < q.n_ct;
     const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
 
+    // S of both key blocks, alternating blocks: product k = (ks, mb)
     f32x16 s[TK / 32];
 #pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-      Frag kfr[D / 16];  // read ahead of the products
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) kfr[ks] = rd.template row_frag<KT>(smem, mb, ks);
-      s[mb] = zero16();
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) E::mma(s[mb], kfr[ks], qf[ks]);
-    }
+    for (int mb = 0; mb < TK / 32; ++mb) s[mb] = zero16();
+    product_chain<TK / 32 * D / 16, kReadAhead, Frag>(
+        [&](int k) __attribute__((always_inline)) { return rd.template row_frag<KT>(smem, k % (TK / 32), k / (TK / 32)); },
+        [&](int k, const Frag& f) __attribute__((always_inline)) { E::mma(s[k % (TK / 32)], f, qf[k / (TK / 32)]); });
     // online softmax; the row max is taken on raw scores (the scale is > 0)
     // and the scale folded into the exponent's multiply-add
     float mx = kNegInf;
@@ -192,17 +189,13 @@ void fwd_kernel(FwdArgs a) {
       pf[mb][1] = E::pack(p + 8);
     }
     l += rs;
-#pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        Frag vt[D / 32];  // read ahead of the products
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) vt[db] = rd.template tr_frag<VT>(smem, 32 * mb + 16 * t, db);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) E::mma(o[db], vt[db], pf[mb][t]);
-      }
-    }
+    // O += V^T P over the tile's keys: product k = (16-key slice mt, column block db)
+    product_chain<TK / 32 * 2 * (D / 32), kReadAhead, Frag>(
+        [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<VT>(smem, 16 * (k / (D / 32)), k % (D / 32)); },
+        [&](int k, const Frag& y) __attribute__((always_inline)) {
+          const int mt = k / (D / 32);
+          E::mma(o[k % (D / 32)], y, pf[mt / 2][mt % 2]);
+        });
     lds_dma_wait();
     __syncthreads();
   };
@@ -349,18 +342,16 @@ void bwd_dq_kernel(BwdArgs a) {
     Frag sf[TK / 32][2];
 #pragma unroll
     for (int mb = 0; mb < TK / 32; ++mb) {
+      // S and dP of key block mb, alternating: even k S (K rows), odd k dP (V rows)
       f32x16 s = zero16(), dp = zero16();
-      Frag kfr[D / 16], vfr[D / 16];  // read ahead of the products
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        kfr[ks] = rd.template row_frag<KT>(smem, mb, ks);
-        vfr[ks] = rd.template row_frag<VT>(smem, mb, ks);
-      }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        E::mma(s, kfr[ks], qf[ks]);
-        E::mma(dp, vfr[ks], gf[ks]);
-      }
+      product_chain<2 * D / 16, kReadAhead, Frag>(
+          [&](int k) __attribute__((always_inline)) {
+            return (k & 1) ? rd.template row_frag<VT>(smem, mb, k / 2) : rd.template row_frag<KT>(smem, mb, k / 2);
+          },
+          [&](int k, const Frag& f) __attribute__((always_inline)) {
+            if (k & 1) E::mma(dp, f, gf[k / 2]);
+            else E::mma(s, f, qf[k / 2]);
+          });
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -375,17 +366,13 @@ void bwd_dq_kernel(BwdArgs a) {
       sf[mb][0] = E::pack(ds);
       sf[mb][1] = E::pack(ds + 8);
     }
-#pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        Frag kt[D / 32];  // read ahead of the products
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) kt[db] = rd.template tr_frag<KT>(smem, 32 * mb + 16 * t, db);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) E::mma(dq[db], kt[db], sf[mb][t]);
-      }
-    }
+    // dQ += K^T dS over the tile's keys: product k = (16-key slice mt, column block db)
+    product_chain<TK / 32 * 2 * (D / 32), kReadAhead, Frag>(
+        [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<KT>(smem, 16 * (k / (D / 32)), k % (D / 32)); },
+        [&](int k, const Frag& y) __attribute__((always_inline)) {
+          const int mt = k / (D / 32);
+          E::mma(dq[k % (D / 32)], y, sf[mt / 2][mt % 2]);
+        });
     lds_dma_wait();
     __syncthreads();
   };

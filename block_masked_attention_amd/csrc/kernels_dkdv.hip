@@ -171,29 +171,29 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // 32 x 32 result tile of block mb of tile TILE: its rows against this
-  // wave's keys, contraction over d with the operand kept in registers
-  auto product = [&](auto tile_tag, int mb, f32x16& c) __attribute__((always_inline)) {
+  // S (P wave) or dP (dS wave) of both row blocks of tile TILE against this
+  // wave's keys / values, alternating blocks: product k = (ks, mb)
+  auto scores = [&](auto tile_tag, f32x16* c) __attribute__((always_inline)) {
     constexpr uint32_t TILE = decltype(tile_tag)::value;
-    Frag fr[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) fr[ks] = rd.template row_frag<TILE>(smem, mb, ks);
-    c = zero16();
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) E::mma(c, fr[ks], kvf[ks]);
+    for (int mb = 0; mb < NMB; ++mb) c[mb] = zero16();
+    product_chain<NMB * D / 16, kReadAhead, Frag>(
+        [&](int k) __attribute__((always_inline)) { return rd.template row_frag<TILE>(smem, k % NMB, k / NMB); },
+        [&](int k, const Frag& f) __attribute__((always_inline)) { E::mma(c[k % NMB], f, kvf[k / NMB]); });
   };
-  // acc += X^T Y over the 32 rows of block mb, X given as packed result-order
-  // fragments, Y the rows of tile TILE read transposed
-  auto accumulate = [&](auto tile_tag, int mb, const Frag* x) __attribute__((always_inline)) {
+  // acc += X^T Y over the TQ rows of tile TILE, X given as packed result-order
+  // fragments [block][half], Y the rows read transposed: product k = (16-row
+  // slice mt, column block db)
+  auto accumulate = [&](auto tile_tag, const Frag (*x)[2]) __attribute__((always_inline)) {
     constexpr uint32_t TILE = decltype(tile_tag)::value;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      Frag y[D / 32];
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) y[db] = rd.template tr_frag<TILE>(smem, 32 * mb + 16 * t, db);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) E::mma(acc[db], x[t], y[db]);
-    }
+    product_chain<NMB * 2 * (D / 32), kReadAhead, Frag>(
+        [&](int k) __attribute__((always_inline)) {
+          return rd.template tr_frag<TILE>(smem, 16 * (k / (D / 32)), k % (D / 32));
+        },
+        [&](int k, const Frag& y) __attribute__((always_inline)) {
+          const int mt = k / (D / 32);
+          E::mma(acc[k % (D / 32)], x[mt / 2][mt % 2], y);
+        });
   };
 
   Pos pos = {0, 0};  // position of the current step
@@ -210,11 +210,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // visibility of (query row, this lane's key) on tiles that need the mask
     const int lo = st.qs ? lo_x : lo_c, hi = st.qs ? hi_x : hi_c;
     auto sees = [&](int row) -> bool __attribute__((always_inline)) { return row >= lo && row < hi; };
+    f32x16 sb[NMB];
+    scores(QT{}, sb);
     Frag pa[NMB][2];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-      f32x16 s;
-      product(QT{}, mb, s);
+      const f32x16& s = sb[mb];
       float p[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -233,8 +234,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       pa[mb][1] = E::pack(p + 8);
     }
     __syncthreads();  // P handed over
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) accumulate(GT{}, mb, pa[mb]);
+    accumulate(GT{}, pa);
     pos = nxt;
     lds_dma_wait();
     __syncthreads();
@@ -247,9 +247,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const Pos nxt = next_pos(pos);
     if (i + 1 < n_it) fetch(decode(nxt), BUF ^ 1);
     f32x16 dp[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) product(GT{}, mb, dp[mb]);
+    scores(GT{}, dp);
     __syncthreads();  // P handed over
+    Frag sa[NMB][2];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       float ds[16];
@@ -263,9 +263,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
         ds[4 * g + 2] = p4.z * (dp[mb][4 * g + 2] - d4.z);
         ds[4 * g + 3] = p4.w * (dp[mb][4 * g + 3] - d4.w);
       }
-      const Frag sa[2] = {E::pack(ds), E::pack(ds + 8)};
-      accumulate(QT{}, mb, sa);
+      sa[mb][0] = E::pack(ds);
+      sa[mb][1] = E::pack(ds + 8);
     }
+    accumulate(QT{}, sa);
     pos = nxt;
     lds_dma_wait();
     __syncthreads();
