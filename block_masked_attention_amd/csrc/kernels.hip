@@ -13,7 +13,7 @@
 //
 // Kernels:
 //   fwd_kernel       query-tile parallel: online softmax over the visible keys
-//   bwd_prep_kernel  D = rowsum(dO * O) and LSE * log2(e) per query row
+//   bwd_prep_kernel  -D = -rowsum(dO * O) and LSE * log2(e) per query row
 //   bwd_dq_kernel    query-tile parallel: dQ = scale * dS K, written once
 //   bwd_dkdv_kernel  key-tile parallel: dV = P^T dO, dK = scale * dS^T Q over
 //                    every query tile (and q head of the KV group) that sees
@@ -175,6 +175,9 @@ void fwd_kernel(FwdArgs a) {
       m = m_new;
     }
     const float m_use = m == kNegInf ? 0.f : m;
+    // the row sum adds the fp32 weights: LSE must be exact, since the
+    // backward rebuilds P from it (summing the bf16-rounded weights instead
+    // shifts LSE by up to 2^-9 and scales every recomputed P of the row)
     Frag pf[TK / 32][2];
     float rs = 0.f;
 #pragma unroll
@@ -235,9 +238,10 @@ void fwd_kernel(FwdArgs a) {
 }
 
 // ======================================================================
-// Backward preprocess: per (row, head) D = rowsum(dO * O) and LSE * log2(e),
+// Backward preprocess: per (row, head) -D = -rowsum(dO * O) and LSE * log2(e),
 // D/8 lanes each, written [H][n_pad]; rows n..n_pad-1 get D = 0, LSE = +inf
-// (query tiles past the end of a stream then contribute nothing).
+// (query tiles past the end of a stream then contribute nothing). D is stored
+// negated so that the dK/dV kernel can start its dP accumulation from it.
 // ======================================================================
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const void* do_,
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
   if (pair < npairs && sub == 0) {
-    Dout[head * n_pad + row] = real ? acc : 0.f;
+    Dout[head * n_pad + row] = real ? -acc : 0.f;
     L2out[head * n_pad + row] = real ? lse[head * n_rows + row] * kLog2e : __builtin_inff();
   }
 }
@@ -307,7 +311,7 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   const int64_t ri = (int64_t)q.head * row_pad(q.n_rows) + q.crow;
   const float lse2 = q.row_ok ? (q.stream ? a.l2_x : a.l2_c)[ri] : __builtin_inff();
-  const float drow = q.row_ok ? (q.stream ? a.d_x : a.d_c)[ri] : 0.f;
+  const float ndrow = q.row_ok ? (q.stream ? a.d_x : a.d_c)[ri] : 0.f;  // -D
 
   TileCopy<T, TK, D, FWD_WAVES> cp;
   cp.init(wave, lane, (int64_t)a.Hkv * D);
@@ -361,7 +365,7 @@ void bwd_dq_kernel(BwdArgs a) {
           const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
           p = vis ? p : 0.f;
         }
-        ds[i] = p * (dp[i] - drow);
+        ds[i] = p * (dp[i] + ndrow);
       }
       sf[mb][0] = E::pack(ds);
       sf[mb][1] = E::pack(ds + 8);

@@ -16,14 +16,14 @@ using namespace dev;
 // Backward, dK/dV. One workgroup = 8 waves owning BWD_TK keys of one KV head.
 // Waves w and w + 4 (which share a SIMD) own the same 32 keys, in two roles:
 //   the P wave    S = Q K^T, P = exp2(S c - LSE2) (masked), dV += P^T dO;
-//   the dS wave   dP = dO V^T, dS = P (dP - D), dK += dS^T Q,
+//   the dS wave   dP - D = dO V^T - D, dS = P (dP - D), dK += dS^T Q,
 // with P handed over through LDS in the exact register layout in which both
 // waves hold their 32 x 32 result tiles. Each step (BWD_TQ query rows of one
 // q head) has two phases separated by a barrier: {S, P | dP} then {dV | dS,
 // dK}, so in each phase one wave's vector work overlaps the other's matrix
 // products. Each wave keeps one accumulator (dV or dK) and one operand (K or
 // V) in registers, which lets two waves share a SIMD. The next step's Q and dO
-// tiles and its LSE2 / D values are copied into the other LDS buffer while the
+// tiles and its LSE2 / -D values are copied into the other LDS buffer while the
 // current one is in use. Tiles whose rows all see every key of the workgroup
 // come first and skip the mask.
 // ======================================================================
@@ -38,7 +38,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(TK == 32 * NW / 2, "two waves per 32 keys");
   static_assert(TQ % 32 == 0 && TQ <= 128, "row data copy: one wave, 16 bytes per lane");
   __shared__ __attribute__((aligned(16))) T smem[4 * TSZ];        // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];  // [buffer][LSE2, D]
+  __shared__ __attribute__((aligned(16))) float r_row[2][2][TQ];  // [buffer][LSE2, -D]
   __shared__ __attribute__((aligned(16))) float4 p_hand[NW / 2][NMB][4][64];  // P handoff
   static_assert(sizeof(smem) + sizeof(r_row) + sizeof(p_hand) <= 160 * 1024, "LDS");
   constexpr uint32_t TB = TSZ * sizeof(T);  // bytes per tile
@@ -148,14 +148,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   // per-lane source of the row-data copy: lanes [0, TQ/4) copy LSE2, the
-  // next TQ/4 lanes D (kept opaque so the per-step stream choice stays a
+  // next TQ/4 lanes -D (kept opaque so the per-step stream choice stays a
   // register select rather than a load of the selected argument)
   const float* rsrc_c = lane < TQ / 4 ? a.l2_c : a.d_c;
   const float* rsrc_x = lane < TQ / 4 ? a.l2_x : a.d_x;
   asm volatile("" : "+v"(rsrc_c), "+v"(rsrc_x));
   TileCopy<T, TQ, D, NW> cp;
   cp.init(wave, lane, (int64_t)a.H * D);
-  // copy step s's Q and dO tiles and its LSE2 / D rows into LDS buffer `buf`
+  // copy step s's Q and dO tiles and its LSE2 / -D rows into LDS buffer `buf`
   auto fetch = [&](const Step& s, int buf) __attribute__((always_inline)) {
     const int n_rows = s.qs ? a.n_corr : a.n_clean_q;
     const T* qsrc = (const T*)(s.qs ? a.q_x : a.q_c) + (int64_t)s.h * D;
@@ -163,7 +163,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     T* dst = smem + buf * 2 * TSZ;
     cp.issue(dst, qsrc, s.q0, n_rows);
     cp.issue(dst + TSZ, gsrc, s.q0, n_rows);
-    if (wave == 0 && lane < TQ / 2) {  // lanes [0, TQ/4): LSE2 of the TQ rows, then D
+    if (wave == 0 && lane < TQ / 2) {  // lanes [0, TQ/4): LSE2 of the TQ rows, then -D
       constexpr int L = TQ / 4;
       const int64_t r0 = (int64_t)s.h * row_pad(n_rows) + s.q0 + 4 * (lane % L);
       const float* src = (s.qs ? rsrc_x : rsrc_c) + r0;
@@ -171,12 +171,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // S (P wave) or dP (dS wave) of both row blocks of tile TILE against this
-  // wave's keys / values, alternating blocks: product k = (ks, mb)
+  // c += S (P wave) or dP (dS wave) of both row blocks of tile TILE against
+  // this wave's keys / values, alternating blocks: product k = (ks, mb)
   auto scores = [&](auto tile_tag, f32x16* c) __attribute__((always_inline)) {
     constexpr uint32_t TILE = decltype(tile_tag)::value;
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) c[mb] = zero16();
     product_chain<NMB * D / 16, kReadAhead, Frag>(
         [&](int k) __attribute__((always_inline)) { return rd.template row_frag<TILE>(smem, k % NMB, k / NMB); },
         [&](int k, const Frag& f) __attribute__((always_inline)) { E::mma(c[k % NMB], f, kvf[k / NMB]); });
@@ -211,6 +209,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int lo = st.qs ? lo_x : lo_c, hi = st.qs ? hi_x : hi_c;
     auto sees = [&](int row) -> bool __attribute__((always_inline)) { return row >= lo && row < hi; };
     f32x16 sb[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) sb[mb] = zero16();
     scores(QT{}, sb);
     Frag pa[NMB][2];
 #pragma unroll
@@ -239,7 +239,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     lds_dma_wait();
     __syncthreads();
   };
-  // dS wave: dP, then (once P is there) dS = P (dP - D), dK += dS^T Q
+  // dS wave: dP - D (the product accumulates onto -D, read from LDS in the
+  // result layout: element i of a row block is row 8(i/4) + 4 h + i%4), then
+  // (once P is there) dS = P (dP - D), dK += dS^T Q
   auto body_ds = [&](auto buf_tag, int i) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     using QT = std::integral_constant<uint32_t, BUF * 2 * TB>;
@@ -247,6 +249,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const Pos nxt = next_pos(pos);
     if (i + 1 < n_it) fetch(decode(nxt), BUF ^ 1);
     f32x16 dp[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *(const float4*)(&r_row[BUF][1][32 * mb + 8 * g + 4 * hf]);
+        dp[mb][4 * g + 0] = d4.x;
+        dp[mb][4 * g + 1] = d4.y;
+        dp[mb][4 * g + 2] = d4.z;
+        dp[mb][4 * g + 3] = d4.w;
+      }
+    }
     scores(GT{}, dp);
     __syncthreads();  // P handed over
     Frag sa[NMB][2];
@@ -255,13 +268,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
       float ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int qr = 32 * mb + 8 * g + 4 * hf;
-        const float4 d4 = *(const float4*)(&r_row[BUF][1][qr]);
         const float4 p4 = p_hand[kg][mb][g][lane];
-        ds[4 * g + 0] = p4.x * (dp[mb][4 * g + 0] - d4.x);
-        ds[4 * g + 1] = p4.y * (dp[mb][4 * g + 1] - d4.y);
-        ds[4 * g + 2] = p4.z * (dp[mb][4 * g + 2] - d4.z);
-        ds[4 * g + 3] = p4.w * (dp[mb][4 * g + 3] - d4.w);
+        ds[4 * g + 0] = p4.x * dp[mb][4 * g + 0];
+        ds[4 * g + 1] = p4.y * dp[mb][4 * g + 1];
+        ds[4 * g + 2] = p4.z * dp[mb][4 * g + 2];
+        ds[4 * g + 3] = p4.w * dp[mb][4 * g + 3];
       }
       sa[mb][0] = E::pack(ds);
       sa[mb][1] = E::pack(ds + 8);

@@ -29,7 +29,7 @@ struct BwdArgs {
   int32_t n_q_items;
   const BwdItem* kv_items;  // dK/dV kernel: key-tile work list
   int32_t n_kv_items;
-  float *d_c, *d_x;        // workspace: D = rowsum(dO * O)      [H][row_pad(n)]
+  float *d_c, *d_x;        // workspace: -D = -rowsum(dO * O)    [H][row_pad(n)]
   float *l2_c, *l2_x;      // workspace: LSE * log2(e), +inf pad [H][row_pad(n)]
   int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;

@@ -83,10 +83,10 @@ void build_plan(const Problem& P, Plan* plan);
 // Workspace layout (byte offsets from the workspace start). Forward: the
 // corrupted block ids and the query-tile work list. Backward: the ids, the
 // query-tile list (dQ kernel), the key-tile list (dK/dV kernel) and
-// D = rowsum(dO * O) of each stream.
-// The backward's per-row data of each stream, D = rowsum(dO * O) and
+// -D = -rowsum(dO * O) of each stream.
+// The backward's per-row data of each stream, -D = -rowsum(dO * O) and
 // LSE * log2(e), are float [H][round_up(n, BWD_TQ)]: every query tile's
-// values are one contiguous run, and rows past n hold D = 0, LSE = +inf.
+// values are one contiguous run, and rows past n hold -D = 0, LSE = +inf.
 struct WsLayout {
   size_t ids = 0, q_items = 0, q_items_bytes = 0, kv_items = 0, kv_items_bytes = 0;
   size_t d_c = 0, d_x = 0, l2_c = 0, l2_x = 0;  // bwd row data
