@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(HERE, "libbdattn.so")
 
 F32 = 0
 BF16 = 1
+CLEAN_BLOCK_CAUSAL = 0
+CLEAN_TOKEN_CAUSAL = 1
 STATUS = {0: "BDATTN_OK", -1: "BDATTN_ERR_INVALID_ARG", -2: "BDATTN_ERR_SHAPE",
           -3: "BDATTN_ERR_UNSUPPORTED", -4: "BDATTN_ERR_COVERAGE",
           -5: "BDATTN_ERR_WORKSPACE", -6: "BDATTN_ERR_HIP"}
@@ -29,7 +31,7 @@ STATUS = {0: "BDATTN_OK", -1: "BDATTN_ERR_INVALID_ARG", -2: "BDATTN_ERR_SHAPE",
 __all__ = ["Problem", "problem", "BdattnError", "lib", "fwd", "bwd", "validate",
            "workspace_size", "mask_render", "visible_pairs", "plan_stats", "version",
            "status_string", "profile_enable", "profile_read", "from_spec", "F32", "BF16",
-           "LIB_PATH"]
+           "CLEAN_BLOCK_CAUSAL", "CLEAN_TOKEN_CAUSAL", "LIB_PATH"]
 
 
 class BdattnError(RuntimeError):
@@ -48,6 +50,7 @@ class Problem(ctypes.Structure):
         ("n_clean_kv", ctypes.c_int64), ("clean_kv_start", ctypes.c_int64),
         ("n_corr_blocks", ctypes.c_int64),
         ("corr_block_ids", ctypes.POINTER(ctypes.c_int32)),
+        ("clean_mask", ctypes.c_int32),
     ]
 
     @property
@@ -58,15 +61,17 @@ class Problem(ctypes.Structure):
 def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_start: int = 0,
             n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
             n_corr_blocks: Optional[int] = None, corr_block_ids: Optional[Sequence[int]] = None,
-            scale: float = 0.0) -> Problem:
+            scale: float = 0.0, clean_mask: int = CLEAN_BLOCK_CAUSAL) -> Problem:
     """Problem descriptor. ``dtype`` is F32/BF16, "f32"/"bf16" or a torch dtype.
     Without ids the corrupted blocks are 0..n_corr_blocks-1 (default: as many
-    as the clean query shard has blocks)."""
+    as the clean query shard has blocks). ``clean_mask`` is CLEAN_BLOCK_CAUSAL
+    or CLEAN_TOKEN_CAUSAL (what a clean query sees of its own block)."""
     dt = _dtype_code(dtype)
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
     p = Problem()
     p.B, p.H, p.Hkv, p.d, p.dtype, p.scale = B, H, Hkv, d, dt, float(scale)
+    p.clean_mask = int(clean_mask)
     p.n_clean_q, p.clean_q_start = n_clean_q, clean_q_start
     p.n_clean_kv, p.clean_kv_start = n_clean_kv, clean_kv_start
     if corr_block_ids is not None:
@@ -86,7 +91,8 @@ def from_spec(spec) -> Problem:
     """Descriptor of a workload spec (any object with the descriptor's fields)."""
     return problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
                    spec.clean_q_start, spec.n_clean_kv, spec.clean_kv_start,
-                   spec.n_corr_blocks, spec.corr_block_ids)
+                   spec.n_corr_blocks, spec.corr_block_ids,
+                   clean_mask=getattr(spec, "clean_mask", CLEAN_BLOCK_CAUSAL))
 
 
 def _dtype_code(dtype) -> int:

@@ -47,7 +47,7 @@ PlanCache& cache() {
 std::string plan_key(const bdattn::Problem& P) {
   std::string k;
   const int32_t head[] = {P.B, P.H, P.Hkv, P.d, P.dtype, P.n_clean_q, P.clean_q_start,
-                          P.n_clean_kv, P.n_corr_blocks};
+                          P.n_clean_kv, P.n_corr_blocks, P.token_causal};
   k.append((const char*)head, sizeof(head));
   k.append((const char*)P.ids.data(), P.ids.size() * sizeof(int32_t));
   return k;
@@ -279,6 +279,7 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
+  a.token_causal = P.token_causal;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[1];
   hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, prof_events(0, 1, ev));
@@ -332,6 +333,7 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
+  a.token_causal = P.token_causal;
   a.scale = P.scale;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[2];

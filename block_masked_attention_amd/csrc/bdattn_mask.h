@@ -2,8 +2,10 @@
 //
 // "Block Parallelism for Efficient Distributed Long-Context Diffusion Language
 // Model Training", §3.2 (Block diffusion language models):
-//   clean query of block qb      sees clean keys of blocks kb <= qb,
-//                                never corrupted keys;
+//   clean query of block qb      sees clean keys of blocks kb <= qb (block-
+//                                causal), or, token-causal, clean keys of
+//                                blocks kb < qb and those of its own block at
+//                                positions up to its own; never corrupted keys;
 //   corrupted query of block qb  sees clean keys of blocks kb < qb and the
 //                                corrupted keys of its own block.
 // Blocks are 0-indexed on global clean positions: block(p) = p / B.
@@ -29,10 +31,11 @@ struct BdRowBounds {
   int32_t xhi;
 };
 
-// Clean query at global position gpos: clean keys of blocks 0..block(gpos).
-BD_HD BdRowBounds bd_clean_row(int32_t gpos, int32_t B) {
+// Clean query at global position gpos: clean keys of blocks 0..block(gpos),
+// or, token-causal, clean keys at positions 0..gpos.
+BD_HD BdRowBounds bd_clean_row(int32_t gpos, int32_t B, bool token_causal) {
   BdRowBounds r;
-  r.cb = (gpos / B + 1) * B;
+  r.cb = token_causal ? gpos + 1 : (gpos / B + 1) * B;
   r.xlo = 0;
   r.xhi = 0;
   return r;

@@ -221,8 +221,8 @@ struct OperandReads {
 
 // Row bounds of local row `row` of a query stream (0 clean, 1 corrupted).
 __device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, int32_t clean_q_start,
-                                                  const int32_t* ids, int32_t B) {
-  if (stream == 0) return bd_clean_row(clean_q_start + row, B);
+                                                  const int32_t* ids, int32_t B, bool token_causal) {
+  if (stream == 0) return bd_clean_row(clean_q_start + row, B, token_causal);
   return bd_corr_row(row, ids[row / B], B);
 }
 

@@ -52,7 +52,8 @@ struct QTile {
 template <int TK>
 __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, int Gw, int H,
                                         int Hkv, int n_clean_q, int n_corr, int clean_q_start,
-                                        const int32_t* ids, int B, int wave, int lq) {
+                                        const int32_t* ids, int B, bool token_causal, int wave,
+                                        int lq) {
   QTile q;
   q.stream = it.hs & 1;
   const int hg = it.hs >> 1;
@@ -64,9 +65,9 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
   q.my_row = q.row0 + (wave / Gw) * 32 + lq;
   q.row_ok = q.my_row < q.n_rows;
   q.crow = min(q.my_row, q.n_rows - 1);
-  q.rb = row_bounds(q.stream, q.crow, clean_q_start, ids, B);
-  const BdRowBounds first = row_bounds(q.stream, q.row0, clean_q_start, ids, B);
-  const BdRowBounds last = row_bounds(q.stream, row_end - 1, clean_q_start, ids, B);
+  q.rb = row_bounds(q.stream, q.crow, clean_q_start, ids, B, token_causal);
+  const BdRowBounds first = row_bounds(q.stream, q.row0, clean_q_start, ids, B, token_causal);
+  const BdRowBounds last = row_bounds(q.stream, row_end - 1, clean_q_start, ids, B, token_causal);
   q.full_end = first.cb / TK * TK;  // clean tiles below need no mask
   q.n_ct = (last.cb + TK - 1) / TK;
   q.xlo = q.stream ? first.xlo : 0;
@@ -94,7 +95,8 @@ void fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const QTile q = q_tile<TK>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
-                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B, wave, lq);
+                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B,
+                             a.token_causal != 0, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
 
@@ -295,7 +297,8 @@ void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const QTile q = q_tile<TK>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
-                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B, wave, lq);
+                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B,
+                             a.token_causal != 0, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
   const T* gsrc = (const T*)(q.stream ? a.do_x : a.do_c);

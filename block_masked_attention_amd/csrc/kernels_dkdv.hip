@@ -60,7 +60,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // Local query rows that see this lane's key form one interval per query
   // stream (§3.2 rules with row-nondecreasing bounds): [lo_c, hi_c) of the
   // clean rows and [lo_x, hi_x) of the corrupted rows.
-  //   clean key of block kb:  clean rows of blocks >= kb; corrupted rows of
+  //   clean key at position p of block kb:  clean rows of blocks >= kb
+  //     (token-causal: clean rows at positions >= p); corrupted rows of
   //     blocks with id > kb, i.e. from the first local block whose id exceeds
   //     kb. The item gives that block j0 for the tile's first key block k0/B;
   //     ids increase strictly, so for kb = k0/B + delta it lies in
@@ -73,7 +74,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       lo_x = key_blk * a.B;
       hi_x = lo_x + a.B;
     } else {
-      lo_c = max(0, key_blk * a.B - a.clean_q_start);
+      lo_c = max(0, (a.token_causal ? my_key : key_blk * a.B) - a.clean_q_start);
       hi_c = a.n_clean_q;
       const int n_blk = a.n_corr / a.B;
       int j = it_x0 / a.B;  // j0: first local corrupted block with id > k0 / B

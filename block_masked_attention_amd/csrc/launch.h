@@ -16,6 +16,7 @@ struct FwdArgs {
   int32_t n_items;
   int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
+  int32_t token_causal;    // clean rows see their own block up to their position only
   float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -33,6 +34,7 @@ struct BwdArgs {
   float *l2_c, *l2_x;      // workspace: LSE * log2(e), +inf pad [H][row_pad(n)]
   int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
+  int32_t token_causal;    // clean rows see their own block up to their position only
   float scale, scale_log2;
 };
 

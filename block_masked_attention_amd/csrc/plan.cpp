@@ -19,7 +19,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
 
 BdRowBounds row_bounds(const Problem& P, int stream, int32_t row) {
-  if (stream == 0) return bd_clean_row(P.clean_q_start + row, P.B);
+  if (stream == 0) return bd_clean_row(P.clean_q_start + row, P.B, P.token_causal != 0);
   return bd_corr_row(row, P.ids[row / P.B], P.B);
 }
 
@@ -32,6 +32,10 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   }
   if (p->dtype != BDATTN_F32 && p->dtype != BDATTN_BF16) {
     *msg = "unknown dtype";
+    return BDATTN_ERR_INVALID_ARG;
+  }
+  if (p->clean_mask != BDATTN_CLEAN_BLOCK_CAUSAL && p->clean_mask != BDATTN_CLEAN_TOKEN_CAUSAL) {
+    *msg = "unknown clean_mask";
     return BDATTN_ERR_INVALID_ARG;
   }
   if (p->B < 1 || p->H < 1 || p->Hkv < 1) {
@@ -67,6 +71,7 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   P.Hkv = p->Hkv;
   P.d = p->d;
   P.dtype = p->dtype;
+  P.token_causal = p->clean_mask == BDATTN_CLEAN_TOKEN_CAUSAL ? 1 : 0;
   P.scale = p->scale > 0.f ? p->scale : float(1.0 / sqrt(double(p->d)));
   P.n_clean_q = int32_t(p->n_clean_q);
   P.clean_q_start = int32_t(p->clean_q_start);
@@ -214,8 +219,10 @@ void build_plan(const Problem& P, Plan* plan) {
     for (int32_t kt = 0; kt * int64_t(BWD_TK) < P.n_clean_kv; ++kt) {
       const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(P.n_clean_kv, k0 + BWD_TK);
       const int32_t kb = k0 / P.B;
-      // clean rows of blocks >= kb; corrupted rows of blocks with id > kb
-      int32_t c0 = std::min<int32_t>(P.n_clean_q, std::max<int32_t>(0, kb * P.B - P.clean_q_start));
+      // clean rows of blocks >= kb (token-causal: at positions >= k0);
+      // corrupted rows of blocks with id > kb
+      const int32_t first_row_pos = P.token_causal ? k0 : kb * P.B;
+      int32_t c0 = std::min<int32_t>(P.n_clean_q, std::max<int32_t>(0, first_row_pos - P.clean_q_start));
       int32_t j = int32_t(std::upper_bound(P.ids.begin(), P.ids.end(), kb) - P.ids.begin());
       int32_t x0 = j * P.B;
       // a q tile needs the mask unless it lies inside the swept rows and its

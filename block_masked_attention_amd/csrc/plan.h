@@ -54,6 +54,7 @@ struct BwdItem {
 
 struct Problem {
   int32_t B, H, Hkv, d, dtype;
+  int32_t token_causal = 0;  // clean_mask == BDATTN_CLEAN_TOKEN_CAUSAL
   float scale;  // resolved (> 0)
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks;
   std::vector<int32_t> ids;  // always materialised (0..n-1 when NULL)

@@ -7,10 +7,12 @@
  *
  *  - §3.2 (Block diffusion language models): a clean copy and a corrupted copy
  *    of the sequence, cut into blocks of B tokens. A clean query of block b sees
- *    the clean keys of blocks 0..b (its whole own block: block-causal). A
- *    corrupted query of target block b sees its own block's corrupted keys
- *    (bidirectionally) and the clean keys of blocks < b, never another block's
- *    corrupted keys.
+ *    the clean keys of blocks 0..b (its whole own block: block-causal), or,
+ *    with clean_mask = BDATTN_CLEAN_TOKEN_CAUSAL, the clean keys of blocks < b
+ *    and those of its own block up to its own position (the section's "causal
+ *    access within block b" read token by token). A corrupted query of target
+ *    block b sees its own block's corrupted keys (bidirectionally) and the
+ *    clean keys of blocks < b, never another block's corrupted keys.
  *  - §4.3 (Context-sharded block parallelism): one rank holds a shard of clean
  *    queries, the clean K/V of the positions its queries need (gathered into
  *    one buffer in original position order), and a set of whole corrupted
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BDATTN_VERSION 1
+#define BDATTN_VERSION 2
 
 typedef enum {
   BDATTN_OK = 0,
@@ -73,6 +75,13 @@ typedef enum {
 } bdattn_status;
 
 typedef enum { BDATTN_F32 = 0, BDATTN_BF16 = 1 } bdattn_dtype;
+
+/* What a clean query sees of its own clean block (§3.2): all of it, or the
+ * keys at positions up to its own. Corrupted queries are not affected. */
+typedef enum {
+  BDATTN_CLEAN_BLOCK_CAUSAL = 0, /* clean keys of blocks <= own block */
+  BDATTN_CLEAN_TOKEN_CAUSAL = 1  /* clean keys at positions <= own position */
+} bdattn_clean_mask;
 
 /* One rank's share of the block-diffusion attention (§4.3), or the whole
  * problem on one GPU. */
@@ -91,6 +100,7 @@ typedef struct {
   /* HOST array of n_corr_blocks global block ids, strictly increasing, or
    * NULL for ids 0..n_corr_blocks-1. Read during the call only. */
   const int32_t* corr_block_ids;
+  int32_t clean_mask; /* bdattn_clean_mask; 0 (block-causal) for zero-initialised descriptors */
 } bdattn_problem;
 
 /* BDATTN_VERSION of the loaded library. */
@@ -104,6 +114,7 @@ const char* bdattn_last_error(void);
 
 /* Host-only check of a problem descriptor (no HIP calls). Rules: B >= 1;
  * H, Hkv >= 1 and H % Hkv == 0; d in {32, 128}; dtype known;
+ * clean_mask known (BDATTN_ERR_INVALID_ARG);
  * n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks >= 0; clean_q_start,
  * n_clean_q and n_clean_kv multiples of B (BDATTN_ERR_SHAPE); ids strictly
  * increasing and >= 0 (BDATTN_ERR_INVALID_ARG); every row count and global

@@ -8,8 +8,10 @@ Every function here is pinned by a CPU test against something other than
 itself (a hand-drawn mask fixture, closed forms at Q = 0, a library attention
 routine, scalar brute force, finite differences, invariants of the method).
 """
-from .bdattn_oracle import (CLEAN, CORRUPTED, Layout, Oracle, key_tokens, layout,
-                            query_tokens, round_bf16, visible)
+from .bdattn_oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Layout, Oracle,
+                            key_positions, key_tokens, layout, query_positions, query_tokens,
+                            round_bf16, visible)
 
-__all__ = ["CLEAN", "CORRUPTED", "Layout", "Oracle", "key_tokens", "layout",
-           "query_tokens", "round_bf16", "visible"]
+__all__ = ["BLOCK_CAUSAL", "CLEAN", "CORRUPTED", "TOKEN_CAUSAL", "Layout", "Oracle",
+           "key_positions", "key_tokens", "layout", "query_positions", "query_tokens",
+           "round_bf16", "visible"]

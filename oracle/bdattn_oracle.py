@@ -9,10 +9,12 @@ Long-Context Diffusion Language Model Training":
 
 * §3.2 (Block diffusion language models): a clean copy and a corrupted copy of
   the sequence, split into blocks. A clean token of block b sees the clean
-  tokens of blocks <= b (the whole own block: the block-causal reading, see
-  ``visible``); a corrupted token of target block b sees its own corrupted
-  block bidirectionally and the clean prefix of blocks < b, and never the
-  corrupted tokens of other blocks.
+  tokens of blocks < b and, of its own block, all of it (the block-causal
+  reading, the default) or the tokens up to its own position (the token-causal
+  reading of the section's "causal access within block b"; see ``visible``);
+  a corrupted token of target block b sees its own corrupted block
+  bidirectionally and the clean prefix of blocks < b, and never the corrupted
+  tokens of other blocks.
 * §4.4 (Proposition 1): the distributed schemes reproduce exactly the plain
   masked computation, so the oracle is the plain definition of masked softmax
   attention over the visible keys, with its textbook analytic backward. No
@@ -41,8 +43,12 @@ import numpy as np
 CLEAN = 0
 CORRUPTED = 1
 
-__all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens",
-           "Oracle", "CLEAN", "CORRUPTED", "round_bf16"]
+BLOCK_CAUSAL = 0  # a clean query sees its whole own clean block
+TOKEN_CAUSAL = 1  # ... or its own clean block up to its own position
+
+__all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens", "query_positions",
+           "key_positions", "Oracle", "CLEAN", "CORRUPTED", "BLOCK_CAUSAL", "TOKEN_CAUSAL",
+           "round_bf16"]
 
 
 @dataclass(frozen=True)
@@ -57,6 +63,7 @@ class Layout:
     n_clean_kv: int
     clean_kv_start: int
     corr_ids: tuple  # global ids of the local corrupted blocks, increasing
+    clean_mask: int = BLOCK_CAUSAL
 
     @property
     def G(self) -> int:
@@ -79,9 +86,11 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
            n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
            n_corr_blocks: Optional[int] = None,
            corr_block_ids: Optional[Sequence[int]] = None,
-           scale: Optional[float] = None, require_coverage: bool = True) -> Layout:
+           scale: Optional[float] = None, require_coverage: bool = True,
+           clean_mask: int = BLOCK_CAUSAL) -> Layout:
     """Describe one problem. Without ids, the corrupted blocks are 0..n-1
     (n defaults to the number of clean blocks of the query shard).
+    ``clean_mask`` is BLOCK_CAUSAL or TOKEN_CAUSAL.
 
     With ``require_coverage`` (the default) the clean K/V buffer must hold
     every clean key some local query sees; otherwise the problem would only
@@ -95,6 +104,8 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
     ids = tuple(int(i) for i in corr_block_ids)
     if H % Hkv:
         raise ValueError("H must be a multiple of Hkv")
+    if clean_mask not in (BLOCK_CAUSAL, TOKEN_CAUSAL):
+        raise ValueError("clean_mask must be BLOCK_CAUSAL or TOKEN_CAUSAL")
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(d)
     if require_coverage:
@@ -106,7 +117,7 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
         if need and (clean_kv_start > 0 or clean_kv_start + n_clean_kv < need):
             raise ValueError("clean K/V buffer does not cover every visible clean key")
     return Layout(B, H, Hkv, d, float(scale), n_clean_q, clean_q_start, n_clean_kv,
-                  clean_kv_start, ids)
+                  clean_kv_start, ids, clean_mask)
 
 
 def query_tokens(lay: Layout):
@@ -129,17 +140,43 @@ def key_tokens(lay: Layout):
     return stream, block
 
 
-def visible(q_stream, q_block, k_stream, k_block):
+def query_positions(lay: Layout):
+    """Sequence position of every query: clean rows at their global clean
+    position, corrupted rows at their position inside the sequence (block id
+    times B plus the offset in the block)."""
+    clean = lay.clean_q_start + np.arange(lay.n_clean_q, dtype=np.int64)
+    corr = (np.repeat(np.asarray(lay.corr_ids, np.int64), lay.B) * lay.B
+            + np.tile(np.arange(lay.B, dtype=np.int64), len(lay.corr_ids)))
+    return np.concatenate([clean, corr])
+
+
+def key_positions(lay: Layout):
+    """Sequence position of every key (clean buffer, then corrupted keys)."""
+    clean = lay.clean_kv_start + np.arange(lay.n_clean_kv, dtype=np.int64)
+    corr = (np.repeat(np.asarray(lay.corr_ids, np.int64), lay.B) * lay.B
+            + np.tile(np.arange(lay.B, dtype=np.int64), len(lay.corr_ids)))
+    return np.concatenate([clean, corr])
+
+
+def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
+            clean_mask=BLOCK_CAUSAL):
     """The four visibility rules of §3.2, broadcast over their arguments.
 
-    clean query, block qb     -> clean key of block kb  iff kb <= qb
+    clean query, block qb     -> clean key of block kb  iff kb < qb, or kb == qb
+                                 (block-causal: the whole own block;
+                                  token-causal: key position <= query position)
     clean query               -> corrupted key          never
     corrupted query, block qb -> clean key of block kb  iff kb <  qb
     corrupted query, block qb -> corrupted key, block kb iff kb == qb
+
+    Positions are needed only for TOKEN_CAUSAL.
     """
     qc = q_stream == CLEAN
     kc = k_stream == CLEAN
-    clean_clean = qc & kc & (k_block <= q_block)
+    own_block = k_block == q_block
+    if clean_mask == TOKEN_CAUSAL:
+        own_block = own_block & (k_pos <= q_pos)
+    clean_clean = qc & kc & ((k_block < q_block) | own_block)
     corr_clean = ~qc & kc & (k_block < q_block)
     corr_corr = ~qc & ~kc & (k_block == q_block)
     return clean_clean | corr_clean | corr_corr
@@ -201,14 +238,15 @@ class Oracle:
             self.dO = None
         self.qs, self.qb = query_tokens(lay)
         self.ks, self.kb = key_tokens(lay)
+        self.qp, self.kp = query_positions(lay), key_positions(lay)
 
     # ---------------------------------------------------------------- helpers
     def _mask(self, qidx, kidx=None):
         if kidx is None:
-            return visible(self.qs[qidx, None], self.qb[qidx, None],
-                           self.ks[None, :], self.kb[None, :])
+            kidx = slice(None)
         return visible(self.qs[qidx, None], self.qb[qidx, None],
-                       self.ks[None, kidx], self.kb[None, kidx])
+                       self.ks[None, kidx], self.kb[None, kidx],
+                       self.qp[qidx, None], self.kp[None, kidx], self.lay.clean_mask)
 
     @staticmethod
     def _columns(cols):

@@ -43,7 +43,8 @@ def _rounding(spec):
 
 def oracle_full(spec, t, rounding=None):
     lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start,
-                 spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks, spec.corr_block_ids)
+                 spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks, spec.corr_block_ids,
+                 clean_mask=spec.clean_mask)
     orc = Oracle(lay, *[f64(t[k]) for k in INPUT_NAMES], *[f64(t[k]) for k in GRAD_NAMES],
                  operand_rounding=rounding)
     f = orc.forward()

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import block_masked_attention_amd as bd
-from oracle import key_tokens, layout, query_tokens, visible
+from oracle import key_positions, key_tokens, layout, query_positions, query_tokens, visible
 from tests.test_oracle import read_golden
 from workloads import CONFIGS
 
@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert bd.version() == 1
+    assert bd.version() == 2
 
 
 def test_status_strings():
@@ -42,10 +42,12 @@ def oracle_mask(p):
     if p.corr_block_ids:
         ids = [p.corr_block_ids[i] for i in range(p.n_corr_blocks)]
     lay = layout(p.B, p.H, p.Hkv, p.d, p.n_clean_q, p.clean_q_start, p.n_clean_kv,
-                 p.clean_kv_start, p.n_corr_blocks, ids)
+                 p.clean_kv_start, p.n_corr_blocks, ids, clean_mask=p.clean_mask)
     qs, qb = query_tokens(lay)
     ks, kb = key_tokens(lay)
-    return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :])
+    qp, kp = query_positions(lay), key_positions(lay)
+    return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
+                   kp[None, :], lay.clean_mask)
 
 
 CASES = [
@@ -59,9 +61,11 @@ CASES = [
     dict(B=32, n_clean_q=0, n_clean_kv=2048, corr_block_ids=[0, 9, 33, 63]),
     dict(B=8, n_clean_q=64, n_corr_blocks=0),
 ]
+# the same shapes with the token-causal clean mask
+CASES_TC = [dict(c, clean_mask=bd.CLEAN_TOKEN_CAUSAL) for c in CASES]
 
 
-@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("case", CASES + CASES_TC)
 def test_mask_render_matches_oracle(case):
     p = bd.problem(H=2, Hkv=1, d=32, dtype="bf16", **case)
     assert bd.validate(p) == 0
@@ -71,11 +75,13 @@ def test_mask_render_matches_oracle(case):
     assert bd.visible_pairs(p) == int(want.sum())
 
 
-@pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt"])
+@pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt",
+                                  "mask_token_causal_L8_B2.txt"])
 def test_mask_render_matches_hand_drawn_fixture(name):
     prm, want = read_golden(name)
     p = bd.problem(prm["B"], 1, 1, 32, "f32", prm["n_clean_q"], prm["clean_q_start"],
-                   prm["n_clean_kv"], corr_block_ids=prm["ids"])
+                   prm["n_clean_kv"], corr_block_ids=prm["ids"],
+                   clean_mask=prm.get("clean_mask", bd.CLEAN_BLOCK_CAUSAL))
     assert np.array_equal(bd.mask_render(p), want)
 
 
@@ -94,6 +100,12 @@ def test_visible_pairs_closed_forms_at_full_size():
                                               (spec.clean_q_start + spec.n_clean_q) // B))
     want += sum(B * B * (b + 1) for b in spec.corr_block_ids)
     assert bd.visible_pairs(p) == want
+    # token-causal: the clean stream is causal, L(L+1)/2 pairs; the corrupted
+    # stream keeps its L(L+B)/2
+    for spec in CONFIGS[:4]:
+        p = bd.from_spec(spec.with_(clean_mask=bd.CLEAN_TOKEN_CAUSAL))
+        L, B = spec.n_clean_q, spec.B
+        assert bd.visible_pairs(p) == L * (L + 1) // 2 + L * (L + B) // 2
 
 
 def _p(**kw):
@@ -117,6 +129,8 @@ def _p(**kw):
     (dict(corr_block_ids=[-1, 2]), -1),
     (dict(corr_block_ids=[0, 9]), -4),  # block 9 needs clean keys < 36
     (dict(n_clean_q=-4), -2),
+    (dict(clean_mask=2), -1),
+    (dict(clean_mask=-1), -1),
 ])
 def test_validation_error_codes(kw, code):
     p = _p(**kw)
@@ -165,7 +179,7 @@ def test_plan_covers_every_visible_tile():
     """The forward work list visits, for every query row tile, exactly the key
     tiles holding a visible key; the backward list has one item per key tile
     and KV head (so every dK/dV row is written)."""
-    for case in CASES:
+    for case in CASES + CASES_TC:
         p = bd.problem(H=4, Hkv=2, d=32, dtype="bf16", **case)
         st = bd.plan_stats(p)
         M = bd.mask_render(p)

@@ -77,6 +77,22 @@ SMALL = [
                              n_clean_q=0, n_clean_kv=640, corr_block_ids=[0, 7, 20])),
     ("bf16_no_corrupted", dict(L=320, B=32, H=4, Hkv=2, d=128, dtype="bf16", std=0.5,
                                corr_block_ids=[])),
+    # token-causal clean mask (clean queries see their own block up to their
+    # position): inside the key tiles of the forward and dQ kernels, across
+    # them (blocks larger than a tile), with ragged blocks, and in rank shares
+    ("f32_token_causal", dict(L=256, B=16, H=2, Hkv=2, d=32, dtype="f32", clean_mask=1)),
+    ("f32_token_causal_share", dict(L=128, B=16, H=4, Hkv=1, d=32, dtype="f32", n_clean_q=64,
+                                    clean_q_start=64, n_clean_kv=128,
+                                    corr_block_ids=[1, 3, 5, 7], clean_mask=1)),
+    ("bf16_token_causal_G4", dict(L=1056, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                  clean_mask=1)),
+    ("bf16_token_causal_B256", dict(L=768, B=256, H=4, Hkv=1, d=128, dtype="bf16", std=0.5,
+                                    clean_mask=1)),
+    ("bf16_token_causal_d32_B5", dict(L=300, B=5, H=6, Hkv=2, d=32, dtype="bf16", std=0.5,
+                                      clean_mask=1)),
+    ("bf16_token_causal_share", dict(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                     n_clean_q=128, clean_q_start=384, n_clean_kv=512,
+                                     corr_block_ids=list(range(3, 16, 4)), clean_mask=1)),
 ]
 
 

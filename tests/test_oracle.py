@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import CLEAN, CORRUPTED, Oracle, key_tokens, layout, query_tokens, visible
+from oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Oracle, key_positions,
+                    key_tokens, layout, query_positions, query_tokens, visible)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -40,7 +41,9 @@ def oracle_of(lay, t):
 def full_mask(lay):
     qs, qb = query_tokens(lay)
     ks, kb = key_tokens(lay)
-    return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :])
+    qp, kp = query_positions(lay), key_positions(lay)
+    return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
+                   kp[None, :], lay.clean_mask)
 
 
 # --------------------------------------------------------------------- mask
@@ -61,11 +64,12 @@ def read_golden(name):
     return params, np.array(rows, dtype=bool)
 
 
-@pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt"])
+@pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt",
+                                  "mask_token_causal_L8_B2.txt"])
 def test_mask_matches_hand_drawn_fixture(name):
     p, want = read_golden(name)
     lay = layout(p["B"], 1, 1, 4, p["n_clean_q"], p["clean_q_start"], p["n_clean_kv"],
-                 corr_block_ids=p["ids"])
+                 corr_block_ids=p["ids"], clean_mask=p.get("clean_mask", BLOCK_CAUSAL))
     got = full_mask(lay)
     assert got.shape == want.shape
     assert np.array_equal(got, want)
@@ -85,6 +89,18 @@ def test_visible_counts_closed_form(L, B):
     assert np.array_equal(M[L:, L:].sum(1), np.full(L, B))
 
 
+@pytest.mark.parametrize("L,B", [(4, 1), (8, 2), (12, 3), (16, 4), (32, 8), (24, 24)])
+def test_visible_counts_closed_form_token_causal(L, B):
+    """Token-causal: the clean query at position p sees exactly the p + 1 clean
+    keys at positions 0..p; corrupted queries still see (qb+1)*B keys."""
+    lay = layout(B, 1, 1, 4, L, clean_mask=TOKEN_CAUSAL)
+    M = full_mask(lay)
+    _, qb = query_tokens(lay)
+    assert np.array_equal(M[:L, :L], np.tril(np.ones((L, L), dtype=bool)))
+    assert not M[:L, L:].any()
+    assert np.array_equal(M[L:].sum(1), (qb[L:] + 1) * B)
+
+
 # ------------------------------------------------------------- closed forms
 def _prefix_sets(lay):
     """Visible key index sets written as ranges (clean prefix length, own
@@ -92,7 +108,11 @@ def _prefix_sets(lay):
     out = []
     nkc = lay.n_clean_kv
     for i in range(lay.n_clean_q):
-        b = (lay.clean_q_start + i) // lay.B
+        pos = lay.clean_q_start + i
+        if lay.clean_mask == TOKEN_CAUSAL:
+            out.append(list(range(0, pos + 1)))
+            continue
+        b = pos // lay.B
         out.append(list(range(0, (b + 1) * lay.B)))
     for j, bid in enumerate(lay.corr_ids):
         own = list(range(nkc + j * lay.B, nkc + (j + 1) * lay.B))
@@ -104,6 +124,9 @@ def _prefix_sets(lay):
 @pytest.mark.parametrize("case", [
     dict(B=4, n_clean_q=32), dict(B=1, n_clean_q=9), dict(B=8, n_clean_q=24),
     dict(B=2, n_clean_q=6, clean_q_start=10, n_clean_kv=16, corr_block_ids=[0, 3, 7]),
+    dict(B=4, n_clean_q=32, clean_mask=TOKEN_CAUSAL),
+    dict(B=3, n_clean_q=9, clean_q_start=6, n_clean_kv=18, corr_block_ids=[1, 2, 5],
+         clean_mask=TOKEN_CAUSAL),
 ])
 def test_q_zero_uniform_weights(case):
     """Q = 0 makes every visible score 0: O_i is the mean of v over V(i) and
@@ -221,9 +244,49 @@ def test_block_size_one_is_causal_attention():
         np.testing.assert_allclose(O_x[i], r[i].numpy(), rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("B", [1, 3, 4, 16])
+def test_token_causal_clean_stream_is_causal_attention(B):
+    """Token-causal: a clean query sees exactly the clean keys at positions up
+    to its own, so the clean stream is plain causal attention at any block
+    size. O_c, LSE_c and dQ_c equal torch's causal scaled_dot_product_attention
+    (float64, CPU, K/V repeated over each group) and its autograd gradient."""
+    L, H, Hkv, d = 48, 4, 2, 6
+    lay = layout(B, H, Hkv, d, L, clean_mask=TOKEN_CAUSAL)
+    t = make(lay, seed=17)
+    orc = oracle_of(lay, t)
+    O_c, _, L_c, _ = orc.forward()
+    dq_c = orc.backward()[0]
+    T = lambda a: torch.tensor(a, dtype=torch.float64)
+    q = T(t["q_c"]).transpose(0, 1)[None].requires_grad_()
+    k = T(t["k_c"]).repeat_interleave(H // Hkv, dim=1).transpose(0, 1)[None]
+    v = T(t["v_c"]).repeat_interleave(H // Hkv, dim=1).transpose(0, 1)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    (o * T(t["do_c"]).transpose(0, 1)[None]).sum().backward()
+    np.testing.assert_allclose(O_c, o[0].transpose(0, 1).detach().numpy(), rtol=1e-12,
+                               atol=1e-13)
+    np.testing.assert_allclose(dq_c, q.grad[0].transpose(0, 1).numpy(), rtol=1e-10,
+                               atol=1e-12)
+    s = (q[0] @ k[0].transpose(-1, -2)).detach() / math.sqrt(d)
+    s = s.masked_fill(~torch.ones(L, L, dtype=torch.bool).tril(), -math.inf)
+    np.testing.assert_allclose(L_c, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_token_causal_equals_block_causal_at_block_size_one():
+    """With one-token blocks the two readings of §3.2 coincide."""
+    lay0 = layout(1, 2, 1, 4, 10)
+    lay1 = layout(1, 2, 1, 4, 10, clean_mask=TOKEN_CAUSAL)
+    t = make(lay0, seed=6)
+    a = oracle_of(lay0, t)
+    b = oracle_of(lay1, t)
+    for x, y in zip(a.forward() + a.backward(), b.forward() + b.backward()):
+        assert np.array_equal(x, y)
+
+
 # ------------------------------------------------------ numerical gradients
-def test_finite_difference_gradients():
-    lay = layout(4, 2, 1, 4, 16)
+@pytest.mark.parametrize("clean_mask", [BLOCK_CAUSAL, TOKEN_CAUSAL])
+def test_finite_difference_gradients(clean_mask):
+    lay = layout(4, 2, 1, 4, 16, clean_mask=clean_mask)
     t = make(lay, seed=21)
     orc = oracle_of(lay, t)
     grads = dict(zip(["q_c", "q_x", "k_c", "v_c", "k_x", "v_x"], orc.backward()))
