@@ -90,12 +90,15 @@ def cpu_baseline(spec, t, seconds: float):
         hq, hk = slice(g * G, (g + 1) * G), slice(g, g + 1)
         if stream == "c":
             r0 = b * B - spec.clean_q_start
-            lay = layout(B, G, 1, d, B, b * B, (b + 1) * B, 0, corr_block_ids=[])
+            lay = layout(B, G, 1, d, B, b * B, (b + 1) * B, 0, corr_block_ids=[],
+                         clean_mask=spec.clean_mask)
             e, ek = np.zeros((0, G, d)), np.zeros((0, 1, d))
             args = (f64(t["q_c"][r0:r0 + B, hq]), f64(t["k_c"][:(b + 1) * B, hk]),
                     f64(t["v_c"][:(b + 1) * B, hk]), e, ek, ek,
                     f64(t["do_c"][r0:r0 + B, hq]), e)
-            pairs = B * (b + 1) * B
+            # a block-causal clean row sees (b+1)B keys; a token-causal one at
+            # position bB + r sees bB + r + 1
+            pairs = B * (b + 1) * B if spec.clean_mask == 0 else B * b * B + B * (B + 1) // 2
         else:
             bid = ids[b]
             rr = slice(b * B, (b + 1) * B)
@@ -139,6 +142,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="256k",
                     help="workload name (tiny, 8k, 64k, 256k, 512k_rank15)")
+    ap.add_argument("--clean-mask", choices=("block", "token"), default="block",
+                    help="what a clean query sees of its own block: all of it (block-causal, "
+                         "the workloads' definition) or the keys up to its own position")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -156,6 +162,9 @@ def main():
     from workloads import GRAD_NAMES, INPUT_NAMES, config, make_inputs
 
     spec = config(args.workload)
+    if args.clean_mask == "token":
+        spec = spec.with_(clean_mask=1)
+    mask_name = "token-causal" if spec.clean_mask else "block-causal"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     p = bd.from_spec(spec)
@@ -219,7 +228,8 @@ def main():
                        executed_tflops=round(executed_d[k] * d * H * pairs / (ms * 1e-3) / 1e12, 1))
     dom = max(kern, key=lambda k: kern[k]["ms"])
     achieved = kern[dom]["useful_tflops"]
-    traffic = read_traffic(spec.name, dom)
+    traffic = read_traffic(spec.name if spec.clean_mask == 0 else spec.name + "_token_causal",
+                           dom)
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak} peak); " +
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
@@ -246,7 +256,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "description": spec.description,
                    "clean_q": nc, "clean_kv": nkv, "corrupted": nx, "B": spec.B, "H": H,
-                   "Hkv": Hkv, "d": d, "visible_pairs_per_head": pairs,
+                   "Hkv": Hkv, "d": d, "clean_mask": mask_name,
+                   "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful_step, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),
         # the same step under the FlashAttention convention (14d per pair and q

@@ -126,7 +126,8 @@ def sub_clean_block(spec, t, b, g, rounding=None):
     r0 = b * B - spec.clean_q_start
     hq = (g * G, (g + 1) * G)
     hk = (g, g + 1)
-    lay = layout(B, G, 1, spec.d, B, b * B, (b + 1) * B, 0, corr_block_ids=[])
+    lay = layout(B, G, 1, spec.d, B, b * B, (b + 1) * B, 0, corr_block_ids=[],
+                 clean_mask=spec.clean_mask)
     e = np.zeros((0, G, spec.d))
     ek = np.zeros((0, 1, spec.d))
     orc = Oracle(lay, _sl(t["q_c"], (r0, r0 + B), hq), _kv(t, "k_c", (0, (b + 1) * B), g),
@@ -145,7 +146,8 @@ def sub_corr_block(spec, t, j, g, rounding=None):
     hq = (g * G, (g + 1) * G)
     hk = (g, g + 1)
     rows = (j * B, (j + 1) * B)
-    lay = layout(B, G, 1, spec.d, 0, 0, bid * B, 0, corr_block_ids=[bid])
+    lay = layout(B, G, 1, spec.d, 0, 0, bid * B, 0, corr_block_ids=[bid],
+                 clean_mask=spec.clean_mask)
     e = np.zeros((0, G, spec.d))
     orc = Oracle(lay, e, _kv(t, "k_c", (0, bid * B), g), _kv(t, "v_c", (0, bid * B), g),
                  _sl(t["q_x"], rows, hq), _sl(t["k_x"], rows, hk), _sl(t["v_x"], rows, hk),
@@ -168,7 +170,7 @@ def sub_clean_keys(spec, t, kb, g, rounding=None):
     hk = (g, g + 1)
     nq = spec.n_clean_q - c0
     lay = layout(B, G, 1, spec.d, nq, spec.clean_q_start + c0, spec.n_clean_kv, 0,
-                 corr_block_ids=[ids[j] for j in jx])
+                 corr_block_ids=[ids[j] for j in jx], clean_mask=spec.clean_mask)
     xr = np.concatenate([np.arange(j * B, (j + 1) * B) for j in jx]) if jx else \
         np.zeros(0, np.int64)
 

@@ -224,9 +224,18 @@ def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
 def test_workload_sampled_parity(idx):
     """Each of the five workloads at full size, launched as the benchmark
     launches it."""
+    workload_parity(CONFIGS[idx])
+
+
+@pytest.mark.parametrize("idx", [1, 2], ids=[CONFIGS[i].name for i in (1, 2)])
+def test_token_causal_workload_sampled_parity(idx):
+    """The 8K and 64K workloads at full size with the token-causal clean mask."""
+    workload_parity(CONFIGS[idx].with_(clean_mask=1))
+
+
+def workload_parity(spec):
     _need_gpu()
-    spec = CONFIGS[idx]
-    say(f"[gpu] workload {spec.name}: {spec.description}")
+    say(f"[gpu] workload {spec.name} (clean mask {spec.clean_mask}): {spec.description}")
     t0 = time.perf_counter()
     t = make_inputs(spec, device="cuda")
     got = run_gpu(spec, t)
