@@ -22,6 +22,12 @@ Long-Context Diffusion Language Model Training":
   the columns its own mask marks visible.
 * §4.3 (Backward pass): gradients of clean K/V sum the contributions of every
   query (clean, or corrupted of a later block) that sees them.
+* Appendix, "Efficient fused operator" (Implementation 1): the attention can be
+  computed as partial attentions over disjoint key sets (the block-diagonal
+  corrupted part, and clean K/V given by original positions), merged through
+  their log-sum-exps. A *partial* layout holds only some keys: the result is
+  the attention over the visible keys present (a row that sees none gets
+  O = 0, LSE = -inf), and ``merge_partials`` combines such results.
 
 Conventions (readings where the pages are silent): blocks are 0-indexed with
 block(p) = floor(p / B) on global clean positions; the scale defaults to
@@ -48,7 +54,7 @@ TOKEN_CAUSAL = 1  # ... or its own clean block up to its own position
 
 __all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens", "query_positions",
            "key_positions", "Oracle", "CLEAN", "CORRUPTED", "BLOCK_CAUSAL", "TOKEN_CAUSAL",
-           "round_bf16"]
+           "round_bf16", "merge_partials"]
 
 
 @dataclass(frozen=True)
@@ -64,6 +70,8 @@ class Layout:
     clean_kv_start: int
     corr_ids: tuple  # global ids of the local corrupted blocks, increasing
     clean_mask: int = BLOCK_CAUSAL
+    partial: bool = False  # keys may be missing: attention over the keys present
+    corr_keys: bool = True  # the local corrupted keys are present
 
     @property
     def G(self) -> int:
@@ -86,15 +94,16 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
            n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
            n_corr_blocks: Optional[int] = None,
            corr_block_ids: Optional[Sequence[int]] = None,
-           scale: Optional[float] = None, require_coverage: bool = True,
-           clean_mask: int = BLOCK_CAUSAL) -> Layout:
+           scale: Optional[float] = None, partial: bool = False,
+           clean_mask: int = BLOCK_CAUSAL, corr_keys: bool = True) -> Layout:
     """Describe one problem. Without ids, the corrupted blocks are 0..n-1
     (n defaults to the number of clean blocks of the query shard).
     ``clean_mask`` is BLOCK_CAUSAL or TOKEN_CAUSAL.
 
-    With ``require_coverage`` (the default) the clean K/V buffer must hold
-    every clean key some local query sees; otherwise the problem would only
-    be a partial attention and a ValueError is raised."""
+    Unless ``partial``, the clean K/V buffer must hold every clean key some
+    local query sees and the corrupted keys must be present (a ValueError
+    otherwise). A partial layout may hold any clean range (``clean_kv_start``
+    > 0 included) and may omit the corrupted keys (``corr_keys=False``)."""
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
     if corr_block_ids is None:
@@ -108,7 +117,9 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
         raise ValueError("clean_mask must be BLOCK_CAUSAL or TOKEN_CAUSAL")
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(d)
-    if require_coverage:
+    if not partial and not corr_keys:
+        raise ValueError("only a partial layout may omit the corrupted keys")
+    if not partial:
         need = 0  # one past the last clean position some query sees
         if n_clean_q:
             need = ((clean_q_start + n_clean_q - 1) // B + 1) * B
@@ -117,7 +128,7 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
         if need and (clean_kv_start > 0 or clean_kv_start + n_clean_kv < need):
             raise ValueError("clean K/V buffer does not cover every visible clean key")
     return Layout(B, H, Hkv, d, float(scale), n_clean_q, clean_q_start, n_clean_kv,
-                  clean_kv_start, ids, clean_mask)
+                  clean_kv_start, ids, clean_mask, bool(partial), bool(corr_keys))
 
 
 def query_tokens(lay: Layout):
@@ -159,7 +170,7 @@ def key_positions(lay: Layout):
 
 
 def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
-            clean_mask=BLOCK_CAUSAL):
+            clean_mask=BLOCK_CAUSAL, corr_keys=True):
     """The four visibility rules of §3.2, broadcast over their arguments.
 
     clean query, block qb     -> clean key of block kb  iff kb < qb, or kb == qb
@@ -169,7 +180,8 @@ def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
     corrupted query, block qb -> clean key of block kb  iff kb <  qb
     corrupted query, block qb -> corrupted key, block kb iff kb == qb
 
-    Positions are needed only for TOKEN_CAUSAL.
+    Positions are needed only for TOKEN_CAUSAL. With ``corr_keys`` False the
+    corrupted keys are absent (a partial problem) and none is visible.
     """
     qc = q_stream == CLEAN
     kc = k_stream == CLEAN
@@ -178,12 +190,35 @@ def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
         own_block = own_block & (k_pos <= q_pos)
     clean_clean = qc & kc & ((k_block < q_block) | own_block)
     corr_clean = ~qc & kc & (k_block < q_block)
-    corr_corr = ~qc & ~kc & (k_block == q_block)
+    corr_corr = ~qc & ~kc & (k_block == q_block) & bool(corr_keys)
     return clean_clean | corr_clean | corr_corr
 
 
 def _f64(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def merge_partials(parts):
+    """Attention over the union of disjoint key sets from the partial results
+    over each set (appendix, Implementation 1). ``parts`` is a list of
+    (O ``[n, H, d]``, LSE ``[H, n]``). Each part's O_i is its softmax-weighted
+    mean over its own keys and exp(LSE_i) its softmax denominator, so
+    LSE = ln sum_i exp(LSE_i) and O = sum_i exp(LSE_i - LSE) O_i. A part with
+    LSE_i = -inf (no key) has weight 0; a row with no key in any part keeps
+    O = 0, LSE = -inf."""
+    Os = [_f64(o) for o, _ in parts]
+    Ls = [_f64(l) for _, l in parts]
+    top = np.max(np.stack(Ls), axis=0)
+    ref = np.where(np.isfinite(top), top, 0.0)
+    w = [np.exp(l - ref) for l in Ls]  # exp(-inf) = 0
+    den = np.sum(w, axis=0)
+    with np.errstate(divide="ignore"):
+        LSE = ref + np.log(den)
+    safe = np.where(den > 0, den, 1.0)
+    O = np.zeros_like(Os[0])
+    for wi, oi in zip(w, Os):
+        O += (wi / safe).T[:, :, None] * oi
+    return O, LSE
 
 
 def round_bf16(x):
@@ -246,7 +281,8 @@ class Oracle:
             kidx = slice(None)
         return visible(self.qs[qidx, None], self.qb[qidx, None],
                        self.ks[None, kidx], self.kb[None, kidx],
-                       self.qp[qidx, None], self.kp[None, kidx], self.lay.clean_mask)
+                       self.qp[qidx, None], self.kp[None, kidx], self.lay.clean_mask,
+                       self.lay.corr_keys)
 
     @staticmethod
     def _columns(cols):
@@ -278,20 +314,27 @@ class Oracle:
         LSE = np.zeros((lay.H, len(qidx)))
         for s, rows in self._chunks(qidx):
             M = self._mask(rows)
-            if not M.any(axis=1).all():
+            seen = M.any(axis=1)
+            if not seen.all() and not lay.partial:
                 raise ValueError("a query row sees no key")
+            # a row that sees no key present (partial layouts only): the empty
+            # sum, O = 0 and LSE = ln 0 = -inf
+            LSE[:, s:s + len(rows)] = -np.inf
             cols = np.flatnonzero(M.any(axis=0))
+            if len(cols) == 0:
+                continue
             Mc = M[:, cols]
             cs = self._columns(cols)
             for g in range(lay.Hkv):
                 Kg, Vg = self.Kh[g][cs], self.Vh[g][cs]  # visible keys of KV head g
                 for h in range(g * lay.G, (g + 1) * lay.G):
                     S = self._scores(rows, Kg, Mc, h)
-                    m = S.max(axis=1)
+                    m = np.where(seen, S.max(axis=1), 0.0)
                     E = np.exp(S - m[:, None])
                     l = E.sum(axis=1)
-                    LSE[h, s:s + len(rows)] = m + np.log(l)
-                    O[s:s + len(rows), h] = (self.rd(E) @ Vg) / l[:, None]
+                    with np.errstate(divide="ignore"):
+                        LSE[h, s:s + len(rows)] = m + np.log(l)
+                    O[s:s + len(rows), h] = (self.rd(E) @ Vg) / np.where(seen, l, 1.0)[:, None]
         return self.rd(O), LSE
 
     def forward(self):
@@ -341,7 +384,10 @@ class Oracle:
                 dVg = np.zeros_like(Vg)
                 for h in range(g * lay.G, (g + 1) * lay.G):
                     S = self._scores(rows, Kg, Mc, h)
-                    P = np.exp(S - LSE[h, sl][:, None])  # exp(-inf) = 0 off the mask
+                    # exp(-inf) = 0 off the mask; a row whose LSE is -inf (no
+                    # key at all) has no weight anywhere
+                    Lr = np.where(np.isfinite(LSE[h, sl]), LSE[h, sl], np.inf)
+                    P = np.exp(S - Lr[:, None])
                     dP = self.dO[rows, h] @ Vg.T
                     dS = self.rd(P * (dP - D[sl, h][:, None]))
                     dQ[sl, h] = lay.scale * (dS @ Kg)

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Oracle, key_positions,
-                    key_tokens, layout, query_positions, query_tokens, visible)
+                    key_tokens, layout, merge_partials, query_positions, query_tokens, visible)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -524,3 +524,78 @@ def test_operand_rounding_mode_is_the_exact_oracle_plus_roundings():
     with pytest.raises(ValueError):
         Oracle(lay, t["q_c"], t["k_c"], t["v_c"], t["q_x"], t["k_x"], t["v_x"],
                operand_rounding="fp8")
+
+
+# ------------------------------------------------- partial attention, merge
+def _split_inputs(lay, t, lo, hi, corr_keys):
+    """Inputs of the partial problem holding clean keys [lo, hi) of a full
+    problem's buffer (and the corrupted keys if corr_keys)."""
+    ids = list(lay.corr_ids)
+    part = layout(lay.B, lay.H, lay.Hkv, lay.d, lay.n_clean_q, lay.clean_q_start, hi - lo, lo,
+                  corr_block_ids=ids, partial=True, clean_mask=lay.clean_mask,
+                  corr_keys=corr_keys)
+    u = dict(t)
+    u["k_c"], u["v_c"] = t["k_c"][lo:hi], t["v_c"][lo:hi]
+    return part, u
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=4, H=4, Hkv=2, d=6, n_clean_q=32),
+    dict(B=4, H=4, Hkv=2, d=6, n_clean_q=32, clean_mask=TOKEN_CAUSAL),
+    dict(B=2, H=2, Hkv=1, d=5, n_clean_q=8, clean_q_start=8, n_clean_kv=16,
+         corr_block_ids=[1, 4, 6]),
+])
+def test_partials_over_a_key_partition_merge_to_the_full_attention(case):
+    """Implementation 1 of the appendix: the block-diagonal corrupted part and
+    clean K/V in shards at their original positions, each a partial attention,
+    merged through their log-sum-exps, give the full result; and the backward
+    of each part, taken with the merged O and LSE, gives the full gradients
+    (dQ summed over the parts, dK/dV of each part's own keys)."""
+    lay = layout(**case)
+    t = make(lay, seed=31)
+    full = oracle_of(lay, t)
+    O_c, O_x, L_c, L_x = full.forward()
+    O = np.concatenate([O_c, O_x])
+    LSE = np.concatenate([L_c, L_x], axis=1)
+    g_full = full.backward(O=O, LSE=LSE)
+    nkv = lay.n_clean_kv
+    cuts = [0, lay.B * (nkv // lay.B // 3), lay.B * (2 * nkv // lay.B // 3), nkv]
+    pieces = [(0, 0, True)] + [(a, b, False) for a, b in zip(cuts, cuts[1:]) if b > a]
+    parts, grads = [], []
+    for lo, hi, ck in pieces:
+        part, u = _split_inputs(lay, t, lo, hi, ck)
+        orc = oracle_of(part, u)
+        o_c, o_x, l_c, l_x = orc.forward()
+        parts.append((np.concatenate([o_c, o_x]), np.concatenate([l_c, l_x], axis=1)))
+        grads.append((lo, hi, ck, orc.backward(O=O, LSE=LSE)))
+    Om, Lm = merge_partials(parts)
+    np.testing.assert_allclose(Om, O, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Lm, LSE, rtol=1e-12, atol=1e-12)
+    dq_c = sum(g[0] for _, _, _, g in grads)
+    dq_x = sum(g[1] for _, _, _, g in grads)
+    np.testing.assert_allclose(dq_c, g_full[0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dq_x, g_full[1], rtol=1e-11, atol=1e-12)
+    for lo, hi, ck, g in grads:
+        np.testing.assert_allclose(g[2], g_full[2][lo:hi], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(g[3], g_full[3][lo:hi], rtol=1e-11, atol=1e-12)
+        want_x = (g_full[4], g_full[5]) if ck else (0 * g_full[4], 0 * g_full[5])
+        np.testing.assert_allclose(g[4], want_x[0], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(g[5], want_x[1], rtol=1e-11, atol=1e-12)
+
+
+def test_partial_rows_without_keys_are_the_empty_sum():
+    """A row that sees no key present gets O = 0, LSE = -inf, and a part with
+    no key leaves a merge unchanged."""
+    lay = layout(4, 2, 1, 3, 16)
+    t = make(lay, seed=2)
+    part, u = _split_inputs(lay, t, 8, 16, False)  # clean keys of blocks 2..3 only
+    o_c, o_x, l_c, l_x = oracle_of(part, u).forward()
+    assert np.all(o_c[:8] == 0) and np.all(np.isneginf(l_c[:, :8]))  # blocks 0, 1: nothing
+    assert np.all(np.isfinite(l_c[:, 8:]))
+    assert np.all(o_x[:12] == 0) and np.all(np.isneginf(l_x[:, :12]))  # blocks 0..2: nothing
+    assert np.all(np.isfinite(l_x[:, 12:]))
+    O = np.concatenate([o_c, o_x])
+    L = np.concatenate([l_c, l_x], axis=1)
+    empty = (np.zeros_like(O), np.full_like(L, -np.inf))
+    Om, Lm = merge_partials([(O, L), empty])
+    assert np.array_equal(Om, O) and np.array_equal(Lm, L)
