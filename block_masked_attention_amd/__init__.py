@@ -31,7 +31,7 @@ STATUS = {0: "BDATTN_OK", -1: "BDATTN_ERR_INVALID_ARG", -2: "BDATTN_ERR_SHAPE",
 __all__ = ["Problem", "problem", "BdattnError", "lib", "fwd", "bwd", "validate",
            "workspace_size", "mask_render", "visible_pairs", "plan_stats", "version",
            "status_string", "profile_enable", "profile_read", "from_spec", "F32", "BF16",
-           "CLEAN_BLOCK_CAUSAL", "CLEAN_TOKEN_CAUSAL", "LIB_PATH"]
+           "CLEAN_BLOCK_CAUSAL", "CLEAN_TOKEN_CAUSAL", "LIB_PATH", "merge"]
 
 
 class BdattnError(RuntimeError):
@@ -51,6 +51,8 @@ class Problem(ctypes.Structure):
         ("n_corr_blocks", ctypes.c_int64),
         ("corr_block_ids", ctypes.POINTER(ctypes.c_int32)),
         ("clean_mask", ctypes.c_int32),
+        ("partial", ctypes.c_int32),
+        ("omit_corr_keys", ctypes.c_int32),
     ]
 
     @property
@@ -61,17 +63,22 @@ class Problem(ctypes.Structure):
 def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_start: int = 0,
             n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
             n_corr_blocks: Optional[int] = None, corr_block_ids: Optional[Sequence[int]] = None,
-            scale: float = 0.0, clean_mask: int = CLEAN_BLOCK_CAUSAL) -> Problem:
+            scale: float = 0.0, clean_mask: int = CLEAN_BLOCK_CAUSAL, partial: bool = False,
+            omit_corr_keys: bool = False) -> Problem:
     """Problem descriptor. ``dtype`` is F32/BF16, "f32"/"bf16" or a torch dtype.
     Without ids the corrupted blocks are 0..n_corr_blocks-1 (default: as many
     as the clean query shard has blocks). ``clean_mask`` is CLEAN_BLOCK_CAUSAL
-    or CLEAN_TOKEN_CAUSAL (what a clean query sees of its own block)."""
+    or CLEAN_TOKEN_CAUSAL (what a clean query sees of its own block).
+    ``partial``: attention over the keys present only (any clean range, the
+    corrupted keys optional with ``omit_corr_keys``); see include/bdattn.h."""
     dt = _dtype_code(dtype)
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
     p = Problem()
     p.B, p.H, p.Hkv, p.d, p.dtype, p.scale = B, H, Hkv, d, dt, float(scale)
     p.clean_mask = int(clean_mask)
+    p.partial = 1 if partial else 0
+    p.omit_corr_keys = 1 if omit_corr_keys else 0
     p.n_clean_q, p.clean_q_start = n_clean_q, clean_q_start
     p.n_clean_kv, p.clean_kv_start = n_clean_kv, clean_kv_start
     if corr_block_ids is not None:
@@ -92,7 +99,9 @@ def from_spec(spec) -> Problem:
     return problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
                    spec.clean_q_start, spec.n_clean_kv, spec.clean_kv_start,
                    spec.n_corr_blocks, spec.corr_block_ids,
-                   clean_mask=getattr(spec, "clean_mask", CLEAN_BLOCK_CAUSAL))
+                   clean_mask=getattr(spec, "clean_mask", CLEAN_BLOCK_CAUSAL),
+                   partial=getattr(spec, "partial", False),
+                   omit_corr_keys=getattr(spec, "omit_corr_keys", False))
 
 
 def _dtype_code(dtype) -> int:
@@ -134,12 +143,14 @@ def lib() -> ctypes.CDLL:
     L.bdattn_fwd.argtypes = [P] + [vp] * 6 + [vp, vp, fp, fp] + [vp, ctypes.c_size_t, vp]
     L.bdattn_bwd.argtypes = ([P] + [vp] * 6 + [vp, vp, fp, fp, vp, vp] + [vp] * 6 +
                              [vp, ctypes.c_size_t, vp])
+    L.bdattn_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               vp, fp, vp, fp, vp, fp, vp]
     L.bdattn_profile_enable.argtypes = [ctypes.c_int]
     L.bdattn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("bdattn_validate", "bdattn_workspace_size", "bdattn_mask_render",
                  "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_bwd",
-                 "bdattn_profile_enable", "bdattn_profile_read"):
+                 "bdattn_merge", "bdattn_profile_enable", "bdattn_profile_read"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -304,8 +315,10 @@ def bwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, do_c, 
         dq_x = torch.empty((nx, H, d), dtype=dt, device=dev)
         dk_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
         dv_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
-        dk_x = torch.empty((nx, Hkv, d), dtype=dt, device=dev)
-        dv_x = torch.empty((nx, Hkv, d), dtype=dt, device=dev)
+        # not written when the corrupted keys are omitted: returned as zeros
+        alloc = torch.zeros if p.omit_corr_keys else torch.empty
+        dk_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
+        dv_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
     else:
         dq_c, dq_x, dk_c, dv_c, dk_x, dv_x = out
     ws = _workspace(p, 1, dev, workspace)
@@ -316,3 +329,26 @@ def bwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, do_c, 
                           _stream(dev, stream))
     _check(st, "bdattn_bwd")
     return dq_c, dq_x, dk_c, dv_c, dk_x, dv_x
+
+
+def merge(o_a, lse_a, o_b, lse_b, *, stream=None, out=None):
+    """Merge two partial results over disjoint key sets (bdattn_merge):
+    o_* ``[n, H, d]`` (fp32 or bf16), lse_* ``[H, n]`` float32. Returns
+    (o, lse); ``out`` may name the inputs themselves."""
+    torch = _torch()
+    n, H, d = (int(x) for x in o_a.shape)
+    dev = o_a.device
+    for t, shp, tdt, nm in ((o_a, (n, H, d), o_a.dtype, "o_a"), (o_b, (n, H, d), o_a.dtype, "o_b"),
+                            (lse_a, (H, n), torch.float32, "lse_a"),
+                            (lse_b, (H, n), torch.float32, "lse_b")):
+        _expect(t, shp, tdt, nm, dev)
+    if out is None:
+        o = torch.empty_like(o_a)
+        lse = torch.empty_like(lse_a)
+    else:
+        o, lse = out
+    st = lib().bdattn_merge(ctypes.c_int64(n), H, d, _dtype_code(o_a.dtype), _ptr(o_a),
+                            _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
+                            _stream(dev, stream))
+    _check(st, "bdattn_merge")
+    return o, lse

@@ -47,7 +47,8 @@ PlanCache& cache() {
 std::string plan_key(const bdattn::Problem& P) {
   std::string k;
   const int32_t head[] = {P.B, P.H, P.Hkv, P.d, P.dtype, P.n_clean_q, P.clean_q_start,
-                          P.n_clean_kv, P.n_corr_blocks, P.token_causal};
+                          P.n_clean_kv, P.n_corr_blocks, P.token_causal, P.clean_kv_start,
+                          P.partial, P.corr_keys};
   k.append((const char*)head, sizeof(head));
   k.append((const char*)P.ids.data(), P.ids.size() * sizeof(int32_t));
   return k;
@@ -280,6 +281,8 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
   a.token_causal = P.token_causal;
+  a.clean_kv_start = P.clean_kv_start;
+  a.corr_keys = P.corr_keys;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[1];
   hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, prof_events(0, 1, ev));
@@ -306,7 +309,8 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
       (st = check_ptr(do_c, nqc, "do_c")) || (st = check_ptr(do_x, nqx, "do_x")) ||
       (st = check_ptr(dq_c, nqc, "dq_c")) || (st = check_ptr(dq_x, nqx, "dq_x")) ||
       (st = check_ptr(dk_c, nkc, "dk_c")) || (st = check_ptr(dv_c, nkc, "dv_c")) ||
-      (st = check_ptr(dk_x, nkx, "dk_x")) || (st = check_ptr(dv_x, nkx, "dv_x")))
+      (st = check_ptr(dk_x, P.corr_keys ? nkx : 0, "dk_x")) ||
+      (st = check_ptr(dv_x, P.corr_keys ? nkx : 0, "dv_x")))
     return st;
   Entry* entry = get_entry(P);
   const bdattn::Plan* plan = &entry->plan;
@@ -334,11 +338,34 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
   a.token_causal = P.token_causal;
+  a.clean_kv_start = P.clean_kv_start;
+  a.corr_keys = P.corr_keys;
   a.scale = P.scale;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[2];
   hipError_t e = bdattn::launch_bwd(a, P.dtype, P.d, s, prof_events(1, 2, ev));
   if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+  return BDATTN_OK;
+}
+
+int bdattn_merge(int64_t n_rows, int32_t H, int32_t d, int32_t dtype, const void* o_a,
+                 const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                 void* hip_stream) {
+  if (dtype != BDATTN_F32 && dtype != BDATTN_BF16) return fail(BDATTN_ERR_INVALID_ARG, "unknown dtype");
+  if (n_rows < 0 || H < 1) return fail(BDATTN_ERR_SHAPE, "n_rows must be >= 0 and H >= 1");
+  if (!bdattn::have_kernels(dtype, d))
+    return fail(BDATTN_ERR_UNSUPPORTED, "no merge kernel for this head dim and dtype");
+  if (n_rows > (int64_t(1) << 40) / (int64_t(H) * d))
+    return fail(BDATTN_ERR_SHAPE, "merge problem too large");
+  const int64_t no = n_rows * H * d, nl = n_rows * H;
+  int st;
+  if ((st = check_ptr(o_a, no, "o_a")) || (st = check_ptr(o_b, no, "o_b")) ||
+      (st = check_ptr(o, no, "o")) || (st = check_ptr(lse_a, nl, "lse_a")) ||
+      (st = check_ptr(lse_b, nl, "lse_b")) || (st = check_ptr(lse, nl, "lse")))
+    return st;
+  hipError_t e = bdattn::launch_merge(n_rows, H, d, dtype, o_a, lse_a, o_b, lse_b, o, lse,
+                                      (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   return BDATTN_OK;
 }
 

@@ -52,7 +52,18 @@ BD_HD BdRowBounds bd_corr_row(int32_t row, int32_t block_id, int32_t B) {
   return r;
 }
 
-// Is clean key `k` (buffer index = global position) visible to the row?
+// The same bounds relative to a clean K/V buffer holding global positions
+// [kv0, kv0 + nkv) (the whole prefix when kv0 = 0 and the buffer covers it):
+// the visible clean keys present are buffer indices [0, cb - kv0), clipped to
+// the buffer; without the corrupted keys, none of those is visible.
+BD_HD BdRowBounds bd_in_buffer(BdRowBounds r, int32_t kv0, int32_t nkv, bool corr_keys) {
+  const int32_t c = r.cb - kv0;
+  r.cb = c < 0 ? 0 : (c > nkv ? nkv : c);
+  if (!corr_keys) r.xlo = r.xhi = 0;
+  return r;
+}
+
+// Is clean key `k` (buffer index) visible to the row (bounds in buffer terms)?
 BD_HD bool bd_sees_clean(const BdRowBounds& r, int32_t k) { return k < r.cb; }
 
 // Is local corrupted key `k` visible to the row?

@@ -219,11 +219,19 @@ struct OperandReads {
   }
 };
 
-// Row bounds of local row `row` of a query stream (0 clean, 1 corrupted).
-__device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, int32_t clean_q_start,
-                                                  const int32_t* ids, int32_t B, bool token_causal) {
-  if (stream == 0) return bd_clean_row(clean_q_start + row, B, token_causal);
-  return bd_corr_row(row, ids[row / B], B);
+// Row bounds of local row `row` of a query stream (0 clean, 1 corrupted), in
+// terms of the keys present: clean buffer indices and local corrupted keys.
+struct RowSpace {
+  int32_t clean_q_start, B;
+  const int32_t* ids;
+  bool token_causal;
+  int32_t kv0, nkv;  // the clean buffer holds global positions [kv0, kv0 + nkv)
+  bool corr_keys;    // the local corrupted keys are present
+};
+__device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, const RowSpace& rs) {
+  const BdRowBounds r = stream == 0 ? bd_clean_row(rs.clean_q_start + row, rs.B, rs.token_causal)
+                                    : bd_corr_row(row, rs.ids[row / rs.B], rs.B);
+  return bd_in_buffer(r, rs.kv0, rs.nkv, rs.corr_keys);
 }
 
 // floor(n / d) for 0 <= n < 2^24, d >= 1, with inv_d = 1.0f / d: a float

@@ -18,6 +18,7 @@
 //   bwd_dkdv_kernel  key-tile parallel: dV = P^T dO, dK = scale * dS^T Q over
 //                    every query tile (and q head of the KV group) that sees
 //                    the keys, written once (kernels_dkdv.hip)
+//   merge_kernel     two partial results over disjoint key sets -> one
 // No kernel uses atomics, so every output is bitwise reproducible.
 //
 // Matrix products use the CDNA4 32x32x16 bf16 MFMA (fp32 accumulate), or, for
@@ -51,9 +52,8 @@ struct QTile {
 
 template <int TK>
 __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, int Gw, int H,
-                                        int Hkv, int n_clean_q, int n_corr, int clean_q_start,
-                                        const int32_t* ids, int B, bool token_causal, int wave,
-                                        int lq) {
+                                        int Hkv, int n_clean_q, int n_corr, const RowSpace& rs,
+                                        int wave, int lq) {
   QTile q;
   q.stream = it.hs & 1;
   const int hg = it.hs >> 1;
@@ -65,9 +65,9 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
   q.my_row = q.row0 + (wave / Gw) * 32 + lq;
   q.row_ok = q.my_row < q.n_rows;
   q.crow = min(q.my_row, q.n_rows - 1);
-  q.rb = row_bounds(q.stream, q.crow, clean_q_start, ids, B, token_causal);
-  const BdRowBounds first = row_bounds(q.stream, q.row0, clean_q_start, ids, B, token_causal);
-  const BdRowBounds last = row_bounds(q.stream, row_end - 1, clean_q_start, ids, B, token_causal);
+  q.rb = row_bounds(q.stream, q.crow, rs);
+  const BdRowBounds first = row_bounds(q.stream, q.row0, rs);
+  const BdRowBounds last = row_bounds(q.stream, row_end - 1, rs);
   q.full_end = first.cb / TK * TK;  // clean tiles below need no mask
   q.n_ct = (last.cb + TK - 1) / TK;
   q.xlo = q.stream ? first.xlo : 0;
@@ -94,9 +94,10 @@ void fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
+  const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
+                    a.n_clean_kv, a.corr_keys != 0};
   const QTile q = q_tile<TK>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
-                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B,
-                             a.token_causal != 0, wave, lq);
+                             a.n_clean_q, a.n_corr, rs, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
 
@@ -223,7 +224,8 @@ void fwd_kernel(FwdArgs a) {
 
   const float lt = l + __shfl_xor(l, 32);
   if (q.row_ok) {
-    const float inv = 1.f / lt;
+    // a row that sees no key present (partial problems): O = 0, LSE = -inf
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
     T* orow = (T*)(q.stream ? a.o_x : a.o_c) + ((int64_t)q.my_row * a.H + q.head) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -234,7 +236,7 @@ void fwd_kernel(FwdArgs a) {
     }
     if (hf == 0) {
       float* lse = q.stream ? a.lse_x : a.lse_c;
-      lse[(int64_t)q.head * q.n_rows + q.my_row] = (m + log2f(lt)) * kLn2;
+      lse[(int64_t)q.head * q.n_rows + q.my_row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : kNegInf;
     }
   }
 }
@@ -276,6 +278,51 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
 }
 
 // ======================================================================
+// Merge of two partial results over disjoint key sets (the appendix's
+// Implementation 1): per (row, head) LSE = ln(exp LSE_a + exp LSE_b) and
+// O = exp(LSE_a - LSE) O_a + exp(LSE_b - LSE) O_b; a part with LSE = -inf
+// weighs 0, and a row with no key in either part gets O = 0, LSE = -inf.
+// D/8 lanes per (row, head), all in one wave, so each lane reads its inputs
+// before any lane writes (outputs may alias inputs).
+// ======================================================================
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const void* oa_, const float* la,
+                                                    const void* ob_, const float* lb, void* o_,
+                                                    float* lse, int64_t n_rows, int32_t H) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  using Frag = typename E::Frag;
+  constexpr int LPR = D / 8;
+  static_assert(64 % LPR == 0, "a (row, head) in one wave");
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = idx / LPR;  // row * H + head
+  const int sub = int(idx % LPR);
+  if (pair >= n_rows * H) return;
+  const int64_t row = pair / H, head = pair % H;
+  const int64_t li = head * n_rows + row;
+  const float a = la[li], b = lb[li];
+  const float m = fmaxf(a, b);
+  float wa = 0.f, wb = 0.f, l = kNegInf;
+  if (m != kNegInf) {
+    wa = expf(a - m);  // exp(-inf) = 0
+    wb = expf(b - m);
+    const float den = wa + wb;
+    l = m + logf(den);
+    wa /= den;
+    wb /= den;
+  }
+  const int64_t off = pair * D + 8 * sub;
+  const Frag fa = E::load((const T*)oa_ + off), fb = E::load((const T*)ob_ + off);
+  const T* ea = (const T*)&fa;
+  const T* eb = (const T*)&fb;
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = wa * E::to_f(ea[e]) + wb * E::to_f(eb[e]);
+  *(Frag*)((T*)o_ + off) = E::pack(x);
+  if (sub == 0) lse[li] = l;
+}
+
+// ======================================================================
 // Backward, dQ. Same query tiles and key sweep as the forward. Per key tile:
 // S^T = K Q^T and dP^T = V dO^T (each lane owns one query row, so its LSE and
 // D are scalars); P^T = exp2(S^T c - LSE2); dS^T = P^T (dP^T - D);
@@ -296,9 +343,10 @@ void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
+  const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
+                    a.n_clean_kv, a.corr_keys != 0};
   const QTile q = q_tile<TK>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
-                             a.n_clean_q, a.n_corr, a.clean_q_start, a.ids, a.B,
-                             a.token_causal != 0, wave, lq);
+                             a.n_clean_q, a.n_corr, rs, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
   const T* gsrc = (const T*)(q.stream ? a.do_x : a.do_c);
@@ -458,6 +506,25 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t s, const K
   if (dtype == BDATTN_BF16 && d == 128) return run_fwd<true, 128>(a, s, ev);
   if (dtype == BDATTN_BF16 && d == 32) return run_fwd<true, 32>(a, s, ev);
   if (dtype == BDATTN_F32 && d == 32) return run_fwd<false, 32>(a, s, ev);
+  return hipErrorInvalidValue;
+}
+
+template <bool BF16, int D>
+hipError_t run_merge(int64_t n_rows, int H, const void* o_a, const float* lse_a, const void* o_b,
+                     const float* lse_b, void* o, float* lse, hipStream_t s) {
+  const int64_t threads = n_rows * H * (D / 8);
+  if (threads > 0)
+    hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
+                       s, o_a, lse_a, o_b, lse_b, o, lse, n_rows, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int64_t n_rows, int H, int d, int dtype, const void* o_a,
+                        const float* lse_a, const void* o_b, const float* lse_b, void* o,
+                        float* lse, hipStream_t s) {
+  if (dtype == BDATTN_BF16 && d == 128) return run_merge<true, 128>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
+  if (dtype == BDATTN_BF16 && d == 32) return run_merge<true, 32>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
+  if (dtype == BDATTN_F32 && d == 32) return run_merge<false, 32>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
   return hipErrorInvalidValue;
 }
 

@@ -69,16 +69,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
   //   corrupted key of local block kb: the corrupted rows of that block.
   int lo_c = 0, hi_c = 0, lo_x = 0, hi_x = 0;
   if (key_ok) {
-    const int key_blk = my_key / a.B;  // clean: global block; corrupted: local block
+    // clean: global position and block (buffer row 0 is position
+    // clean_kv_start); corrupted: local key and local block
+    const int key_pos = kstream ? my_key : my_key + a.clean_kv_start;
+    const int key_blk = key_pos / a.B;
     if (kstream) {
       lo_x = key_blk * a.B;
       hi_x = lo_x + a.B;
     } else {
-      lo_c = max(0, (a.token_causal ? my_key : key_blk * a.B) - a.clean_q_start);
+      lo_c = max(0, (a.token_causal ? key_pos : key_blk * a.B) - a.clean_q_start);
       hi_c = a.n_clean_q;
       const int n_blk = a.n_corr / a.B;
-      int j = it_x0 / a.B;  // j0: first local corrupted block with id > k0 / B
-      const int j_end = min(n_blk, j + (key_blk - key0 / a.B));
+      int j = it_x0 / a.B;  // j0: first local corrupted block with id > the tile's first block
+      const int j_end = min(n_blk, j + (key_blk - (key0 + a.clean_kv_start) / a.B));
       while (j < j_end && a.ids[j] <= key_blk) ++j;
       lo_x = j * a.B;
       hi_x = a.n_corr;

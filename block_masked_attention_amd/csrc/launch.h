@@ -17,6 +17,8 @@ struct FwdArgs {
   int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
   int32_t token_causal;    // clean rows see their own block up to their position only
+  int32_t clean_kv_start;  // global position of clean buffer row 0
+  int32_t corr_keys;       // the local corrupted keys are present
   float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -35,6 +37,8 @@ struct BwdArgs {
   int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
   int32_t token_causal;    // clean rows see their own block up to their position only
+  int32_t clean_kv_start;  // global position of clean buffer row 0
+  int32_t corr_keys;       // the local corrupted keys are present
   float scale, scale_log2;
 };
 
@@ -54,5 +58,9 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t stream,
                       const KernelEvents* ev);
 // The key-tile dK/dV kernel alone (called by launch_bwd after the dQ kernel).
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t stream);
+// Merge of two partial results (bdattn_merge).
+hipError_t launch_merge(int64_t n_rows, int H, int d, int dtype, const void* o_a,
+                        const float* lse_a, const void* o_b, const float* lse_b, void* o,
+                        float* lse, hipStream_t stream);
 
 }  // namespace bdattn

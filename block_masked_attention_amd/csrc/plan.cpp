@@ -18,9 +18,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
 
+// Bounds of a local row in terms of the keys present (clean buffer indices).
 BdRowBounds row_bounds(const Problem& P, int stream, int32_t row) {
-  if (stream == 0) return bd_clean_row(P.clean_q_start + row, P.B, P.token_causal != 0);
-  return bd_corr_row(row, P.ids[row / P.B], P.B);
+  const BdRowBounds r = stream == 0 ? bd_clean_row(P.clean_q_start + row, P.B, P.token_causal != 0)
+                                    : bd_corr_row(row, P.ids[row / P.B], P.B);
+  return bd_in_buffer(r, P.clean_kv_start, P.n_clean_kv, P.corr_keys != 0);
 }
 
 }  // namespace
@@ -36,6 +38,14 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   }
   if (p->clean_mask != BDATTN_CLEAN_BLOCK_CAUSAL && p->clean_mask != BDATTN_CLEAN_TOKEN_CAUSAL) {
     *msg = "unknown clean_mask";
+    return BDATTN_ERR_INVALID_ARG;
+  }
+  if ((p->partial != 0 && p->partial != 1) || (p->omit_corr_keys != 0 && p->omit_corr_keys != 1)) {
+    *msg = "partial and omit_corr_keys must be 0 or 1";
+    return BDATTN_ERR_INVALID_ARG;
+  }
+  if (p->omit_corr_keys && !p->partial) {
+    *msg = "only a partial problem may omit the corrupted keys";
     return BDATTN_ERR_INVALID_ARG;
   }
   if (p->B < 1 || p->H < 1 || p->Hkv < 1) {
@@ -60,8 +70,12 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
     *msg = "n_clean_q, clean_q_start and n_clean_kv must be multiples of B";
     return BDATTN_ERR_SHAPE;
   }
+  if (p->partial && p->clean_kv_start % B) {
+    *msg = "clean_kv_start must be a multiple of B";
+    return BDATTN_ERR_SHAPE;
+  }
   if (p->clean_q_start + p->n_clean_q > kMax32 || p->n_clean_kv > kMax32 ||
-      p->n_corr_blocks * B > kMax32 || p->clean_kv_start > kMax32) {
+      p->n_corr_blocks * B > kMax32 || p->clean_kv_start + p->n_clean_kv > kMax32) {
     *msg = "sizes must stay below 2^31 rows";
     return BDATTN_ERR_SHAPE;
   }
@@ -72,6 +86,9 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   P.d = p->d;
   P.dtype = p->dtype;
   P.token_causal = p->clean_mask == BDATTN_CLEAN_TOKEN_CAUSAL ? 1 : 0;
+  P.clean_kv_start = int32_t(p->clean_kv_start);
+  P.partial = p->partial;
+  P.corr_keys = p->omit_corr_keys ? 0 : 1;
   P.scale = p->scale > 0.f ? p->scale : float(1.0 / sqrt(double(p->d)));
   P.n_clean_q = int32_t(p->n_clean_q);
   P.clean_q_start = int32_t(p->clean_q_start);
@@ -93,6 +110,10 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
     }
   } else {
     std::iota(P.ids.begin(), P.ids.end(), 0);
+  }
+  if (P.partial) {  // any clean range: the attention over the keys present
+    *out = std::move(P);
+    return BDATTN_OK;
   }
   // Coverage: the buffer starts at position 0 and holds every clean key a
   // local query sees: the whole last block of the query shard, and the
@@ -130,7 +151,8 @@ size_t n_q_items(const Problem& P) {
 }
 
 size_t n_kv_items(const Problem& P) {
-  size_t tiles = size_t(ceil_div(P.n_clean_kv, BWD_TK)) + size_t(ceil_div(P.n_corr(), BWD_TK));
+  size_t tiles = size_t(ceil_div(P.n_clean_kv, BWD_TK)) +
+                 (P.corr_keys ? size_t(ceil_div(P.n_corr(), BWD_TK)) : 0);
   return tiles * size_t(P.Hkv);
 }
 
@@ -218,10 +240,11 @@ void build_plan(const Problem& P, Plan* plan) {
     };
     for (int32_t kt = 0; kt * int64_t(BWD_TK) < P.n_clean_kv; ++kt) {
       const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(P.n_clean_kv, k0 + BWD_TK);
-      const int32_t kb = k0 / P.B;
-      // clean rows of blocks >= kb (token-causal: at positions >= k0);
+      const int32_t g0 = P.clean_kv_start + k0;  // global position of the tile's first key
+      const int32_t kb = g0 / P.B;
+      // clean rows of blocks >= kb (token-causal: at positions >= g0);
       // corrupted rows of blocks with id > kb
-      const int32_t first_row_pos = P.token_causal ? k0 : kb * P.B;
+      const int32_t first_row_pos = P.token_causal ? g0 : kb * P.B;
       int32_t c0 = std::min<int32_t>(P.n_clean_q, std::max<int32_t>(0, first_row_pos - P.clean_q_start));
       int32_t j = int32_t(std::upper_bound(P.ids.begin(), P.ids.end(), kb) - P.ids.begin());
       int32_t x0 = j * P.B;
@@ -249,7 +272,7 @@ void build_plan(const Problem& P, Plan* plan) {
       BwdItem it{kt, 0, c0, P.n_clean_q, x0, nx, cf, xf};
       tiles.push_back({kt, 0, it, (P.n_clean_q - c0) + int64_t(nx - x0), qt, masked});
     }
-    for (int32_t kt = 0; kt * int64_t(BWD_TK) < nx; ++kt) {
+    for (int32_t kt = 0; P.corr_keys && kt * int64_t(BWD_TK) < nx; ++kt) {
       const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(nx, k0 + BWD_TK);
       const int32_t x0 = k0 / P.B * P.B, x1 = std::min<int32_t>(nx, ceil_div(k1, P.B) * P.B);
       BwdItem it{kt, 1, 0, 0, x0, x1, 0, x1};

@@ -55,6 +55,9 @@ struct BwdItem {
 struct Problem {
   int32_t B, H, Hkv, d, dtype;
   int32_t token_causal = 0;  // clean_mask == BDATTN_CLEAN_TOKEN_CAUSAL
+  int32_t clean_kv_start = 0;  // global position of clean buffer row 0 (partial problems)
+  int32_t partial = 0;         // attention over the keys present only
+  int32_t corr_keys = 1;       // the local corrupted keys are present
   float scale;  // resolved (> 0)
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks;
   std::vector<int32_t> ids;  // always materialised (0..n-1 when NULL)

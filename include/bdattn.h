@@ -23,6 +23,10 @@
  *    and returns the query gradients together with the gradients of the local
  *    corrupted K/V and of the clean K/V buffer, the latter summed over every
  *    local query that sees each clean key (§4.3, Backward pass).
+ *    Implementation 1 computes the attention as separate launches over
+ *    disjoint key sets, the block-diagonal corrupted part and clean K/V given
+ *    by original positions, merged through their log-sum-exps: a descriptor
+ *    with partial = 1 is one such launch, and bdattn_merge combines them.
  *
  * Softmax attention per query row i and q head h (KV head g = h / (H/Hkv)):
  *   s_ij = scale <q_i, k_j>,  LSE_i = ln sum_{j visible} exp(s_ij),
@@ -101,6 +105,20 @@ typedef struct {
    * NULL for ids 0..n_corr_blocks-1. Read during the call only. */
   const int32_t* corr_block_ids;
   int32_t clean_mask; /* bdattn_clean_mask; 0 (block-causal) for zero-initialised descriptors */
+  /* 0: the complete attention; the clean buffer must start at position 0 and
+   * hold every clean key a local query sees (BDATTN_ERR_COVERAGE otherwise).
+   * 1: a partial attention over the keys present, in the sense of the
+   * appendix's Implementation 1: clean keys at global positions
+   * [clean_kv_start, clean_kv_start + n_clean_kv) (clean_kv_start any multiple
+   * of B) and, unless omit_corr_keys, the local corrupted keys; the
+   * visibility rules are unchanged. The forward then returns O and LSE over
+   * the visible keys present (O = 0 and LSE = -inf for a row that sees none);
+   * merge such results with bdattn_merge. The backward, given the MERGED O and
+   * LSE of the complete attention, returns each gradient's part through the
+   * keys present: dQ summed over a partition of the keys is the full dQ;
+   * dK/dV of the keys present are complete. */
+  int32_t partial;
+  int32_t omit_corr_keys; /* 1: the local corrupted keys are absent (partial only) */
 } bdattn_problem;
 
 /* BDATTN_VERSION of the loaded library. */
@@ -114,13 +132,15 @@ const char* bdattn_last_error(void);
 
 /* Host-only check of a problem descriptor (no HIP calls). Rules: B >= 1;
  * H, Hkv >= 1 and H % Hkv == 0; d in {32, 128}; dtype known;
- * clean_mask known (BDATTN_ERR_INVALID_ARG);
+ * clean_mask known, partial and omit_corr_keys 0 or 1, omit_corr_keys only
+ * with partial (BDATTN_ERR_INVALID_ARG);
  * n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks >= 0; clean_q_start,
  * n_clean_q and n_clean_kv multiples of B (BDATTN_ERR_SHAPE); ids strictly
  * increasing and >= 0 (BDATTN_ERR_INVALID_ARG); every row count and global
- * position below 2^31; coverage: clean_kv_start == 0 and n_clean_kv reaches
- * the end of the last block of the query shard and the start of the last
- * local corrupted block (BDATTN_ERR_COVERAGE). */
+ * position below 2^31; coverage unless partial: clean_kv_start == 0 and
+ * n_clean_kv reaches the end of the last block of the query shard and the
+ * start of the last local corrupted block (BDATTN_ERR_COVERAGE); partial:
+ * clean_kv_start a multiple of B (BDATTN_ERR_SHAPE). */
 int bdattn_validate(const bdattn_problem* p);
 
 /* Bytes of workspace needed by bdattn_fwd (pass 0) or bdattn_bwd (pass 1).
@@ -159,7 +179,9 @@ int bdattn_fwd(const bdattn_problem* p,
 /* Backward (Implementation 2 of the appendix): from the forward's saved
  * o_c/o_x and lse_c/lse_x and the upstream do_c/do_x, writes dq_c, dq_x,
  * dk_c/dv_c [n_clean_kv,Hkv,d] (clean keys no local query sees get zeros)
- * and dk_x/dv_x [n_corr,Hkv,d]. LSE is not differentiated. */
+ * and dk_x/dv_x [n_corr,Hkv,d] (not written, and may be NULL, when
+ * omit_corr_keys). LSE is not differentiated. With partial = 1, o_c/o_x and
+ * lse_c/lse_x must be those of the complete attention (see bdattn_problem). */
 int bdattn_bwd(const bdattn_problem* p,
                const void* q_c, const void* k_c, const void* v_c,
                const void* q_x, const void* k_x, const void* v_x,
@@ -168,6 +190,19 @@ int bdattn_bwd(const bdattn_problem* p,
                const void* do_c, const void* do_x,
                void* dq_c, void* dq_x, void* dk_c, void* dv_c, void* dk_x, void* dv_x,
                void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Merge two partial attention results over disjoint key sets (appendix,
+ * Implementation 1): per row i and head h, with weights w = exp(LSE - LSE'),
+ *   lse[h,i] = ln(exp(lse_a[h,i]) + exp(lse_b[h,i])),
+ *   o[i,h,:] = (exp(lse_a - lse) o_a[i,h,:] + exp(lse_b - lse) o_b[i,h,:]).
+ * A part with LSE = -inf has weight 0; a row with -inf in both gets o = 0,
+ * lse = -inf. o_a/o_b/o are [n_rows, H, d] of `dtype` (32 or 128 for d), LSE
+ * [H, n_rows] float32; o may alias o_a or o_b and lse lse_a or lse_b (each
+ * element is read before it is written by the same thread). Device pointers,
+ * 16-byte aligned; enqueued on hip_stream. */
+int bdattn_merge(int64_t n_rows, int32_t H, int32_t d, int32_t dtype,
+                 const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                 void* o, float* lse, void* hip_stream);
 
 /* Optional instrumentation for benchmarks. With profiling on (per calling
  * thread), bdattn_fwd and bdattn_bwd record a pair of HIP events on the

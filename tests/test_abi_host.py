@@ -42,12 +42,13 @@ def oracle_mask(p):
     if p.corr_block_ids:
         ids = [p.corr_block_ids[i] for i in range(p.n_corr_blocks)]
     lay = layout(p.B, p.H, p.Hkv, p.d, p.n_clean_q, p.clean_q_start, p.n_clean_kv,
-                 p.clean_kv_start, p.n_corr_blocks, ids, clean_mask=p.clean_mask)
+                 p.clean_kv_start, p.n_corr_blocks, ids, clean_mask=p.clean_mask,
+                 partial=bool(p.partial), corr_keys=not p.omit_corr_keys)
     qs, qb = query_tokens(lay)
     ks, kb = key_tokens(lay)
     qp, kp = query_positions(lay), key_positions(lay)
     return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
-                   kp[None, :], lay.clean_mask)
+                   kp[None, :], lay.clean_mask, lay.corr_keys)
 
 
 CASES = [
@@ -63,9 +64,20 @@ CASES = [
 ]
 # the same shapes with the token-causal clean mask
 CASES_TC = [dict(c, clean_mask=bd.CLEAN_TOKEN_CAUSAL) for c in CASES]
+# partial problems: clean K/V ranges at original positions, with or without
+# the corrupted keys (the split form of the appendix's Implementation 1)
+CASES_PARTIAL = [
+    dict(B=4, n_clean_q=32, n_clean_kv=12, clean_kv_start=8, partial=True, omit_corr_keys=True),
+    dict(B=4, n_clean_q=32, n_clean_kv=0, partial=True),
+    dict(B=2, n_clean_q=8, clean_q_start=8, n_clean_kv=6, clean_kv_start=4,
+         corr_block_ids=[1, 4, 6], partial=True),
+    dict(B=16, n_clean_q=256, n_clean_kv=96, clean_kv_start=160, partial=True,
+         omit_corr_keys=True, clean_mask=bd.CLEAN_TOKEN_CAUSAL),
+    dict(B=32, n_clean_q=1056, n_clean_kv=384, clean_kv_start=320, partial=True),
+]
 
 
-@pytest.mark.parametrize("case", CASES + CASES_TC)
+@pytest.mark.parametrize("case", CASES + CASES_TC + CASES_PARTIAL)
 def test_mask_render_matches_oracle(case):
     p = bd.problem(H=2, Hkv=1, d=32, dtype="bf16", **case)
     assert bd.validate(p) == 0
@@ -131,6 +143,8 @@ def _p(**kw):
     (dict(n_clean_q=-4), -2),
     (dict(clean_mask=2), -1),
     (dict(clean_mask=-1), -1),
+    (dict(omit_corr_keys=True), -1),  # only a partial problem may omit them
+    (dict(partial=True, clean_kv_start=2, n_clean_kv=8), -2),
 ])
 def test_validation_error_codes(kw, code):
     p = _p(**kw)
@@ -179,7 +193,7 @@ def test_plan_covers_every_visible_tile():
     """The forward work list visits, for every query row tile, exactly the key
     tiles holding a visible key; the backward list has one item per key tile
     and KV head (so every dK/dV row is written)."""
-    for case in CASES + CASES_TC:
+    for case in CASES + CASES_TC + CASES_PARTIAL:
         p = bd.problem(H=4, Hkv=2, d=32, dtype="bf16", **case)
         st = bd.plan_stats(p)
         M = bd.mask_render(p)
@@ -204,5 +218,5 @@ def test_plan_covers_every_visible_tile():
         heads_groups = int(p.H) // Gw
         assert st["fwd_items"] == want_items * heads_groups
         assert st["fwd_tiles"] == want_tiles * heads_groups
-        kt = -(-nkv // 128) + -(-nx // 128)
+        kt = -(-nkv // 128) + (0 if p.omit_corr_keys else -(-nx // 128))
         assert st["bwd_items"] == kt * int(p.Hkv)

@@ -43,7 +43,7 @@ def full_mask(lay):
     ks, kb = key_tokens(lay)
     qp, kp = query_positions(lay), key_positions(lay)
     return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
-                   kp[None, :], lay.clean_mask)
+                   kp[None, :], lay.clean_mask, lay.corr_keys)
 
 
 # --------------------------------------------------------------------- mask
