@@ -1,0 +1,220 @@
+"""rocprofv3 harness for the bdattn kernels: duration, shader clock, matrix-core
+(MFMA) utilisation, LDS utilisation and HBM traffic per kernel, for one
+workload of ``bench.py``.
+
+Each measurement is its own rocprofv3 run of ``bench.py`` (one step), started
+as a child process with a time limit:
+
+  trace   --kernel-trace --stats                     kernel durations
+  fetch   --pmc FETCH_SIZE, with a 1 GiB plain copy  HBM reads
+  write   --pmc WRITE_SIZE, with a 1 GiB plain copy  HBM writes
+  sq1     --pmc SQ wave/instruction counters         issue and waits
+  sq2     --pmc SQ MFMA/LDS counters                 MFMA busy, LDS busy
+
+rocprofv3 does not split counters over passes, so every counter set stays
+within the per-block limits of one pass. The copy is read and written once,
+so it calibrates FETCH_SIZE and WRITE_SIZE (KiB per dispatch) to bytes. The
+shader clock of a kernel is GRBM_GUI_ACTIVE / XCDs / duration. MFMA busy is
+SQ_VALU_MFMA_BUSY_CYCLES over (SIMDs x cycles), and LDS busy is
+SQ_LDS_IDX_ACTIVE over (CUs x cycles); the counts of XCDs, SIMDs and CUs are
+read from the profiler's agent description.
+
+Usage (repository root, on the GPU machine):
+
+    python -m block_masked_attention_amd.rocprof --workload 256k --out DIR
+
+It prints one JSON line and writes DIR/summary.json and DIR/summary.md; the
+raw rocprofv3 output stays in DIR/<pass>/.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MAIN_KERNELS = ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kernel",
+                "merge_kernel")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
+SQ1 = ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+       "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+       "GRBM_GUI_ACTIVE"]
+SQ2 = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_IDX_ACTIVE",
+       "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU",
+       "GRBM_GUI_ACTIVE"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def short_name(kernel: str) -> str:
+    """'void bdattn::(anonymous namespace)::bwd_dq_kernel<true, 128>(...)' ->
+    'bwd_dq_kernel<true, 128>'; other kernels keep their name up to '('."""
+    m = re.search(r"::(\w+<[^>]*>)\(", kernel)
+    if m:
+        return m.group(1)
+    return kernel.split("(")[0].replace("void ", "").strip()
+
+
+def run_pass(name, flags, bench_args, out_dir, limit):
+    """One rocprofv3 run of bench.py; returns its output directory. The
+    program follows '--' directly (no launcher in between)."""
+    d = os.path.join(out_dir, name)
+    shutil.rmtree(d, ignore_errors=True)
+    cmd = (["rocprofv3"] + flags + ["-f", "csv", "-d", d, "-o", "run", "--", sys.executable,
+                                    os.path.join(ROOT, "bench.py")] + bench_args)
+    log(f"[rocprof] pass {name}: {' '.join(cmd)}")
+    with open(os.path.join(out_dir, f"{name}.log"), "w") as fh:
+        try:
+            res = subprocess.run(cmd, cwd=ROOT, stdout=fh, stderr=subprocess.STDOUT,
+                                 timeout=limit)
+            rc = res.returncode
+        except subprocess.TimeoutExpired:  # the child is killed (SIGKILL)
+            raise RuntimeError(f"rocprofv3 pass {name} exceeded {limit} s")
+    # rocprofv3 may end with a signal after the program finished and wrote its
+    # results; the results decide
+    if not any(f.endswith(".csv") for f in os.listdir(d) if os.path.isfile(os.path.join(d, f))):
+        raise RuntimeError(f"rocprofv3 pass {name} wrote no results (exit status {rc})")
+    log(f"[rocprof] pass {name} done (exit status {rc})")
+    return d
+
+
+def read_csv(d, suffix):
+    path = os.path.join(d, f"run_{suffix}.csv")
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def durations(d):
+    """Average ms per call and call count of every kernel of a trace pass."""
+    out = {}
+    for r in read_csv(d, "kernel_stats"):
+        out[short_name(r["Name"])] = dict(ms=float(r["AverageNs"]) / 1e6, calls=int(r["Calls"]))
+    return out
+
+
+def counters(d):
+    """Counter totals per kernel, divided by the kernel's dispatch count."""
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in read_csv(d, "counter_collection"):
+        k = short_name(r["Kernel_Name"])
+        tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    return {k: {c: v / len(disp[k]) for c, v in cs.items()} for k, cs in tot.items()}
+
+
+def agent(d):
+    for r in read_csv(d, "agent_info"):
+        if r.get("Name", "").startswith("gfx"):
+            return dict(simds=int(r["Simd_Count"]), cus=int(r["Cu_Count"]),
+                        xcds=int(r.get("Num_Xcc") or 1), name=r["Name"])
+    raise RuntimeError("no GPU agent in the profiler's agent description")
+
+
+def summarise(dur, fetch, write, sq1, sq2, dev):
+    copy_fetch = fetch.get(COPY_KERNEL, {}).get("FETCH_SIZE")
+    copy_write = write.get(COPY_KERNEL, {}).get("WRITE_SIZE")
+    f_scale = COPY_BYTES / (copy_fetch * 1024) if copy_fetch else None
+    w_scale = COPY_BYTES / (copy_write * 1024) if copy_write else None
+    rows = {}
+    for k, t in dur.items():
+        if not k.startswith(MAIN_KERNELS):
+            continue
+        s = t["ms"] * 1e-3
+        r = dict(ms=round(t["ms"], 3), calls=t["calls"])
+        if k in fetch and f_scale:
+            r["hbm_read_gb"] = round(fetch[k]["FETCH_SIZE"] * 1024 * f_scale / 1e9, 2)
+        if k in write and w_scale:
+            r["hbm_write_gb"] = round(write[k]["WRITE_SIZE"] * 1024 * w_scale / 1e9, 3)
+        if "hbm_read_gb" in r and "hbm_write_gb" in r:
+            r["hbm_gbps"] = round((r["hbm_read_gb"] + r["hbm_write_gb"]) / s, 1)
+        clocks = [c["GRBM_GUI_ACTIVE"] / dev["xcds"] / s / 1e9
+                  for c in (sq1.get(k), sq2.get(k)) if c and "GRBM_GUI_ACTIVE" in c]
+        if clocks:
+            ghz = sum(clocks) / len(clocks)
+            cycles = ghz * 1e9 * s
+            r["clock_ghz"] = round(ghz, 3)
+            c2 = sq2.get(k, {})
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c2:
+                r["mfma_busy"] = round(c2["SQ_VALU_MFMA_BUSY_CYCLES"] / (dev["simds"] * cycles), 4)
+            if "SQ_LDS_IDX_ACTIVE" in c2:
+                r["lds_busy"] = round(c2["SQ_LDS_IDX_ACTIVE"] / (dev["cus"] * cycles), 4)
+            if c2.get("SQ_INSTS_MFMA"):
+                m = c2["SQ_INSTS_MFMA"]
+                r["valu_per_mfma"] = round(c2["SQ_INSTS_VALU"] / m, 2)
+                r["lds_per_mfma"] = round(c2["SQ_INSTS_LDS"] / m, 2)
+                r["salu_per_mfma"] = round(c2["SQ_INSTS_SALU"] / m, 2)
+            if "SQ_LDS_BANK_CONFLICT" in c2:
+                r["lds_bank_conflicts"] = c2["SQ_LDS_BANK_CONFLICT"]
+        rows[k] = r
+    return dict(device=dev, fetch_scale=f_scale, write_scale=w_scale, kernels=rows)
+
+
+def markdown(summary, workload, cmd):
+    cols = [("ms", "ms"), ("clock_ghz", "clock GHz"), ("mfma_busy", "MFMA busy"),
+            ("lds_busy", "LDS busy"), ("valu_per_mfma", "VALU/MFMA"),
+            ("hbm_read_gb", "HBM read GB"), ("hbm_write_gb", "HBM write GB"),
+            ("hbm_gbps", "HBM GB/s")]
+    out = [f"# bdattn kernels, {workload} workload: rocprofv3 summary", "",
+           "Command (run from the repository root on one GPU):", "", "```", cmd, "```", "",
+           f"Device {summary['device']['name']}: {summary['device']['cus']} CUs, "
+           f"{summary['device']['simds']} SIMDs, {summary['device']['xcds']} XCDs. HBM counters "
+           f"scaled by a 1 GiB plain copy (factors {summary['fetch_scale']:.3f} fetch, "
+           f"{summary['write_scale']:.3f} write).", "",
+           "| kernel | " + " | ".join(c[1] for c in cols) + " |",
+           "|---|" + "---|" * len(cols)]
+    for k, r in summary["kernels"].items():
+        cells = []
+        for key, _ in cols:
+            v = r.get(key)
+            if v is None:
+                cells.append("")
+            elif key in ("mfma_busy", "lds_busy"):
+                cells.append(f"{100 * v:.0f}%")
+            else:
+                cells.append(f"{v:g}")
+        out.append(f"| `{k}` | " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--workload", default="256k")
+    ap.add_argument("--out", required=True, help="directory for the raw output and summaries")
+    ap.add_argument("--limit", type=int, default=300, help="seconds allowed per pass")
+    args = ap.parse_args()
+    if shutil.which("rocprofv3") is None:
+        sys.exit("rocprofv3 not found")
+    os.makedirs(args.out, exist_ok=True)
+    os.environ.setdefault("TMPDIR", "/tmp")
+    b = ["--workload", args.workload, "--no-cpu-baseline", "--steps", "1"]
+    d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", "1"], args.out,
+                       args.limit)
+    cal = b + ["--warmup", "0", "--copy-calibration"]
+    d_fetch = run_pass("fetch", ["--pmc", "FETCH_SIZE"], cal, args.out, args.limit)
+    d_write = run_pass("write", ["--pmc", "WRITE_SIZE"], cal, args.out, args.limit)
+    d_sq1 = run_pass("sq1", ["--pmc"] + SQ1, b + ["--warmup", "0"], args.out, args.limit)
+    d_sq2 = run_pass("sq2", ["--pmc"] + SQ2, b + ["--warmup", "0"], args.out, args.limit)
+    summary = summarise(durations(d_trace), counters(d_fetch), counters(d_write),
+                        counters(d_sq1), counters(d_sq2), agent(d_trace))
+    summary["workload"] = args.workload
+    cmd = f"python -m block_masked_attention_amd.rocprof --workload {args.workload} --out {args.out}"
+    with open(os.path.join(args.out, "summary.json"), "w") as fh:
+        json.dump(summary, fh, indent=1)
+    with open(os.path.join(args.out, "summary.md"), "w") as fh:
+        fh.write(markdown(summary, args.workload, cmd))
+    print(json.dumps(summary), flush=True)
+
+
+if __name__ == "__main__":
+    main()

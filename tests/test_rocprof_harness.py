@@ -1,0 +1,69 @@
+"""The rocprof harness's arithmetic on synthetic rocprofv3 output (no GPU):
+kernel names, per-dispatch counter averages, the copy calibration of the HBM
+counters, and the derived clock, MFMA and LDS utilisation."""
+import csv
+import os
+
+import pytest
+
+from block_masked_attention_amd import rocprof
+
+K = "void bdattn::(anonymous namespace)::bwd_dq_kernel<true, 128>(bdattn::BwdArgs)"
+
+
+def _write(d, name, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, f"run_{name}.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _counters(d, per_kernel):
+    rows = []
+    for i, (k, cs) in enumerate(per_kernel):
+        for disp in range(cs.pop("_dispatches", 1)):
+            for c, v in cs.items():
+                rows.append(dict(Dispatch_Id=f"{i}.{disp}", Kernel_Name=k, Counter_Name=c,
+                                 Counter_Value=v))
+    _write(d, "counter_collection", rows)
+
+
+def test_short_names():
+    assert rocprof.short_name(K) == "bwd_dq_kernel<true, 128>"
+    assert rocprof.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_summary_arithmetic(tmp_path):
+    t = str(tmp_path)
+    _write(t + "/trace", "kernel_stats", [dict(Name=K, Calls=2, AverageNs=2.0e6)])  # 2 ms
+    _write(t + "/trace", "agent_info", [dict(Name="gfx950", Simd_Count=1024, Cu_Count=256,
+                                             Num_Xcc=8)])
+    # the copy reads 2^30 bytes but FETCH_SIZE reports half of it: scale 2
+    _counters(t + "/fetch", [(rocprof.COPY_KERNEL, dict(FETCH_SIZE=524288)),
+                             (K, dict(FETCH_SIZE=1000.0, _dispatches=2))])
+    _counters(t + "/write", [(rocprof.COPY_KERNEL, dict(WRITE_SIZE=1048576)),
+                             (K, dict(WRITE_SIZE=500.0))])
+    cycles = 2.0e9 * 2.0e-3  # a 2 GHz clock over 2 ms
+    _counters(t + "/sq1", [(K, dict(GRBM_GUI_ACTIVE=8 * cycles))])
+    _counters(t + "/sq2", [(K, dict(GRBM_GUI_ACTIVE=8 * cycles,
+                                    SQ_VALU_MFMA_BUSY_CYCLES=0.5 * 1024 * cycles,
+                                    SQ_LDS_IDX_ACTIVE=0.25 * 256 * cycles,
+                                    SQ_INSTS_MFMA=100.0, SQ_INSTS_VALU=300.0,
+                                    SQ_INSTS_LDS=150.0, SQ_INSTS_SALU=50.0,
+                                    SQ_LDS_BANK_CONFLICT=0.0))])
+    s = rocprof.summarise(rocprof.durations(t + "/trace"), rocprof.counters(t + "/fetch"),
+                          rocprof.counters(t + "/write"), rocprof.counters(t + "/sq1"),
+                          rocprof.counters(t + "/sq2"), rocprof.agent(t + "/trace"))
+    assert s["fetch_scale"] == pytest.approx(2.0) and s["write_scale"] == pytest.approx(1.0)
+    r = s["kernels"]["bwd_dq_kernel<true, 128>"]
+    assert r["ms"] == pytest.approx(2.0) and r["calls"] == 2
+    # 1000 KiB per dispatch (2000 over two dispatches), times the scale 2
+    assert r["hbm_read_gb"] == pytest.approx(1000 * 1024 * 2 / 1e9, abs=0.01)
+    assert r["hbm_write_gb"] == pytest.approx(500 * 1024 / 1e9, abs=1e-3)
+    assert r["clock_ghz"] == pytest.approx(2.0)
+    assert r["mfma_busy"] == pytest.approx(0.5)
+    assert r["lds_busy"] == pytest.approx(0.25)
+    assert r["valu_per_mfma"] == pytest.approx(3.0) and r["lds_per_mfma"] == pytest.approx(1.5)
+    md = rocprof.markdown(s, "256k", "python -m block_masked_attention_amd.rocprof")
+    assert "| `bwd_dq_kernel<true, 128>` | 2 | 2 | 50% | 25% |" in md
