@@ -134,6 +134,48 @@ def cpu_baseline(spec, t, seconds: float):
             "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def time_split_forward(bd, spec, t, shards, reps):
+    """The forward as the appendix's Implementation 1 runs it: one partial
+    launch for the block-diagonal corrupted part, one per clean K/V shard (at
+    original positions), and a merge after each shard. Returns the mean ms
+    per forward over `reps` after one untimed pass."""
+    import torch
+
+    from workloads import INPUT_NAMES
+
+    B, nkv = spec.B, spec.n_clean_kv
+    cuts = [B * (i * (nkv // B) // shards) for i in range(shards + 1)]
+    parts = [(0, 0, True)] + [(a, b, False) for a, b in zip(cuts, cuts[1:]) if b > a]
+    probs, ins = [], []
+    for lo, hi, ck in parts:
+        probs.append(bd.problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
+                                spec.clean_q_start, hi - lo, lo, spec.n_corr_blocks,
+                                spec.corr_block_ids, clean_mask=spec.clean_mask, partial=True,
+                                omit_corr_keys=not ck))
+        u = dict(t)
+        u["k_c"], u["v_c"] = t["k_c"][lo:hi], t["v_c"][lo:hi]  # row ranges stay contiguous
+        ins.append([u[k] for k in INPUT_NAMES])
+    wss = [torch.empty(bd.workspace_size(p, 0), dtype=torch.uint8, device=t["q_c"].device)
+           for p in probs]
+    acc = bd.fwd(probs[0], *ins[0], workspace=wss[0])
+    part = [torch.empty_like(x) for x in acc]
+
+    def once():
+        bd.fwd(probs[0], *ins[0], workspace=wss[0], out=acc)
+        for p, a, w in zip(probs[1:], ins[1:], wss[1:]):
+            bd.fwd(p, *a, workspace=w, out=part)
+            bd.merge(acc[0], acc[2], part[0], part[2], out=(acc[0], acc[2]))
+            bd.merge(acc[1], acc[3], part[1], part[3], out=(acc[1], acc[3]))
+
+    once()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    return {"shards": shards, "launches": len(parts), "ms": round((time.perf_counter() - t0) * 1e3 / reps, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -145,6 +187,10 @@ def main():
     ap.add_argument("--clean-mask", choices=("block", "token"), default="block",
                     help="what a clean query sees of its own block: all of it (block-causal, "
                          "the workloads' definition) or the keys up to its own position")
+    ap.add_argument("--split-forward", type=int, default=0, metavar="N",
+                    help="also time the forward in the split form: the block-diagonal corrupted "
+                         "launch plus N clean K/V shards at original positions, merged "
+                         "(reported under 'split_forward', after the main timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -235,6 +281,12 @@ def main():
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
                   f"executed TFLOP/s)" for k, v in kern.items()))
 
+    split = None
+    if args.split_forward > 0:
+        split = time_split_forward(bd, spec, t, args.split_forward, max(1, args.steps))
+        log(f"[bench] split forward ({args.split_forward} clean shards + block-diagonal part, "
+            f"merged): {split['ms']:.2f} ms against {kern['fwd']['ms']:.2f} ms fused")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the float64 oracle on a sample (~{args.cpu_seconds:.0f} s)")
@@ -272,6 +324,8 @@ def main():
                                             f"({executed_d[dom]}*d executed)"},
         "cpu_baseline": cpu,
     }
+    if split is not None:
+        out["split_forward"] = split
     print(json.dumps(out), flush=True)
 
 
