@@ -64,9 +64,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
   //     (token-causal: clean rows at positions >= p); corrupted rows of
   //     blocks with id > kb, i.e. from the first local block whose id exceeds
   //     kb. The item gives that block j0 for the tile's first key block k0/B;
-  //     ids increase strictly, so for kb = k0/B + delta it lies in
-  //     [j0, j0 + delta] and a short scan finds it;
-  //   corrupted key of local block kb: the corrupted rows of that block.
+  //     ids do not decrease, so a scan from j0 over the local blocks with ids
+  //     in (k0/B, kb] finds it (a few blocks: the tile spans BWD_TK keys,
+  //     and a repeated id is another copy of the same block);
+  //   corrupted key of local block kb: the corrupted rows of that block (its
+  //     own copy only).
   int lo_c = 0, hi_c = 0, lo_x = 0, hi_x = 0;
   if (key_ok) {
     // clean: global position and block (buffer row 0 is position
@@ -81,8 +83,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       hi_c = a.n_clean_q;
       const int n_blk = a.n_corr / a.B;
       int j = it_x0 / a.B;  // j0: first local corrupted block with id > the tile's first block
-      const int j_end = min(n_blk, j + (key_blk - (key0 + a.clean_kv_start) / a.B));
-      while (j < j_end && a.ids[j] <= key_blk) ++j;
+      while (j < n_blk && a.ids[j] <= key_blk) ++j;
       lo_x = j * a.B;
       hi_x = a.n_corr;
     }

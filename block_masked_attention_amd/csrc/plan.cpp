@@ -98,8 +98,8 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   if (p->corr_block_ids) {
     for (int32_t i = 0; i < P.n_corr_blocks; ++i) {
       int32_t v = p->corr_block_ids[i];
-      if (v < 0 || (i > 0 && v <= P.ids[i - 1])) {
-        *msg = "corr_block_ids must be >= 0 and strictly increasing";
+      if (v < 0 || (i > 0 && v < P.ids[i - 1])) {
+        *msg = "corr_block_ids must be >= 0 and non-decreasing";
         return BDATTN_ERR_INVALID_ARG;
       }
       if (int64_t(v) * B > kMax32) {

@@ -101,8 +101,12 @@ typedef struct {
   int64_t n_clean_kv;     /* clean K/V buffer ...                            */
   int64_t clean_kv_start; /* ... at global positions [start, start+n); must be 0 */
   int64_t n_corr_blocks;  /* local corrupted blocks (each B tokens)          */
-  /* HOST array of n_corr_blocks global block ids, strictly increasing, or
-   * NULL for ids 0..n_corr_blocks-1. Read during the call only. */
+  /* HOST array of n_corr_blocks global block ids, non-decreasing, or NULL
+   * for ids 0..n_corr_blocks-1. Read during the call only. A repeated id is
+   * another corrupted copy of the same block (complementary masking, which
+   * trains a block under a mask and its complement, as Fast-dLLM v2 does):
+   * each local block sees the clean prefix of its id and only its own
+   * corrupted keys. */
   const int32_t* corr_block_ids;
   int32_t clean_mask; /* bdattn_clean_mask; 0 (block-causal) for zero-initialised descriptors */
   /* 0: the complete attention; the clean buffer must start at position 0 and
@@ -135,8 +139,8 @@ const char* bdattn_last_error(void);
  * clean_mask known, partial and omit_corr_keys 0 or 1, omit_corr_keys only
  * with partial (BDATTN_ERR_INVALID_ARG);
  * n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks >= 0; clean_q_start,
- * n_clean_q and n_clean_kv multiples of B (BDATTN_ERR_SHAPE); ids strictly
- * increasing and >= 0 (BDATTN_ERR_INVALID_ARG); every row count and global
+ * n_clean_q and n_clean_kv multiples of B (BDATTN_ERR_SHAPE); ids
+ * non-decreasing and >= 0 (BDATTN_ERR_INVALID_ARG); every row count and global
  * position below 2^31; coverage unless partial: clean_kv_start == 0 and
  * n_clean_kv reaches the end of the last block of the query shard and the
  * start of the last local corrupted block (BDATTN_ERR_COVERAGE); partial:

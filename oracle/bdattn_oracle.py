@@ -53,7 +53,7 @@ BLOCK_CAUSAL = 0  # a clean query sees its whole own clean block
 TOKEN_CAUSAL = 1  # ... or its own clean block up to its own position
 
 __all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens", "query_positions",
-           "key_positions", "Oracle", "CLEAN", "CORRUPTED", "BLOCK_CAUSAL", "TOKEN_CAUSAL",
+           "key_positions", "corrupted_copies", "Oracle", "CLEAN", "CORRUPTED", "BLOCK_CAUSAL", "TOKEN_CAUSAL",
            "round_bf16", "merge_partials"]
 
 
@@ -169,8 +169,17 @@ def key_positions(lay: Layout):
     return np.concatenate([clean, corr])
 
 
+def corrupted_copies(lay: Layout, n_clean: int):
+    """Local corrupted block (copy) index of every token of a query or key
+    list with ``n_clean`` clean tokens first; -1 for clean tokens. Two local
+    blocks with the same id are two corrupted copies of that block
+    (complementary masking)."""
+    return np.concatenate([np.full(n_clean, -1, np.int64),
+                           np.repeat(np.arange(len(lay.corr_ids), dtype=np.int64), lay.B)])
+
+
 def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
-            clean_mask=BLOCK_CAUSAL, corr_keys=True):
+            clean_mask=BLOCK_CAUSAL, corr_keys=True, q_copy=None, k_copy=None):
     """The four visibility rules of §3.2, broadcast over their arguments.
 
     clean query, block qb     -> clean key of block kb  iff kb < qb, or kb == qb
@@ -178,7 +187,9 @@ def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
                                   token-causal: key position <= query position)
     clean query               -> corrupted key          never
     corrupted query, block qb -> clean key of block kb  iff kb <  qb
-    corrupted query, block qb -> corrupted key, block kb iff kb == qb
+    corrupted query, block qb -> corrupted key, block kb iff kb == qb, of its
+                                 own copy (``q_copy``/``k_copy``, when a rank
+                                 holds two corrupted copies of a block)
 
     Positions are needed only for TOKEN_CAUSAL. With ``corr_keys`` False the
     corrupted keys are absent (a partial problem) and none is visible.
@@ -191,6 +202,8 @@ def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
     clean_clean = qc & kc & ((k_block < q_block) | own_block)
     corr_clean = ~qc & kc & (k_block < q_block)
     corr_corr = ~qc & ~kc & (k_block == q_block) & bool(corr_keys)
+    if q_copy is not None:
+        corr_corr = corr_corr & (k_copy == q_copy)
     return clean_clean | corr_clean | corr_corr
 
 
@@ -274,6 +287,7 @@ class Oracle:
         self.qs, self.qb = query_tokens(lay)
         self.ks, self.kb = key_tokens(lay)
         self.qp, self.kp = query_positions(lay), key_positions(lay)
+        self.qcp, self.kcp = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
 
     # ---------------------------------------------------------------- helpers
     def _mask(self, qidx, kidx=None):
@@ -282,7 +296,7 @@ class Oracle:
         return visible(self.qs[qidx, None], self.qb[qidx, None],
                        self.ks[None, kidx], self.kb[None, kidx],
                        self.qp[qidx, None], self.kp[None, kidx], self.lay.clean_mask,
-                       self.lay.corr_keys)
+                       self.lay.corr_keys, self.qcp[qidx, None], self.kcp[None, kidx])
 
     @staticmethod
     def _columns(cols):

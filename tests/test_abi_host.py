@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import block_masked_attention_amd as bd
-from oracle import key_positions, key_tokens, layout, query_positions, query_tokens, visible
+from oracle import (corrupted_copies, key_positions, key_tokens, layout, query_positions,
+                    query_tokens, visible)
 from tests.test_oracle import read_golden
 from workloads import CONFIGS
 
@@ -47,8 +48,9 @@ def oracle_mask(p):
     qs, qb = query_tokens(lay)
     ks, kb = key_tokens(lay)
     qp, kp = query_positions(lay), key_positions(lay)
+    qc, kc = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
     return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
-                   kp[None, :], lay.clean_mask, lay.corr_keys)
+                   kp[None, :], lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :])
 
 
 CASES = [
@@ -61,6 +63,9 @@ CASES = [
     dict(B=4, n_clean_q=16, clean_q_start=32, n_clean_kv=64, corr_block_ids=[2, 5, 11, 15]),
     dict(B=32, n_clean_q=0, n_clean_kv=2048, corr_block_ids=[0, 9, 33, 63]),
     dict(B=8, n_clean_q=64, n_corr_blocks=0),
+    # two corrupted copies of some blocks (complementary masking)
+    dict(B=4, n_clean_q=32, corr_block_ids=[0, 0, 1, 3, 3, 5, 7, 7]),
+    dict(B=32, n_clean_q=1024, corr_block_ids=[b for b in range(32) for _ in (0, 1)]),
 ]
 # the same shapes with the token-causal clean mask
 CASES_TC = [dict(c, clean_mask=bd.CLEAN_TOKEN_CAUSAL) for c in CASES]
@@ -88,7 +93,8 @@ def test_mask_render_matches_oracle(case):
 
 
 @pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt",
-                                  "mask_token_causal_L8_B2.txt"])
+                                  "mask_token_causal_L8_B2.txt",
+                                  "mask_complementary_L8_B2.txt"])
 def test_mask_render_matches_hand_drawn_fixture(name):
     prm, want = read_golden(name)
     p = bd.problem(prm["B"], 1, 1, 32, "f32", prm["n_clean_q"], prm["clean_q_start"],
@@ -137,7 +143,7 @@ def _p(**kw):
     (dict(clean_q_start=16, n_clean_kv=16), -4),
     (dict(clean_kv_start=4, n_clean_kv=32), -4),
     (dict(corr_block_ids=[3, 2]), -1),
-    (dict(corr_block_ids=[1, 1]), -1),
+    (dict(corr_block_ids=[2, 1]), -1),
     (dict(corr_block_ids=[-1, 2]), -1),
     (dict(corr_block_ids=[0, 9]), -4),  # block 9 needs clean keys < 36
     (dict(n_clean_q=-4), -2),

@@ -93,6 +93,14 @@ SMALL = [
     ("bf16_token_causal_share", dict(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
                                      n_clean_q=128, clean_q_start=384, n_clean_kv=512,
                                      corr_block_ids=list(range(3, 16, 4)), clean_mask=1)),
+    # complementary masking: two corrupted copies of the same target block
+    ("f32_complementary", dict(L=128, B=16, H=2, Hkv=1, d=32, dtype="f32",
+                               corr_block_ids=[0, 0, 1, 2, 2, 5, 7, 7])),
+    ("bf16_complementary", dict(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                corr_block_ids=[b for b in range(16) for _ in (0, 1)])),
+    ("bf16_complementary_share", dict(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                      n_clean_q=128, clean_q_start=384, n_clean_kv=512,
+                                      corr_block_ids=[3, 3, 7, 7, 11, 11, 15, 15])),
 ]
 
 

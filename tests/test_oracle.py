@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Oracle, key_positions,
-                    key_tokens, layout, merge_partials, query_positions, query_tokens, visible)
+from oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Oracle, corrupted_copies,
+                    key_positions, key_tokens, layout, merge_partials, query_positions,
+                    query_tokens, visible)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -42,8 +43,9 @@ def full_mask(lay):
     qs, qb = query_tokens(lay)
     ks, kb = key_tokens(lay)
     qp, kp = query_positions(lay), key_positions(lay)
+    qc, kc = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
     return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
-                   kp[None, :], lay.clean_mask, lay.corr_keys)
+                   kp[None, :], lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :])
 
 
 # --------------------------------------------------------------------- mask
@@ -65,7 +67,8 @@ def read_golden(name):
 
 
 @pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt",
-                                  "mask_token_causal_L8_B2.txt"])
+                                  "mask_token_causal_L8_B2.txt",
+                                  "mask_complementary_L8_B2.txt"])
 def test_mask_matches_hand_drawn_fixture(name):
     p, want = read_golden(name)
     lay = layout(p["B"], 1, 1, 4, p["n_clean_q"], p["clean_q_start"], p["n_clean_kv"],
@@ -599,3 +602,39 @@ def test_partial_rows_without_keys_are_the_empty_sum():
     empty = (np.zeros_like(O), np.full_like(L, -np.inf))
     Om, Lm = merge_partials([(O, L), empty])
     assert np.array_equal(Om, O) and np.array_equal(Lm, L)
+
+
+# ------------------------------------------------- complementary masking
+def test_corrupted_copies_of_a_block_are_independent():
+    """Two corrupted copies of the same block (complementary masking) each
+    give exactly what a problem holding only that copy gives: outputs, query
+    gradients and their own dK/dV; the clean dK/dV are the sum of the two
+    problems' (§3.2 separability, applied to copies)."""
+    B, H, Hkv, d, L = 4, 2, 1, 5, 16
+    both = layout(B, H, Hkv, d, L, corr_block_ids=[2, 2])
+    t = make(both, seed=41)
+    got = oracle_of(both, t)
+    O_c, O_x, L_c, L_x = got.forward()
+    g = got.backward()
+    dk_c, dv_c = np.zeros_like(g[2]), np.zeros_like(g[3])
+    for j in range(2):
+        one = layout(B, H, Hkv, d, L, corr_block_ids=[2])
+        u = dict(t)
+        rows = slice(j * B, (j + 1) * B)
+        for k in ("q_x", "k_x", "v_x", "do_x"):
+            u[k] = t[k][rows]
+        # the clean stream's share: count it once, in the first problem
+        if j == 1:
+            u["do_c"] = np.zeros_like(t["do_c"])
+        ref = oracle_of(one, u)
+        o_c, o_x, l_c, l_x = ref.forward()
+        r = ref.backward()
+        np.testing.assert_allclose(O_x[rows], o_x, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(L_x[:, rows], l_x, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g[1][rows], r[1], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(g[4][rows], r[4], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(g[5][rows], r[5], rtol=1e-11, atol=1e-12)
+        dk_c += r[2]
+        dv_c += r[3]
+    np.testing.assert_allclose(g[2], dk_c, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(g[3], dv_c, rtol=1e-11, atol=1e-12)
