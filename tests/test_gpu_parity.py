@@ -261,3 +261,41 @@ def workload_parity(spec):
         say(f"  bf16-operand oracle samples: {time.perf_counter() - t0:.1f} s")
     errs = compare(spec, have, want, names=list(want), label=spec.name, ideal=ideal)
     assert_parity(spec, errs, spec.name)
+
+
+def _random_specs(n=16, seed=2024):
+    """Seeded random small problems mixing every option of the descriptor:
+    block size, GQA ratio, head dim and dtype, a rank's share (clean query
+    range, clean buffer length), a subset of corrupted blocks with repeated
+    ids (complementary copies), and the clean mask."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dtype, d = [("f32", 32), ("bf16", 32), ("bf16", 128)][int(rng.integers(3))]
+        B = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 48, 64]))
+        nb = int(rng.integers(2, max(3, 640 // B) + 1))
+        Hkv = int(rng.choice([1, 2, 4]))
+        H = Hkv * int(rng.choice([1, 2, 3, 4]))
+        cq0 = int(rng.integers(0, nb))
+        cq1 = int(rng.integers(cq0, nb + 1))
+        ids = sorted(rng.choice(nb, size=int(rng.integers(0, nb + 1)), replace=False).tolist())
+        if ids and rng.random() < 0.4:  # complementary copies of some blocks
+            ids = sorted(ids + rng.choice(ids, size=int(rng.integers(1, len(ids) + 1))).tolist())
+        if cq1 == cq0 and not ids:
+            continue
+        need = max(cq1, max(ids) if ids else 0)  # clean blocks the local queries see
+        n_kv = int(rng.integers(need, nb + 1)) * B
+        out.append((f"rand{len(out)}_{dtype}_d{d}_B{B}_H{H}_{Hkv}",
+                    dict(L=cq1 * B, B=B, H=H, Hkv=Hkv, d=d, dtype=dtype,
+                         std=1.0 if dtype == "f32" else 0.5,
+                         n_clean_q=(cq1 - cq0) * B, clean_q_start=cq0 * B, n_clean_kv=n_kv,
+                         corr_block_ids=ids, clean_mask=int(rng.integers(2)))))
+    return out
+
+
+RANDOM = _random_specs()
+
+
+@pytest.mark.parametrize("label,kw", RANDOM, ids=[r[0] for r in RANDOM])
+def test_random_small_problems(label, kw):
+    full_parity(small_spec(name=label, seed=zlib.crc32(label.encode()) % 10000, **kw), label)
