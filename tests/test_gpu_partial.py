@@ -146,3 +146,75 @@ def test_split_forward_merge_and_backward_equal_the_full_problem(label, kw):
     ideal = oracle_full(spec, t, "bf16") if spec.dtype == "bf16" else None
     errs = compare(spec, got, want, label=label, ideal=ideal)
     assert_parity(spec, errs, label)
+
+
+def _random_partials(n=10, seed=4242):
+    """Seeded random partial problems: a complete problem (block size, GQA,
+    share, block subset with repeats, clean mask) and a random clean K/V
+    range at original positions, with the corrupted keys kept or omitted."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dtype, d = [("f32", 32), ("bf16", 128)][int(rng.integers(2))]
+        B = int(rng.choice([1, 2, 4, 16, 32, 64]))
+        nb = int(rng.integers(3, max(4, 512 // B) + 1))
+        Hkv = int(rng.choice([1, 2]))
+        H = Hkv * int(rng.choice([1, 2, 4]))
+        cq0 = int(rng.integers(0, nb))
+        ids = sorted(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False).tolist())
+        if rng.random() < 0.3:
+            ids = sorted(ids + [ids[0]])
+        lo = int(rng.integers(0, nb)) * B
+        hi = int(rng.integers(lo // B, nb + 1)) * B
+        out.append((f"rpart{len(out)}_{dtype}_B{B}_[{lo},{hi})",
+                    dict(L=nb * B, B=B, H=H, Hkv=Hkv, d=d, dtype=dtype,
+                         std=1.0 if dtype == "f32" else 0.5, n_clean_q=(nb - cq0) * B,
+                         clean_q_start=cq0 * B, n_clean_kv=nb * B, corr_block_ids=ids,
+                         clean_mask=int(rng.integers(2))), lo, hi, bool(rng.integers(2))))
+    return out
+
+
+RANDOM_PARTIALS = _random_partials()
+
+
+@pytest.mark.parametrize("label,kw,lo,hi,ck", RANDOM_PARTIALS, ids=[r[0] for r in RANDOM_PARTIALS])
+def test_random_partial_problems(label, kw, lo, hi, ck):
+    """One random partial launch, forward and backward: the forward against
+    the oracle's partial layout (rows with no key present exactly O = 0,
+    LSE = -inf); the backward, given the complete problem's O and LSE, against
+    the oracle's partial backward with the oracle's complete O and LSE."""
+    _need_gpu()
+    spec = small_spec(name=label, seed=91, **kw)
+    t = make_inputs(spec, device="cuda")
+    u = part_inputs(t, lo, hi)
+    p = part_problem(spec, lo, hi, ck)
+    got = dict(zip(OUT_NAMES[:4], (f64(x) for x in bd.fwd(p, *[u[k] for k in INPUT_NAMES]))))
+    orc = part_oracle(spec, t, lo, hi, ck)
+    want = dict(zip(OUT_NAMES[:4], orc.forward()))
+    for s in ("c", "x"):
+        empty = np.isneginf(want["lse_" + s])
+        assert np.array_equal(np.isneginf(got["lse_" + s]), empty), f"{label}: empty rows ({s})"
+        got["lse_" + s] = np.where(empty, 0.0, got["lse_" + s])
+        want["lse_" + s] = np.where(empty, 0.0, want["lse_" + s])
+    ideal = part_oracle_bf16(spec, t, lo, hi, ck) if spec.dtype == "bf16" else None
+    errs = compare(spec, got, want, names=list(want), label=label, ideal=ideal)
+    # backward through the keys present, with the complete problem's O and LSE
+    full = bd.fwd(bd.from_spec(spec), *[t[k] for k in INPUT_NAMES])
+    g = bd.bwd(p, *[u[k] for k in INPUT_NAMES], *full, t["do_c"], t["do_x"])
+    ref = oracle_full(spec, t)
+    ob = orc.backward(O=np.concatenate([ref["o_c"], ref["o_x"]]),
+                      LSE=np.concatenate([ref["lse_c"], ref["lse_x"]], axis=1))
+    names = ["dq_c", "dq_x", "dk_c", "dv_c"] + (["dk_x", "dv_x"] if ck else [])
+    gw = dict(zip(OUT_NAMES[4:], g))
+    bw = dict(zip(OUT_NAMES[4:], ob))
+    bideal = None
+    if spec.dtype == "bf16":
+        obr = Oracle(orc.lay, *[f64(u[k]) for k in INPUT_NAMES], *[f64(u[k]) for k in GRAD_NAMES],
+                     operand_rounding="bf16")
+        rb = oracle_full(spec, t, "bf16")
+        bideal = dict(zip(OUT_NAMES[4:], obr.backward(
+            O=np.concatenate([rb["o_c"], rb["o_x"]]),
+            LSE=np.concatenate([rb["lse_c"], rb["lse_x"]], axis=1))))
+    errs.update(compare(spec, {k: gw[k] for k in names}, {k: bw[k] for k in names}, names=names,
+                        label=label, ideal=bideal))
+    assert_parity(spec, errs, label)
