@@ -28,6 +28,11 @@ Long-Context Diffusion Language Model Training":
   their log-sum-exps. A *partial* layout holds only some keys: the result is
   the attention over the visible keys present (a row that sees none gets
   O = 0, LSE = -inf), and ``merge_partials`` combines such results.
+* Packed documents (variable-length training sequences, §5.1; Block Diffusion,
+  named in §2, generates sequences of any length): several documents share
+  one sequence, each starting on a block boundary, with its blocks counted
+  from its own start, and attention never crosses from one document into
+  another. The four rules above then hold inside each document.
 
 Conventions (readings where the pages are silent): blocks are 0-indexed with
 block(p) = floor(p / B) on global clean positions; the scale defaults to
@@ -54,7 +59,7 @@ TOKEN_CAUSAL = 1  # ... or its own clean block up to its own position
 
 __all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens", "query_positions",
            "key_positions", "corrupted_copies", "Oracle", "CLEAN", "CORRUPTED", "BLOCK_CAUSAL", "TOKEN_CAUSAL",
-           "round_bf16", "merge_partials"]
+           "round_bf16", "merge_partials", "documents"]
 
 
 @dataclass(frozen=True)
@@ -72,6 +77,7 @@ class Layout:
     clean_mask: int = BLOCK_CAUSAL
     partial: bool = False  # keys may be missing: attention over the keys present
     corr_keys: bool = True  # the local corrupted keys are present
+    docs: tuple = ()  # start positions of packed documents (empty: one document)
 
     @property
     def G(self) -> int:
@@ -95,7 +101,8 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
            n_corr_blocks: Optional[int] = None,
            corr_block_ids: Optional[Sequence[int]] = None,
            scale: Optional[float] = None, partial: bool = False,
-           clean_mask: int = BLOCK_CAUSAL, corr_keys: bool = True) -> Layout:
+           clean_mask: int = BLOCK_CAUSAL, corr_keys: bool = True,
+           doc_starts: Optional[Sequence[int]] = None) -> Layout:
     """Describe one problem. Without ids, the corrupted blocks are 0..n-1
     (n defaults to the number of clean blocks of the query shard).
     ``clean_mask`` is BLOCK_CAUSAL or TOKEN_CAUSAL.
@@ -103,7 +110,11 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
     Unless ``partial``, the clean K/V buffer must hold every clean key some
     local query sees and the corrupted keys must be present (a ValueError
     otherwise). A partial layout may hold any clean range (``clean_kv_start``
-    > 0 included) and may omit the corrupted keys (``corr_keys=False``)."""
+    > 0 included) and may omit the corrupted keys (``corr_keys=False``).
+
+    ``doc_starts`` packs several documents into the sequence: their start
+    positions, increasing, the first 0, each a multiple of B (a document
+    starts a new block). None or a single 0 is one document."""
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
     if corr_block_ids is None:
@@ -117,6 +128,12 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
         raise ValueError("clean_mask must be BLOCK_CAUSAL or TOKEN_CAUSAL")
     if scale is None or scale <= 0:
         scale = 1.0 / math.sqrt(d)
+    docs = tuple(int(x) for x in (doc_starts or ()))
+    if docs:
+        if docs[0] != 0 or any(b <= a for a, b in zip(docs, docs[1:])) or any(x % B for x in docs):
+            raise ValueError("doc_starts must start at 0, increase and be multiples of B")
+        if len(docs) == 1:
+            docs = ()
     if not partial and not corr_keys:
         raise ValueError("only a partial layout may omit the corrupted keys")
     if not partial:
@@ -128,7 +145,7 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
         if need and (clean_kv_start > 0 or clean_kv_start + n_clean_kv < need):
             raise ValueError("clean K/V buffer does not cover every visible clean key")
     return Layout(B, H, Hkv, d, float(scale), n_clean_q, clean_q_start, n_clean_kv,
-                  clean_kv_start, ids, clean_mask, bool(partial), bool(corr_keys))
+                  clean_kv_start, ids, clean_mask, bool(partial), bool(corr_keys), docs)
 
 
 def query_tokens(lay: Layout):
@@ -169,6 +186,15 @@ def key_positions(lay: Layout):
     return np.concatenate([clean, corr])
 
 
+def documents(lay: Layout, pos):
+    """Index of the packed document holding each sequence position (all 0
+    for a single document)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    if not lay.docs:
+        return np.zeros(pos.shape, np.int64)
+    return np.searchsorted(np.asarray(lay.docs, np.int64), pos, side="right") - 1
+
+
 def corrupted_copies(lay: Layout, n_clean: int):
     """Local corrupted block (copy) index of every token of a query or key
     list with ``n_clean`` clean tokens first; -1 for clean tokens. Two local
@@ -179,7 +205,8 @@ def corrupted_copies(lay: Layout, n_clean: int):
 
 
 def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
-            clean_mask=BLOCK_CAUSAL, corr_keys=True, q_copy=None, k_copy=None):
+            clean_mask=BLOCK_CAUSAL, corr_keys=True, q_copy=None, k_copy=None,
+            q_doc=None, k_doc=None):
     """The four visibility rules of §3.2, broadcast over their arguments.
 
     clean query, block qb     -> clean key of block kb  iff kb < qb, or kb == qb
@@ -190,6 +217,9 @@ def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
     corrupted query, block qb -> corrupted key, block kb iff kb == qb, of its
                                  own copy (``q_copy``/``k_copy``, when a rank
                                  holds two corrupted copies of a block)
+
+    With packed documents (``q_doc``/``k_doc``: the document of each token)
+    a pair is visible only inside one document.
 
     Positions are needed only for TOKEN_CAUSAL. With ``corr_keys`` False the
     corrupted keys are absent (a partial problem) and none is visible.
@@ -204,7 +234,10 @@ def visible(q_stream, q_block, k_stream, k_block, q_pos=None, k_pos=None,
     corr_corr = ~qc & ~kc & (k_block == q_block) & bool(corr_keys)
     if q_copy is not None:
         corr_corr = corr_corr & (k_copy == q_copy)
-    return clean_clean | corr_clean | corr_corr
+    vis = clean_clean | corr_clean | corr_corr
+    if q_doc is not None:
+        vis = vis & (q_doc == k_doc)
+    return vis
 
 
 def _f64(a):
@@ -288,6 +321,7 @@ class Oracle:
         self.ks, self.kb = key_tokens(lay)
         self.qp, self.kp = query_positions(lay), key_positions(lay)
         self.qcp, self.kcp = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
+        self.qd, self.kd = documents(lay, self.qp), documents(lay, self.kp)
 
     # ---------------------------------------------------------------- helpers
     def _mask(self, qidx, kidx=None):
@@ -296,7 +330,8 @@ class Oracle:
         return visible(self.qs[qidx, None], self.qb[qidx, None],
                        self.ks[None, kidx], self.kb[None, kidx],
                        self.qp[qidx, None], self.kp[None, kidx], self.lay.clean_mask,
-                       self.lay.corr_keys, self.qcp[qidx, None], self.kcp[None, kidx])
+                       self.lay.corr_keys, self.qcp[qidx, None], self.kcp[None, kidx],
+                       self.qd[qidx, None], self.kd[None, kidx])
 
     @staticmethod
     def _columns(cols):

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Oracle, corrupted_copies,
-                    key_positions, key_tokens, layout, merge_partials, query_positions,
+                    documents, key_positions, key_tokens, layout, merge_partials, query_positions,
                     query_tokens, visible)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -44,8 +44,10 @@ def full_mask(lay):
     ks, kb = key_tokens(lay)
     qp, kp = query_positions(lay), key_positions(lay)
     qc, kc = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
+    qd, kd = documents(lay, qp), documents(lay, kp)
     return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
-                   kp[None, :], lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :])
+                   kp[None, :], lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :],
+                   qd[:, None], kd[None, :])
 
 
 # --------------------------------------------------------------------- mask
@@ -59,7 +61,8 @@ def read_golden(name):
             if line.startswith("params"):
                 for kv in line.split()[1:]:
                     k, v = kv.split("=")
-                    params[k] = [int(x) for x in v.split(",")] if k == "ids" else int(v)
+                    params[k] = ([int(x) for x in v.split(",")] if k in ("ids", "docs")
+                                 else int(v))
                 continue
             bits = line.split()[1].replace("|", "")
             rows.append([c == "1" for c in bits])
@@ -68,11 +71,13 @@ def read_golden(name):
 
 @pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt",
                                   "mask_token_causal_L8_B2.txt",
-                                  "mask_complementary_L8_B2.txt"])
+                                  "mask_complementary_L8_B2.txt",
+                                  "mask_docs_L12_B2.txt"])
 def test_mask_matches_hand_drawn_fixture(name):
     p, want = read_golden(name)
     lay = layout(p["B"], 1, 1, 4, p["n_clean_q"], p["clean_q_start"], p["n_clean_kv"],
-                 corr_block_ids=p["ids"], clean_mask=p.get("clean_mask", BLOCK_CAUSAL))
+                 corr_block_ids=p["ids"], clean_mask=p.get("clean_mask", BLOCK_CAUSAL),
+                 doc_starts=p.get("docs"))
     got = full_mask(lay)
     assert got.shape == want.shape
     assert np.array_equal(got, want)
@@ -638,3 +643,64 @@ def test_corrupted_copies_of_a_block_are_independent():
         dv_c += r[3]
     np.testing.assert_allclose(g[2], dk_c, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(g[3], dv_c, rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------- packed documents
+def test_packed_document_pair_count_closed_form():
+    """Full documents of lengths L_i packed into one sequence: each is its
+    own block-diffusion problem, L_i (L_i + B) pairs per head (token-causal:
+    L_i (L_i + 1) / 2 + L_i (L_i + B) / 2)."""
+    B = 4
+    lens = [8, 4, 20, 12]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).tolist()
+    L = sum(lens)
+    for cm, per in ((BLOCK_CAUSAL, lambda n: n * (n + B)),
+                    (TOKEN_CAUSAL, lambda n: n * (n + 1) // 2 + n * (n + B) // 2)):
+        lay = layout(B, 1, 1, 4, L, doc_starts=starts, clean_mask=cm)
+        assert int(full_mask(lay).sum()) == sum(per(n) for n in lens)
+
+
+def test_bad_document_starts_are_rejected():
+    for bad in ([4, 8], [0, 6], [0, 8, 8], [0, 12, 8]):
+        with pytest.raises(ValueError):
+            layout(4, 1, 1, 4, 32, doc_starts=bad)
+
+
+@pytest.mark.parametrize("clean_mask", [BLOCK_CAUSAL, TOKEN_CAUSAL])
+def test_packed_documents_equal_independent_problems(clean_mask):
+    """A packed sequence is the documents run one by one: each document alone
+    (positions counted from its own start, its corrupted blocks renumbered
+    from its first block) gives exactly the packed problem's outputs and
+    gradients on its rows and keys. Corrupted blocks include a repeated id
+    (two copies) and a document without any."""
+    B, H, Hkv, d = 2, 4, 2, 8
+    lens = [6, 2, 10, 4]  # multiples of B
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    L = sum(lens)
+    ids = [0, 2, 2, 4, 5, 7, 8]  # document 3 (blocks 9, 10) has none
+    lay = layout(B, H, Hkv, d, L, corr_block_ids=ids, doc_starts=starts.tolist(),
+                 clean_mask=clean_mask)
+    t = make(lay, seed=11)
+    ref = oracle_of(lay, t)
+    O_c, O_x, L_c, L_x = ref.forward()
+    g = ref.backward()
+    x_rows = np.repeat(np.asarray(ids), B) * B  # block position of each corrupted row
+    for s0, n in zip(starts, lens):
+        b0 = s0 // B
+        mine = [i for i in ids if b0 <= i < b0 + n // B]
+        xr = np.flatnonzero((x_rows >= s0) & (x_rows < s0 + n))
+        sub = layout(B, H, Hkv, d, n, corr_block_ids=[i - b0 for i in mine],
+                     clean_mask=clean_mask)
+        c = slice(s0, s0 + n)
+        u = dict(q_c=t["q_c"][c], k_c=t["k_c"][c], v_c=t["v_c"][c], do_c=t["do_c"][c],
+                 q_x=t["q_x"][xr], k_x=t["k_x"][xr], v_x=t["v_x"][xr], do_x=t["do_x"][xr])
+        one = oracle_of(sub, u)
+        o_c, o_x, l_c, l_x = one.forward()
+        np.testing.assert_allclose(O_c[c], o_c, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L_c[:, c], l_c, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(O_x[xr], o_x, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L_x[:, xr], l_x, rtol=0, atol=1e-13)
+        h = one.backward()
+        for full, part, idx in ((g[0], h[0], c), (g[1], h[1], xr), (g[2], h[2], c),
+                                (g[3], h[3], c), (g[4], h[4], xr), (g[5], h[5], xr)):
+            np.testing.assert_allclose(full[idx], part, rtol=0, atol=1e-12)
