@@ -53,6 +53,8 @@ class Problem(ctypes.Structure):
         ("clean_mask", ctypes.c_int32),
         ("partial", ctypes.c_int32),
         ("omit_corr_keys", ctypes.c_int32),
+        ("n_docs", ctypes.c_int32),
+        ("doc_starts", ctypes.POINTER(ctypes.c_int32)),
     ]
 
     @property
@@ -64,13 +66,16 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
             n_clean_kv: Optional[int] = None, clean_kv_start: int = 0,
             n_corr_blocks: Optional[int] = None, corr_block_ids: Optional[Sequence[int]] = None,
             scale: float = 0.0, clean_mask: int = CLEAN_BLOCK_CAUSAL, partial: bool = False,
-            omit_corr_keys: bool = False) -> Problem:
+            omit_corr_keys: bool = False,
+            doc_starts: Optional[Sequence[int]] = None) -> Problem:
     """Problem descriptor. ``dtype`` is F32/BF16, "f32"/"bf16" or a torch dtype.
     Without ids the corrupted blocks are 0..n_corr_blocks-1 (default: as many
     as the clean query shard has blocks). ``clean_mask`` is CLEAN_BLOCK_CAUSAL
     or CLEAN_TOKEN_CAUSAL (what a clean query sees of its own block).
     ``partial``: attention over the keys present only (any clean range, the
-    corrupted keys optional with ``omit_corr_keys``); see include/bdattn.h."""
+    corrupted keys optional with ``omit_corr_keys``); see include/bdattn.h.
+    ``doc_starts`` packs documents into the sequence: their start positions
+    (the first 0, increasing, multiples of B); attention stays inside each."""
     dt = _dtype_code(dtype)
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
@@ -91,6 +96,13 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
             n_corr_blocks = n_clean_q // B if B > 0 else 0
         p.n_corr_blocks = n_corr_blocks
         p.corr_block_ids = None
+    if doc_starts is not None and len(doc_starts) > 0:
+        docs = np.ascontiguousarray(np.asarray(doc_starts, dtype=np.int32))
+        p._docs = docs  # keep alive
+        p.n_docs = len(docs)
+        p.doc_starts = docs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        p.n_docs, p.doc_starts = 0, None
     return p
 
 
@@ -101,7 +113,8 @@ def from_spec(spec) -> Problem:
                    spec.n_corr_blocks, spec.corr_block_ids,
                    clean_mask=getattr(spec, "clean_mask", CLEAN_BLOCK_CAUSAL),
                    partial=getattr(spec, "partial", False),
-                   omit_corr_keys=getattr(spec, "omit_corr_keys", False))
+                   omit_corr_keys=getattr(spec, "omit_corr_keys", False),
+                   doc_starts=getattr(spec, "doc_starts", None))
 
 
 def _dtype_code(dtype) -> int:

@@ -51,6 +51,9 @@ std::string plan_key(const bdattn::Problem& P) {
                           P.partial, P.corr_keys};
   k.append((const char*)head, sizeof(head));
   k.append((const char*)P.ids.data(), P.ids.size() * sizeof(int32_t));
+  const int32_t nd = int32_t(P.docs.size());
+  k.append((const char*)&nd, sizeof(nd));
+  k.append((const char*)P.docs.data(), P.docs.size() * sizeof(int32_t));
   return k;
 }
 
@@ -83,7 +86,7 @@ int check_ptr(const void* p, int64_t elems, const char* name) {
   return BDATTN_OK;
 }
 
-// Copy the corrupted block ids and the work lists (staged once in pinned host
+// Copy the corrupted block ids, the document table and the work lists (staged once in pinned host
 // memory) into the workspace head, asynchronously on the caller's stream.
 int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t s) {
   const size_t bytes = w.staged;
@@ -97,6 +100,7 @@ int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t 
       memset(h, 0, bytes);
       const bdattn::Plan& plan = e->plan;
       memcpy((char*)h + w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t));
+      memcpy((char*)h + w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan));
       memcpy((char*)h + w.q_items, plan.fwd.data(), w.q_items_bytes);
       if (pass == 1) memcpy((char*)h + w.kv_items, plan.bwd.data(), w.kv_items_bytes);
       e->staged[pass] = h;
@@ -275,6 +279,7 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
   a.o_c = o_c; a.o_x = o_x; a.lse_c = lse_c; a.lse_x = lse_x;
   a.ids = (const int32_t*)(ws + w.ids);
+  a.docs = P.spans.empty() ? nullptr : (const BdDocSpan*)(ws + w.spans);
   a.items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_items = int32_t(plan->fwd.size());
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
@@ -326,6 +331,7 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.o_c = o_c; a.o_x = o_x; a.do_c = do_c; a.do_x = do_x; a.lse_c = lse_c; a.lse_x = lse_x;
   a.dq_c = dq_c; a.dq_x = dq_x; a.dk_c = dk_c; a.dv_c = dv_c; a.dk_x = dk_x; a.dv_x = dv_x;
   a.ids = (const int32_t*)(ws + w.ids);
+  a.docs = P.spans.empty() ? nullptr : (const BdDocSpan*)(ws + w.spans);
   a.q_items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_q_items = int32_t(plan->fwd.size());
   a.kv_items = (const bdattn::BwdItem*)(ws + w.kv_items);

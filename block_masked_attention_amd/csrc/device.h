@@ -227,10 +227,13 @@ struct RowSpace {
   bool token_causal;
   int32_t kv0, nkv;  // the clean buffer holds global positions [kv0, kv0 + nkv)
   bool corr_keys;    // the local corrupted keys are present
+  const BdDocSpan* docs;  // document of each global block (nullptr: one document)
 };
 __device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, const RowSpace& rs) {
-  const BdRowBounds r = stream == 0 ? bd_clean_row(rs.clean_q_start + row, rs.B, rs.token_causal)
-                                    : bd_corr_row(row, rs.ids[row / rs.B], rs.B);
+  BdRowBounds r = stream == 0 ? bd_clean_row(rs.clean_q_start + row, rs.B, rs.token_causal)
+                              : bd_corr_row(row, rs.ids[row / rs.B], rs.B);
+  if (rs.docs)  // the document of the row's block (a corrupted row's: its id's)
+    r = bd_in_document(r, rs.docs[stream == 0 ? (rs.clean_q_start + row) / rs.B : rs.ids[row / rs.B]]);
   return bd_in_buffer(r, rs.kv0, rs.nkv, rs.corr_keys);
 }
 

@@ -41,16 +41,18 @@ using namespace dev;
 // Query-tile work item shared by the forward and the dQ kernel: `rows`
 // consecutive rows of one stream for Gw q heads of one KV group; wave w covers
 // 32 rows of one head. The keys are swept in tiles of TK staged through LDS
-// (K and V, row-major, double buffered): the clean prefix [0, last cb), then,
-// for corrupted rows, the local corrupted keys of their blocks.
+// (K and V, row-major, double buffered): the clean keys [first clo, last cb),
+// then, for corrupted rows, the local corrupted keys of their blocks. Clean
+// tiles [jf0, jf1) lie inside every row's clean interval and skip the mask;
+// without packed documents (DOCS false) every clo is 0 and j0 = jf0 = 0.
 // ======================================================================
 struct QTile {
-  int stream, head, kvh, n_rows, row0, my_row, crow, n_ct, n_xt, xlo, full_end;
+  int stream, head, kvh, n_rows, row0, my_row, crow, n_ct, n_xt, xlo, j0, jf0, jf1;
   bool row_ok;
   BdRowBounds rb;
 };
 
-template <int TK>
+template <int TK, bool DOCS>
 __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, int Gw, int H,
                                         int Hkv, int n_clean_q, int n_corr, const RowSpace& rs,
                                         int wave, int lq) {
@@ -68,8 +70,11 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
   q.rb = row_bounds(q.stream, q.crow, rs);
   const BdRowBounds first = row_bounds(q.stream, q.row0, rs);
   const BdRowBounds last = row_bounds(q.stream, row_end - 1, rs);
-  q.full_end = first.cb / TK * TK;  // clean tiles below need no mask
-  q.n_ct = (last.cb + TK - 1) / TK;
+  q.j0 = DOCS ? first.clo / TK : 0;
+  // (with documents, rows that see no clean key at all sweep none)
+  q.n_ct = DOCS && last.cb <= first.clo ? q.j0 : (last.cb + TK - 1) / TK;
+  q.jf0 = DOCS ? min(q.n_ct, max(q.j0, (last.clo + TK - 1) / TK)) : 0;
+  q.jf1 = max(q.jf0, min(q.n_ct, first.cb / TK));
   q.xlo = q.stream ? first.xlo : 0;
   q.n_xt = q.stream ? (last.xhi - first.xlo + TK - 1) / TK : 0;
   return q;
@@ -79,7 +84,7 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
 // Forward. Per key tile: S^T = K Q^T (keys x queries, so each lane owns one
 // query row); mask only on tiles that need it; online softmax; O^T += V^T P^T.
 // ======================================================================
-template <bool BF16, int D>
+template <bool BF16, int D, bool DOCS>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   using E = Elem<BF16>;
@@ -95,8 +100,8 @@ void fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
-                    a.n_clean_kv, a.corr_keys != 0};
-  const QTile q = q_tile<TK>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
+                    a.n_clean_kv, a.corr_keys != 0, DOCS ? a.docs : nullptr};
+  const QTile q = q_tile<TK, DOCS>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
                              a.n_clean_q, a.n_corr, rs, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
@@ -159,7 +164,8 @@ void fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         if (MASK) {
           const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
+          const bool vis = cl ? (DOCS ? bd_sees_clean(q.rb, key) : key < q.rb.cb)
+                              : bd_sees_corr(q.rb, key);
           s[mb][i] = vis ? s[mb][i] : kNegInf;
         }
         mx = fmaxf(mx, s[mb][i]);
@@ -214,13 +220,13 @@ void fwd_kernel(FwdArgs a) {
     }
     if (j < j1) body(mask_tag, Int<0>{}, j);
   };
-  if (n_tiles > 0) fetch(0, 0);
+  if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
   vm_drain();
   __syncthreads();
-  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
-  const int j_full = min(q.n_ct, q.full_end / TK);
-  sweep(std::false_type{}, 0, j_full);
-  sweep(std::true_type{}, j_full, n_tiles);
+  // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
+  if constexpr (DOCS) sweep(std::true_type{}, q.j0, q.jf0);
+  sweep(std::false_type{}, q.jf0, q.jf1);
+  sweep(std::true_type{}, q.jf1, n_tiles);
 
   const float lt = l + __shfl_xor(l, 32);
   if (q.row_ok) {
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* oa_, const float
 // D are scalars); P^T = exp2(S^T c - LSE2); dS^T = P^T (dP^T - D);
 // dQ^T += K^T dS^T with K^T read transposed from the K tile.
 // ======================================================================
-template <bool BF16, int D>
+template <bool BF16, int D, bool DOCS>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<BF16>;
@@ -344,8 +350,8 @@ void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, hf = lane >> 5;
   const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
-                    a.n_clean_kv, a.corr_keys != 0};
-  const QTile q = q_tile<TK>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
+                    a.n_clean_kv, a.corr_keys != 0, DOCS ? a.docs : nullptr};
+  const QTile q = q_tile<TK, DOCS>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
                              a.n_clean_q, a.n_corr, rs, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
@@ -413,7 +419,8 @@ void bwd_dq_kernel(BwdArgs a) {
         float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
         if (MASK) {
           const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool vis = cl ? bd_sees_clean(q.rb, key) : bd_sees_corr(q.rb, key);
+          const bool vis = cl ? (DOCS ? bd_sees_clean(q.rb, key) : key < q.rb.cb)
+                              : bd_sees_corr(q.rb, key);
           p = vis ? p : 0.f;
         }
         ds[i] = p * (dp[i] + ndrow);
@@ -440,13 +447,13 @@ void bwd_dq_kernel(BwdArgs a) {
     }
     if (j < j1) body(mask_tag, Int<0>{}, j);
   };
-  if (n_tiles > 0) fetch(0, 0);
+  if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
   vm_drain();
   __syncthreads();
-  // tiles [0, j_full) lie inside every row's clean prefix and skip the mask
-  const int j_full = min(q.n_ct, q.full_end / TK);
-  sweep(std::false_type{}, 0, j_full);
-  sweep(std::true_type{}, j_full, n_tiles);
+  // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
+  if constexpr (DOCS) sweep(std::true_type{}, q.j0, q.jf0);
+  sweep(std::false_type{}, q.jf0, q.jf1);
+  sweep(std::true_type{}, q.jf1, n_tiles);
 
   if (q.row_ok) {
     T* out = (T*)(q.stream ? a.dq_x : a.dq_c) + ((int64_t)q.my_row * a.H + q.head) * D;
@@ -464,8 +471,10 @@ void bwd_dq_kernel(BwdArgs a) {
 template <bool BF16, int D>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  if (a.n_items > 0)
-    hipLaunchKernelGGL((fwd_kernel<BF16, D>), dim3(a.n_items), dim3(FWD_WAVES * 64), 0, s, a);
+  if (a.n_items > 0 && a.docs)
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, true>), dim3(a.n_items), dim3(FWD_WAVES * 64), 0, s, a);
+  else if (a.n_items > 0)
+    hipLaunchKernelGGL((fwd_kernel<BF16, D, false>), dim3(a.n_items), dim3(FWD_WAVES * 64), 0, s, a);
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   return hipGetLastError();
 }
@@ -484,8 +493,10 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
                        st ? a.d_x : a.d_c, st ? a.l2_x : a.l2_c, n, n_pad, a.H);
   }
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  if (a.n_q_items > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D>), dim3(a.n_q_items), dim3(FWD_WAVES * 64), 0, s, a);
+  if (a.n_q_items > 0 && a.docs)
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true>), dim3(a.n_q_items), dim3(FWD_WAVES * 64), 0, s, a);
+  else if (a.n_q_items > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false>), dim3(a.n_q_items), dim3(FWD_WAVES * 64), 0, s, a);
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   if (ev) (void)hipEventRecord(ev[1].start, s);
   hipError_t e = hipGetLastError();

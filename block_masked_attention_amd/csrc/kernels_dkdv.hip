@@ -68,7 +68,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   //     in (k0/B, kb] finds it (a few blocks: the tile spans BWD_TK keys,
   //     and a repeated id is another copy of the same block);
   //   corrupted key of local block kb: the corrupted rows of that block (its
-  //     own copy only).
+  //     own copy only);
+  //   packed documents: no row after the end of the key's document.
   int lo_c = 0, hi_c = 0, lo_x = 0, hi_x = 0;
   if (key_ok) {
     // clean: global position and block (buffer row 0 is position
@@ -86,6 +87,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
       while (j < n_blk && a.ids[j] <= key_blk) ++j;
       lo_x = j * a.B;
       hi_x = a.n_corr;
+      if (a.docs) {
+        const BdDocSpan sp = a.docs[key_blk];
+        hi_c = (int)min((int64_t)a.n_clean_q, max((int64_t)0, (int64_t)sp.hi - a.clean_q_start));
+        hi_x = sp.xhi;
+      }
     }
   }
 
@@ -212,7 +218,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int n_rows = st.qs ? a.n_corr : a.n_clean_q;
     // visibility of (query row, this lane's key) on tiles that need the mask
     const int lo = st.qs ? lo_x : lo_c, hi = st.qs ? hi_x : hi_c;
-    auto sees = [&](int row) -> bool __attribute__((always_inline)) { return row >= lo && row < hi; };
+    auto sees = [&](int row) __attribute__((always_inline)) { return row >= lo && row < hi; };
     f32x16 sb[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) sb[mb] = zero16();

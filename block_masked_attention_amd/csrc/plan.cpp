@@ -20,9 +20,30 @@ int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
 
 // Bounds of a local row in terms of the keys present (clean buffer indices).
 BdRowBounds row_bounds(const Problem& P, int stream, int32_t row) {
-  const BdRowBounds r = stream == 0 ? bd_clean_row(P.clean_q_start + row, P.B, P.token_causal != 0)
-                                    : bd_corr_row(row, P.ids[row / P.B], P.B);
+  const int32_t blk = stream == 0 ? (P.clean_q_start + row) / P.B : P.ids[row / P.B];
+  BdRowBounds r = stream == 0 ? bd_clean_row(P.clean_q_start + row, P.B, P.token_causal != 0)
+                              : bd_corr_row(row, blk, P.B);
+  if (!P.spans.empty()) r = bd_in_document(r, P.spans[blk]);
   return bd_in_buffer(r, P.clean_kv_start, P.n_clean_kv, P.corr_keys != 0);
+}
+
+// Document entry of every global block a row or key can name: document start,
+// end, and the local corrupted rows before the end.
+void build_spans(Problem* P) {
+  int64_t nb = (int64_t(P->clean_q_start) + P->n_clean_q) / P->B;
+  nb = std::max<int64_t>(nb, (int64_t(P->clean_kv_start) + P->n_clean_kv) / P->B);
+  if (!P->ids.empty()) nb = std::max<int64_t>(nb, int64_t(P->ids.back()) + 1);
+  P->spans.assign(size_t(nb), BdDocSpan{0, 0, 0, 0});
+  size_t d = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t pos = b * P->B;
+    while (d + 1 < P->docs.size() && P->docs[d + 1] <= pos) ++d;
+    BdDocSpan& s = P->spans[size_t(b)];
+    s.lo = P->docs[d];
+    s.hi = d + 1 < P->docs.size() ? P->docs[d + 1] : int32_t(kMax32);
+    const int64_t end_blk = d + 1 < P->docs.size() ? P->docs[d + 1] / P->B : kMax32;
+    s.xhi = int32_t(std::lower_bound(P->ids.begin(), P->ids.end(), end_blk) - P->ids.begin()) * P->B;
+  }
 }
 
 }  // namespace
@@ -111,6 +132,24 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   } else {
     std::iota(P.ids.begin(), P.ids.end(), 0);
   }
+  if (p->n_docs < 0 || (p->n_docs > 0 && !p->doc_starts)) {
+    *msg = "n_docs must be >= 0, with doc_starts given when > 0";
+    return BDATTN_ERR_INVALID_ARG;
+  }
+  for (int32_t i = 0; i < p->n_docs; ++i) {
+    const int32_t v = p->doc_starts[i];
+    if ((i == 0 && v != 0) || (i > 0 && v <= P.docs.back())) {
+      *msg = "doc_starts must start at 0 and increase";
+      return BDATTN_ERR_INVALID_ARG;
+    }
+    if (v % P.B) {
+      *msg = "doc_starts must be multiples of B";
+      return BDATTN_ERR_SHAPE;
+    }
+    P.docs.push_back(v);
+  }
+  if (P.docs.size() > 1) build_spans(&P);
+  else P.docs.clear();
   if (P.partial) {  // any clean range: the attention over the keys present
     *out = std::move(P);
     return BDATTN_OK;
@@ -161,6 +200,8 @@ WsLayout workspace_layout(const Problem& P, int pass) {
   size_t off = 0;
   w.ids = off;
   off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, P.ids.size()), WS_ALIGN);
+  w.spans = off;
+  off = align_up(off + sizeof(BdDocSpan) * P.spans.size(), WS_ALIGN);
   w.q_items = off;
   w.q_items_bytes = n_q_items(P) * sizeof(FwdItem);
   off = align_up(off + std::max<size_t>(1, w.q_items_bytes), WS_ALIGN);
@@ -205,9 +246,13 @@ void build_plan(const Problem& P, Plan* plan) {
       for (int32_t t = 0; t * int64_t(R) < n; ++t) {
         const int32_t r0 = t * R, r1 = std::min<int32_t>(n, r0 + R);
         BdRowBounds first = row_bounds(P, s, r0), last = row_bounds(P, s, r1 - 1);
-        const int32_t full_end = first.cb / FWD_TK * FWD_TK;  // tiles below are unmasked
-        const int32_t nct = ceil_div(last.cb, FWD_TK);
-        int64_t cost = nct, masked = nct - full_end / FWD_TK;
+        // clean key tiles [j0, nct) are swept; [jf0, jf1) need no mask (the
+        // kernels' split of the same bounds)
+        const int32_t j0 = first.clo / FWD_TK;
+        const int32_t nct = last.cb <= first.clo ? j0 : ceil_div(last.cb, FWD_TK);
+        const int32_t jf0 = std::min(nct, std::max(j0, ceil_div(last.clo, FWD_TK)));
+        const int32_t jf1 = std::max(jf0, std::min(nct, first.cb / FWD_TK));
+        int64_t cost = nct - j0, masked = (jf0 - j0) + (nct - jf1);
         if (s == 1) {
           const int32_t nxt = ceil_div(last.xhi - first.xlo, FWD_TK);
           cost += nxt;
@@ -248,29 +293,46 @@ void build_plan(const Problem& P, Plan* plan) {
       int32_t c0 = std::min<int32_t>(P.n_clean_q, std::max<int32_t>(0, first_row_pos - P.clean_q_start));
       int32_t j = int32_t(std::upper_bound(P.ids.begin(), P.ids.end(), kb) - P.ids.begin());
       int32_t x0 = j * P.B;
+      // packed documents: no row after the end of the last key's document
+      // sees the tile
+      int32_t c1 = P.n_clean_q, x1 = nx;
+      bool one_doc = true;
+      if (!P.spans.empty()) {
+        const BdDocSpan& first = P.spans[size_t(g0 / P.B)];
+        const BdDocSpan& last = P.spans[size_t((P.clean_kv_start + k1 - 1) / P.B)];
+        c1 = int32_t(std::min<int64_t>(P.n_clean_q,
+                                       std::max<int64_t>(0, int64_t(last.hi) - P.clean_q_start)));
+        c1 = std::max(c0, c1);
+        x1 = std::max(x0, last.xhi);
+        one_doc = first.hi == last.hi;
+      }
       // a q tile needs the mask unless it lies inside the swept rows and its
       // first row sees the whole key tile (row bounds are nondecreasing, so
-      // the unmasked tiles are the top ones of each stream)
-      int64_t qt = qtiles(c0, P.n_clean_q) + qtiles(x0, nx), masked = 0;
-      int32_t cf = P.n_clean_q, xf = nx;
-      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r < P.n_clean_q; r += BWD_TQ) {
-        if (r < c0 || row_bounds(P, 0, r).cb < k1 || k1 - k0 < BWD_TK) {
+      // the unmasked tiles are the top ones of each stream); with documents,
+      // only when every key of the tile is in one document and the top tile
+      // ends at that document's end or the stream's
+      const bool c_top = one_doc && (c1 == P.n_clean_q || c1 % BWD_TQ == 0);
+      const bool x_top = one_doc && (x1 == nx || x1 % BWD_TQ == 0);
+      int64_t qt = qtiles(c0, c1) + qtiles(x0, x1), masked = 0;
+      int32_t cf = c1, xf = x1;
+      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r < c1; r += BWD_TQ) {
+        if (!c_top || r < c0 || row_bounds(P, 0, r).cb < k1 || k1 - k0 < BWD_TK) {
           ++masked;
         } else {
           cf = r;
           break;
         }
       }
-      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r < nx; r += BWD_TQ) {
-        if (r < x0 || row_bounds(P, 1, r).cb < k1 || k1 - k0 < BWD_TK) {
+      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r < x1; r += BWD_TQ) {
+        if (!x_top || r < x0 || row_bounds(P, 1, r).cb < k1 || k1 - k0 < BWD_TK) {
           ++masked;
         } else {
           xf = r;
           break;
         }
       }
-      BwdItem it{kt, 0, c0, P.n_clean_q, x0, nx, cf, xf};
-      tiles.push_back({kt, 0, it, (P.n_clean_q - c0) + int64_t(nx - x0), qt, masked});
+      BwdItem it{kt, 0, c0, c1, x0, x1, cf, xf};
+      tiles.push_back({kt, 0, it, (c1 - c0) + int64_t(x1 - x0), qt, masked});
     }
     for (int32_t kt = 0; P.corr_keys && kt * int64_t(BWD_TK) < nx; ++kt) {
       const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(nx, k0 + BWD_TK);
@@ -296,10 +358,13 @@ void build_plan(const Problem& P, Plan* plan) {
 
 int64_t visible_pairs(const Problem& P) {
   int64_t pairs = 0;
-  for (int32_t r = 0; r < P.n_clean_q; ++r) pairs += row_bounds(P, 0, r).cb;
+  for (int32_t r = 0; r < P.n_clean_q; ++r) {
+    const BdRowBounds b = row_bounds(P, 0, r);
+    pairs += b.cb - b.clo;
+  }
   for (int32_t r = 0; r < P.n_corr(); ++r) {
-    BdRowBounds b = row_bounds(P, 1, r);
-    pairs += int64_t(b.cb) + (b.xhi - b.xlo);
+    const BdRowBounds b = row_bounds(P, 1, r);
+    pairs += int64_t(b.cb - b.clo) + (b.xhi - b.xlo);
   }
   return pairs;
 }

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BDATTN_VERSION 2
+#define BDATTN_VERSION 3
 
 typedef enum {
   BDATTN_OK = 0,
@@ -123,6 +123,16 @@ typedef struct {
    * dK/dV of the keys present are complete. */
   int32_t partial;
   int32_t omit_corr_keys; /* 1: the local corrupted keys are absent (partial only) */
+  /* Packed documents: several variable-length sequences in one problem (the
+   * paper trains on variable sequence lengths, §5.1). HOST array of n_docs
+   * start positions, increasing, the first 0, each a multiple of B; document
+   * i holds the global positions [doc_starts[i], doc_starts[i+1]), the last
+   * one runs to the end. Blocks are counted from each document's start and
+   * no (query, key) pair crosses two documents; a corrupted block belongs to
+   * the document holding its id. n_docs <= 1 or NULL: one document. Read
+   * during the call only. */
+  int32_t n_docs;
+  const int32_t* doc_starts;
 } bdattn_problem;
 
 /* BDATTN_VERSION of the loaded library. */
@@ -144,7 +154,9 @@ const char* bdattn_last_error(void);
  * position below 2^31; coverage unless partial: clean_kv_start == 0 and
  * n_clean_kv reaches the end of the last block of the query shard and the
  * start of the last local corrupted block (BDATTN_ERR_COVERAGE); partial:
- * clean_kv_start a multiple of B (BDATTN_ERR_SHAPE). */
+ * clean_kv_start a multiple of B (BDATTN_ERR_SHAPE); n_docs >= 0, and with
+ * n_docs > 0 doc_starts non-NULL, starting at 0, increasing and below 2^31
+ * (BDATTN_ERR_INVALID_ARG), each a multiple of B (BDATTN_ERR_SHAPE). */
 int bdattn_validate(const bdattn_problem* p);
 
 /* Bytes of workspace needed by bdattn_fwd (pass 0) or bdattn_bwd (pass 1).

@@ -7,7 +7,8 @@ from oracle import layout
 def oracle_layout(spec):
     return layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start,
                   spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks,
-                  spec.corr_block_ids, clean_mask=spec.clean_mask)
+                  spec.corr_block_ids, clean_mask=spec.clean_mask,
+                  doc_starts=getattr(spec, "doc_starts", None))
 
 
 def f64(t):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import block_masked_attention_amd as bd
-from oracle import (corrupted_copies, key_positions, key_tokens, layout, query_positions,
+from oracle import (corrupted_copies, documents, key_positions, key_tokens, layout, query_positions,
                     query_tokens, visible)
 from tests.test_oracle import read_golden
 from workloads import CONFIGS
@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert bd.version() == 2
+    assert bd.version() == 3
 
 
 def test_status_strings():
@@ -42,15 +42,18 @@ def oracle_mask(p):
     ids = None
     if p.corr_block_ids:
         ids = [p.corr_block_ids[i] for i in range(p.n_corr_blocks)]
+    docs = [p.doc_starts[i] for i in range(p.n_docs)] if p.n_docs else None
     lay = layout(p.B, p.H, p.Hkv, p.d, p.n_clean_q, p.clean_q_start, p.n_clean_kv,
                  p.clean_kv_start, p.n_corr_blocks, ids, clean_mask=p.clean_mask,
-                 partial=bool(p.partial), corr_keys=not p.omit_corr_keys)
+                 partial=bool(p.partial), corr_keys=not p.omit_corr_keys, doc_starts=docs)
     qs, qb = query_tokens(lay)
     ks, kb = key_tokens(lay)
     qp, kp = query_positions(lay), key_positions(lay)
     qc, kc = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
+    qd, kd = documents(lay, qp), documents(lay, kp)
     return visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None],
-                   kp[None, :], lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :])
+                   kp[None, :], lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :],
+                   qd[:, None], kd[None, :])
 
 
 CASES = [
@@ -81,8 +84,25 @@ CASES_PARTIAL = [
     dict(B=32, n_clean_q=1056, n_clean_kv=384, clean_kv_start=320, partial=True),
 ]
 
+# packed documents: block-aligned starts, documents of one block, documents
+# not aligned to the kernels' tiles, shares, token-causal, partial ranges
+CASES_DOCS = [
+    dict(B=2, n_clean_q=12, corr_block_ids=[0, 1, 2, 3, 5], doc_starts=[0, 4, 6]),
+    dict(B=32, n_clean_q=1024, doc_starts=[0, 96, 160, 192, 512, 544]),
+    dict(B=32, n_clean_q=1024, doc_starts=[0, 96, 160, 192, 512, 544],
+         clean_mask=bd.CLEAN_TOKEN_CAUSAL),
+    dict(B=16, n_clean_q=256, clean_q_start=256, n_clean_kv=512,
+         corr_block_ids=[3, 5, 5, 17, 18, 30], doc_starts=[0, 80, 288, 400]),
+    dict(B=1, n_clean_q=200, doc_starts=[0, 1, 2, 70, 71, 199]),
+    dict(B=64, n_clean_q=1024, doc_starts=list(range(0, 1024, 64))),
+    dict(B=16, n_clean_q=512, n_clean_kv=160, clean_kv_start=192, partial=True,
+         doc_starts=[0, 208, 320]),
+    dict(B=16, n_clean_q=512, n_clean_kv=128, clean_kv_start=128, partial=True,
+         omit_corr_keys=True, doc_starts=[0, 144, 400]),
+]
 
-@pytest.mark.parametrize("case", CASES + CASES_TC + CASES_PARTIAL)
+
+@pytest.mark.parametrize("case", CASES + CASES_TC + CASES_PARTIAL + CASES_DOCS)
 def test_mask_render_matches_oracle(case):
     p = bd.problem(H=2, Hkv=1, d=32, dtype="bf16", **case)
     assert bd.validate(p) == 0
@@ -94,12 +114,14 @@ def test_mask_render_matches_oracle(case):
 
 @pytest.mark.parametrize("name", ["mask_L8_B2.txt", "mask_share_B2.txt",
                                   "mask_token_causal_L8_B2.txt",
-                                  "mask_complementary_L8_B2.txt"])
+                                  "mask_complementary_L8_B2.txt",
+                                  "mask_docs_L12_B2.txt"])
 def test_mask_render_matches_hand_drawn_fixture(name):
     prm, want = read_golden(name)
     p = bd.problem(prm["B"], 1, 1, 32, "f32", prm["n_clean_q"], prm["clean_q_start"],
                    prm["n_clean_kv"], corr_block_ids=prm["ids"],
-                   clean_mask=prm.get("clean_mask", bd.CLEAN_BLOCK_CAUSAL))
+                   clean_mask=prm.get("clean_mask", bd.CLEAN_BLOCK_CAUSAL),
+                   doc_starts=prm.get("docs"))
     assert np.array_equal(bd.mask_render(p), want)
 
 
@@ -151,6 +173,10 @@ def _p(**kw):
     (dict(clean_mask=-1), -1),
     (dict(omit_corr_keys=True), -1),  # only a partial problem may omit them
     (dict(partial=True, clean_kv_start=2, n_clean_kv=8), -2),
+    (dict(doc_starts=[4, 8]), -1),
+    (dict(doc_starts=[0, 8, 8]), -1),
+    (dict(doc_starts=[0, 12, 8]), -1),
+    (dict(doc_starts=[0, 6]), -2),
 ])
 def test_validation_error_codes(kw, code):
     p = _p(**kw)
@@ -161,6 +187,12 @@ def test_validation_error_codes(kw, code):
 def test_unknown_dtype_and_null_problem():
     p = _p()
     p.dtype = 7
+    assert bd.validate(p) == -1
+    p = _p()
+    p.n_docs = -1
+    assert bd.validate(p) == -1
+    p = _p()
+    p.n_docs = 2  # no array
     assert bd.validate(p) == -1
     assert bd.lib().bdattn_validate(None) == -1
 
@@ -199,7 +231,7 @@ def test_plan_covers_every_visible_tile():
     """The forward work list visits, for every query row tile, exactly the key
     tiles holding a visible key; the backward list has one item per key tile
     and KV head (so every dK/dV row is written)."""
-    for case in CASES + CASES_TC + CASES_PARTIAL:
+    for case in CASES + CASES_TC + CASES_PARTIAL + CASES_DOCS:
         p = bd.problem(H=4, Hkv=2, d=32, dtype="bf16", **case)
         st = bd.plan_stats(p)
         M = bd.mask_render(p)
@@ -214,8 +246,8 @@ def test_plan_covers_every_visible_tile():
                 vis = rows.any(0)
                 cl = np.flatnonzero(vis[:nkv])
                 ntiles = 0
-                if len(cl):
-                    ntiles += (cl.max() // 64) + 1  # clean keys swept from 0
+                if len(cl):  # clean keys swept from 0 (documents: from the first one visible)
+                    ntiles += (cl.max() // 64) + 1 - (cl.min() // 64 if p.n_docs else 0)
                 xk = np.flatnonzero(vis[nkv:])
                 if len(xk):
                     ntiles += (xk.max() - xk.min()) // 64 + 1
@@ -223,6 +255,9 @@ def test_plan_covers_every_visible_tile():
                 want_tiles += ntiles
         heads_groups = int(p.H) // Gw
         assert st["fwd_items"] == want_items * heads_groups
-        assert st["fwd_tiles"] == want_tiles * heads_groups
+        if p.n_docs:  # an item may start its sweep at an earlier document's first key
+            assert want_tiles * heads_groups <= st["fwd_tiles"] <= (want_tiles + want_items) * heads_groups
+        else:
+            assert st["fwd_tiles"] == want_tiles * heads_groups
         kt = -(-nkv // 128) + (0 if p.omit_corr_keys else -(-nx // 128))
         assert st["bwd_items"] == kt * int(p.Hkv)

@@ -295,6 +295,52 @@ def _random_specs(n=16, seed=2024):
 
 RANDOM = _random_specs()
 
+# packed documents (block-aligned starts): documents not aligned to the
+# kernels' 64- and 128-row tiles, one-block documents, aligned documents (the
+# backward's unmasked tiles), shares and complementary copies
+DOCS = [
+    ("docs_bf16_unaligned_G4", dict(L=2048, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                    doc_starts=[0, 96, 160, 192, 1024, 1056])),
+    ("docs_bf16_aligned_B64", dict(L=1024, B=64, H=4, Hkv=1, d=128, dtype="bf16", std=0.5,
+                                   doc_starts=[0, 256, 512, 768])),
+    ("docs_bf16_token_causal", dict(L=1024, B=32, H=4, Hkv=2, d=128, dtype="bf16", std=0.5,
+                                    doc_starts=[0, 64, 448, 480], clean_mask=1)),
+    ("docs_f32_share_copies", dict(L=512, B=16, H=4, Hkv=2, d=32, dtype="f32",
+                                   n_clean_q=256, clean_q_start=256, n_clean_kv=512,
+                                   corr_block_ids=[3, 5, 5, 17, 18, 18, 30],
+                                   doc_starts=[0, 80, 288, 400])),
+    ("docs_f32_B1", dict(L=200, B=1, H=2, Hkv=1, d=32, dtype="f32",
+                         doc_starts=[0, 1, 2, 70, 71, 199])),
+    ("docs_bf16_d32_one_block_each", dict(L=512, B=32, H=6, Hkv=2, d=32, dtype="bf16", std=0.5,
+                                          doc_starts=list(range(0, 512, 32)))),
+]
+
+
+@pytest.mark.parametrize("label,kw", DOCS, ids=[c[0] for c in DOCS])
+def test_packed_documents(label, kw):
+    full_parity(small_spec(name=label, seed=zlib.crc32(label.encode()) % 10000, **kw), label)
+
+
+def _random_doc_specs(n=8, seed=77):
+    """Seeded random packed problems: a random problem (as above) whose
+    sequence is cut into random block-aligned documents."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i, (label, kw) in enumerate(_random_specs(n, seed)):
+        nb = kw["L"] // kw["B"]
+        cuts = sorted(set(rng.choice(np.arange(1, max(2, nb)), size=int(rng.integers(1, 6))).tolist()))
+        kw = dict(kw, doc_starts=[0] + [c * kw["B"] for c in cuts if c < nb])
+        out.append((label.replace("rand", "randdocs"), kw))
+    return out
+
+
+RANDOM_DOCS = _random_doc_specs()
+
+
+@pytest.mark.parametrize("label,kw", RANDOM_DOCS, ids=[r[0] for r in RANDOM_DOCS])
+def test_random_packed_documents(label, kw):
+    full_parity(small_spec(name=label, seed=zlib.crc32(label.encode()) % 10000, **kw), label)
+
 
 @pytest.mark.parametrize("label,kw", RANDOM, ids=[r[0] for r in RANDOM])
 def test_random_small_problems(label, kw):

@@ -32,6 +32,8 @@ CASES = [
     ("bf16_split_share", dict(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5,
                               n_clean_q=128, clean_q_start=384, n_clean_kv=512,
                               corr_block_ids=list(range(3, 16, 4)))),
+    ("bf16_split_docs", dict(L=1024, B=32, H=4, Hkv=2, d=128, dtype="bf16", std=0.5,
+                             doc_starts=[0, 96, 320, 352, 704])),
 ]
 
 
@@ -51,7 +53,8 @@ def pieces(spec):
 def part_problem(spec, lo, hi, ck):
     return bd.problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
                       spec.clean_q_start, hi - lo, lo, spec.n_corr_blocks, spec.corr_block_ids,
-                      clean_mask=spec.clean_mask, partial=True, omit_corr_keys=not ck)
+                      clean_mask=spec.clean_mask, partial=True, omit_corr_keys=not ck,
+                      doc_starts=spec.doc_starts)
 
 
 def part_inputs(t, lo, hi):
@@ -63,7 +66,7 @@ def part_inputs(t, lo, hi):
 def part_oracle(spec, t, lo, hi, ck):
     lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start, hi - lo,
                  lo, corr_block_ids=spec.corr_block_ids, n_corr_blocks=spec.n_corr_blocks,
-                 partial=True, clean_mask=spec.clean_mask, corr_keys=ck)
+                 partial=True, clean_mask=spec.clean_mask, corr_keys=ck, doc_starts=spec.doc_starts)
     u = part_inputs(t, lo, hi)
     return Oracle(lay, *[f64(u[k]) for k in INPUT_NAMES], *[f64(u[k]) for k in GRAD_NAMES])
 
@@ -96,7 +99,7 @@ def test_partial_forwards_match_the_oracle(label, kw):
 def part_oracle_bf16(spec, t, lo, hi, ck):
     lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start, hi - lo,
                  lo, corr_block_ids=spec.corr_block_ids, n_corr_blocks=spec.n_corr_blocks,
-                 partial=True, clean_mask=spec.clean_mask, corr_keys=ck)
+                 partial=True, clean_mask=spec.clean_mask, corr_keys=ck, doc_starts=spec.doc_starts)
     u = part_inputs(t, lo, hi)
     f = Oracle(lay, *[f64(u[k]) for k in INPUT_NAMES], operand_rounding="bf16").forward()
     out = dict(zip(OUT_NAMES[:4], f))

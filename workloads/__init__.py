@@ -56,6 +56,8 @@ class Spec:
     # what a clean query sees of its own block: 0 all of it (block-causal),
     # 1 the keys up to its own position (token-causal)
     clean_mask: int = 0
+    # packed documents: start positions (first 0, multiples of B); None: one
+    doc_starts: Optional[Tuple[int, ...]] = None
 
     @property
     def n_corr(self) -> int:
@@ -165,7 +167,7 @@ def make_inputs(spec: Spec, device="cpu", seed: Optional[int] = None):
 def small_spec(L=256, B=16, H=2, Hkv=2, d=32, dtype="f32", seed=7, std=1.0,
                n_clean_q=None, clean_q_start=0, n_clean_kv=None,
                corr_block_ids: Optional[Sequence[int]] = None, name="small",
-               outlier_frac=0.0, outlier_mult=1.0, clean_mask=0) -> Spec:
+               outlier_frac=0.0, outlier_mult=1.0, clean_mask=0, doc_starts=None) -> Spec:
     """A full-sequence (or, with ids/offsets, one-share) problem for tests."""
     n_clean_q = L if n_clean_q is None else n_clean_q
     n_clean_kv = L if n_clean_kv is None else n_clean_kv
@@ -178,7 +180,8 @@ def small_spec(L=256, B=16, H=2, Hkv=2, d=32, dtype="f32", seed=7, std=1.0,
                 n_clean_q=n_clean_q, clean_q_start=clean_q_start,
                 n_clean_kv=n_clean_kv, clean_kv_start=0, n_corr_blocks=ncb,
                 corr_block_ids=ids, std=std, seed=seed,
-                outlier_frac=outlier_frac, outlier_mult=outlier_mult, clean_mask=clean_mask)
+                outlier_frac=outlier_frac, outlier_mult=outlier_mult, clean_mask=clean_mask,
+                doc_starts=tuple(int(x) for x in doc_starts) if doc_starts else None)
 
 
 __all__.append("small_spec")
