@@ -12,6 +12,7 @@ float64 CPU oracle timed on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 256k]
 """
 import argparse
+import bisect
 import json
 import os
 import platform
@@ -33,15 +34,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels_dkdv.hip", "device.h", "bdattn_mask.h", "launch.h"):
-        with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def read_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source and this workload;
@@ -50,6 +42,7 @@ def read_traffic(workload: str, kernel: str):
         return None
     txt = open(TRAFFIC_FILE).read()
     m = {k: v for k, v in re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M)}
+    from block_masked_attention_amd.rocprof import kernel_source_hash
     if (m.get("kernel_source") != kernel_source_hash() or m.get("workload") != workload
             or m.get("kernel") != kernel):
         return None
@@ -74,6 +67,9 @@ def cpu_baseline(spec, t, seconds: float):
         list(range(spec.n_corr_blocks))
     cb0 = spec.clean_q_start // B
     ncb = spec.n_clean_q // B
+    docs = list(spec.doc_starts or [0])
+    doc_start = lambda pos: docs[bisect.bisect_right(docs, pos) - 1]  # of the document at pos
+    sub_docs = lambda end: [x for x in docs if x < end]  # document starts before `end`
     order = []
     for i in range(max(ncb, len(ids))):  # spread: stride through both streams
         frac = ((i * 0.6180339887) % 1.0)
@@ -91,23 +87,26 @@ def cpu_baseline(spec, t, seconds: float):
         if stream == "c":
             r0 = b * B - spec.clean_q_start
             lay = layout(B, G, 1, d, B, b * B, (b + 1) * B, 0, corr_block_ids=[],
-                         clean_mask=spec.clean_mask)
+                         clean_mask=spec.clean_mask, doc_starts=sub_docs((b + 1) * B))
             e, ek = np.zeros((0, G, d)), np.zeros((0, 1, d))
             args = (f64(t["q_c"][r0:r0 + B, hq]), f64(t["k_c"][:(b + 1) * B, hk]),
                     f64(t["v_c"][:(b + 1) * B, hk]), e, ek, ek,
                     f64(t["do_c"][r0:r0 + B, hq]), e)
-            # a block-causal clean row sees (b+1)B keys; a token-causal one at
-            # position bB + r sees bB + r + 1
-            pairs = B * (b + 1) * B if spec.clean_mask == 0 else B * b * B + B * (B + 1) // 2
+            # a block-causal clean row sees (b+1)B - s keys (s: its document's
+            # start); a token-causal one at position bB + r sees bB + r + 1 - s
+            s0 = doc_start(b * B)
+            pairs = (B * ((b + 1) * B - s0) if spec.clean_mask == 0
+                     else B * (b * B - s0) + B * (B + 1) // 2)
         else:
             bid = ids[b]
             rr = slice(b * B, (b + 1) * B)
-            lay = layout(B, G, 1, d, 0, 0, bid * B, 0, corr_block_ids=[bid])
+            lay = layout(B, G, 1, d, 0, 0, bid * B, 0, corr_block_ids=[bid],
+                         doc_starts=sub_docs(bid * B + 1))
             e = np.zeros((0, G, d))
             args = (e, f64(t["k_c"][:bid * B, hk]), f64(t["v_c"][:bid * B, hk]),
                     f64(t["q_x"][rr, hq]), f64(t["k_x"][rr, hk]), f64(t["v_x"][rr, hk]),
                     e, f64(t["do_x"][rr, hq]))
-            pairs = B * (bid + 1) * B
+            pairs = B * (bid * B - doc_start(bid * B) + B)
         t0 = time.perf_counter()
         orc = Oracle(lay, *args)
         orc.forward()
@@ -151,6 +150,7 @@ def time_split_forward(bd, spec, t, shards, reps):
         probs.append(bd.problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
                                 spec.clean_q_start, hi - lo, lo, spec.n_corr_blocks,
                                 spec.corr_block_ids, clean_mask=spec.clean_mask, partial=True,
+                                doc_starts=spec.doc_starts,
                                 omit_corr_keys=not ck))
         u = dict(t)
         u["k_c"], u["v_c"] = t["k_c"][lo:hi], t["v_c"][lo:hi]  # row ranges stay contiguous
@@ -191,6 +191,9 @@ def main():
                     help="also time the forward in the split form: the block-diagonal corrupted "
                          "launch plus N clean K/V shards at original positions, merged "
                          "(reported under 'split_forward', after the main timing)")
+    ap.add_argument("--docs", type=int, default=1, metavar="N",
+                    help="pack N documents into the workload's sequence: N-1 distinct seeded "
+                         "random block boundaries cut it (attention stays inside each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +214,14 @@ def main():
     if args.clean_mask == "token":
         spec = spec.with_(clean_mask=1)
     mask_name = "token-causal" if spec.clean_mask else "block-causal"
+    if args.docs > 1:
+        import numpy as np
+        nb = (spec.clean_q_start + spec.n_clean_q) // spec.B  # blocks of the sequence
+        if args.docs > nb:
+            sys.exit(f"--docs {args.docs}: the sequence has only {nb} blocks")
+        cuts = np.sort(np.random.default_rng(1234).choice(np.arange(1, nb), args.docs - 1,
+                                                          replace=False))
+        spec = spec.with_(doc_starts=(0,) + tuple(int(c) * spec.B for c in cuts))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     p = bd.from_spec(spec)
@@ -274,8 +285,8 @@ def main():
                        executed_tflops=round(executed_d[k] * d * H * pairs / (ms * 1e-3) / 1e12, 1))
     dom = max(kern, key=lambda k: kern[k]["ms"])
     achieved = kern[dom]["useful_tflops"]
-    traffic = read_traffic(spec.name if spec.clean_mask == 0 else spec.name + "_token_causal",
-                           dom)
+    traffic = read_traffic(spec.name if spec.clean_mask == 0 and args.docs == 1 else
+                           spec.name + "_variant", dom)
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak} peak); " +
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
@@ -308,7 +319,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "description": spec.description,
                    "clean_q": nc, "clean_kv": nkv, "corrupted": nx, "B": spec.B, "H": H,
-                   "Hkv": Hkv, "d": d, "clean_mask": mask_name,
+                   "Hkv": Hkv, "d": d, "clean_mask": mask_name, "documents": args.docs,
                    "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful_step, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),

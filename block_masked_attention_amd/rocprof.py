@@ -24,7 +24,12 @@ Usage (repository root, on the GPU machine):
     python -m block_masked_attention_amd.rocprof --workload 256k --out DIR
 
 It prints one JSON line and writes DIR/summary.json and DIR/summary.md; the
-raw rocprofv3 output stays in DIR/<pass>/.
+raw rocprofv3 output stays in DIR/<pass>/. With ``--profiles P`` it also
+writes the four summaries kept in the repository under P:
+bdattn_<workload>_{rocprof_summary,kernel_trace,hbm_traffic,sq_counters}.md.
+The HBM traffic file ends with machine-readable lines (dominant kernel,
+workload, kernel source hash, HBM bytes per launch) that bench.py reports as
+the roofline's ``traffic`` while the kernel sources are unchanged.
 """
 from __future__ import annotations
 
@@ -39,6 +44,8 @@ import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("kernels.hip", "kernels_dkdv.hip", "device.h", "bdattn_mask.h", "launch.h")
+BENCH_NAME = {"fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv"}
 MAIN_KERNELS = ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kernel",
                 "merge_kernel")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -53,6 +60,16 @@ SQ2 = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_IDX_ACT
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources whose counters a profile describes."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def short_name(kernel: str) -> str:
@@ -109,7 +126,8 @@ def counters(d):
         k = short_name(r["Kernel_Name"])
         tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
         disp[k].add(r["Dispatch_Id"])
-    return {k: {c: v / len(disp[k]) for c, v in cs.items()} for k, cs in tot.items()}
+    return {k: dict({c: v / len(disp[k]) for c, v in cs.items()}, _dispatches=len(disp[k]))
+            for k, cs in tot.items()}
 
 
 def agent(d):
@@ -186,12 +204,115 @@ def markdown(summary, workload, cmd):
     return "\n".join(out) + "\n"
 
 
+def _base(k):
+    return k.split("<")[0]
+
+
+def _main_rows(d_trace):
+    return [r for r in read_csv(d_trace, "kernel_stats") if short_name(r["Name"]).startswith(MAIN_KERNELS)]
+
+
+def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, summary):
+    """The four repository summaries of one harness run (tables only)."""
+    sys.path.insert(0, ROOT)
+    from workloads import config
+    spec = config(workload)
+    desc = (f"clean {spec.n_clean_q} + corrupted {spec.n_corr} tokens, B={spec.B}, GQA "
+            f"{spec.H}/{spec.Hkv}, d={spec.d}, {spec.dtype}; one forward and one backward")
+    head = ["Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
+            f"Workload {workload}: {desc}. Kernel source hash {kernel_source_hash()}.", ""]
+    os.makedirs(dest, exist_ok=True)
+    name = lambda kind: os.path.join(dest, f"bdattn_{workload}_{kind}.md")
+    # 1. the harness summary
+    with open(name("rocprof_summary"), "w") as fh:
+        fh.write(markdown(summary, workload, cmd))
+        fh.write("\nClock = GRBM_GUI_ACTIVE / XCDs / duration (the mean of the two SQ passes); "
+                 "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles); LDS busy = "
+                 "SQ_LDS_IDX_ACTIVE / (CUs x cycles); HBM bytes per launch from FETCH_SIZE and "
+                 "WRITE_SIZE, scaled by the plain copy. Each figure comes from its own rocprofv3 "
+                 "run of one bench step (block_masked_attention_amd/rocprof.py lists the "
+                 "passes); durations come from the kernel-trace pass.\n")
+    # 2. kernel trace
+    rows = _main_rows(d_trace)
+    out = [f"# bdattn kernels, {workload} workload: rocprofv3 kernel trace", ""] + head + [
+        "The `trace` pass: `rocprofv3 --kernel-trace --stats` over `bench.py --workload "
+        f"{workload} --no-cpu-baseline --steps 1 --warmup 1`.", "",
+        "| kernel | calls | avg ms | min ms | max ms | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                   f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {r['Percentage']} |")
+    out += ["", "The rest of the GPU time is torch's input generation (random fill and scaling)."]
+    with open(name("kernel_trace"), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    # 3. HBM traffic, with the machine-readable lines
+    cf, cw = fetch.get(COPY_KERNEL, {}), write.get(COPY_KERNEL, {})
+    out = [f"# bdattn kernels, {workload} workload: HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE)",
+           ""] + head + [
+        "The `fetch` and `write` passes: `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` over "
+        f"`bench.py --workload {workload} --no-cpu-baseline --steps 1 --warmup 0 "
+        "--copy-calibration`. The calibration copy (`__amd_rocclr_copyBuffer`) reads and writes "
+        f"exactly {COPY_BYTES // 1024} KiB; the counters read FETCH_SIZE = "
+        f"{cf.get('FETCH_SIZE', 0):.0f} KiB and WRITE_SIZE = {cw.get('WRITE_SIZE', 0):.0f} KiB for "
+        f"it, so the scale factors are {summary['fetch_scale']:.3f} (fetch) and "
+        f"{summary['write_scale']:.3f} (write). Counts are per launch.", "",
+        "| kernel | launches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (GB, scaled) | write (GB, scaled) |",
+        "|---|---|---|---|---|---|"]
+    for k, r in summary["kernels"].items():
+        f, w = fetch.get(k, {}), write.get(k, {})
+        out.append(f"| `{k}` | {f.get('_dispatches', '')} | {f.get('FETCH_SIZE', 0):.0f} | "
+                   f"{w.get('WRITE_SIZE', 0):.0f} | {r.get('hbm_read_gb', '')} | {r.get('hbm_write_gb', '')} |")
+    main = {k: r for k, r in summary["kernels"].items() if _base(k) in BENCH_NAME}
+    dom = max(main, key=lambda k: main[k]["ms"])
+    r = main[dom]
+    nbytes = (fetch[dom]["FETCH_SIZE"] * summary["fetch_scale"]
+              + write[dom]["WRITE_SIZE"] * summary["write_scale"]) * 1024
+    out += ["", f"Dominant kernel (longest): `{dom}`, {nbytes / 1e9:.1f} GB per launch beyond the "
+            f"L2 over {r['ms']:.0f} ms ({nbytes / 1e9 / (r['ms'] * 1e-3):.0f} GB/s).", "",
+            "Machine-readable lines for bench.py (valid only for the kernel source hash below):", "",
+            f"kernel: {BENCH_NAME[_base(dom)]}", f"workload: {workload}",
+            f"kernel_source: {kernel_source_hash()}",
+            f"hbm_bytes_per_launch: {nbytes:.6e}"]
+    with open(name("hbm_traffic"), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    # 4. SQ counters
+    ks = [k for k in summary["kernels"] if _base(k) in BENCH_NAME]
+    out = [f"# bdattn kernels, {workload} workload: SQ counters (rocprofv3 --pmc)", ""] + head + [
+        "The `sq1` and `sq2` passes run `rocprofv3 --pmc` with these counter sets over "
+        f"`bench.py --workload {workload} --no-cpu-baseline --steps 1 --warmup 0`: sq1 = "
+        f"{' '.join(SQ1)}; sq2 = {' '.join(SQ2)}. Clock = GRBM_GUI_ACTIVE / {dev['xcds']} XCDs / "
+        f"duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({dev['simds']} SIMDs x cycles); LDS "
+        f"busy = SQ_LDS_IDX_ACTIVE / ({dev['cus']} CUs x cycles).", "",
+        "| counter | " + " | ".join(f"`{k}`" for k in ks) + " |", "|---|" + "---|" * len(ks),
+        "| duration (ms, kernel trace) | " + " | ".join(f"{summary['kernels'][k]['ms']:.0f}" for k in ks) + " |"]
+    for c in dict.fromkeys(SQ1 + SQ2):
+        vals = []
+        for k in ks:
+            v = [x[k][c] for x in (sq1, sq2) if k in x and c in x[k]]
+            vals.append(" / ".join(f"{y:.4g}" for y in v))
+        out.append(f"| {c} | " + " | ".join(vals) + " |")
+    for key, label, fmt in (("clock_ghz", "derived: shader clock (GHz)", "{:.2f}"),
+                            ("mfma_busy", "derived: MFMA busy", "{:.0%}"),
+                            ("lds_busy", "derived: LDS busy", "{:.0%}"),
+                            ("valu_per_mfma", "derived: VALU instructions per MFMA", "{:.2f}"),
+                            ("lds_per_mfma", "derived: LDS instructions per MFMA", "{:.2f}"),
+                            ("salu_per_mfma", "derived: SALU instructions per MFMA", "{:.2f}")):
+        out.append(f"| {label} | " + " | ".join(fmt.format(summary['kernels'][k][key])
+                                              if key in summary['kernels'][k] else "" for k in ks) + " |")
+    out.append("")
+    out.append("GRBM_GUI_ACTIVE is read in both passes (sq1 / sq2).")
+    with open(name("sq_counters"), "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    log(f"[rocprof] wrote the four summaries under {dest}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--workload", default="256k")
     ap.add_argument("--out", required=True, help="directory for the raw output and summaries")
     ap.add_argument("--limit", type=int, default=300, help="seconds allowed per pass")
+    ap.add_argument("--profiles", default=None,
+                    help="also write the repository summaries of this run into this directory")
     args = ap.parse_args()
     if shutil.which("rocprofv3") is None:
         sys.exit("rocprofv3 not found")
@@ -209,10 +330,15 @@ def main():
                         counters(d_sq1), counters(d_sq2), agent(d_trace))
     summary["workload"] = args.workload
     cmd = f"python -m block_masked_attention_amd.rocprof --workload {args.workload} --out {args.out}"
+    if args.profiles:
+        cmd += f" --profiles {args.profiles}"
     with open(os.path.join(args.out, "summary.json"), "w") as fh:
         json.dump(summary, fh, indent=1)
     with open(os.path.join(args.out, "summary.md"), "w") as fh:
         fh.write(markdown(summary, args.workload, cmd))
+    if args.profiles:
+        write_profiles(args.profiles, args.workload, cmd, d_trace, counters(d_fetch),
+                       counters(d_write), counters(d_sq1), counters(d_sq2), agent(d_trace), summary)
     print(json.dumps(summary), flush=True)
 
 

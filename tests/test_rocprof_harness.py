@@ -67,3 +67,41 @@ def test_summary_arithmetic(tmp_path):
     assert r["valu_per_mfma"] == pytest.approx(3.0) and r["lds_per_mfma"] == pytest.approx(1.5)
     md = rocprof.markdown(s, "256k", "python -m block_masked_attention_amd.rocprof")
     assert "| `bwd_dq_kernel<true, 128>` | 2 | 2 | 50% | 25% |" in md
+
+
+def test_repository_summaries(tmp_path):
+    """The four summaries written from one run: every table present, and the
+    machine-readable traffic lines name the longest main kernel, the current
+    kernel source hash and its scaled HBM bytes per launch."""
+    import re
+
+    t = str(tmp_path)
+    F = "void bdattn::(anonymous namespace)::fwd_kernel<true, 128, false>(bdattn::FwdArgs)"
+    _write(t + "/trace", "kernel_stats", [
+        dict(Name=K, Calls=1, AverageNs=3.0e6, MinNs=3.0e6, MaxNs=3.0e6, Percentage=60.0),
+        dict(Name=F, Calls=1, AverageNs=2.0e6, MinNs=2.0e6, MaxNs=2.0e6, Percentage=40.0)])
+    _write(t + "/trace", "agent_info", [dict(Name="gfx950", Simd_Count=1024, Cu_Count=256,
+                                             Num_Xcc=8)])
+    _counters(t + "/fetch", [(rocprof.COPY_KERNEL, dict(FETCH_SIZE=524288)),
+                             (K, dict(FETCH_SIZE=1000.0)), (F, dict(FETCH_SIZE=10.0))])
+    _counters(t + "/write", [(rocprof.COPY_KERNEL, dict(WRITE_SIZE=1048576)),
+                             (K, dict(WRITE_SIZE=500.0)), (F, dict(WRITE_SIZE=5.0))])
+    _counters(t + "/sq1", [(K, dict(GRBM_GUI_ACTIVE=1e7)), (F, dict(GRBM_GUI_ACTIVE=1e7))])
+    _counters(t + "/sq2", [(K, dict(GRBM_GUI_ACTIVE=1e7, SQ_INSTS_MFMA=10.0, SQ_INSTS_VALU=30.0,
+                                    SQ_INSTS_LDS=5.0, SQ_INSTS_SALU=1.0)),
+                           (F, dict(GRBM_GUI_ACTIVE=1e7))])
+    args = [rocprof.counters(t + "/" + p) for p in ("fetch", "write", "sq1", "sq2")]
+    dev = rocprof.agent(t + "/trace")
+    s = rocprof.summarise(rocprof.durations(t + "/trace"), *args, dev)
+    dest = str(tmp_path / "profiles")
+    rocprof.write_profiles(dest, "8k", "python -m block_masked_attention_amd.rocprof ...",
+                           t + "/trace", *args, dev, s)
+    for kind in ("rocprof_summary", "kernel_trace", "hbm_traffic", "sq_counters"):
+        assert os.path.getsize(os.path.join(dest, f"bdattn_8k_{kind}.md")) > 200
+    txt = open(os.path.join(dest, "bdattn_8k_hbm_traffic.md")).read()
+    m = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M))
+    assert m["kernel"] == "bwd_dq" and m["workload"] == "8k"
+    assert m["kernel_source"] == rocprof.kernel_source_hash()
+    assert float(m["hbm_bytes_per_launch"]) == pytest.approx((1000 * 2 + 500) * 1024, rel=1e-3)
+    sq = open(os.path.join(dest, "bdattn_8k_sq_counters.md")).read()
+    assert "| derived: VALU instructions per MFMA | 3.00 |" in sq
