@@ -142,13 +142,12 @@ def clear_host_cache():
 
 def sub_clean_block(spec, t, b, g, rounding=None):
     """Oracle for the clean query block with global id b, q heads of KV head g."""
-    assert not spec.doc_starts, "sub-problems of one document only"
     B, G = spec.B, spec.H // spec.Hkv
     r0 = b * B - spec.clean_q_start
     hq = (g * G, (g + 1) * G)
     hk = (g, g + 1)
     lay = layout(B, G, 1, spec.d, B, b * B, (b + 1) * B, 0, corr_block_ids=[],
-                 clean_mask=spec.clean_mask)
+                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts)
     e = np.zeros((0, G, spec.d))
     ek = np.zeros((0, 1, spec.d))
     orc = Oracle(lay, _sl(t["q_c"], (r0, r0 + B), hq), _kv(t, "k_c", (0, (b + 1) * B), g),
@@ -162,14 +161,13 @@ def sub_clean_block(spec, t, b, g, rounding=None):
 def sub_corr_block(spec, t, j, g, rounding=None):
     """Oracle for local corrupted block j (global id ids[j]), KV head g: its
     O, LSE, dQ and its own dK/dV (seen by no other block)."""
-    assert not spec.doc_starts, "sub-problems of one document only"
     B, G = spec.B, spec.H // spec.Hkv
     bid = spec.corr_block_ids[j] if spec.corr_block_ids is not None else j
     hq = (g * G, (g + 1) * G)
     hk = (g, g + 1)
     rows = (j * B, (j + 1) * B)
     lay = layout(B, G, 1, spec.d, 0, 0, bid * B, 0, corr_block_ids=[bid],
-                 clean_mask=spec.clean_mask)
+                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts)
     e = np.zeros((0, G, spec.d))
     orc = Oracle(lay, e, _kv(t, "k_c", (0, bid * B), g), _kv(t, "v_c", (0, bid * B), g),
                  _sl(t["q_x"], rows, hq), _sl(t["k_x"], rows, hk), _sl(t["v_x"], rows, hk),
@@ -182,18 +180,23 @@ def sub_corr_block(spec, t, j, g, rounding=None):
 
 def sub_clean_keys(spec, t, kb, g, rounding=None):
     """dK/dV of the clean keys of block kb (KV head g) from every query that
-    sees them: clean rows of blocks >= kb, corrupted blocks with id > kb."""
-    assert not spec.doc_starts, "sub-problems of one document only"
+    sees them: clean rows of blocks >= kb, corrupted blocks with id > kb (with
+    packed documents the oracle's mask drops those of later documents)."""
     B, G = spec.B, spec.H // spec.Hkv
     ids = list(spec.corr_block_ids) if spec.corr_block_ids is not None else \
         list(range(spec.n_corr_blocks))
     c0 = max(0, kb * B - spec.clean_q_start)
-    jx = [j for j, bid in enumerate(ids) if bid > kb]
+    # rows of later documents never see the keys: with packed documents the
+    # sub-problem stops at the end of the keys' document
+    end = next((x for x in (spec.doc_starts or ()) if x > kb * B), None)
+    jx = [j for j, bid in enumerate(ids) if bid > kb and (end is None or bid * B < end)]
     hq = (g * G, (g + 1) * G)
     hk = (g, g + 1)
-    nq = spec.n_clean_q - c0
+    c1 = spec.n_clean_q if end is None else min(spec.n_clean_q, max(c0, end - spec.clean_q_start))
+    nq = c1 - c0
     lay = layout(B, G, 1, spec.d, nq, spec.clean_q_start + c0, spec.n_clean_kv, 0,
-                 corr_block_ids=[ids[j] for j in jx], clean_mask=spec.clean_mask)
+                 corr_block_ids=[ids[j] for j in jx], clean_mask=spec.clean_mask,
+                 doc_starts=spec.doc_starts)
     xr = np.concatenate([np.arange(j * B, (j + 1) * B) for j in jx]) if jx else \
         np.zeros(0, np.int64)
 
@@ -201,10 +204,10 @@ def sub_clean_keys(spec, t, kb, g, rounding=None):
         x = t[name][torch.as_tensor(xr, device=t[name].device, dtype=torch.long)]
         return f64(x[:, heads[0]:heads[1]])
 
-    orc = Oracle(lay, _sl(t["q_c"], (c0, spec.n_clean_q), hq),
+    orc = Oracle(lay, _sl(t["q_c"], (c0, c1), hq),
                  _kv(t, "k_c", (0, spec.n_clean_kv), g), _kv(t, "v_c", (0, spec.n_clean_kv), g),
                  xs("q_x", hq), xs("k_x", hk), xs("v_x", hk),
-                 _sl(t["do_c"], (c0, spec.n_clean_q), hq), xs("do_x", hq),
+                 _sl(t["do_c"], (c0, c1), hq), xs("do_x", hq),
                  operand_rounding=rounding)
     keys = orc.key_index(0, np.arange(kb * B, (kb + 1) * B))
     dk, dv = orc.keys_backward(keys)

@@ -191,6 +191,10 @@ def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
     corr = sorted({0, spec.n_corr_blocks - 1} |
                   set(rng.integers(0, spec.n_corr_blocks, n_blocks).tolist()))
     key_blocks = [cb1 - 1, cb1 - 3]
+    if spec.doc_starts:  # query blocks on both sides of two document starts, and the
+        for s in [x // B for x in spec.doc_starts[1:3]]:  # last keys before each
+            clean_blocks = sorted(set(clean_blocks) | {b for b in (s - 1, s) if cb0 <= b < cb1})
+            key_blocks = sorted(set(key_blocks) | {s - 1})
     want = {k: [] for k in OUT_NAMES}
     have = {k: [] for k in OUT_NAMES}
     for g in kv_groups:
@@ -235,13 +239,29 @@ def test_workload_sampled_parity(idx):
     workload_parity(CONFIGS[idx])
 
 
+def packed(spec, n, seed=1234):
+    """The workload with n documents cut at n - 1 seeded random block
+    boundaries (as bench.py --docs n cuts them)."""
+    nb = (spec.clean_q_start + spec.n_clean_q) // spec.B
+    cuts = np.sort(np.random.default_rng(seed).choice(np.arange(1, nb), n - 1, replace=False))
+    return spec.with_(doc_starts=(0,) + tuple(int(c) * spec.B for c in cuts))
+
+
+@pytest.mark.parametrize("idx,n", [(2, 8), (3, 16)], ids=["64k_docs8", "256k_docs16"])
+def test_packed_documents_workload_sampled_parity(idx, n):
+    """The 64K workload with 8 packed documents and the 256K one with 16, at
+    full size, launched as `bench.py --docs n` launches them; the samples
+    include the blocks on both sides of two document starts (one KV group)."""
+    workload_parity(packed(CONFIGS[idx], n), groups=(0,))
+
+
 @pytest.mark.parametrize("idx", [1, 2], ids=[CONFIGS[i].name for i in (1, 2)])
 def test_token_causal_workload_sampled_parity(idx):
     """The 8K and 64K workloads at full size with the token-causal clean mask."""
     workload_parity(CONFIGS[idx].with_(clean_mask=1))
 
 
-def workload_parity(spec):
+def workload_parity(spec, groups=None):
     _need_gpu()
     say(f"[gpu] workload {spec.name} (clean mask {spec.clean_mask}): {spec.description}")
     t0 = time.perf_counter()
@@ -252,7 +272,8 @@ def workload_parity(spec):
         assert torch.isfinite(v).all(), f"{k} has non-finite values"
     _identities(spec, t, got)
     say(f"  identities checked: {time.perf_counter() - t0:.1f} s")
-    groups = (0,) if spec.Hkv == 1 else (0, spec.Hkv - 1)
+    if groups is None:
+        groups = (0,) if spec.Hkv == 1 else (0, spec.Hkv - 1)
     have, want = _sampled(spec, t, got, kv_groups=groups)
     say(f"  exact oracle samples: {time.perf_counter() - t0:.1f} s")
     ideal = None
