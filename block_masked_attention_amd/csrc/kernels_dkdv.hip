@@ -45,7 +45,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   const BwdItem item = a.kv_items[blockIdx.x];
   const int it_x0 = item.x0, it_x1 = item.x1, it_c0 = item.c0, it_c1 = item.c1;
-  const int it_xf = item.xf, it_cf = item.cf;
+  const int it_xf = item.xf, it_cf = item.cf, it_xfe = item.xfe, it_cfe = item.cfe;
   const int kstream = item.hs & 1, kvh = item.hs >> 1;
   const int G = a.H / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -113,14 +113,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
   for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
 
   // Step order: the query tiles that see every key of the workgroup (those
-  // starting at or after xf / cf) come first, then the ones that need the
+  // inside [xf, xfe) / [cf, cfe)) come first, then the ones that need the
   // mask; within each, corrupted tiles then clean ones, each from the last
-  // tile down, every q head of the group per tile. A step is (tile index t in
-  // that order, head offset hi), advanced without divisions.
+  // tile down, every q head of the group per tile. The masked tiles of a
+  // stream are the u (0 or 1) tiles above the unmasked ones, then the tiles
+  // below them. A step is (tile index t in that order, head offset hi),
+  // advanced without divisions.
   auto ntiles = [](int r0, int r1) { return r1 > r0 ? (r1 - 1) / TQ - r0 / TQ + 1 : 0; };
   const int top_x = (it_x1 - 1) / TQ, top_c = (it_c1 - 1) / TQ;
-  const int nf_x = it_xf < it_x1 ? top_x - it_xf / TQ + 1 : 0;
-  const int nf_c = it_cf < it_c1 ? top_c - it_cf / TQ + 1 : 0;
+  const int nf_x = ntiles(it_xf, it_xfe), nf_c = ntiles(it_cf, it_cfe);
+  const int u_x = nf_x ? top_x - (it_xfe - 1) / TQ : 0;
+  const int u_c = nf_c ? top_c - (it_cfe - 1) / TQ : 0;
   const int nm_x = ntiles(it_x0, it_x1) - nf_x, nm_c = ntiles(it_c0, it_c1) - nf_c;
   const int n_full = (nf_x + nf_c) * G;
   const int n_it = n_full + (nm_x + nm_c) * G;
@@ -136,17 +139,17 @@ void bwd_dkdv_kernel(BwdArgs a) {
     int t = p.t;
     if (t < nf_x) {
       s.qs = 1;
-      s.q0 = (top_x - t) * TQ;
+      s.q0 = (top_x - u_x - t) * TQ;
     } else if ((t -= nf_x) < nf_c) {
       s.qs = 0;
-      s.q0 = (top_c - t) * TQ;
+      s.q0 = (top_c - u_c - t) * TQ;
     } else if ((t -= nf_c) < nm_x) {
       s.qs = 1;
-      s.q0 = (top_x - nf_x - t) * TQ;
+      s.q0 = (top_x - (t < u_x ? 0 : nf_x) - t) * TQ;
     } else {
       t -= nm_x;
       s.qs = 0;
-      s.q0 = (top_c - nf_c - t) * TQ;
+      s.q0 = (top_c - (t < u_c ? 0 : nf_c) - t) * TQ;
     }
     return s;
   };

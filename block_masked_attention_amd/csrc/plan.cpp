@@ -309,35 +309,38 @@ void build_plan(const Problem& P, Plan* plan) {
       // a q tile needs the mask unless it lies inside the swept rows and its
       // first row sees the whole key tile (row bounds are nondecreasing, so
       // the unmasked tiles are the top ones of each stream); with documents,
-      // only when every key of the tile is in one document and the top tile
-      // ends at that document's end or the stream's
-      const bool c_top = one_doc && (c1 == P.n_clean_q || c1 % BWD_TQ == 0);
-      const bool x_top = one_doc && (x1 == nx || x1 % BWD_TQ == 0);
-      int64_t qt = qtiles(c0, c1) + qtiles(x0, x1), masked = 0;
-      int32_t cf = c1, xf = x1;
-      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r < c1; r += BWD_TQ) {
-        if (!c_top || r < c0 || row_bounds(P, 0, r).cb < k1 || k1 - k0 < BWD_TK) {
-          ++masked;
-        } else {
+      // only when every key of the tile is in one document, and below the
+      // last tile boundary before that document's end unless the document
+      // ends with the stream (rows past a stream's end contribute nothing)
+      int32_t cfe = !one_doc ? c0 : (c1 == P.n_clean_q ? c1 : c1 / BWD_TQ * BWD_TQ);
+      int32_t xfe = !one_doc ? x0 : (x1 == nx ? x1 : x1 / BWD_TQ * BWD_TQ);
+      int64_t qt = qtiles(c0, c1) + qtiles(x0, x1), masked = qt;
+      int32_t cf = cfe, xf = xfe;
+      for (int32_t r = c0 / BWD_TQ * BWD_TQ; r + BWD_TQ <= cfe || (r < cfe && cfe == P.n_clean_q);
+           r += BWD_TQ) {
+        if (r >= c0 && row_bounds(P, 0, r).cb >= k1 && k1 - k0 == BWD_TK) {
           cf = r;
+          masked -= qtiles(cf, cfe);
           break;
         }
       }
-      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r < x1; r += BWD_TQ) {
-        if (!x_top || r < x0 || row_bounds(P, 1, r).cb < k1 || k1 - k0 < BWD_TK) {
-          ++masked;
-        } else {
+      for (int32_t r = x0 / BWD_TQ * BWD_TQ; r + BWD_TQ <= xfe || (r < xfe && xfe == nx);
+           r += BWD_TQ) {
+        if (r >= x0 && row_bounds(P, 1, r).cb >= k1 && k1 - k0 == BWD_TK) {
           xf = r;
+          masked -= qtiles(xf, xfe);
           break;
         }
       }
-      BwdItem it{kt, 0, c0, c1, x0, x1, cf, xf};
+      if (cf >= cfe) cf = cfe = c1;  // no unmasked tile: the kernel reads [c1, c1)
+      if (xf >= xfe) xf = xfe = x1;
+      BwdItem it{kt, 0, c0, c1, x0, x1, cf, xf, cfe, xfe};
       tiles.push_back({kt, 0, it, (c1 - c0) + int64_t(x1 - x0), qt, masked});
     }
     for (int32_t kt = 0; P.corr_keys && kt * int64_t(BWD_TK) < nx; ++kt) {
       const int32_t k0 = kt * BWD_TK, k1 = std::min<int32_t>(nx, k0 + BWD_TK);
       const int32_t x0 = k0 / P.B * P.B, x1 = std::min<int32_t>(nx, ceil_div(k1, P.B) * P.B);
-      BwdItem it{kt, 1, 0, 0, x0, x1, 0, x1};
+      BwdItem it{kt, 1, 0, 0, x0, x1, 0, x1, 0, x1};
       const int64_t qt = qtiles(x0, x1);
       tiles.push_back({kt, 1, it, x1 - x0, qt, qt});
     }

@@ -42,14 +42,16 @@ struct FwdItem {
 
 // One backward work item: key tile `ktile` of the key stream (bit 0 of hs) of
 // KV head hs >> 1; sweeps clean query rows [c0, c1) and corrupted rows
-// [x0, x1). Query tiles (BWD_TQ rows, aligned) starting at or after cf
-// (clean) / xf (corrupted) see every key of the tile and skip the mask; cf =
-// c1 / xf = x1 when no tile does.
+// [x0, x1). Query tiles (BWD_TQ rows, aligned) inside [cf, cfe) (clean) /
+// [xf, xfe) (corrupted) see every key of the tile and skip the mask; the end
+// is c1 / x1, or with packed documents the last tile boundary below it (the
+// top tile then holds rows of a later document and keeps the mask). cf = cfe
+// / xf = xfe when no tile skips it.
 struct BwdItem {
   int32_t ktile;
   int32_t hs;
   int32_t c0, c1, x0, x1;
-  int32_t cf, xf;
+  int32_t cf, xf, cfe, xfe;
 };
 
 struct Problem {
