@@ -27,7 +27,7 @@ if ROOT not in sys.path:
 METRIC = "bdattn fwd+bwd useful TFLOP/s at 256K ctx; % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bdattn_256k_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bdattn_{}_hbm_traffic.md")
 
 
 def log(*a):
@@ -38,9 +38,10 @@ def read_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source and this workload;
     else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
-    txt = open(TRAFFIC_FILE).read()
+    txt = open(path).read()
     m = {k: v for k, v in re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M)}
     from block_masked_attention_amd.rocprof import kernel_source_hash
     if (m.get("kernel_source") != kernel_source_hash() or m.get("workload") != workload
@@ -285,8 +286,9 @@ def main():
                        executed_tflops=round(executed_d[k] * d * H * pairs / (ms * 1e-3) / 1e12, 1))
     dom = max(kern, key=lambda k: kern[k]["ms"])
     achieved = kern[dom]["useful_tflops"]
-    traffic = read_traffic(spec.name if spec.clean_mask == 0 and args.docs == 1 else
-                           spec.name + "_variant", dom)
+    from block_masked_attention_amd.rocprof import profile_key
+    traffic = read_traffic(profile_key(spec.name, args.docs)
+                           + ("_token_causal" if spec.clean_mask else ""), dom)
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak} peak); " +
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "

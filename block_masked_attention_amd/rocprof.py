@@ -212,13 +212,23 @@ def _main_rows(d_trace):
     return [r for r in read_csv(d_trace, "kernel_stats") if short_name(r["Name"]).startswith(MAIN_KERNELS)]
 
 
-def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, summary):
+def profile_key(workload, docs=1):
+    """Name of a profiled configuration: the workload, with the number of
+    packed documents when there are several."""
+    return workload + (f"_docs{docs}" if docs > 1 else "")
+
+
+def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, summary, docs=1):
     """The four repository summaries of one harness run (tables only)."""
     sys.path.insert(0, ROOT)
     from workloads import config
     spec = config(workload)
     desc = (f"clean {spec.n_clean_q} + corrupted {spec.n_corr} tokens, B={spec.B}, GQA "
             f"{spec.H}/{spec.Hkv}, d={spec.d}, {spec.dtype}; one forward and one backward")
+    if docs > 1:
+        desc += f"; {docs} packed documents (bench.py --docs {docs})"
+    bench_extra = f" --docs {docs}" if docs > 1 else ""
+    workload = profile_key(workload, docs)
     head = ["Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
             f"Workload {workload}: {desc}. Kernel source hash {kernel_source_hash()}.", ""]
     os.makedirs(dest, exist_ok=True)
@@ -236,7 +246,7 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     rows = _main_rows(d_trace)
     out = [f"# bdattn kernels, {workload} workload: rocprofv3 kernel trace", ""] + head + [
         "The `trace` pass: `rocprofv3 --kernel-trace --stats` over `bench.py --workload "
-        f"{workload} --no-cpu-baseline --steps 1 --warmup 1`.", "",
+        f"{spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 1`.", "",
         "| kernel | calls | avg ms | min ms | max ms | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
@@ -249,7 +259,7 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     out = [f"# bdattn kernels, {workload} workload: HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE)",
            ""] + head + [
         "The `fetch` and `write` passes: `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` over "
-        f"`bench.py --workload {workload} --no-cpu-baseline --steps 1 --warmup 0 "
+        f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 0 "
         "--copy-calibration`. The calibration copy (`__amd_rocclr_copyBuffer`) reads and writes "
         f"exactly {COPY_BYTES // 1024} KiB; the counters read FETCH_SIZE = "
         f"{cf.get('FETCH_SIZE', 0):.0f} KiB and WRITE_SIZE = {cw.get('WRITE_SIZE', 0):.0f} KiB for "
@@ -278,7 +288,7 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     ks = [k for k in summary["kernels"] if _base(k) in BENCH_NAME]
     out = [f"# bdattn kernels, {workload} workload: SQ counters (rocprofv3 --pmc)", ""] + head + [
         "The `sq1` and `sq2` passes run `rocprofv3 --pmc` with these counter sets over "
-        f"`bench.py --workload {workload} --no-cpu-baseline --steps 1 --warmup 0`: sq1 = "
+        f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 0`: sq1 = "
         f"{' '.join(SQ1)}; sq2 = {' '.join(SQ2)}. Clock = GRBM_GUI_ACTIVE / {dev['xcds']} XCDs / "
         f"duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({dev['simds']} SIMDs x cycles); LDS "
         f"busy = SQ_LDS_IDX_ACTIVE / ({dev['cus']} CUs x cycles).", "",
@@ -311,6 +321,7 @@ def main():
     ap.add_argument("--workload", default="256k")
     ap.add_argument("--out", required=True, help="directory for the raw output and summaries")
     ap.add_argument("--limit", type=int, default=300, help="seconds allowed per pass")
+    ap.add_argument("--docs", type=int, default=1, help="packed documents (bench.py --docs)")
     ap.add_argument("--profiles", default=None,
                     help="also write the repository summaries of this run into this directory")
     args = ap.parse_args()
@@ -319,6 +330,8 @@ def main():
     os.makedirs(args.out, exist_ok=True)
     os.environ.setdefault("TMPDIR", "/tmp")
     b = ["--workload", args.workload, "--no-cpu-baseline", "--steps", "1"]
+    if args.docs > 1:
+        b += ["--docs", str(args.docs)]
     d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", "1"], args.out,
                        args.limit)
     cal = b + ["--warmup", "0", "--copy-calibration"]
@@ -328,17 +341,20 @@ def main():
     d_sq2 = run_pass("sq2", ["--pmc"] + SQ2, b + ["--warmup", "0"], args.out, args.limit)
     summary = summarise(durations(d_trace), counters(d_fetch), counters(d_write),
                         counters(d_sq1), counters(d_sq2), agent(d_trace))
-    summary["workload"] = args.workload
+    summary["workload"] = profile_key(args.workload, args.docs)
     cmd = f"python -m block_masked_attention_amd.rocprof --workload {args.workload} --out {args.out}"
+    if args.docs > 1:
+        cmd += f" --docs {args.docs}"
     if args.profiles:
         cmd += f" --profiles {args.profiles}"
     with open(os.path.join(args.out, "summary.json"), "w") as fh:
         json.dump(summary, fh, indent=1)
     with open(os.path.join(args.out, "summary.md"), "w") as fh:
-        fh.write(markdown(summary, args.workload, cmd))
+        fh.write(markdown(summary, profile_key(args.workload, args.docs), cmd))
     if args.profiles:
         write_profiles(args.profiles, args.workload, cmd, d_trace, counters(d_fetch),
-                       counters(d_write), counters(d_sq1), counters(d_sq2), agent(d_trace), summary)
+                       counters(d_write), counters(d_sq1), counters(d_sq2), agent(d_trace), summary,
+                       docs=args.docs)
     print(json.dumps(summary), flush=True)
 
 
