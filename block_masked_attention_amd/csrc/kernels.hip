@@ -164,7 +164,11 @@ void fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         if (MASK) {
           const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool vis = cl ? (DOCS ? bd_sees_clean(q.rb, key) : key < q.rb.cb)
+          // (documents: clo <= key < cb as one unsigned compare; a test of the
+          // same form as the corrupted one lets the compiler pick the bound
+          // fields by address, which moves the bounds to scratch memory)
+          const bool vis = cl ? (DOCS ? uint32_t(key - q.rb.clo) < uint32_t(q.rb.cb - q.rb.clo)
+                                      : key < q.rb.cb)
                               : bd_sees_corr(q.rb, key);
           s[mb][i] = vis ? s[mb][i] : kNegInf;
         }
@@ -419,7 +423,11 @@ void bwd_dq_kernel(BwdArgs a) {
         float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
         if (MASK) {
           const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          const bool vis = cl ? (DOCS ? bd_sees_clean(q.rb, key) : key < q.rb.cb)
+          // (documents: clo <= key < cb as one unsigned compare; a test of the
+          // same form as the corrupted one lets the compiler pick the bound
+          // fields by address, which moves the bounds to scratch memory)
+          const bool vis = cl ? (DOCS ? uint32_t(key - q.rb.clo) < uint32_t(q.rb.cb - q.rb.clo)
+                                      : key < q.rb.cb)
                               : bd_sees_corr(q.rb, key);
           p = vis ? p : 0.f;
         }
