@@ -247,10 +247,12 @@ def packed(spec, n, seed=1234):
     return spec.with_(doc_starts=(0,) + tuple(int(c) * spec.B for c in cuts))
 
 
-@pytest.mark.parametrize("idx,n", [(2, 8), (3, 16)], ids=["64k_docs8", "256k_docs16"])
+@pytest.mark.parametrize("idx,n", [(2, 8), (3, 16), (1, 128), (2, 1024)],
+                         ids=["64k_docs8", "256k_docs16", "8k_docs128", "64k_docs1024"])
 def test_packed_documents_workload_sampled_parity(idx, n):
-    """The 64K workload with 8 packed documents and the 256K one with 16, at
-    full size, launched as `bench.py --docs n` launches them; the samples
+    """Full-size workloads with packed documents, launched as `bench.py
+    --docs n` launches them: 64K with 8 and 256K with 16 documents, and many
+    short ones (8K with 128, 64K with 1024: 64 tokens on average); the samples
     include the blocks on both sides of two document starts (one KV group)."""
     workload_parity(packed(CONFIGS[idx], n), groups=(0,))
 
