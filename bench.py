@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "bdattn fwd+bwd useful TFLOP/s at 256K ctx; % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+PEAK_CLOCK_GHZ = 2.4  # the shader clock both peaks assume
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bdattn_{}_hbm_traffic.md")
 
 
@@ -34,23 +35,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def read_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source and this workload;
-    else None."""
+def read_profile(workload: str, kernel: str):
+    """(HBM bytes per launch, shader clock in GHz or None) of `kernel` from
+    the committed rocprofv3 counter summary, if it was taken on the current
+    kernel source and this workload; else (None, None)."""
     path = TRAFFIC_FILE.format(workload)
     if not os.path.exists(path):
-        return None
+        return None, None
     txt = open(path).read()
     m = {k: v for k, v in re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M)}
     from block_masked_attention_amd.rocprof import kernel_source_hash
     if (m.get("kernel_source") != kernel_source_hash() or m.get("workload") != workload
             or m.get("kernel") != kernel):
-        return None
+        return None, None
     try:
-        return float(m["hbm_bytes_per_launch"])
+        clock = float(m["clock_ghz"]) if "clock_ghz" in m else None
+        return float(m["hbm_bytes_per_launch"]), clock
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 def cpu_baseline(spec, t, seconds: float):
@@ -287,8 +289,8 @@ def main():
     dom = max(kern, key=lambda k: kern[k]["ms"])
     achieved = kern[dom]["useful_tflops"]
     from block_masked_attention_amd.rocprof import profile_key
-    traffic = read_traffic(profile_key(spec.name, args.docs)
-                           + ("_token_causal" if spec.clean_mask else ""), dom)
+    traffic, clock = read_profile(profile_key(spec.name, args.docs)
+                                  + ("_token_causal" if spec.clean_mask else ""), dom)
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak} peak); " +
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
@@ -334,7 +336,12 @@ def main():
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "flops_per_pair_head": f"{useful_d[dom]}*d useful "
-                                            f"({executed_d[dom]}*d executed)"},
+                                            f"({executed_d[dom]}*d executed)",
+                     # the peak scaled to the kernel's shader clock measured by rocprofv3
+                     # (the 2.5 PFLOP/s peak assumes 2.4 GHz), from the same profile
+                     "clock_ghz": clock,
+                     "frac_at_clock": (round(achieved / (peak * clock / PEAK_CLOCK_GHZ), 4)
+                                       if clock else None)},
         "cpu_baseline": cpu,
     }
     if split is not None:

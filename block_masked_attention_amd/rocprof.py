@@ -28,8 +28,8 @@ raw rocprofv3 output stays in DIR/<pass>/. With ``--profiles P`` it also
 writes the four summaries kept in the repository under P:
 bdattn_<workload>_{rocprof_summary,kernel_trace,hbm_traffic,sq_counters}.md.
 The HBM traffic file ends with machine-readable lines (dominant kernel,
-workload, kernel source hash, HBM bytes per launch) that bench.py reports as
-the roofline's ``traffic`` while the kernel sources are unchanged.
+workload, kernel source hash, HBM bytes per launch, shader clock) that
+bench.py reports in its roofline while the kernel sources are unchanged.
 """
 from __future__ import annotations
 
@@ -282,6 +282,8 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
             f"kernel: {BENCH_NAME[_base(dom)]}", f"workload: {workload}",
             f"kernel_source: {kernel_source_hash()}",
             f"hbm_bytes_per_launch: {nbytes:.6e}"]
+    if "clock_ghz" in r:  # the kernel's mean shader clock over the two SQ passes
+        out.append(f"clock_ghz: {r['clock_ghz']}")
     with open(name("hbm_traffic"), "w") as fh:
         fh.write("\n".join(out) + "\n")
     # 4. SQ counters

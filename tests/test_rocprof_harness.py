@@ -103,5 +103,7 @@ def test_repository_summaries(tmp_path):
     assert m["kernel"] == "bwd_dq" and m["workload"] == "8k"
     assert m["kernel_source"] == rocprof.kernel_source_hash()
     assert float(m["hbm_bytes_per_launch"]) == pytest.approx((1000 * 2 + 500) * 1024, rel=1e-3)
+    # 1e7 GUI-active cycles over 8 XCDs in 3 ms: 0.4167 GHz
+    assert float(m["clock_ghz"]) == pytest.approx(1e7 / 8 / 3e-3 / 1e9, abs=1e-3)
     sq = open(os.path.join(dest, "bdattn_8k_sq_counters.md")).read()
     assert "| derived: VALU instructions per MFMA | 3.00 |" in sq
