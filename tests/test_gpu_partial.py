@@ -221,3 +221,27 @@ def test_random_partial_problems(label, kw, lo, hi, ck):
     errs.update(compare(spec, {k: gw[k] for k in names}, {k: bw[k] for k in names}, names=names,
                         label=label, ideal=bideal))
     assert_parity(spec, errs, label)
+
+
+def _random_doc_partials(n=6, seed=4343):
+    """The random partial problems above with the sequence cut into random
+    block-aligned documents."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for label, kw, lo, hi, ck in _random_partials(n, seed):
+        nb = kw["L"] // kw["B"]
+        cuts = sorted(set(rng.choice(np.arange(1, nb), size=int(rng.integers(1, 5))).tolist()))
+        kw = dict(kw, doc_starts=[0] + [c * kw["B"] for c in cuts])
+        out.append((label.replace("rpart", "rpartdocs"), kw, lo, hi, ck))
+    return out
+
+
+RANDOM_DOC_PARTIALS = _random_doc_partials()
+
+
+@pytest.mark.parametrize("label,kw,lo,hi,ck", RANDOM_DOC_PARTIALS,
+                         ids=[r[0] for r in RANDOM_DOC_PARTIALS])
+def test_random_partial_problems_with_documents(label, kw, lo, hi, ck):
+    """A random partial launch over packed documents, forward and backward,
+    checked as the one-document random partial launches are."""
+    test_random_partial_problems(label, kw, lo, hi, ck)
