@@ -704,3 +704,38 @@ def test_packed_documents_equal_independent_problems(clean_mask):
         for full, part, idx in ((g[0], h[0], c), (g[1], h[1], xr), (g[2], h[2], c),
                                 (g[3], h[3], c), (g[4], h[4], xr), (g[5], h[5], xr)):
             np.testing.assert_allclose(full[idx], part, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("slip", ["left_side", "corrupted_by_own_position", "no_documents"])
+def test_planted_document_mistakes_are_caught(monkeypatch, slip):
+    """Plausible slips in the document rule break the hand-drawn document
+    fixture: a document boundary assigned to the earlier document, a
+    corrupted query placed by its local row instead of its block's position,
+    documents ignored."""
+    import oracle.bdattn_oracle as ob
+
+    right = ob.documents
+
+    def planted(lay, pos):
+        pos = np.asarray(pos, dtype=np.int64)
+        if slip == "left_side":
+            return np.searchsorted(np.asarray(lay.docs, np.int64), pos, side="left") - 1
+        if slip == "no_documents":
+            return np.zeros(pos.shape, np.int64)
+        return right(lay, pos)
+
+    p, want = read_golden("mask_docs_L12_B2.txt")
+    lay = layout(p["B"], 1, 1, 4, p["n_clean_q"], p["clean_q_start"], p["n_clean_kv"],
+                 corr_block_ids=p["ids"], doc_starts=p["docs"])
+    monkeypatch.setattr(ob, "documents", planted)
+    qs, qb = query_tokens(lay)
+    ks, kb = key_tokens(lay)
+    qp, kp = query_positions(lay), key_positions(lay)
+    if slip == "corrupted_by_own_position":
+        qp = np.concatenate([qp[:lay.n_clean_q], lay.n_clean_q + np.arange(lay.n_corr)])
+    qd, kd = ob.documents(lay, qp), ob.documents(lay, kp)
+    got = visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None], kp[None, :],
+                  lay.clean_mask, lay.corr_keys,
+                  corrupted_copies(lay, lay.n_clean_q)[:, None],
+                  corrupted_copies(lay, lay.n_clean_kv)[None, :], qd[:, None], kd[None, :])
+    assert not np.array_equal(got, want)
