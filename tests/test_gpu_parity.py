@@ -247,14 +247,16 @@ def packed(spec, n, seed=1234):
     return spec.with_(doc_starts=(0,) + tuple(int(c) * spec.B for c in cuts))
 
 
-@pytest.mark.parametrize("idx,n", [(2, 8), (3, 16), (1, 128), (2, 1024)],
-                         ids=["64k_docs8", "256k_docs16", "8k_docs128", "64k_docs1024"])
-def test_packed_documents_workload_sampled_parity(idx, n):
+@pytest.mark.parametrize("idx,n,cm", [(2, 8, 0), (3, 16, 0), (1, 128, 0), (2, 1024, 0), (2, 8, 1)],
+                         ids=["64k_docs8", "256k_docs16", "8k_docs128", "64k_docs1024",
+                              "64k_docs8_token_causal"])
+def test_packed_documents_workload_sampled_parity(idx, n, cm):
     """Full-size workloads with packed documents, launched as `bench.py
-    --docs n` launches them: 64K with 8 and 256K with 16 documents, and many
-    short ones (8K with 128, 64K with 1024: 64 tokens on average); the samples
-    include the blocks on both sides of two document starts (one KV group)."""
-    workload_parity(packed(CONFIGS[idx], n), groups=(0,))
+    --docs n` launches them: 64K with 8 and 256K with 16 documents, many
+    short ones (8K with 128, 64K with 1024: 64 tokens on average), and 64K
+    with 8 under the token-causal clean mask; the samples include the blocks
+    on both sides of two document starts (one KV group)."""
+    workload_parity(packed(CONFIGS[idx].with_(clean_mask=cm), n), groups=(0,))
 
 
 @pytest.mark.parametrize("idx", [1, 2], ids=[CONFIGS[i].name for i in (1, 2)])
