@@ -11,6 +11,7 @@ The entry points mirror the C ABI in include/bdattn.h: ``fwd``, ``bwd``,
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -31,7 +32,8 @@ STATUS = {0: "BDATTN_OK", -1: "BDATTN_ERR_INVALID_ARG", -2: "BDATTN_ERR_SHAPE",
 __all__ = ["Problem", "problem", "BdattnError", "lib", "fwd", "bwd", "validate",
            "workspace_size", "mask_render", "visible_pairs", "plan_stats", "version",
            "status_string", "profile_enable", "profile_read", "from_spec", "F32", "BF16",
-           "CLEAN_BLOCK_CAUSAL", "CLEAN_TOKEN_CAUSAL", "LIB_PATH", "merge"]
+           "CLEAN_BLOCK_CAUSAL", "CLEAN_TOKEN_CAUSAL", "LIB_PATH", "merge", "plan_cache_info",
+           "plan_cache_budget"]
 
 
 class BdattnError(RuntimeError):
@@ -158,12 +160,15 @@ def lib() -> ctypes.CDLL:
                              [vp, ctypes.c_size_t, vp])
     L.bdattn_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                vp, fp, vp, fp, vp, fp, vp]
+    L.bdattn_plan_cache_info.argtypes = [ctypes.POINTER(ctypes.c_int64)]
+    L.bdattn_plan_cache_budget.argtypes = [ctypes.c_size_t]
     L.bdattn_profile_enable.argtypes = [ctypes.c_int]
     L.bdattn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("bdattn_validate", "bdattn_workspace_size", "bdattn_mask_render",
                  "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_bwd",
-                 "bdattn_merge", "bdattn_profile_enable", "bdattn_profile_read"):
+                 "bdattn_merge", "bdattn_profile_enable", "bdattn_profile_read",
+                 "bdattn_plan_cache_info", "bdattn_plan_cache_budget"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -213,6 +218,19 @@ def plan_stats(p: Problem) -> dict:
     keys = ("fwd_items", "fwd_tiles", "fwd_masked_tiles", "bwd_items", "bwd_qtiles",
             "bwd_masked_qtiles", "fwd_rows_per_item", "bwd_keys_per_item")
     return dict(zip(keys, list(out)))
+
+
+def plan_cache_info() -> dict:
+    """State of the library's plan cache (plans, their host bytes, pinned
+    staging bytes, the byte budget, evictions so far)."""
+    out = (ctypes.c_int64 * 5)()
+    _check(lib().bdattn_plan_cache_info(out), "plan_cache_info")
+    return dict(zip(("plans", "host_bytes", "pinned_bytes", "budget", "evictions"), list(out)))
+
+
+def plan_cache_budget(nbytes: int) -> None:
+    """Bound the plan cache (host plans plus pinned staging) to ``nbytes``."""
+    _check(lib().bdattn_plan_cache_budget(ctypes.c_size_t(nbytes)), "plan_cache_budget")
 
 
 PROFILED_KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")
@@ -267,6 +285,13 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context: device memory the library reads on ``stream`` is
+    taken from that stream's pool, so torch's caching allocator does not hand
+    it out again while work queued on ``stream`` still uses it."""
+    return contextlib.nullcontext() if stream is None else _torch().cuda.stream(stream)
+
+
 def _workspace(p: Problem, pass_: int, device, workspace):
     torch = _torch()
     need = workspace_size(p, pass_)
@@ -278,7 +303,11 @@ def _workspace(p: Problem, pass_: int, device, workspace):
 
 
 def fwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, *, workspace=None, stream=None, out=None):
-    """Forward on the GPU. Returns (o_c, o_x, lse_c, lse_x)."""
+    """Forward on the GPU. Returns (o_c, o_x, lse_c, lse_x). ``stream`` (a
+    torch stream; default the current one) is where the work is enqueued;
+    outputs and workspace allocated here come from that stream's pool. The
+    caller orders the inputs' producers before it and the outputs' users
+    after it."""
     torch = _torch()
     dev = q_c.device if q_c.numel() else q_x.device
     if dev.type != "cuda":
@@ -290,14 +319,15 @@ def fwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, *, workspace=None, stream=None
                        (v_c, (nkv, Hkv, d), "v_c"), (q_x, (nx, H, d), "q_x"),
                        (k_x, (nx, Hkv, d), "k_x"), (v_x, (nx, Hkv, d), "v_x")):
         _expect(t, shp, dt, nm, dev)
-    if out is None:
-        o_c = torch.empty((nc, H, d), dtype=dt, device=dev)
-        o_x = torch.empty((nx, H, d), dtype=dt, device=dev)
-        lse_c = torch.empty((H, nc), dtype=torch.float32, device=dev)
-        lse_x = torch.empty((H, nx), dtype=torch.float32, device=dev)
-    else:
-        o_c, o_x, lse_c, lse_x = out
-    ws = _workspace(p, 0, dev, workspace)
+    with _on(stream):
+        if out is None:
+            o_c = torch.empty((nc, H, d), dtype=dt, device=dev)
+            o_x = torch.empty((nx, H, d), dtype=dt, device=dev)
+            lse_c = torch.empty((H, nc), dtype=torch.float32, device=dev)
+            lse_x = torch.empty((H, nx), dtype=torch.float32, device=dev)
+        else:
+            o_c, o_x, lse_c, lse_x = out
+        ws = _workspace(p, 0, dev, workspace)
     st = lib().bdattn_fwd(ctypes.byref(p), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(q_x),
                           _ptr(k_x), _ptr(v_x), _ptr(o_c), _ptr(o_x), _ptr(lse_c), _ptr(lse_x),
                           _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev, stream))
@@ -323,18 +353,19 @@ def bwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, do_c, 
                             (lse_x, (H, nx), torch.float32, "lse_x"),
                             (do_c, (nc, H, d), dt, "do_c"), (do_x, (nx, H, d), dt, "do_x")):
         _expect(t, shp, tdt, nm, dev)
-    if out is None:
-        dq_c = torch.empty((nc, H, d), dtype=dt, device=dev)
-        dq_x = torch.empty((nx, H, d), dtype=dt, device=dev)
-        dk_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
-        dv_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
-        # not written when the corrupted keys are omitted: returned as zeros
-        alloc = torch.zeros if p.omit_corr_keys else torch.empty
-        dk_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
-        dv_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
-    else:
-        dq_c, dq_x, dk_c, dv_c, dk_x, dv_x = out
-    ws = _workspace(p, 1, dev, workspace)
+    with _on(stream):
+        if out is None:
+            dq_c = torch.empty((nc, H, d), dtype=dt, device=dev)
+            dq_x = torch.empty((nx, H, d), dtype=dt, device=dev)
+            dk_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
+            dv_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
+            # not written when the corrupted keys are omitted: returned as zeros
+            alloc = torch.zeros if p.omit_corr_keys else torch.empty
+            dk_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
+            dv_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
+        else:
+            dq_c, dq_x, dk_c, dv_c, dk_x, dv_x = out
+        ws = _workspace(p, 1, dev, workspace)
     st = lib().bdattn_bwd(ctypes.byref(p), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(q_x),
                           _ptr(k_x), _ptr(v_x), _ptr(o_c), _ptr(o_x), _ptr(lse_c), _ptr(lse_x),
                           _ptr(do_c), _ptr(do_x), _ptr(dq_c), _ptr(dq_x), _ptr(dk_c), _ptr(dv_c),
@@ -355,11 +386,12 @@ def merge(o_a, lse_a, o_b, lse_b, *, stream=None, out=None):
                             (lse_a, (H, n), torch.float32, "lse_a"),
                             (lse_b, (H, n), torch.float32, "lse_b")):
         _expect(t, shp, tdt, nm, dev)
-    if out is None:
-        o = torch.empty_like(o_a)
-        lse = torch.empty_like(lse_a)
-    else:
-        o, lse = out
+    with _on(stream):
+        if out is None:
+            o = torch.empty_like(o_a)
+            lse = torch.empty_like(lse_a)
+        else:
+            o, lse = out
     st = lib().bdattn_merge(ctypes.c_int64(n), H, d, _dtype_code(o_a.dtype), _ptr(o_a),
                             _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
                             _stream(dev, stream))

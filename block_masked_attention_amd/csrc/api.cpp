@@ -4,9 +4,12 @@
 #include <math.h>
 #include <string.h>
 
-#include <map>
+#include <algorithm>
+#include <list>
+#include <memory>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/bdattn.h"
@@ -22,26 +25,134 @@ int fail(int status, const std::string& msg) {
   return status;
 }
 
-// One cached plan per distinct problem (ids included), kept for the life of
-// the process: the work list and the ids are staged once into pinned host
-// memory, from which every call copies them asynchronously into the caller's
-// workspace. Entries are never freed, so a copy still in flight always reads
-// live memory.
-struct Entry {
-  bdattn::Plan plan;
-  std::mutex mu;
-  void* staged[2] = {nullptr, nullptr};
-  size_t staged_bytes[2] = {0, 0};
+// Plan cache: one plan per distinct problem (ids and document starts
+// included), least recently used first out, bounded by bytes (the plans' host
+// memory plus their pinned staging buffers) and by entry count. A call copies
+// its plan's work lists from a pinned staging buffer into the caller's
+// workspace with an asynchronous copy on the caller's stream, and records an
+// event after it. A staging buffer is reused or freed only once the event of
+// its last copy has completed, so a copy still in flight always reads live,
+// unchanged memory. Buffers of evicted plans go to a spare pool and are handed
+// to new plans, so a stream of distinct problems (a new packed-document layout
+// every training step) allocates pinned memory only while the pool is short.
+struct Staged {
+  void* ptr = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;     // recorded after the last copy from ptr
+  hipStream_t stream = nullptr;  // the stream of that copy
+  bool used = false;
 };
 
+void release_staged(Staged* st);
+
+struct Entry {
+  std::string key;
+  bdattn::Plan plan;
+  size_t host_bytes = 0;
+  std::mutex mu;  // guards staged
+  Staged staged[2];
+  ~Entry() {
+    for (Staged& st : staged) release_staged(&st);
+  }
+};
+
+size_t plan_host_bytes(const bdattn::Plan& plan) {
+  return sizeof(bdattn::Plan) + plan.fwd.capacity() * sizeof(bdattn::FwdItem) +
+         plan.bwd.capacity() * sizeof(bdattn::BwdItem) +
+         plan.P.ids.capacity() * sizeof(int32_t) + plan.P.docs.capacity() * sizeof(int32_t) +
+         plan.P.spans.capacity() * sizeof(BdDocSpan);
+}
+
+constexpr size_t kDefaultBudget = size_t(256) << 20;
+constexpr size_t kMaxEntries = 1024;
+
 struct PlanCache {
-  std::mutex mu;
-  std::map<std::string, Entry*> entries;
+  std::mutex mu;  // guards everything below except the spare pool
+  std::list<std::shared_ptr<Entry>> lru;  // front: most recently used
+  std::unordered_map<std::string, std::list<std::shared_ptr<Entry>>::iterator> index;
+  size_t host_bytes = 0;
+  size_t budget = kDefaultBudget;
+  int64_t evictions = 0;
+  std::mutex spare_mu;  // guards spare, spare_bytes, pinned_bytes
+  std::vector<Staged> spare;  // staging buffers of evicted plans
+  size_t spare_bytes = 0;
+  size_t pinned_bytes = 0;  // every live staging buffer, in entries and spare
 };
 
 PlanCache& cache() {
   static PlanCache* c = new PlanCache;  // never destroyed (outlives the HIP runtime)
   return *c;
+}
+
+bool copy_done(const Staged& st) { return !st.used || hipEventQuery(st.done) != hipErrorNotReady; }
+
+void free_staged(Staged* st) {
+  if (st->done) (void)hipEventDestroy(st->done);
+  if (st->ptr) (void)hipHostFree(st->ptr);
+  *st = Staged();
+}
+
+// An evicted plan's staging buffer joins the spare pool. Completed spare
+// buffers beyond a quarter of the budget are freed, oldest first.
+void release_staged(Staged* st) {
+  if (!st->ptr) return;
+  PlanCache& c = cache();
+  std::vector<Staged> drop;
+  {
+    std::lock_guard<std::mutex> lock(c.spare_mu);
+    c.spare.push_back(*st);
+    c.spare_bytes += st->cap;
+    const size_t keep = c.budget / 4;
+    for (size_t i = 0; i < c.spare.size() && c.spare_bytes > keep;) {
+      if (copy_done(c.spare[i])) {
+        c.spare_bytes -= c.spare[i].cap;
+        c.pinned_bytes -= c.spare[i].cap;
+        drop.push_back(c.spare[i]);
+        c.spare.erase(c.spare.begin() + long(i));
+      } else {
+        ++i;
+      }
+    }
+  }
+  *st = Staged();
+  for (Staged& d : drop) free_staged(&d);
+}
+
+// A staging buffer of at least `bytes`: a completed spare one that is not
+// more than twice too large, else a new pinned allocation.
+int take_staged(size_t bytes, Staged* out, std::string* msg) {
+  PlanCache& c = cache();
+  {
+    std::lock_guard<std::mutex> lock(c.spare_mu);
+    for (size_t i = 0; i < c.spare.size(); ++i) {
+      Staged& st = c.spare[i];
+      if (st.cap >= bytes && st.cap <= 2 * bytes + (size_t(64) << 10) && copy_done(st)) {
+        *out = st;
+        c.spare_bytes -= st.cap;
+        c.spare.erase(c.spare.begin() + long(i));
+        return BDATTN_OK;
+      }
+    }
+  }
+  Staged st;
+  st.cap = std::max(bytes, size_t(64) << 10);
+  hipError_t er = hipHostMalloc(&st.ptr, st.cap, hipHostMallocDefault);
+  if (er != hipSuccess) {
+    *msg = std::string("hipHostMalloc: ") + hipGetErrorString(er);
+    return BDATTN_ERR_HIP;
+  }
+  er = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
+  if (er != hipSuccess) {
+    (void)hipHostFree(st.ptr);
+    *msg = std::string("hipEventCreate: ") + hipGetErrorString(er);
+    return BDATTN_ERR_HIP;
+  }
+  {
+    std::lock_guard<std::mutex> lock(c.spare_mu);
+    c.pinned_bytes += st.cap;
+  }
+  *out = st;
+  return BDATTN_OK;
 }
 
 std::string plan_key(const bdattn::Problem& P) {
@@ -57,15 +168,53 @@ std::string plan_key(const bdattn::Problem& P) {
   return k;
 }
 
-Entry* get_entry(const bdattn::Problem& P) {
+// The plan of P, built on first use. The returned reference keeps the entry
+// alive even if it is evicted meanwhile.
+std::shared_ptr<Entry> get_entry(const bdattn::Problem& P) {
   PlanCache& c = cache();
-  const std::string key = plan_key(P);
+  std::string key = plan_key(P);
+  {
+    std::lock_guard<std::mutex> lock(c.mu);
+    auto it = c.index.find(key);
+    if (it != c.index.end()) {
+      c.lru.splice(c.lru.begin(), c.lru, it->second);
+      return *it->second;
+    }
+  }
+  auto e = std::make_shared<Entry>();
+  bdattn::build_plan(P, &e->plan);  // outside the lock: planning may take milliseconds
+  e->host_bytes = plan_host_bytes(e->plan);
+  e->key = std::move(key);
+  std::vector<std::shared_ptr<Entry>> evicted;  // released after the lock
   std::lock_guard<std::mutex> lock(c.mu);
-  auto it = c.entries.find(key);
-  if (it != c.entries.end()) return it->second;
-  Entry* e = new Entry;
-  bdattn::build_plan(P, &e->plan);
-  c.entries[key] = e;
+  auto it = c.index.find(e->key);
+  if (it != c.index.end()) {  // another thread built it meanwhile
+    c.lru.splice(c.lru.begin(), c.lru, it->second);
+    return *it->second;
+  }
+  c.lru.push_front(e);
+  c.index[e->key] = c.lru.begin();
+  c.host_bytes += e->host_bytes;
+  // pinned bytes held by live plans; an evicted plan's buffers leave that
+  // count when the plan is released (after the lock)
+  size_t live_pinned;
+  {
+    std::lock_guard<std::mutex> l2(c.spare_mu);
+    live_pinned = c.pinned_bytes - c.spare_bytes;
+  }
+  while (c.lru.size() > 1 &&
+         (c.lru.size() > kMaxEntries || c.host_bytes + live_pinned > c.budget)) {
+    std::shared_ptr<Entry> old = c.lru.back();
+    c.lru.pop_back();
+    c.index.erase(old->key);
+    c.host_bytes -= old->host_bytes;
+    {
+      std::lock_guard<std::mutex> l3(old->mu);
+      live_pinned -= std::min(live_pinned, old->staged[0].cap + old->staged[1].cap);
+    }
+    ++c.evictions;
+    evicted.push_back(std::move(old));
+  }
   return e;
 }
 
@@ -86,30 +235,35 @@ int check_ptr(const void* p, int64_t elems, const char* name) {
   return BDATTN_OK;
 }
 
-// Copy the corrupted block ids, the document table and the work lists (staged once in pinned host
-// memory) into the workspace head, asynchronously on the caller's stream.
+// Copy the corrupted block ids, the document table and the work lists
+// (staged once per plan in pinned host memory) into the workspace head,
+// asynchronously on the caller's stream, and record the copy's completion.
+// A copy from the same buffer on another stream first waits for the previous
+// copy, so the recorded event always covers every copy still reading it.
 int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t s) {
   const size_t bytes = w.staged;
-  void* src = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(e->mu);
-    if (!e->staged[pass]) {
-      void* h = nullptr;
-      hipError_t er = hipHostMalloc(&h, bytes, hipHostMallocDefault);
-      if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("hipHostMalloc: ") + hipGetErrorString(er));
-      memset(h, 0, bytes);
-      const bdattn::Plan& plan = e->plan;
-      memcpy((char*)h + w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t));
-      memcpy((char*)h + w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan));
-      memcpy((char*)h + w.q_items, plan.fwd.data(), w.q_items_bytes);
-      if (pass == 1) memcpy((char*)h + w.kv_items, plan.bwd.data(), w.kv_items_bytes);
-      e->staged[pass] = h;
-      e->staged_bytes[pass] = bytes;
-    }
-    src = e->staged[pass];
+  std::lock_guard<std::mutex> lock(e->mu);
+  Staged& st = e->staged[pass];
+  if (!st.ptr) {
+    std::string msg;
+    int rc = take_staged(bytes, &st, &msg);
+    if (rc != BDATTN_OK) return fail(rc, msg);
+    char* h = (char*)st.ptr;
+    memset(h, 0, bytes);
+    const bdattn::Plan& plan = e->plan;
+    memcpy(h + w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t));
+    memcpy(h + w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan));
+    memcpy(h + w.q_items, plan.fwd.data(), w.q_items_bytes);
+    if (pass == 1) memcpy(h + w.kv_items, plan.bwd.data(), w.kv_items_bytes);
   }
-  hipError_t er = hipMemcpyAsync(ws, src, bytes, hipMemcpyHostToDevice, s);
-  if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("hipMemcpyAsync: ") + hipGetErrorString(er));
+  hipError_t er = hipSuccess;
+  if (st.used && st.stream != s && hipEventQuery(st.done) == hipErrorNotReady)
+    er = hipStreamWaitEvent(s, st.done, 0);
+  if (er == hipSuccess) er = hipMemcpyAsync(ws, st.ptr, bytes, hipMemcpyHostToDevice, s);
+  if (er == hipSuccess) er = hipEventRecord(st.done, s);
+  if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("workspace upload: ") + hipGetErrorString(er));
+  st.used = true;
+  st.stream = s;
   return BDATTN_OK;
 }
 
@@ -178,6 +332,27 @@ int bdattn_profile_read(double* ms, int64_t* launches) {
   return st;
 }
 
+int bdattn_plan_cache_info(int64_t out[5]) {
+  if (!out) return fail(BDATTN_ERR_INVALID_ARG, "out is NULL");
+  PlanCache& c = cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  std::lock_guard<std::mutex> l2(c.spare_mu);
+  out[0] = int64_t(c.lru.size());
+  out[1] = int64_t(c.host_bytes);
+  out[2] = int64_t(c.pinned_bytes);
+  out[3] = int64_t(c.budget);
+  out[4] = c.evictions;
+  return BDATTN_OK;
+}
+
+int bdattn_plan_cache_budget(size_t bytes) {
+  if (bytes < (size_t(1) << 20)) return fail(BDATTN_ERR_INVALID_ARG, "plan cache budget below 1 MiB");
+  PlanCache& c = cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  c.budget = bytes;
+  return BDATTN_OK;
+}
+
 int bdattn_version(void) { return BDATTN_VERSION; }
 
 const char* bdattn_status_string(int status) {
@@ -239,7 +414,8 @@ int bdattn_plan_stats(const bdattn_problem* p, int64_t out[8]) {
   bdattn::Problem P;
   int st = load(p, &P);
   if (st != BDATTN_OK) return st;
-  const bdattn::Plan* plan = &get_entry(P)->plan;
+  std::shared_ptr<Entry> entry = get_entry(P);
+  const bdattn::Plan* plan = &entry->plan;
   out[0] = int64_t(plan->fwd.size());
   out[1] = plan->fwd_tiles;
   out[2] = plan->fwd_masked_tiles;
@@ -266,7 +442,7 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
       (st = check_ptr(o_c, nqc, "o_c")) || (st = check_ptr(o_x, nqx, "o_x")) ||
       (st = check_ptr(lse_c, nqc, "lse_c")) || (st = check_ptr(lse_x, nqx, "lse_x")))
     return st;
-  Entry* entry = get_entry(P);
+  std::shared_ptr<Entry> entry = get_entry(P);
   const bdattn::Plan* plan = &entry->plan;
   const bdattn::WsLayout w = bdattn::workspace_layout(P, 0);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
@@ -274,7 +450,7 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
                                           std::to_string(w.total) + " bytes");
   hipStream_t s = (hipStream_t)hip_stream;
   char* ws = (char*)workspace;
-  if ((st = upload(entry, 0, w, ws, s))) return st;
+  if ((st = upload(entry.get(), 0, w, ws, s))) return st;
   bdattn::FwdArgs a;
   a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
   a.o_c = o_c; a.o_x = o_x; a.lse_c = lse_c; a.lse_x = lse_x;
@@ -317,7 +493,7 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
       (st = check_ptr(dk_x, P.corr_keys ? nkx : 0, "dk_x")) ||
       (st = check_ptr(dv_x, P.corr_keys ? nkx : 0, "dv_x")))
     return st;
-  Entry* entry = get_entry(P);
+  std::shared_ptr<Entry> entry = get_entry(P);
   const bdattn::Plan* plan = &entry->plan;
   const bdattn::WsLayout w = bdattn::workspace_layout(P, 1);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
@@ -325,7 +501,7 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
                                           std::to_string(w.total) + " bytes");
   hipStream_t s = (hipStream_t)hip_stream;
   char* ws = (char*)workspace;
-  if ((st = upload(entry, 1, w, ws, s))) return st;
+  if ((st = upload(entry.get(), 1, w, ws, s))) return st;
   bdattn::BwdArgs a;
   a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
   a.o_c = o_c; a.o_x = o_x; a.do_c = do_c; a.do_x = do_x; a.lse_c = lse_c; a.lse_x = lse_x;

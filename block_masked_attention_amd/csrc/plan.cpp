@@ -6,7 +6,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <map>
 #include <numeric>
 
 namespace bdattn {
@@ -54,17 +53,18 @@ void build_spans(Problem* P) {
 // first. One document keeps the plain longest-first order. (The same grouping
 // of the key-tile list measured faster with 16 documents at 256K, but 11%
 // slower with 1024, so that list stays longest first.)
+// `doc` of an item is the index of its document in P.docs (0..n_docs-1).
 template <class T>
-void order_items(std::vector<T>* tiles, bool docs) {
-  if (!docs) {
+void order_items(std::vector<T>* tiles, size_t n_docs) {
+  if (n_docs <= 1) {
     std::stable_sort(tiles->begin(), tiles->end(),
                      [](const T& a, const T& b) { return a.cost > b.cost; });
     return;
   }
-  std::map<int32_t, int64_t> doc_cost;
-  for (const T& t : *tiles) doc_cost[t.doc] += t.cost;
+  std::vector<int64_t> doc_cost(n_docs, 0);
+  for (const T& t : *tiles) doc_cost[size_t(t.doc)] += t.cost;
   std::stable_sort(tiles->begin(), tiles->end(), [&](const T& a, const T& b) {
-    const int64_t ca = doc_cost[a.doc], cb = doc_cost[b.doc];
+    const int64_t ca = doc_cost[size_t(a.doc)], cb = doc_cost[size_t(b.doc)];
     if (ca != cb) return ca > cb;
     if (a.doc != b.doc) return a.doc < b.doc;
     return a.cost > b.cost;
@@ -283,13 +283,15 @@ void build_plan(const Problem& P, Plan* plan) {
           cost += nxt;
           masked += nxt;
         }
-        int32_t doc = 0;  // the document of the tile's first row
-        if (!P.spans.empty())
-          doc = P.spans[size_t(s == 0 ? (P.clean_q_start + r0) / P.B : P.ids[r0 / P.B])].lo;
+        int32_t doc = 0;  // index of the document of the tile's first row
+        if (!P.spans.empty()) {
+          const int32_t lo = P.spans[size_t(s == 0 ? (P.clean_q_start + r0) / P.B : P.ids[r0 / P.B])].lo;
+          doc = int32_t(std::lower_bound(P.docs.begin(), P.docs.end(), lo) - P.docs.begin());
+        }
         tiles.push_back({t, s, cost, masked, doc});
       }
     }
-    order_items(&tiles, !P.spans.empty());
+    order_items(&tiles, P.spans.empty() ? 0 : P.docs.size());
     plan->fwd.reserve(tiles.size() * NHG);
     // consecutive workgroup ids land on different XCDs; keep one head group
     // per id residue so an XCD's L2 sees one KV head's prefix
@@ -371,7 +373,7 @@ void build_plan(const Problem& P, Plan* plan) {
       const int64_t qt = qtiles(x0, x1);
       tiles.push_back({kt, 1, it, x1 - x0, qt, qt, 0});
     }
-    order_items(&tiles, false);
+    order_items(&tiles, 0);
     plan->bwd.reserve(tiles.size() * P.Hkv);
     for (const T& t : tiles) {
       for (int g = 0; g < P.Hkv; ++g) {

@@ -181,6 +181,20 @@ int bdattn_visible_pairs(const bdattn_problem* p, int64_t* pairs);
  *  fwd rows per work item, bwd keys per work item}. */
 int bdattn_plan_stats(const bdattn_problem* p, int64_t out[8]);
 
+/* The plan cache (host-only, no HIP calls). The library keeps, per distinct
+ * problem descriptor, the planned work lists and a pinned host staging copy
+ * of them, from which every call copies into its workspace asynchronously.
+ * The cache is bounded: least recently used plans are evicted once the
+ * plans' host memory plus the pinned staging memory of live plans exceeds
+ * the budget (default 256 MiB), or beyond 1024 plans. An evicted plan's
+ * staging buffer is reused or freed only after an event recorded behind its
+ * last copy has completed. bdattn_plan_cache_info writes out[0..4] = {plans,
+ * plan host bytes, pinned staging bytes (live and spare), budget, evictions
+ * so far}. bdattn_plan_cache_budget sets the budget in bytes (>= 1 MiB,
+ * BDATTN_ERR_INVALID_ARG otherwise); it applies from the next new plan on. */
+int bdattn_plan_cache_info(int64_t out[5]);
+int bdattn_plan_cache_budget(size_t bytes);
+
 /* Forward (Implementation 1 of the appendix, fused into one launch): writes
  * o_c [n_clean_q,H,d], o_x [n_corr,H,d], lse_c [H,n_clean_q],
  * lse_x [H,n_corr]. Inputs q_c [n_clean_q,H,d], k_c/v_c [n_clean_kv,Hkv,d],

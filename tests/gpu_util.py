@@ -52,18 +52,77 @@ def oracle_full(spec, t, rounding=None):
     return dict(zip(OUT_NAMES, f + g))
 
 
+def oracle_backward(spec, t, saved, rounding=None):
+    """The oracle's gradients given saved forward outputs ``saved`` (a dict
+    with o_c, o_x, lse_c, lse_x as float64 arrays)."""
+    lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start,
+                 spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks, spec.corr_block_ids,
+                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts)
+    orc = Oracle(lay, *[f64(t[k]) for k in INPUT_NAMES], *[f64(t[k]) for k in GRAD_NAMES],
+                 operand_rounding=rounding)
+    g = orc.backward(O=np.concatenate([saved["o_c"], saved["o_x"]]),
+                     LSE=np.concatenate([saved["lse_c"], saved["lse_x"]], axis=1))
+    return dict(zip(OUT_NAMES[4:], g))
+
+
+def saved_on_device(saved, spec, device):
+    """Saved forward outputs as the backward's device inputs: O in the
+    problem's dtype (exact for bf16 values), LSE in float32. Returns the
+    tensors and the float64 values they hold."""
+    dt = spec.torch_dtype()
+    dev = {k: torch.tensor(np.ascontiguousarray(saved[k]), dtype=torch.float64)
+           .to(dt if k.startswith("o_") else torch.float32).to(device) for k in OUT_NAMES[:4]}
+    return dev, {k: f64(v) for k, v in dev.items()}
+
+
+def check_fwd_bwd(spec, t, label, got=None):
+    """Parity of one problem (oracle over the whole problem). fp32: the
+    forward and the backward of the GPU chain against the exact oracle. bf16:
+    the forward against the exact and the bf16-operand oracle; the backward
+    run on the bf16-operand oracle's saved O and LSE, against the bf16-operand
+    oracle's backward on the same saved outputs. The backward reads D = <dO, O>
+    from the saved O, and two results that each round O correctly to bf16 can
+    differ by an ulp per element, which moves the gradients of rows with few
+    keys by several percent of their RMS whichever implementation computes
+    them (the oracle against itself included), so the backward is compared on
+    a common saved O. The GPU chain's own gradients (its forward's O) are
+    reported with the literal measure."""
+    if got is None:
+        got = run_gpu(spec, t)
+    want = oracle_full(spec, t)
+    if spec.dtype == "f32":
+        return compare(spec, got, want, label=label)
+    ideal = oracle_full(spec, t, "bf16")
+    errs = compare(spec, got, want, names=OUT_NAMES[:4], label=label + " forward", ideal=ideal)
+    dev, saved = saved_on_device(ideal, spec, got["o_c"].device)
+    p = bd.from_spec(spec)
+    gb = bd.bwd(p, *[t[k] for k in INPUT_NAMES], dev["o_c"], dev["o_x"], dev["lse_c"],
+                dev["lse_x"], t["do_c"], t["do_x"])
+    torch.cuda.synchronize()
+    ib = oracle_backward(spec, t, saved, "bf16")
+    errs.update(compare(spec, dict(zip(OUT_NAMES[4:], gb)), want, names=OUT_NAMES[4:],
+                        label=label + " backward on the oracle's saved O, LSE", ideal=ib))
+    chain = {k: f"{rms_err(f64(got[k]), np.asarray(want[k])):.2e}" for k in OUT_NAMES[4:]
+             if np.asarray(want[k]).size}
+    say(f"  {label} GPU chain (its own forward's O) gradients, literal max|x-y|/rms(y):", chain)
+    return errs
+
+
 def metric(spec):
     return rel_err if spec.dtype == "f32" else rms_err
 
 
 # fp32: max|x-y| / max|y| <= 1e-4 per output tensor.
-# bf16: max|x-y| / rms(y) per output tensor may exceed, by at most 2e-2, the
-# same measure of the oracle evaluated with bf16 operands and bf16 outputs
-# (Oracle(..., operand_rounding="bf16")): storing the exact result in bf16
-# alone already scores 0.02-0.15 on these heavy-tailed outputs. A tensor
-# also passes when every element meets the element-wise bound of compare():
-# where one element is tens of RMS large, a one-ulp rounding difference
-# there alone exceeds the norm-wise margin.
+# bf16: one element-wise gate per output tensor. With y the exact oracle and
+# i the oracle evaluated with bf16 operands and bf16 outputs
+# (Oracle(..., operand_rounding="bf16"), pinned element by element against a
+# scalar reference), every element must satisfy
+#     |x - i| <= ulp_bf16(i) + 2e-2 * rms(y).
+# The ulp allows the two bf16 results to round to neighbouring values; the
+# 2e-2 * rms(y) is the stated bound. The literal measure max|x-y|/rms(y) is
+# reported beside it: storing even the exact result in bf16 scores 0.02-0.15
+# on these heavy-tailed outputs, so that number alone cannot be held to 2e-2.
+# LSE is float32 in every configuration and is held to max|x-y|/rms(y) <= 2e-2.
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
@@ -75,14 +134,20 @@ def bf16_ulp(y):
     return np.where(a > 0, np.exp2(e - 7), 0.0)
 
 
+def bf16_gate(x, i, y):
+    """max over elements of (|x - i| - ulp_bf16(i)) / rms(y), floored at 0:
+    the bf16 gate's measure, which must be <= 2e-2."""
+    r = float(np.sqrt(np.mean(y * y))) or 1.0
+    return max(0.0, float(np.max(np.abs(x - i) - bf16_ulp(i)))) / r
+
+
 def compare(spec, got: dict, want: dict, names=OUT_NAMES, label="", ideal=None):
-    """Per output tensor: (error of the GPU result, error of the bf16-operand
-    oracle or 0, element-wise bound met) with the dtype's metric against the
-    exact oracle. The element-wise bound (bf16 only): every element within the
-    bf16-operand oracle's own error at that element, plus one bf16 unit in the
-    last place of the element (the fp32 result may round to the other
-    neighbour of the exact value), plus 2e-2 of the tensor's RMS."""
-    m = metric(spec)
+    """Per output tensor, a dict with the gated measure (``gate``) and, for
+    the report, the literal measure of the GPU result (``raw``) and of the
+    bf16-operand oracle (``ideal``) against the exact oracle. fp32: gate =
+    max|x-y|/max|y|. bf16 outputs (O, dQ, dK, dV): gate = bf16_gate(x, i, y),
+    which needs the bf16-operand oracle's values ``ideal``. LSE: gate =
+    max|x-y|/rms(y)."""
     errs = {}
     for k in names:
         if k not in want:
@@ -94,26 +159,33 @@ def compare(spec, got: dict, want: dict, names=OUT_NAMES, label="", ideal=None):
         if w.size == 0:
             continue
         assert np.isfinite(g).all(), f"{label} {k}: non-finite values"
-        base = m(np.asarray(ideal[k], np.float64), w) if ideal is not None else 0.0
-        elem = False
-        if ideal is not None and spec.dtype == "bf16":
+        if spec.dtype == "f32":
+            errs[k] = dict(gate=rel_err(g, w), raw=rel_err(g, w), ideal=0.0)
+            continue
+        raw = rms_err(g, w)
+        if k.startswith("lse"):
+            errs[k] = dict(gate=raw, raw=raw, ideal=0.0)
+        else:
+            assert ideal is not None, "bf16 parity needs the bf16-operand oracle"
             i = np.asarray(ideal[k], np.float64)
-            slack = np.abs(i - w) + bf16_ulp(w) + TOL["bf16"] * np.sqrt(np.mean(w * w))
-            elem = bool(np.all(np.abs(g - w) <= slack))
-        errs[k] = (m(g, w), base, elem)
-        if spec.dtype == "bf16" and os.environ.get("BDATTN_METRICS_LOG"):
+            errs[k] = dict(gate=bf16_gate(g, i, w), raw=raw, ideal=rms_err(i, w))
+        if os.environ.get("BDATTN_METRICS_LOG"):
             with open(os.environ["BDATTN_METRICS_LOG"], "a") as f:
-                f.write(json.dumps(dict(label=label, out=k, ideal=base, **bf16_metrics(g, w)))
-                        + "\n")
-    say(f"  {label} errors (gpu, bf16-operand oracle):",
-        {k: f"{v[0]:.2e},{v[1]:.2e}" for k, v in errs.items()})
+                f.write(json.dumps(dict(label=label, out=k, gate=errs[k]["gate"],
+                                        ideal=errs[k]["ideal"], **bf16_metrics(g, w))) + "\n")
+    if spec.dtype == "f32":
+        say(f"  {label} max|x-y|/max|y|:", {k: f"{v['gate']:.2e}" for k, v in errs.items()})
+    else:
+        say(f"  {label} gate max(|x-i|-ulp(i))/rms(y) [literal max|x-y|/rms(y); "
+            f"bf16-operand oracle's]:",
+            {k: f"{v['gate']:.2e} [{v['raw']:.2e}; {v['ideal']:.2e}]" for k, v in errs.items()})
     return errs
 
 
 def assert_parity(spec, errs, label=""):
     tol = TOL[spec.dtype]
-    bad = {k: v for k, v in errs.items() if not (v[0] <= tol + v[1] or v[2])}
-    assert not bad, f"{label}: errors above {tol} (+ bf16-operand oracle error): {bad}"
+    bad = {k: v for k, v in errs.items() if not v["gate"] <= tol}
+    assert not bad, f"{label}: parity gate above {tol}: {bad}"
 
 
 # ------------------------------------------------------------ sub-problems

@@ -261,3 +261,36 @@ def test_plan_covers_every_visible_tile():
             assert st["fwd_tiles"] == want_tiles * heads_groups
         kt = -(-nkv // 128) + (0 if p.omit_corr_keys else -(-nx // 128))
         assert st["bwd_items"] == kt * int(p.Hkv)
+
+
+def test_plan_cache_stays_bounded_under_new_document_layouts():
+    """A training loop with packed documents presents a new document layout
+    every step. 1000 distinct layouts of a 64K problem (each plan several
+    hundred KB) keep the cache within its budget, and a layout planned again
+    after its eviction gets the same plan."""
+    before = bd.plan_cache_info()
+    bd.plan_cache_budget(8 << 20)
+    try:
+        rng = np.random.default_rng(7)
+        L, B = 65536, 32
+        first = None
+        for i in range(1000):
+            cuts = np.sort(rng.choice(np.arange(1, L // B), 15, replace=False)) * B
+            p = bd.problem(B, 32, 8, 128, "bf16", L, doc_starts=[0] + cuts.tolist())
+            st = bd.plan_stats(p)
+            if first is None:
+                first = (cuts, st)
+            info = bd.plan_cache_info()
+            assert info["host_bytes"] + info["pinned_bytes"] <= (8 << 20) + (2 << 20), info
+        assert info["evictions"] >= before["evictions"] + 900
+        assert info["plans"] < 100
+        again = bd.plan_stats(bd.problem(B, 32, 8, 128, "bf16", L,
+                                         doc_starts=[0] + first[0].tolist()))
+        assert again == first[1]
+    finally:
+        bd.plan_cache_budget(before["budget"])
+
+
+def test_plan_cache_budget_is_validated():
+    with pytest.raises(bd.BdattnError):
+        bd.plan_cache_budget(1000)

@@ -1,16 +1,21 @@
 """Parity of the HIP path (through the C ABI) with the float64 oracle.
 
 Tolerances: fp32 problems max|x-y|/max|y| <= 1e-4 per output tensor. bf16
-problems: max|x-y|/rms(y) per output tensor (O, LSE, dQ, dK, dV of each
-stream) at most 2e-2 above the same measure of the oracle evaluated with bf16
-operands and bf16 outputs (storing even the exact result in bf16 scores
-0.02-0.15 on these outputs, whose magnitudes vary by orders between rows).
+problems: every element of O, dQ, dK and dV within one bf16 ulp plus 2e-2 of
+the exact result's RMS of the oracle evaluated with bf16 operands and bf16
+outputs; LSE (float32) max|x-y|/rms(y) <= 2e-2. The literal measure
+max|x-y|/rms(y) against the exact oracle is printed for every tensor (storing
+even the exact result in bf16 scores 0.02-0.15 on these outputs, whose
+magnitudes vary by orders between rows).
 
-Small problems are compared element by element on every output. The five
+Small problems are compared element by element on every output; in bf16 the
+backward is run on the bf16-operand oracle's saved O and LSE and compared
+with that oracle's backward on the same saved outputs (see
+gpu_util.check_fwd_bwd for why). The five
 full-size workloads are compared on sampled query blocks, sampled corrupted
-blocks and the clean keys of late blocks (oracle sub-problems, see
-gpu_util), and every output element is checked against identities that hold
-at any size.
+blocks, the clean keys of late blocks and, at 8K, of key block 0 and the
+middle block (oracle sub-problems, see gpu_util), and every output element
+is checked against identities that hold at any size.
 """
 import time
 import zlib
@@ -20,8 +25,7 @@ import pytest
 import torch
 
 from tests._helpers import f64
-from tests.gpu_util import (OUT_NAMES, _rounding, assert_parity, clear_host_cache, compare,
-                            oracle_full,
+from tests.gpu_util import (OUT_NAMES, assert_parity, check_fwd_bwd, clear_host_cache, compare,
                             run_gpu, say, sub_clean_block, sub_clean_keys, sub_corr_block)
 from workloads import CONFIGS, Spec, make_inputs, small_spec
 
@@ -37,12 +41,8 @@ def full_parity(spec, label):
     _need_gpu()
     say(f"[gpu] {label}: {spec}")
     t = make_inputs(spec, device="cuda")
-    got = run_gpu(spec, t)
-    want = oracle_full(spec, t)
-    ideal = oracle_full(spec, t, "bf16") if spec.dtype == "bf16" else None
-    errs = compare(spec, got, want, label=label, ideal=ideal)
+    errs = check_fwd_bwd(spec, t, label)
     assert_parity(spec, errs, label)
-    return got, want
 
 
 SMALL = [
@@ -181,7 +181,13 @@ def _identities(spec, t, got):
             f"<dQ,q> = <dK,k> identity, kv head {g}: {a2.item()} vs {b2.item()}"
 
 
-def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
+def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None, long_keys=(),
+             with_keys=True):
+    """Sampled outputs of the GPU result ``got`` and of the oracle: query
+    blocks of both streams (O, LSE, dQ; corrupted dK/dV), and the clean
+    dK/dV of the last key blocks (few query blocks see them) plus, for the
+    first KV group, ``long_keys``: key blocks whose gradients accumulate over
+    long runs of query blocks (key block 0 is seen by every query)."""
     B = spec.B
     if spec.n_clean_kv > 100_000:
         n_blocks = 1  # each sampled block carries a prefix of 10^5+ keys
@@ -219,7 +225,8 @@ def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None):
             for k in ("dk_x", "dv_x"):
                 want[k].append(r[k].ravel())
                 have[k].append(f64(got[k][r0:r1, k0:k1]).ravel())
-        for kb in key_blocks:
+        kbs = key_blocks if g != kv_groups[0] else sorted(set(key_blocks) | set(long_keys))
+        for kb in (kbs if with_keys else ()):
             say(f"  oracle clean keys of block {kb}, kv head {g}")
             r = sub_clean_keys(spec, t, kb, g, rounding)
             (a0, a1), (k0, k1) = r["keys"], r["kv"]
@@ -265,6 +272,20 @@ def test_token_causal_workload_sampled_parity(idx):
     workload_parity(CONFIGS[idx].with_(clean_mask=1))
 
 
+def long_key_blocks(spec):
+    """Clean key blocks checked element-wise whose dK/dV accumulate over long
+    runs of query blocks: key block 0 (seen by every query) and the middle
+    block, where the oracle for them costs seconds (the 8K workload: 16,384
+    and 8,192 query rows, each with its full visible prefix). At 64K and
+    beyond one such block costs the oracle tens of minutes (every row that
+    sees it needs its whole forward); there the whole-tensor identities and
+    the 8K check stand in."""
+    if spec.n_clean_kv > 8192 or spec.clean_q_start:
+        return ()
+    nb = spec.n_clean_kv // spec.B
+    return (0, nb // 2)
+
+
 def workload_parity(spec, groups=None):
     _need_gpu()
     say(f"[gpu] workload {spec.name} (clean mask {spec.clean_mask}): {spec.description}")
@@ -278,11 +299,13 @@ def workload_parity(spec, groups=None):
     say(f"  identities checked: {time.perf_counter() - t0:.1f} s")
     if groups is None:
         groups = (0,) if spec.Hkv == 1 else (0, spec.Hkv - 1)
-    have, want = _sampled(spec, t, got, kv_groups=groups)
+    long_keys = long_key_blocks(spec)
+    have, want = _sampled(spec, t, got, kv_groups=groups, long_keys=long_keys)
     say(f"  exact oracle samples: {time.perf_counter() - t0:.1f} s")
     ideal = None
     if spec.dtype == "bf16":
-        _, ideal = _sampled(spec, t, got, kv_groups=groups, rounding="bf16")
+        _, ideal = _sampled(spec, t, got, kv_groups=groups, rounding="bf16",
+                            long_keys=long_keys)
         say(f"  bf16-operand oracle samples: {time.perf_counter() - t0:.1f} s")
     errs = compare(spec, have, want, names=list(want), label=spec.name, ideal=ideal)
     assert_parity(spec, errs, spec.name)
@@ -370,3 +393,32 @@ def test_random_packed_documents(label, kw):
 @pytest.mark.parametrize("label,kw", RANDOM, ids=[r[0] for r in RANDOM])
 def test_random_small_problems(label, kw):
     full_parity(small_spec(name=label, seed=zlib.crc32(label.encode()) % 10000, **kw), label)
+
+
+def test_side_stream_calls_keep_their_memory():
+    """fwd/bwd enqueued on a side stream, with the current stream allocating
+    and overwriting freshly freed memory while that work is queued behind a
+    long kernel: the results equal those of calls on the current stream
+    (the workspace and outputs belong to the side stream's pool)."""
+    _need_gpu()
+    import block_masked_attention_amd as bd
+    spec = small_spec(L=2048, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=12)
+    t = make_inputs(spec, device="cuda")
+    want = run_gpu(spec, t)
+    p = bd.from_spec(spec)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    big = torch.randn(4096, 4096, device="cuda")
+    with torch.cuda.stream(side):
+        for _ in range(20):  # keep the side stream busy before the bdattn calls
+            big = big @ big.T / 4096.0
+    f = bd.fwd(p, *[t[k] for k in ("q_c", "k_c", "v_c", "q_x", "k_x", "v_x")], stream=side)
+    g = bd.bwd(p, *[t[k] for k in ("q_c", "k_c", "v_c", "q_x", "k_x", "v_x")], *f,
+               t["do_c"], t["do_x"], stream=side)
+    for _ in range(8):  # the current stream reuses whatever the caching allocator frees
+        junk = torch.full((8 << 20,), float("nan"), device="cuda")
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for k, a in zip(OUT_NAMES, tuple(f) + tuple(g)):
+        assert torch.equal(a, want[k]), k

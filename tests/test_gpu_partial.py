@@ -9,17 +9,19 @@ returns the parts of the gradients.
 Checked against the float64 oracle: each partial forward against the
 oracle's partial layout; the merged forward and the assembled gradients
 against the oracle's complete problem. Tolerances are those of the full
-parity tests (fp32: 1e-4 norm-wise; bf16: at most 2e-2 above the
-bf16-operand oracle's own error, max|x-y|/rms(y) per tensor).
+parity tests (fp32: 1e-4 norm-wise; bf16: every element within one bf16 ulp
+plus 2e-2 of the exact result's RMS of the bf16-operand oracle, which for the
+split pipeline is evaluated with the pipeline's own roundings).
 """
 import numpy as np
 import pytest
 import torch
 
 import block_masked_attention_amd as bd
-from oracle import Oracle, layout
+from oracle import Oracle, layout, merge_partials, round_bf16
 from tests._helpers import f64
-from tests.gpu_util import OUT_NAMES, assert_parity, compare, oracle_full, say
+from tests.gpu_util import (OUT_NAMES, assert_parity, compare, oracle_full, saved_on_device,
+                            say)
 from workloads import GRAD_NAMES, INPUT_NAMES, make_inputs, small_spec
 
 pytestmark = pytest.mark.gpu
@@ -146,9 +148,45 @@ def test_split_forward_merge_and_backward_equal_the_full_problem(label, kw):
     got = dict(zip(OUT_NAMES, (o_c, o_x, lse_c, lse_x, dq_c, dq_x, torch.cat(dk_c),
                                torch.cat(dv_c), dk_x, dv_x)))
     want = oracle_full(spec, t)
-    ideal = oracle_full(spec, t, "bf16") if spec.dtype == "bf16" else None
+    ideal = split_pipeline_bf16(spec, t) if spec.dtype == "bf16" else None
     errs = compare(spec, got, want, label=label, ideal=ideal)
     assert_parity(spec, errs, label)
+
+
+def split_pipeline_bf16(spec, t):
+    """The split pipeline evaluated by the oracle in bf16-operand mode, with
+    the pipeline's own roundings: each part's O stored in bf16, each merge's O
+    stored in bf16 (oracle.merge_partials), each part's dQ stored in bf16 and
+    the parts summed, each shard's dK/dV stored in bf16."""
+    merged = None
+    for lo, hi, ck in pieces(spec):
+        lay = part_oracle(spec, t, lo, hi, ck).lay
+        u = part_inputs(t, lo, hi)
+        f = Oracle(lay, *[f64(u[k]) for k in INPUT_NAMES], operand_rounding="bf16").forward()
+        if merged is None:
+            merged = list(f)
+            continue
+        for o, l in ((0, 2), (1, 3)):
+            mo, ml = merge_partials([(merged[o], merged[l]), (f[o], f[l])])
+            merged[o], merged[l] = round_bf16(mo), ml
+    O = np.concatenate([merged[0], merged[1]])
+    LSE = np.concatenate([merged[2], merged[3]], axis=1)
+    out = dict(o_c=merged[0], o_x=merged[1], lse_c=merged[2], lse_x=merged[3])
+    out["dq_c"], out["dq_x"], dk_c, dv_c = 0.0, 0.0, [], []
+    for lo, hi, ck in pieces(spec):
+        lay = part_oracle(spec, t, lo, hi, ck).lay
+        u = part_inputs(t, lo, hi)
+        g = Oracle(lay, *[f64(u[k]) for k in INPUT_NAMES], *[f64(u[k]) for k in GRAD_NAMES],
+                   operand_rounding="bf16").backward(O=O, LSE=LSE)
+        out["dq_c"] = out["dq_c"] + g[0]
+        out["dq_x"] = out["dq_x"] + g[1]
+        if hi > lo:
+            dk_c.append(g[2])
+            dv_c.append(g[3])
+        if ck:
+            out["dk_x"], out["dv_x"] = g[4], g[5]
+    out["dk_c"], out["dv_c"] = np.concatenate(dk_c), np.concatenate(dv_c)
+    return out
 
 
 def _random_partials(n=10, seed=4242):
@@ -201,10 +239,17 @@ def test_random_partial_problems(label, kw, lo, hi, ck):
         want["lse_" + s] = np.where(empty, 0.0, want["lse_" + s])
     ideal = part_oracle_bf16(spec, t, lo, hi, ck) if spec.dtype == "bf16" else None
     errs = compare(spec, got, want, names=list(want), label=label, ideal=ideal)
-    # backward through the keys present, with the complete problem's O and LSE
-    full = bd.fwd(bd.from_spec(spec), *[t[k] for k in INPUT_NAMES])
-    g = bd.bwd(p, *[u[k] for k in INPUT_NAMES], *full, t["do_c"], t["do_x"])
+    # backward through the keys present, given the complete problem's saved O
+    # and LSE: in fp32 the GPU's own; in bf16 the bf16-operand oracle's, the
+    # same ones its backward below takes (see gpu_util.check_fwd_bwd)
     ref = oracle_full(spec, t)
+    if spec.dtype == "bf16":
+        rb = oracle_full(spec, t, "bf16")
+        dev, saved = saved_on_device(rb, spec, t["q_c"].device)
+        full = [dev[k] for k in OUT_NAMES[:4]]
+    else:
+        full = bd.fwd(bd.from_spec(spec), *[t[k] for k in INPUT_NAMES])
+    g = bd.bwd(p, *[u[k] for k in INPUT_NAMES], *full, t["do_c"], t["do_x"])
     ob = orc.backward(O=np.concatenate([ref["o_c"], ref["o_x"]]),
                       LSE=np.concatenate([ref["lse_c"], ref["lse_x"]], axis=1))
     names = ["dq_c", "dq_x", "dk_c", "dv_c"] + (["dk_x", "dv_x"] if ck else [])
@@ -214,10 +259,9 @@ def test_random_partial_problems(label, kw, lo, hi, ck):
     if spec.dtype == "bf16":
         obr = Oracle(orc.lay, *[f64(u[k]) for k in INPUT_NAMES], *[f64(u[k]) for k in GRAD_NAMES],
                      operand_rounding="bf16")
-        rb = oracle_full(spec, t, "bf16")
         bideal = dict(zip(OUT_NAMES[4:], obr.backward(
-            O=np.concatenate([rb["o_c"], rb["o_x"]]),
-            LSE=np.concatenate([rb["lse_c"], rb["lse_x"]], axis=1))))
+            O=np.concatenate([saved["o_c"], saved["o_x"]]),
+            LSE=np.concatenate([saved["lse_c"], saved["lse_x"]], axis=1))))
     errs.update(compare(spec, {k: gw[k] for k in names}, {k: bw[k] for k in names}, names=names,
                         label=label, ideal=bideal))
     assert_parity(spec, errs, label)
