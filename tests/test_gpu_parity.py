@@ -422,3 +422,38 @@ def test_side_stream_calls_keep_their_memory():
     torch.cuda.synchronize()
     for k, a in zip(OUT_NAMES, tuple(f) + tuple(g)):
         assert torch.equal(a, want[k]), k
+
+
+def test_plan_cache_recycles_staging_under_in_flight_calls():
+    """150 forward calls, each with a new packed-document layout, enqueued
+    back to back without waiting, under a 2 MiB plan-cache budget: plans are
+    evicted while their staging copies may still be queued. Every kept result
+    equals a later call on the same layout, and pinned memory stays bounded."""
+    _need_gpu()
+    import block_masked_attention_amd as bd
+    spec = small_spec(L=4096, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=21)
+    t = make_inputs(spec, device="cuda")
+    ins = [t[k] for k in ("q_c", "k_c", "v_c", "q_x", "k_x", "v_x")]
+    before = bd.plan_cache_info()
+    bd.plan_cache_budget(2 << 20)
+    try:
+        rng = np.random.default_rng(3)
+        layouts, kept = [], {}
+        for i in range(150):
+            cuts = np.sort(rng.choice(np.arange(1, 128), 7, replace=False)) * 32
+            docs = [0] + cuts.tolist()
+            layouts.append(docs)
+            out = bd.fwd(bd.from_spec(spec.with_(doc_starts=tuple(docs))), *ins)
+            if i % 30 == 0:
+                kept[i] = out
+            info = bd.plan_cache_info()
+            assert info["pinned_bytes"] <= (3 << 20), info
+        torch.cuda.synchronize()
+        assert bd.plan_cache_info()["evictions"] > before["evictions"] + 100
+        for i, out in kept.items():
+            again = bd.fwd(bd.from_spec(spec.with_(doc_starts=tuple(layouts[i]))), *ins)
+            torch.cuda.synchronize()
+            for a, b in zip(out, again):
+                assert torch.equal(a, b), i
+    finally:
+        bd.plan_cache_budget(before["budget"])
