@@ -156,6 +156,7 @@ def lib() -> ctypes.CDLL:
     L.bdattn_visible_pairs.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     L.bdattn_plan_stats.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     L.bdattn_fwd.argtypes = [P] + [vp] * 6 + [vp, vp, fp, fp] + [vp, ctypes.c_size_t, vp]
+    L.bdattn_fwd_noalloc.argtypes = [P] + [vp] * 6 + [vp, vp, fp, fp] + [vp]
     L.bdattn_bwd.argtypes = ([P] + [vp] * 6 + [vp, vp, fp, fp, vp, vp] + [vp] * 6 +
                              [vp, ctypes.c_size_t, vp])
     L.bdattn_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -166,7 +167,8 @@ def lib() -> ctypes.CDLL:
     L.bdattn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
     for name in ("bdattn_validate", "bdattn_workspace_size", "bdattn_mask_render",
-                 "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_bwd",
+                 "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_fwd_noalloc",
+                 "bdattn_bwd",
                  "bdattn_merge", "bdattn_profile_enable", "bdattn_profile_read",
                  "bdattn_plan_cache_info", "bdattn_plan_cache_budget"):
         getattr(L, name).restype = ctypes.c_int

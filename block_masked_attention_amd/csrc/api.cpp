@@ -299,6 +299,51 @@ const bdattn::KernelEvents* prof_events(int first, int n, bdattn::KernelEvents* 
   return ev;
 }
 
+// Scratch of the allocation-free forward: one array per device, holding
+// the block ids, the document table and the query-tile work list of the last
+// such call on that device. In host code `scratch` names a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t er = hipGetDevice(&dev);
+  if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(er));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BDATTN_ERR_HIP, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    er = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (er != hipSuccess || !ptr)
+      return fail(BDATTN_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(er));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BDATTN_OK;
+}
+
+// Work-list copy of the allocation-free forward: from the plan's host
+// vectors (pageable memory, consumed before each copy call returns), so no
+// pinned staging buffer is taken.
+int upload_direct(const bdattn::Plan& plan, const bdattn::WsLayout& w, char* ws, hipStream_t s) {
+  struct Part { size_t off; const void* src; size_t bytes; };
+  const Part parts[] = {{w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t)},
+                        {w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan)},
+                        {w.q_items, plan.fwd.data(), w.q_items_bytes}};
+  for (const Part& pt : parts) {
+    if (!pt.bytes) continue;
+    hipError_t er = hipMemcpyAsync(ws + pt.off, pt.src, pt.bytes, hipMemcpyHostToDevice, s);
+    if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("scratch upload: ") + hipGetErrorString(er));
+  }
+  return BDATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -427,9 +472,18 @@ int bdattn_plan_stats(const bdattn_problem* p, int64_t out[8]) {
   return BDATTN_OK;
 }
 
-int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const void* v_c,
-               const void* q_x, const void* k_x, const void* v_x, void* o_c, void* o_x,
-               float* lse_c, float* lse_x, void* workspace, size_t ws_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward's shared body. With `ws` set, the work lists go into the
+// caller's workspace from the plan's pinned staging copy; with `ws` null
+// (the allocation-free forward), into this device's `scratch` array, copied
+// straight from the plan's host vectors.
+int fwd_impl(const bdattn_problem* p, const void* q_c, const void* k_c, const void* v_c,
+             const void* q_x, const void* k_x, const void* v_x, void* o_c, void* o_x,
+             float* lse_c, float* lse_x, void* workspace, size_t ws_bytes, void* hip_stream,
+             bool noalloc) {
   bdattn::Problem P;
   int st = bdattn_validate(p);
   if (st != BDATTN_OK) return st;
@@ -442,15 +496,23 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
       (st = check_ptr(o_c, nqc, "o_c")) || (st = check_ptr(o_x, nqx, "o_x")) ||
       (st = check_ptr(lse_c, nqc, "lse_c")) || (st = check_ptr(lse_x, nqx, "lse_x")))
     return st;
-  std::shared_ptr<Entry> entry = get_entry(P);
-  const bdattn::Plan* plan = &entry->plan;
   const bdattn::WsLayout w = bdattn::workspace_layout(P, 0);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) || ws_bytes < w.total)
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (noalloc) {
+    if (w.total > kScratchBytes)
+      return fail(BDATTN_ERR_WORKSPACE, "the problem needs " + std::to_string(w.total) +
+                                            " bytes of forward scratch; the allocation-free "
+                                            "forward holds " + std::to_string(kScratchBytes));
+    if ((st = scratch_address(&workspace))) return st;
+  } else if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % bdattn::WS_ALIGN) ||
+             ws_bytes < w.total) {
     return fail(BDATTN_ERR_WORKSPACE, "forward workspace missing, misaligned or smaller than " +
                                           std::to_string(w.total) + " bytes");
-  hipStream_t s = (hipStream_t)hip_stream;
+  }
+  std::shared_ptr<Entry> entry = get_entry(P);
+  const bdattn::Plan* plan = &entry->plan;
   char* ws = (char*)workspace;
-  if ((st = upload(entry.get(), 0, w, ws, s))) return st;
+  if ((st = noalloc ? upload_direct(*plan, w, ws, s) : upload(entry.get(), 0, w, ws, s))) return st;
   bdattn::FwdArgs a;
   a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.q_x = q_x; a.k_x = k_x; a.v_x = v_x;
   a.o_c = o_c; a.o_x = o_x; a.lse_c = lse_c; a.lse_x = lse_x;
@@ -466,9 +528,27 @@ int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.corr_keys = P.corr_keys;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[1];
-  hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, prof_events(0, 1, ev));
+  hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, noalloc ? nullptr : prof_events(0, 1, ev));
   if (e != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("forward launch: ") + hipGetErrorString(e));
   return BDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bdattn_fwd(const bdattn_problem* p, const void* q_c, const void* k_c, const void* v_c,
+               const void* q_x, const void* k_x, const void* v_x, void* o_c, void* o_x,
+               float* lse_c, float* lse_x, void* workspace, size_t ws_bytes, void* hip_stream) {
+  return fwd_impl(p, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, workspace, ws_bytes,
+                  hip_stream, false);
+}
+
+int bdattn_fwd_noalloc(const bdattn_problem* p, const void* q_c, const void* k_c,
+                       const void* v_c, const void* q_x, const void* k_x, const void* v_x,
+                       void* o_c, void* o_x, float* lse_c, float* lse_x, void* hip_stream) {
+  return fwd_impl(p, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, nullptr, 0,
+                  hip_stream, true);
 }
 
 int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const void* v_c,

@@ -206,6 +206,25 @@ int bdattn_fwd(const bdattn_problem* p,
                void* o_c, void* o_x, float* lse_c, float* lse_x,
                void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* The forward for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments and results as bdattn_fwd (bitwise: the same kernels), without
+ * the workspace: the block ids, document table and work list go into a
+ * scratch array the library holds in device memory, one per device, of at
+ * most 8 MiB (a problem whose bdattn_workspace_size(pass 0) exceeds it gets
+ * BDATTN_ERR_WORKSPACE; 8 MiB holds a 1M-token sequence at 64 q heads). The
+ * call allocates no device and no pinned host memory; the first call on a
+ * device looks up that device's array, and the first call with a new
+ * problem plans it on the host. The work list is copied from pageable host
+ * memory, so the call may wait for that copy to be staged. Every call on a
+ * device shares the device's array: calls in one stream are ordered and
+ * safe, calls that overlap on one device (other streams, other threads)
+ * race. */
+int bdattn_fwd_noalloc(const bdattn_problem* p,
+                       const void* q_c, const void* k_c, const void* v_c,
+                       const void* q_x, const void* k_x, const void* v_x,
+                       void* o_c, void* o_x, float* lse_c, float* lse_x, void* hip_stream);
+
 /* Backward (Implementation 2 of the appendix): from the forward's saved
  * o_c/o_x and lse_c/lse_x and the upstream do_c/do_x, writes dq_c, dq_x,
  * dk_c/dv_c [n_clean_kv,Hkv,d] (clean keys no local query sees get zeros)
