@@ -146,15 +146,19 @@ def time_split_forward(bd, spec, t, shards, reps):
     from workloads import INPUT_NAMES
 
     B, nkv = spec.B, spec.n_clean_kv
+    if spec.kv_chunk_len:  # a gathered buffer: one clean launch over all of it
+        shards = 1
     cuts = [B * (i * (nkv // B) // shards) for i in range(shards + 1)]
     parts = [(0, 0, True)] + [(a, b, False) for a, b in zip(cuts, cuts[1:]) if b > a]
     probs, ins = [], []
     for lo, hi, ck in parts:
+        gathered = spec.kv_chunk_len if hi > lo else 0
         probs.append(bd.problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
                                 spec.clean_q_start, hi - lo, lo, spec.n_corr_blocks,
                                 spec.corr_block_ids, clean_mask=spec.clean_mask, partial=True,
                                 doc_starts=spec.doc_starts,
-                                omit_corr_keys=not ck))
+                                omit_corr_keys=not ck, kv_chunk_len=gathered,
+                                kv_chunk_pos=spec.kv_chunk_pos if gathered else None))
         u = dict(t)
         u["k_c"], u["v_c"] = t["k_c"][lo:hi], t["v_c"][lo:hi]  # row ranges stay contiguous
         ins.append([u[k] for k in INPUT_NAMES])
@@ -197,6 +201,11 @@ def main():
     ap.add_argument("--docs", type=int, default=1, metavar="N",
                     help="pack N documents into the workload's sequence: N-1 distinct seeded "
                          "random block boundaries cut it (attention stays inside each)")
+    ap.add_argument("--gathered", type=int, default=0, metavar="P",
+                    help="hold the clean K/V buffer in the zigzag all-gather order of P ranks "
+                         "(2P chunks; rank r brings position chunks r and 2P-1-r), each key "
+                         "masked by its original position; with --split-forward the clean part "
+                         "is one launch over the whole gathered buffer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -225,6 +234,14 @@ def main():
         cuts = np.sort(np.random.default_rng(1234).choice(np.arange(1, nb), args.docs - 1,
                                                           replace=False))
         spec = spec.with_(doc_starts=(0,) + tuple(int(c) * spec.B for c in cuts))
+    if args.gathered > 0:
+        P = args.gathered
+        C = spec.n_clean_kv // (2 * P)
+        if spec.n_clean_kv % (2 * P) or C % 128 or C % spec.B or spec.clean_kv_start:
+            sys.exit(f"--gathered {P}: the clean buffer does not split into 2P chunks of a "
+                     "multiple of 128 and of B keys")
+        spec = spec.with_(kv_chunk_len=C, kv_chunk_pos=tuple(
+            c * C for r in range(P) for c in (r, 2 * P - 1 - r)))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     p = bd.from_spec(spec)
@@ -291,6 +308,8 @@ def main():
     from block_masked_attention_amd.rocprof import profile_key
     traffic, clock = read_profile(profile_key(spec.name, args.docs)
                                   + ("_token_causal" if spec.clean_mask else ""), dom)
+    if args.gathered:  # the committed profiles are of the position-ordered buffer
+        traffic, clock = None, None
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak} peak); " +
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
@@ -299,7 +318,7 @@ def main():
     split = None
     if args.split_forward > 0:
         split = time_split_forward(bd, spec, t, args.split_forward, max(1, args.steps))
-        log(f"[bench] split forward ({args.split_forward} clean shards + block-diagonal part, "
+        log(f"[bench] split forward ({split['shards']} clean launch(es) + block-diagonal part, "
             f"merged): {split['ms']:.2f} ms against {kern['fwd']['ms']:.2f} ms fused")
 
     cpu = None
@@ -324,6 +343,8 @@ def main():
         "config": {"workload": spec.name, "description": spec.description,
                    "clean_q": nc, "clean_kv": nkv, "corrupted": nx, "B": spec.B, "H": H,
                    "Hkv": Hkv, "d": d, "clean_mask": mask_name, "documents": args.docs,
+                   "clean_kv_order": (f"zigzag all-gather of {args.gathered} ranks"
+                                      if args.gathered else "positions"),
                    "visible_pairs_per_head": pairs,
                    "useful_flops_per_step": useful_step, "parallelism": "none (1 GPU)"},
         "pct_of_peak": round(100 * value / peak, 2),

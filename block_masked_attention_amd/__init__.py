@@ -57,6 +57,8 @@ class Problem(ctypes.Structure):
         ("omit_corr_keys", ctypes.c_int32),
         ("n_docs", ctypes.c_int32),
         ("doc_starts", ctypes.POINTER(ctypes.c_int32)),
+        ("kv_chunk_len", ctypes.c_int32),
+        ("kv_chunk_pos", ctypes.POINTER(ctypes.c_int32)),
     ]
 
     @property
@@ -69,7 +71,8 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
             n_corr_blocks: Optional[int] = None, corr_block_ids: Optional[Sequence[int]] = None,
             scale: float = 0.0, clean_mask: int = CLEAN_BLOCK_CAUSAL, partial: bool = False,
             omit_corr_keys: bool = False,
-            doc_starts: Optional[Sequence[int]] = None) -> Problem:
+            doc_starts: Optional[Sequence[int]] = None, kv_chunk_len: int = 0,
+            kv_chunk_pos: Optional[Sequence[int]] = None) -> Problem:
     """Problem descriptor. ``dtype`` is F32/BF16, "f32"/"bf16" or a torch dtype.
     Without ids the corrupted blocks are 0..n_corr_blocks-1 (default: as many
     as the clean query shard has blocks). ``clean_mask`` is CLEAN_BLOCK_CAUSAL
@@ -77,7 +80,10 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
     ``partial``: attention over the keys present only (any clean range, the
     corrupted keys optional with ``omit_corr_keys``); see include/bdattn.h.
     ``doc_starts`` packs documents into the sequence: their start positions
-    (the first 0, increasing, multiples of B); attention stays inside each."""
+    (the first 0, increasing, multiples of B); attention stays inside each.
+    ``kv_chunk_len`` / ``kv_chunk_pos``: a gathered clean K/V buffer, chunks of
+    ``kv_chunk_len`` keys whose global start positions are ``kv_chunk_pos``
+    (any order, together covering the buffer's position range)."""
     dt = _dtype_code(dtype)
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
@@ -105,6 +111,13 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
         p.doc_starts = docs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     else:
         p.n_docs, p.doc_starts = 0, None
+    p.kv_chunk_len = int(kv_chunk_len)
+    if kv_chunk_pos is not None and len(kv_chunk_pos) > 0:
+        cpos = np.ascontiguousarray(np.asarray(kv_chunk_pos, dtype=np.int32))
+        p._cpos = cpos  # keep alive
+        p.kv_chunk_pos = cpos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    else:
+        p.kv_chunk_pos = None
     return p
 
 
@@ -116,7 +129,9 @@ def from_spec(spec) -> Problem:
                    clean_mask=getattr(spec, "clean_mask", CLEAN_BLOCK_CAUSAL),
                    partial=getattr(spec, "partial", False),
                    omit_corr_keys=getattr(spec, "omit_corr_keys", False),
-                   doc_starts=getattr(spec, "doc_starts", None))
+                   doc_starts=getattr(spec, "doc_starts", None),
+                   kv_chunk_len=getattr(spec, "kv_chunk_len", 0),
+                   kv_chunk_pos=getattr(spec, "kv_chunk_pos", None))
 
 
 def _dtype_code(dtype) -> int:

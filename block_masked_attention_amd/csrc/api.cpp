@@ -165,6 +165,9 @@ std::string plan_key(const bdattn::Problem& P) {
   const int32_t nd = int32_t(P.docs.size());
   k.append((const char*)&nd, sizeof(nd));
   k.append((const char*)P.docs.data(), P.docs.size() * sizeof(int32_t));
+  const int32_t nm = int32_t(P.kv_map.size());
+  k.append((const char*)&nm, sizeof(nm));
+  k.append((const char*)P.kv_map.data(), P.kv_map.size() * sizeof(int32_t));
   return k;
 }
 
@@ -253,6 +256,7 @@ int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t 
     const bdattn::Plan& plan = e->plan;
     memcpy(h + w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t));
     memcpy(h + w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan));
+    memcpy(h + w.kv_map, plan.P.kv_map.data(), plan.P.kv_map.size() * sizeof(int32_t));
     memcpy(h + w.q_items, plan.fwd.data(), w.q_items_bytes);
     if (pass == 1) memcpy(h + w.kv_items, plan.bwd.data(), w.kv_items_bytes);
   }
@@ -335,6 +339,7 @@ int upload_direct(const bdattn::Plan& plan, const bdattn::WsLayout& w, char* ws,
   struct Part { size_t off; const void* src; size_t bytes; };
   const Part parts[] = {{w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t)},
                         {w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan)},
+                        {w.kv_map, plan.P.kv_map.data(), plan.P.kv_map.size() * sizeof(int32_t)},
                         {w.q_items, plan.fwd.data(), w.q_items_bytes}};
   for (const Part& pt : parts) {
     if (!pt.bytes) continue;
@@ -518,6 +523,8 @@ int fwd_impl(const bdattn_problem* p, const void* q_c, const void* k_c, const vo
   a.o_c = o_c; a.o_x = o_x; a.lse_c = lse_c; a.lse_x = lse_x;
   a.ids = (const int32_t*)(ws + w.ids);
   a.docs = P.spans.empty() ? nullptr : (const BdDocSpan*)(ws + w.spans);
+  a.kv_map = P.kv_map.empty() ? nullptr : (const int32_t*)(ws + w.kv_map);
+  a.n_kv_map = int32_t(P.kv_map.size());
   a.items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_items = int32_t(plan->fwd.size());
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
@@ -588,6 +595,8 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.dq_c = dq_c; a.dq_x = dq_x; a.dk_c = dk_c; a.dv_c = dv_c; a.dk_x = dk_x; a.dv_x = dv_x;
   a.ids = (const int32_t*)(ws + w.ids);
   a.docs = P.spans.empty() ? nullptr : (const BdDocSpan*)(ws + w.spans);
+  a.kv_map = P.kv_map.empty() ? nullptr : (const int32_t*)(ws + w.kv_map);
+  a.n_kv_map = int32_t(P.kv_map.size());
   a.q_items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_q_items = int32_t(plan->fwd.size());
   a.kv_items = (const bdattn::BwdItem*)(ws + w.kv_items);

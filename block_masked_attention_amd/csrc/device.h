@@ -237,6 +237,30 @@ __device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, const
   return bd_in_buffer(r, rs.kv0, rs.nkv, rs.corr_keys);
 }
 
+// Buffer rows of the clean key tiles of a gathered buffer: map[j] is the
+// buffer tile of key tile j in position order. Tiles are asked for in
+// increasing order. Lane i holds the entry of tile base + i, refilled every
+// 64 tiles, so a lookup is a register read (v_readlane) except at a refill,
+// whose load is lane-varying and so a vector load.
+template <int TK>
+struct KeyTileMap {
+  const int32_t* map;
+  int n, base, v;
+  __device__ __forceinline__ void init(const int32_t* m, int n_, int j0, int lane) {
+    map = m;
+    n = n_;
+    base = j0;
+    v = map[min(j0 + lane, n - 1)];
+  }
+  __device__ __forceinline__ int row(int j, int lane) {
+    if (j - base >= 64) {
+      base = j;
+      v = map[min(j + lane, n - 1)];
+    }
+    return __builtin_amdgcn_readlane(v, j - base) * TK;
+  }
+};
+
 // floor(n / d) for 0 <= n < 2^24, d >= 1, with inv_d = 1.0f / d: a float
 // estimate that is off by at most one, then corrected with integer checks.
 __device__ __forceinline__ int div_small(int n, int d, float inv_d) {

@@ -84,7 +84,7 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
 // Forward. Per key tile: S^T = K Q^T (keys x queries, so each lane owns one
 // query row); mask only on tiles that need it; online softmax; O^T += V^T P^T.
 // ======================================================================
-template <bool BF16, int D, bool DOCS>
+template <bool BF16, int D, bool DOCS, bool MAPPED>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   using E = Elem<BF16>;
@@ -121,10 +121,18 @@ void fwd_kernel(FwdArgs a) {
   const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
   const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
   const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
+  // gathered buffer (MAPPED): clean key tile j (position order) sits at
+  // buffer tile kv_map[j]; the masks keep working in position order
+  KeyTileMap<TK> km;
+  if constexpr (MAPPED) {
+    if (q.n_ct > q.j0) km.init(a.kv_map, a.n_kv_map, q.j0, lane);
+  }
   // stage key tile j (K then V) into LDS buffer `buf`
   auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
     const bool cl = j < q.n_ct;
-    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+    int k0;
+    if constexpr (MAPPED) k0 = cl ? km.row(j, lane) : q.xlo + (j - q.n_ct) * TK;
+    else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
     const int nk = cl ? a.n_clean_kv : a.n_corr;
     T* dst = smem + buf * 2 * TSZ;
     cp.issue(dst, cl ? kc : kx, k0, nk);
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* oa_, const float
 // D are scalars); P^T = exp2(S^T c - LSE2); dS^T = P^T (dP^T - D);
 // dQ^T += K^T dS^T with K^T read transposed from the K tile.
 // ======================================================================
-template <bool BF16, int D, bool DOCS>
+template <bool BF16, int D, bool DOCS, bool MAPPED>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<BF16>;
@@ -380,10 +388,18 @@ void bwd_dq_kernel(BwdArgs a) {
   const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
   const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
   const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
+  // gathered buffer (MAPPED): clean key tile j (position order) sits at
+  // buffer tile kv_map[j]; the masks keep working in position order
+  KeyTileMap<TK> km;
+  if constexpr (MAPPED) {
+    if (q.n_ct > q.j0) km.init(a.kv_map, a.n_kv_map, q.j0, lane);
+  }
   // stage key tile j (K then V) into LDS buffer `buf`
   auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
     const bool cl = j < q.n_ct;
-    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+    int k0;
+    if constexpr (MAPPED) k0 = cl ? km.row(j, lane) : q.xlo + (j - q.n_ct) * TK;
+    else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
     const int nk = cl ? a.n_clean_kv : a.n_corr;
     T* dst = smem + buf * 2 * TSZ;
     cp.issue(dst, cl ? kc : kx, k0, nk);
@@ -479,10 +495,14 @@ void bwd_dq_kernel(BwdArgs a) {
 template <bool BF16, int D>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  if (a.n_items > 0 && a.docs)
-    hipLaunchKernelGGL((fwd_kernel<BF16, D, true>), dim3(a.n_items), dim3(FWD_WAVES * 64), 0, s, a);
-  else if (a.n_items > 0)
-    hipLaunchKernelGGL((fwd_kernel<BF16, D, false>), dim3(a.n_items), dim3(FWD_WAVES * 64), 0, s, a);
+  const dim3 grid(a.n_items), block(FWD_WAVES * 64);
+  if (a.n_items > 0 && a.kv_map) {  // a gathered clean buffer
+    if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, true>), grid, block, 0, s, a);
+  } else if (a.n_items > 0) {
+    if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, false>), grid, block, 0, s, a);
+  }
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   return hipGetLastError();
 }
@@ -501,10 +521,14 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
                        st ? a.d_x : a.d_c, st ? a.l2_x : a.l2_c, n, n_pad, a.H);
   }
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  if (a.n_q_items > 0 && a.docs)
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true>), dim3(a.n_q_items), dim3(FWD_WAVES * 64), 0, s, a);
-  else if (a.n_q_items > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false>), dim3(a.n_q_items), dim3(FWD_WAVES * 64), 0, s, a);
+  const dim3 grid(a.n_q_items), block(FWD_WAVES * 64);
+  if (a.n_q_items > 0 && a.kv_map) {  // a gathered clean buffer
+    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, true>), grid, block, 0, s, a);
+  } else if (a.n_q_items > 0) {
+    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false>), grid, block, 0, s, a);
+  }
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   if (ev) (void)hipEventRecord(ev[1].start, s);
   hipError_t e = hipGetLastError();

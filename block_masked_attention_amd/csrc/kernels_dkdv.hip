@@ -95,11 +95,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  // a gathered clean buffer: this wave's 32 keys (inside one FWD_TK-key tile
+  // of position order) sit at buffer rows key + kv_off
+  int kv_off = 0;
+  if (!kstream && a.kv_map && key0 + 32 * kg < n_keys) {
+    const int g0 = key0 + 32 * kg;
+    kv_off = a.kv_map[g0 / FWD_TK] * FWD_TK + g0 % FWD_TK - g0;
+  }
   // this lane's key (P wave) or value (dS wave) as B operand, natural over d
   Frag kvf[D / 16];
   {
     const T* src = (const T*)(p_role ? (kstream ? a.k_x : a.k_c) : (kstream ? a.v_x : a.v_c));
-    const int64_t off = ((int64_t)min(my_key, n_keys - 1) * a.Hkv + kvh) * D;
+    const int64_t off = ((int64_t)min(my_key, n_keys - 1) * a.Hkv + kvh) * D + (int64_t)kv_off * a.Hkv * D;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       kvf[ks] = key_ok ? E::load(src + off + 16 * ks + 8 * hf) : E::zero();
@@ -329,7 +336,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key0 + 32 * kg + 8 * (i >> 2) + 4 * hf + (i & 3);
-      if (key < n_keys) out[((int64_t)key * a.Hkv + kvh) * D + 32 * db + lk] = E::from_f(acc[db][i] * osc);
+      if (key < n_keys) out[((int64_t)(key + kv_off) * a.Hkv + kvh) * D + 32 * db + lk] = E::from_f(acc[db][i] * osc);
     }
   }
 }

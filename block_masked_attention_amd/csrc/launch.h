@@ -13,6 +13,8 @@ struct FwdArgs {
   float *lse_c, *lse_x;
   const int32_t* ids;      // device: global id of each local corrupted block
   const BdDocSpan* docs;   // device: document of each global block, or nullptr
+  const int32_t* kv_map;   // device: buffer tile of each clean key tile, or nullptr
+  int32_t n_kv_map;
   const FwdItem* items;    // device work list
   int32_t n_items;
   int32_t B, H, Hkv, Gw, rows_per_item;
@@ -30,6 +32,8 @@ struct BwdArgs {
   void *dq_c, *dq_x, *dk_c, *dv_c, *dk_x, *dv_x;
   const int32_t* ids;
   const BdDocSpan* docs;   // device: document of each global block, or nullptr
+  const int32_t* kv_map;   // device: buffer tile of each clean key tile, or nullptr
+  int32_t n_kv_map;
   const FwdItem* q_items;  // dQ kernel: the forward's query-tile work list
   int32_t n_q_items;
   const BwdItem* kv_items;  // dK/dV kernel: key-tile work list

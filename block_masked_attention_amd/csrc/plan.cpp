@@ -175,6 +175,37 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   }
   if (P.docs.size() > 1) build_spans(&P);
   else P.docs.clear();
+  if (p->kv_chunk_len < 0) {
+    *msg = "kv_chunk_len must be >= 0";
+    return BDATTN_ERR_SHAPE;
+  }
+  if (p->kv_chunk_len > 0) {  // a gathered clean buffer: chunks at their positions
+    const int64_t C = p->kv_chunk_len;
+    if (C % 128 || C % B || P.n_clean_kv % C) {
+      *msg = "kv_chunk_len must be a multiple of 128 and of B that divides n_clean_kv";
+      return BDATTN_ERR_SHAPE;
+    }
+    const int64_t n = P.n_clean_kv / C;
+    if (n > 0 && !p->kv_chunk_pos) {
+      *msg = "kv_chunk_pos is NULL";
+      return BDATTN_ERR_INVALID_ARG;
+    }
+    // chunk c of the position range [clean_kv_start, +n_clean_kv) -> buffer chunk
+    std::vector<int32_t> at(size_t(n), -1);
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t rel = int64_t(p->kv_chunk_pos[i]) - p->clean_kv_start;
+      if (rel < 0 || rel % C || rel / C >= n || at[size_t(rel / C)] >= 0) {
+        *msg = "the chunks of kv_chunk_pos must cover [clean_kv_start, clean_kv_start + "
+               "n_clean_kv) exactly, each starting on a chunk boundary";
+        return BDATTN_ERR_INVALID_ARG;
+      }
+      at[size_t(rel / C)] = int32_t(i);
+    }
+    const int32_t tpc = int32_t(C / FWD_TK);
+    P.kv_map.resize(size_t(n) * tpc);
+    for (int64_t c = 0; c < n; ++c)
+      for (int32_t t = 0; t < tpc; ++t) P.kv_map[size_t(c * tpc + t)] = at[size_t(c)] * tpc + t;
+  }
   if (P.partial) {  // any clean range: the attention over the keys present
     *out = std::move(P);
     return BDATTN_OK;
@@ -227,6 +258,8 @@ WsLayout workspace_layout(const Problem& P, int pass) {
   off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, P.ids.size()), WS_ALIGN);
   w.spans = off;
   off = align_up(off + sizeof(BdDocSpan) * P.spans.size(), WS_ALIGN);
+  w.kv_map = off;
+  off = align_up(off + sizeof(int32_t) * P.kv_map.size(), WS_ALIGN);
   w.q_items = off;
   w.q_items_bytes = n_q_items(P) * sizeof(FwdItem);
   off = align_up(off + std::max<size_t>(1, w.q_items_bytes), WS_ALIGN);
@@ -408,7 +441,12 @@ void mask_render(const Problem& P, uint8_t* out) {
     const int32_t row = int32_t(stream == 0 ? q : q - P.n_clean_q);
     BdRowBounds b = row_bounds(P, stream, row);
     uint8_t* o = out + q * nk;
-    for (int32_t k = 0; k < P.n_clean_kv; ++k) o[k] = bd_sees_clean(b, k) ? 1 : 0;
+    // (a gathered buffer: the key at buffer row k sits at position-order index
+    // map(k); rows follow the buffer)
+    for (int32_t k = 0; k < P.n_clean_kv; ++k) {
+      const int32_t kb = P.kv_map.empty() ? k : P.kv_map[k / FWD_TK] * FWD_TK + k % FWD_TK;
+      o[kb] = bd_sees_clean(b, k) ? 1 : 0;
+    }
     for (int32_t k = 0; k < P.n_corr(); ++k) o[P.n_clean_kv + k] = bd_sees_corr(b, k) ? 1 : 0;
   }
 }

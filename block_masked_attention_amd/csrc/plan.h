@@ -65,6 +65,9 @@ struct Problem {
   std::vector<int32_t> ids;  // always materialised (0..n-1 when NULL)
   std::vector<int32_t> docs;  // packed document starts (empty: one document)
   std::vector<BdDocSpan> spans;  // per global block, with documents (else empty)
+  // gathered clean K/V buffer: buffer tile (FWD_TK keys) of each clean key
+  // tile in position order (empty: the buffer is in position order)
+  std::vector<int32_t> kv_map;
   int32_t n_corr() const { return n_corr_blocks * B; }
   int32_t G() const { return H / Hkv; }
 };
@@ -96,7 +99,8 @@ void build_plan(const Problem& P, Plan* plan);
 // LSE * log2(e), are float [H][round_up(n, BWD_TQ)]: every query tile's
 // values are one contiguous run, and rows past n hold -D = 0, LSE = +inf.
 struct WsLayout {
-  size_t ids = 0, spans = 0, q_items = 0, q_items_bytes = 0, kv_items = 0, kv_items_bytes = 0;
+  size_t ids = 0, spans = 0, kv_map = 0, q_items = 0, q_items_bytes = 0, kv_items = 0,
+         kv_items_bytes = 0;
   size_t d_c = 0, d_x = 0, l2_c = 0, l2_x = 0;  // bwd row data
   size_t staged = 0;  // bytes copied from the host (ids and work lists)
   size_t total = 0;

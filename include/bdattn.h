@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BDATTN_VERSION 3
+#define BDATTN_VERSION 4
 
 typedef enum {
   BDATTN_OK = 0,
@@ -133,6 +133,19 @@ typedef struct {
    * during the call only. */
   int32_t n_docs;
   const int32_t* doc_starts;
+  /* A gathered clean K/V buffer (the appendix's Implementation 1 masks with
+   * each gathered key's original clean token position; the context-sharded
+   * all-gather of §4.3 delivers the chunks rank by rank, e.g. in zigzag
+   * order). 0: the buffer is in position order. > 0: the buffer is
+   * n_clean_kv / kv_chunk_len chunks of kv_chunk_len keys (a multiple of 128
+   * and of B); chunk i holds the keys at global positions
+   * [kv_chunk_pos[i], kv_chunk_pos[i] + kv_chunk_len). HOST array, read
+   * during the call only. The chunks, in any order, must together cover
+   * exactly [clean_kv_start, clean_kv_start + n_clean_kv)
+   * (BDATTN_ERR_INVALID_ARG otherwise; BDATTN_ERR_SHAPE for a length that is
+   * not such a multiple). dk_c/dv_c rows follow the buffer's order. */
+  int32_t kv_chunk_len;
+  const int32_t* kv_chunk_pos;
 } bdattn_problem;
 
 /* BDATTN_VERSION of the loaded library. */

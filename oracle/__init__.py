@@ -9,10 +9,10 @@ itself (a hand-drawn mask fixture, closed forms at Q = 0, a library attention
 routine, scalar brute force, finite differences, invariants of the method).
 """
 from .bdattn_oracle import (BLOCK_CAUSAL, CLEAN, CORRUPTED, TOKEN_CAUSAL, Layout, Oracle,
-                            corrupted_copies, documents, key_positions, key_tokens, layout, merge_partials, query_positions,
+                            clean_key_positions, corrupted_copies, documents, key_positions, key_tokens, layout, merge_partials, query_positions,
                             query_tokens, round_bf16, visible)
 
 __all__ = ["BLOCK_CAUSAL", "CLEAN", "CORRUPTED", "TOKEN_CAUSAL", "Layout", "Oracle",
-           "corrupted_copies", "documents",
+           "clean_key_positions", "corrupted_copies", "documents",
            "key_positions", "key_tokens", "layout", "merge_partials", "query_positions",
            "query_tokens", "round_bf16", "visible"]

@@ -27,7 +27,10 @@ Long-Context Diffusion Language Model Training":
   corrupted part, and clean K/V given by original positions), merged through
   their log-sum-exps. A *partial* layout holds only some keys: the result is
   the attention over the visible keys present (a row that sees none gets
-  O = 0, LSE = -inf), and ``merge_partials`` combines such results.
+  O = 0, LSE = -inf), and ``merge_partials`` combines such results. The clean
+  keys may come in any order, each with its original clean position (the
+  gathered buffer of that paragraph): a layout then names the position of
+  every row of its clean K/V buffer.
 * Packed documents (variable-length training sequences, §5.1; Block Diffusion,
   named in §2, generates sequences of any length): several documents share
   one sequence, each starting on a block boundary, with its blocks counted
@@ -59,7 +62,7 @@ TOKEN_CAUSAL = 1  # ... or its own clean block up to its own position
 
 __all__ = ["Layout", "layout", "visible", "query_tokens", "key_tokens", "query_positions",
            "key_positions", "corrupted_copies", "Oracle", "CLEAN", "CORRUPTED", "BLOCK_CAUSAL", "TOKEN_CAUSAL",
-           "round_bf16", "merge_partials", "documents"]
+           "round_bf16", "merge_partials", "documents", "clean_key_positions"]
 
 
 @dataclass(frozen=True)
@@ -78,6 +81,7 @@ class Layout:
     partial: bool = False  # keys may be missing: attention over the keys present
     corr_keys: bool = True  # the local corrupted keys are present
     docs: tuple = ()  # start positions of packed documents (empty: one document)
+    kv_pos: tuple = ()  # position of each clean K/V buffer row (empty: clean_kv_start + row)
 
     @property
     def G(self) -> int:
@@ -102,7 +106,8 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
            corr_block_ids: Optional[Sequence[int]] = None,
            scale: Optional[float] = None, partial: bool = False,
            clean_mask: int = BLOCK_CAUSAL, corr_keys: bool = True,
-           doc_starts: Optional[Sequence[int]] = None) -> Layout:
+           doc_starts: Optional[Sequence[int]] = None,
+           clean_kv_positions: Optional[Sequence[int]] = None) -> Layout:
     """Describe one problem. Without ids, the corrupted blocks are 0..n-1
     (n defaults to the number of clean blocks of the query shard).
     ``clean_mask`` is BLOCK_CAUSAL or TOKEN_CAUSAL.
@@ -114,7 +119,12 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
 
     ``doc_starts`` packs several documents into the sequence: their start
     positions, increasing, the first 0, each a multiple of B (a document
-    starts a new block). None or a single 0 is one document."""
+    starts a new block). None or a single 0 is one document.
+
+    ``clean_kv_positions`` gives the original clean position of every row of
+    the clean K/V buffer, distinct, in any order (a gathered buffer);
+    ``clean_kv_start`` is then unused. Without it, row r is at position
+    ``clean_kv_start + r``."""
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
     if corr_block_ids is None:
@@ -136,16 +146,32 @@ def layout(B: int, H: int, Hkv: int, d: int, n_clean_q: int, clean_q_start: int 
             docs = ()
     if not partial and not corr_keys:
         raise ValueError("only a partial layout may omit the corrupted keys")
+    kv_pos = ()
+    if clean_kv_positions is not None:
+        kv_pos = tuple(int(x) for x in clean_kv_positions)
+        if len(kv_pos) != n_clean_kv or len(set(kv_pos)) != len(kv_pos) or min(kv_pos, default=0) < 0:
+            raise ValueError("clean_kv_positions: one distinct position >= 0 per buffer row")
     if not partial:
         need = 0  # one past the last clean position some query sees
         if n_clean_q:
             need = ((clean_q_start + n_clean_q - 1) // B + 1) * B
         if ids:
             need = max(need, max(ids) * B)
-        if need and (clean_kv_start > 0 or clean_kv_start + n_clean_kv < need):
+        if kv_pos:
+            covered = need <= len(kv_pos) and set(range(need)) <= set(kv_pos)
+        else:
+            covered = clean_kv_start == 0 and n_clean_kv >= need
+        if need and not covered:
             raise ValueError("clean K/V buffer does not cover every visible clean key")
     return Layout(B, H, Hkv, d, float(scale), n_clean_q, clean_q_start, n_clean_kv,
-                  clean_kv_start, ids, clean_mask, bool(partial), bool(corr_keys), docs)
+                  clean_kv_start, ids, clean_mask, bool(partial), bool(corr_keys), docs, kv_pos)
+
+
+def clean_key_positions(lay: Layout):
+    """Original clean position of every row of the clean K/V buffer."""
+    if lay.kv_pos:
+        return np.asarray(lay.kv_pos, dtype=np.int64)
+    return lay.clean_kv_start + np.arange(lay.n_clean_kv, dtype=np.int64)
 
 
 def query_tokens(lay: Layout):
@@ -160,7 +186,7 @@ def query_tokens(lay: Layout):
 
 def key_tokens(lay: Layout):
     """(stream, block) of every key: the clean buffer, then corrupted."""
-    pos = lay.clean_kv_start + np.arange(lay.n_clean_kv, dtype=np.int64)
+    pos = clean_key_positions(lay)
     stream = np.concatenate([np.full(lay.n_clean_kv, CLEAN, np.int8),
                              np.full(lay.n_corr, CORRUPTED, np.int8)])
     block = np.concatenate([pos // lay.B,
@@ -180,7 +206,7 @@ def query_positions(lay: Layout):
 
 def key_positions(lay: Layout):
     """Sequence position of every key (clean buffer, then corrupted keys)."""
-    clean = lay.clean_kv_start + np.arange(lay.n_clean_kv, dtype=np.int64)
+    clean = clean_key_positions(lay)
     corr = (np.repeat(np.asarray(lay.corr_ids, np.int64), lay.B) * lay.B
             + np.tile(np.arange(lay.B, dtype=np.int64), len(lay.corr_ids)))
     return np.concatenate([clean, corr])

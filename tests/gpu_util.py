@@ -44,7 +44,8 @@ def _rounding(spec):
 def oracle_full(spec, t, rounding=None):
     lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start,
                  spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks, spec.corr_block_ids,
-                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts)
+                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts,
+                 clean_kv_positions=spec.kv_positions() if spec.kv_chunk_len else None)
     orc = Oracle(lay, *[f64(t[k]) for k in INPUT_NAMES], *[f64(t[k]) for k in GRAD_NAMES],
                  operand_rounding=rounding)
     f = orc.forward()
@@ -57,7 +58,8 @@ def oracle_backward(spec, t, saved, rounding=None):
     with o_c, o_x, lse_c, lse_x as float64 arrays)."""
     lay = layout(spec.B, spec.H, spec.Hkv, spec.d, spec.n_clean_q, spec.clean_q_start,
                  spec.n_clean_kv, spec.clean_kv_start, spec.n_corr_blocks, spec.corr_block_ids,
-                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts)
+                 clean_mask=spec.clean_mask, doc_starts=spec.doc_starts,
+                 clean_kv_positions=spec.kv_positions() if spec.kv_chunk_len else None)
     orc = Oracle(lay, *[f64(t[k]) for k in INPUT_NAMES], *[f64(t[k]) for k in GRAD_NAMES],
                  operand_rounding=rounding)
     g = orc.backward(O=np.concatenate([saved["o_c"], saved["o_x"]]),

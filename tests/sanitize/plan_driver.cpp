@@ -4,7 +4,7 @@
 // Reads one problem descriptor per line on stdin:
 //   B H Hkv d dtype n_clean_q clean_q_start n_clean_kv clean_kv_start
 //   n_corr_blocks clean_mask partial omit_corr_keys has_ids n_ids ids...
-//   n_docs docs...
+//   n_docs docs... kv_chunk_len n_chunks chunk_pos...
 // and for each prints the validation status and, for a valid problem, the
 // exact pair count, both workspace sizes, the planner statistics and, over
 // the dense mask's visible entries (flat index i = row * n_keys + key), their
@@ -85,6 +85,11 @@ int main() {
     const size_t n_docs = size_t(v[i++]);
     std::vector<int32_t> docs(n_docs);
     for (size_t k = 0; k < n_docs; ++k) docs[k] = int32_t(v[i++]);
+    d.kv_chunk_len = i < v.size() ? int32_t(v[i++]) : 0;
+    const size_t n_cp = i < v.size() ? size_t(v[i++]) : 0;
+    std::vector<int32_t> cpos(n_cp);
+    for (size_t k = 0; k < n_cp && i < v.size(); ++k) cpos[k] = int32_t(v[i++]);
+    d.kv_chunk_pos = n_cp ? cpos.data() : nullptr;
     d.corr_block_ids = has_ids ? ids.data() : nullptr;
     d.n_docs = int32_t(n_docs);
     d.doc_starts = n_docs ? docs.data() : nullptr;

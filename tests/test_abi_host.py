@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert bd.version() == 3
+    assert bd.version() == 4
 
 
 def test_status_strings():
@@ -294,3 +294,66 @@ def test_plan_cache_stays_bounded_under_new_document_layouts():
 def test_plan_cache_budget_is_validated():
     with pytest.raises(bd.BdattnError):
         bd.plan_cache_budget(1000)
+
+
+# a gathered clean K/V buffer: chunks of 128+ keys in any order (zigzag
+# all-gather order of P ranks: rank r brings position chunks r and 2P-1-r)
+def _zigzag(P, C, lo=0):
+    return [lo + c * C for r in range(P) for c in (r, 2 * P - 1 - r)]
+
+
+CASES_GATHERED = [
+    dict(B=32, n_clean_q=1024, kv_chunk_len=128, kv_chunk_pos=_zigzag(4, 128)),
+    dict(B=16, n_clean_q=512, clean_q_start=512, n_clean_kv=1024, corr_block_ids=[3, 9, 40, 63],
+         kv_chunk_len=256, kv_chunk_pos=[768, 0, 512, 256]),
+    dict(B=32, n_clean_q=1024, kv_chunk_len=128, kv_chunk_pos=_zigzag(4, 128),
+         clean_mask=bd.CLEAN_TOKEN_CAUSAL, doc_starts=[0, 96, 320, 704]),
+    dict(B=32, n_clean_q=1024, n_clean_kv=512, clean_kv_start=256, partial=True,
+         kv_chunk_len=128, kv_chunk_pos=[640, 256, 512, 384]),
+]
+
+
+@pytest.mark.parametrize("case", CASES_GATHERED)
+def test_gathered_buffer_mask_and_plan(case):
+    """The library's mask of a gathered buffer equals the oracle's mask with
+    each buffer row at its original position, and its plan does the same work
+    as the position-ordered buffer."""
+    p = bd.problem(H=4, Hkv=2, d=128, dtype="bf16", **case)
+    assert bd.validate(p) == 0, bd.lib().bdattn_last_error()
+    ids = [p.corr_block_ids[i] for i in range(p.n_corr_blocks)] if p.corr_block_ids else None
+    docs = [p.doc_starts[i] for i in range(p.n_docs)] if p.n_docs else None
+    C = case["kv_chunk_len"]
+    pos = [s + r for s in case["kv_chunk_pos"] for r in range(C)]
+    lay = layout(p.B, p.H, p.Hkv, p.d, p.n_clean_q, p.clean_q_start, p.n_clean_kv,
+                 p.clean_kv_start, p.n_corr_blocks, ids, clean_mask=p.clean_mask,
+                 partial=bool(p.partial), corr_keys=not p.omit_corr_keys, doc_starts=docs,
+                 clean_kv_positions=pos)
+    qs, qb = query_tokens(lay)
+    ks, kb = key_tokens(lay)
+    qp, kp = query_positions(lay), key_positions(lay)
+    qc, kc = corrupted_copies(lay, lay.n_clean_q), corrupted_copies(lay, lay.n_clean_kv)
+    qd, kd = documents(lay, qp), documents(lay, kp)
+    want = visible(qs[:, None], qb[:, None], ks[None, :], kb[None, :], qp[:, None], kp[None, :],
+                   lay.clean_mask, lay.corr_keys, qc[:, None], kc[None, :], qd[:, None], kd[None, :])
+    assert np.array_equal(bd.mask_render(p), want)
+    plain = dict(case)
+    plain.pop("kv_chunk_pos")
+    plain["kv_chunk_len"] = 0
+    q = bd.problem(H=4, Hkv=2, d=128, dtype="bf16", **plain)
+    assert bd.plan_stats(p) == bd.plan_stats(q)
+    assert bd.visible_pairs(p) == bd.visible_pairs(q)
+    assert bd.workspace_size(p, 1) > bd.workspace_size(q, 1)  # the tile map travels along
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_chunk_len=64, kv_chunk_pos=list(range(0, 1024, 64))), -2),  # not a multiple of 128
+    (dict(kv_chunk_len=384, kv_chunk_pos=[0, 384]), -2),                 # does not divide 1024
+    (dict(kv_chunk_len=128), -1),                                        # no positions
+    (dict(kv_chunk_len=128, kv_chunk_pos=[0, 128, 256, 384, 512, 640, 768, 768]), -1),
+    (dict(kv_chunk_len=128, kv_chunk_pos=[0, 128, 256, 384, 512, 640, 768, 960]), -1),
+    (dict(kv_chunk_len=128, kv_chunk_pos=[128, 256, 384, 512, 640, 768, 896, 1024]), -1),
+    (dict(kv_chunk_len=-128), -2),
+])
+def test_gathered_buffer_validation(kw, code):
+    p = bd.problem(B=32, H=4, Hkv=2, d=128, dtype="bf16", n_clean_q=1024, **kw)
+    assert bd.validate(p) == code

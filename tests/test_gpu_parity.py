@@ -193,9 +193,11 @@ def _sampled(spec, t, got, n_blocks=3, kv_groups=(0,), rounding=None, long_keys=
         n_blocks = 1  # each sampled block carries a prefix of 10^5+ keys
     rng = np.random.default_rng(spec.seed)
     cb0, cb1 = spec.clean_q_start // B, (spec.clean_q_start + spec.n_clean_q) // B
-    clean_blocks = sorted({cb0, cb1 - 1} | set(rng.integers(cb0, cb1, n_blocks).tolist()))
+    clean_blocks = sorted({cb0, cb1 - 1} | set(rng.integers(cb0, cb1, n_blocks).tolist())) \
+        if cb1 > cb0 else []
     corr = sorted({0, spec.n_corr_blocks - 1} |
-                  set(rng.integers(0, spec.n_corr_blocks, n_blocks).tolist()))
+                  set(rng.integers(0, spec.n_corr_blocks, n_blocks).tolist())) \
+        if spec.n_corr_blocks else []
     key_blocks = [cb1 - 1, cb1 - 3]
     if spec.doc_starts:  # query blocks on both sides of two document starts, and the
         for s in [x // B for x in spec.doc_starts[1:3]]:  # last keys before each

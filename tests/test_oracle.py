@@ -739,3 +739,48 @@ def test_planted_document_mistakes_are_caught(monkeypatch, slip):
                   corrupted_copies(lay, lay.n_clean_q)[:, None],
                   corrupted_copies(lay, lay.n_clean_kv)[None, :], qd[:, None], kd[None, :])
     assert not np.array_equal(got, want)
+
+
+# ------------------------------------------ gathered clean buffer (positions)
+@pytest.mark.parametrize("partial", [False, True])
+def test_gathered_clean_buffer_is_a_row_permutation(partial):
+    """Appendix, Implementation 1: the clean K/V may arrive gathered in any
+    order, each key masked by its original position. A layout naming every
+    buffer row's position gives the same O, LSE and dQ as the position-ordered
+    buffer, and dK/dV permuted like the buffer rows (zigzag order of P = 4
+    ranks: rank r brings chunks r and 2P-1-r)."""
+    B, P, C = 2, 4, 4
+    L = 2 * P * C
+    lo = 0 if not partial else 8
+    kw = dict(corr_block_ids=[1, 5, 6, 11, 14])
+    if partial:
+        kw.update(partial=True)
+    chunks = [c for r in range(P) for c in (r, 2 * P - 1 - r)]
+    pos = [c * C + i for c in chunks for i in range(C)]
+    if partial:  # chunks of the range [8, 32) only
+        pos = [p for p in pos if p >= lo]
+    n_kv = len(pos)
+    ordered = layout(B, 4, 2, 4, L, 0, n_kv, lo, **kw)
+    gathered = layout(B, 4, 2, 4, L, 0, n_kv, lo, clean_kv_positions=pos, **kw)
+    t = make(ordered, seed=61)
+    perm = np.asarray(pos) - lo  # buffer row i holds ordered row perm[i]
+    tg = dict(t, k_c=t["k_c"][perm], v_c=t["v_c"][perm])
+    a = oracle_of(ordered, t)
+    b = oracle_of(gathered, tg)
+    fa, fb = a.forward(), b.forward()
+    ga, gb = a.backward(), b.backward()
+    for x, y in zip(fa, fb):
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-13)
+    for i, (x, y) in enumerate(zip(ga, gb)):
+        if i in (2, 3):  # clean dK, dV follow the buffer's rows
+            x = x[perm]
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-12)
+    # the rows really moved: the first gathered rows are not the first positions
+    assert not np.array_equal(perm, np.arange(n_kv))
+
+
+def test_gathered_buffer_must_cover_the_visible_keys():
+    with pytest.raises(ValueError):  # position 3 is missing
+        layout(2, 1, 1, 4, 4, clean_kv_positions=[0, 1, 2, 5])
+    with pytest.raises(ValueError):  # a repeated position
+        layout(2, 1, 1, 4, 4, clean_kv_positions=[0, 1, 1, 3])

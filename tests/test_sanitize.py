@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import block_masked_attention_amd as bd
-from tests.test_abi_host import CASES, CASES_DOCS, CASES_PARTIAL, CASES_TC
+from tests.test_abi_host import CASES, CASES_DOCS, CASES_GATHERED, CASES_PARTIAL, CASES_TC
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_masked_attention_amd", "csrc")
@@ -30,6 +30,9 @@ INVALID = [
     dict(clean_mask=2), dict(omit_corr_keys=True), dict(partial=True, clean_kv_start=2, n_clean_kv=8),
     dict(doc_starts=[4, 8]), dict(doc_starts=[0, 8, 8]), dict(doc_starts=[0, 6]),
     dict(n_clean_q=1 << 31), dict(corr_block_ids=[1 << 30]),
+    dict(n_clean_q=256, kv_chunk_len=128, kv_chunk_pos=[128, 128]),
+    dict(n_clean_q=256, kv_chunk_len=128, kv_chunk_pos=[0, 384]),
+    dict(n_clean_q=256, kv_chunk_len=96, kv_chunk_pos=[0, 96]),
 ]
 
 
@@ -71,9 +74,12 @@ def _problem(kw):
 def _line(p):
     ids = [p.corr_block_ids[i] for i in range(p.n_corr_blocks)] if p.corr_block_ids else []
     docs = [p.doc_starts[i] for i in range(p.n_docs)] if p.n_docs else []
+    cpos = [p.kv_chunk_pos[i] for i in range(p.n_clean_kv // p.kv_chunk_len)] \
+        if p.kv_chunk_len > 0 and p.kv_chunk_pos else []
     v = [p.B, p.H, p.Hkv, p.d, p.dtype, p.n_clean_q, p.clean_q_start, p.n_clean_kv,
          p.clean_kv_start, p.n_corr_blocks, p.clean_mask, p.partial, p.omit_corr_keys,
-         1 if p.corr_block_ids else 0, len(ids), *ids, len(docs), *docs]
+         1 if p.corr_block_ids else 0, len(ids), *ids, len(docs), *docs, p.kv_chunk_len,
+         len(cpos), *cpos]
     return " ".join(str(int(x)) for x in v)
 
 
@@ -102,7 +108,8 @@ def test_planner_under_address_and_undefined_behaviour_sanitizers():
     if gxx is None:
         pytest.skip("g++ not available")
     cases = [dict(H=4, Hkv=2, d=32, dtype="bf16", **c)
-             for c in CASES + CASES_TC + CASES_PARTIAL + CASES_DOCS] + INVALID + _random_cases()
+             for c in CASES + CASES_TC + CASES_PARTIAL + CASES_DOCS + CASES_GATHERED] + INVALID \
+        + _random_cases()
     probs = [_problem(c) for c in cases]
     with tempfile.TemporaryDirectory(prefix="bdattn_san_") as tmp:
         exe = os.path.join(tmp, "plan_driver")

@@ -58,6 +58,17 @@ class Spec:
     clean_mask: int = 0
     # packed documents: start positions (first 0, multiples of B); None: one
     doc_starts: Optional[Tuple[int, ...]] = None
+    # a gathered clean K/V buffer: chunks of kv_chunk_len rows, chunk i at
+    # global positions [kv_chunk_pos[i], +kv_chunk_len); 0: position order
+    kv_chunk_len: int = 0
+    kv_chunk_pos: Optional[Tuple[int, ...]] = None
+
+    def kv_positions(self):
+        """Global position of every clean K/V buffer row (a list)."""
+        if not self.kv_chunk_len:
+            return list(range(self.clean_kv_start, self.clean_kv_start + self.n_clean_kv))
+        C = self.kv_chunk_len
+        return [p + r for p in self.kv_chunk_pos for r in range(C)]
 
     @property
     def n_corr(self) -> int:
