@@ -33,7 +33,8 @@ __all__ = ["Problem", "problem", "BdattnError", "lib", "fwd", "bwd", "validate",
            "workspace_size", "mask_render", "visible_pairs", "plan_stats", "version",
            "status_string", "profile_enable", "profile_read", "from_spec", "F32", "BF16",
            "CLEAN_BLOCK_CAUSAL", "CLEAN_TOKEN_CAUSAL", "LIB_PATH", "merge", "plan_cache_info",
-           "plan_cache_budget"]
+           "plan_cache_budget", "LceProblem", "lce_problem", "lce_workspace_size", "lce_fwd",
+           "lce_bwd", "lce_fwd_bwd"]
 
 
 class BdattnError(RuntimeError):
@@ -121,6 +122,22 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
     return p
 
 
+class LceProblem(ctypes.Structure):
+    """ctypes mirror of ``bdattn_lce_problem`` (include/bdattn_lce.h)."""
+    _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("ignore_index", ctypes.c_int32)]
+
+
+def lce_problem(n_tokens: int, hidden: int, vocab: int, chunk: int = 4096,
+                ignore_index: int = -100) -> LceProblem:
+    """Linear cross-entropy descriptor: N tokens, hidden size D, vocabulary
+    V, tokens per chunk, the ignored target value."""
+    p = LceProblem()
+    p.n_tokens, p.hidden, p.vocab, p.chunk, p.ignore_index = n_tokens, hidden, vocab, chunk, ignore_index
+    return p
+
+
 def from_spec(spec) -> Problem:
     """Descriptor of a workload spec (any object with the descriptor's fields)."""
     return problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
@@ -176,6 +193,11 @@ def lib() -> ctypes.CDLL:
                              [vp, ctypes.c_size_t, vp])
     L.bdattn_merge.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                vp, fp, vp, fp, vp, fp, vp]
+    LP = ctypes.POINTER(LceProblem)
+    L.bdattn_lce_workspace_size.argtypes = [LP, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.bdattn_lce_fwd.argtypes = [LP, vp, vp, vp, fp, fp, vp, ctypes.c_size_t, vp]
+    L.bdattn_lce_bwd.argtypes = [LP, vp, vp, vp, fp, fp, vp, fp, vp, ctypes.c_size_t, vp]
+    L.bdattn_lce_fwd_bwd.argtypes = [LP, vp, vp, vp, fp, fp, fp, vp, fp, vp, ctypes.c_size_t, vp]
     L.bdattn_plan_cache_info.argtypes = [ctypes.POINTER(ctypes.c_int64)]
     L.bdattn_plan_cache_budget.argtypes = [ctypes.c_size_t]
     L.bdattn_profile_enable.argtypes = [ctypes.c_int]
@@ -185,7 +207,8 @@ def lib() -> ctypes.CDLL:
                  "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_fwd_noalloc",
                  "bdattn_bwd",
                  "bdattn_merge", "bdattn_profile_enable", "bdattn_profile_read",
-                 "bdattn_plan_cache_info", "bdattn_plan_cache_budget"):
+                 "bdattn_plan_cache_info", "bdattn_plan_cache_budget", "bdattn_lce_workspace_size",
+                 "bdattn_lce_fwd", "bdattn_lce_bwd", "bdattn_lce_fwd_bwd"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -390,6 +413,82 @@ def bwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, do_c, 
                           _stream(dev, stream))
     _check(st, "bdattn_bwd")
     return dq_c, dq_x, dk_c, dv_c, dk_x, dv_x
+
+
+def lce_workspace_size(p: LceProblem, pass_: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().bdattn_lce_workspace_size(ctypes.byref(p), pass_, ctypes.byref(n)),
+           "lce_workspace_size")
+    return n.value
+
+
+def _lce_check(p, h, w, targets):
+    torch = _torch()
+    N, D, V = int(p.n_tokens), int(p.hidden), int(p.vocab)
+    dev = w.device
+    if dev.type != "cuda":
+        raise ValueError("the linear cross-entropy runs on a GPU")
+    _expect(h, (N, D), torch.bfloat16, "h", dev)
+    _expect(w, (V, D), torch.bfloat16, "w", dev)
+    _expect(targets, (N,), torch.int32, "targets", dev)
+    return N, D, V, dev
+
+
+def lce_fwd(p: LceProblem, h, w, targets, *, workspace=None, stream=None):
+    """Linear cross-entropy forward: (loss [N], lse [N]) float32. ``h``
+    [N, D] and ``w`` [V, D] bf16, ``targets`` [N] int32."""
+    torch = _torch()
+    N, D, V, dev = _lce_check(p, h, w, targets)
+    with _on(stream):
+        loss = torch.empty(N, dtype=torch.float32, device=dev)
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+        ws = workspace if workspace is not None else torch.empty(
+            lce_workspace_size(p, 0), dtype=torch.uint8, device=dev)
+    _check(lib().bdattn_lce_fwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets), _ptr(loss),
+                                _ptr(lse), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                _stream(dev, stream)), "bdattn_lce_fwd")
+    return loss, lse
+
+
+def lce_bwd(p: LceProblem, h, w, targets, lse, dloss, *, workspace=None, stream=None):
+    """Linear cross-entropy backward from the forward's ``lse`` and the
+    per-token upstream gradient ``dloss`` (float32 [N]): (dh [N, D] bf16,
+    dw [V, D] float32)."""
+    torch = _torch()
+    N, D, V, dev = _lce_check(p, h, w, targets)
+    _expect(lse, (N,), torch.float32, "lse", dev)
+    _expect(dloss, (N,), torch.float32, "dloss", dev)
+    with _on(stream):
+        dh = torch.empty(N, D, dtype=torch.bfloat16, device=dev)
+        dw = torch.empty(V, D, dtype=torch.float32, device=dev)
+        ws = workspace if workspace is not None else torch.empty(
+            lce_workspace_size(p, 1), dtype=torch.uint8, device=dev)
+    _check(lib().bdattn_lce_bwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets), _ptr(lse),
+                                _ptr(dloss), _ptr(dh), _ptr(dw), _ptr(ws),
+                                ctypes.c_size_t(ws.numel()), _stream(dev, stream)), "bdattn_lce_bwd")
+    return dh, dw
+
+
+def lce_fwd_bwd(p: LceProblem, h, w, targets, dloss, *, workspace=None, stream=None, out=None):
+    """Forward and backward in one pass: (loss, lse, dh, dw)."""
+    torch = _torch()
+    N, D, V, dev = _lce_check(p, h, w, targets)
+    _expect(dloss, (N,), torch.float32, "dloss", dev)
+    with _on(stream):
+        if out is None:
+            loss = torch.empty(N, dtype=torch.float32, device=dev)
+            lse = torch.empty(N, dtype=torch.float32, device=dev)
+            dh = torch.empty(N, D, dtype=torch.bfloat16, device=dev)
+            dw = torch.empty(V, D, dtype=torch.float32, device=dev)
+        else:
+            loss, lse, dh, dw = out
+        ws = workspace if workspace is not None else torch.empty(
+            lce_workspace_size(p, 1), dtype=torch.uint8, device=dev)
+    _check(lib().bdattn_lce_fwd_bwd(ctypes.byref(p), _ptr(h), _ptr(w), _ptr(targets),
+                                    _ptr(dloss), _ptr(loss), _ptr(lse), _ptr(dh), _ptr(dw),
+                                    _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev, stream)),
+           "bdattn_lce_fwd_bwd")
+    return loss, lse, dh, dw
 
 
 def merge(o_a, lse_a, o_b, lse_b, *, stream=None, out=None):

@@ -13,8 +13,9 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dkdv.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dkdv.hip", "lce.hip"]
 HEADERS = ["bdattn_mask.h", "plan.h", "launch.h", "device.h"]
+ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
 
 # Packed fp32 ops are disabled for all device code (hipcc -O3 would otherwise
 # form them from plain float code).
@@ -67,7 +68,9 @@ def build(verbose: bool = False) -> str:
         if errors:
             raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
         tmp = LIB + ".tmp"
-        link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for _, o, _ in jobs] + ["-o", tmp]
+        # rocBLAS carries the linear cross-entropy's projections
+        link = ([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for _, o, _ in jobs] +
+                ["-L", ROCM_LIB, "-Wl,-rpath," + ROCM_LIB, "-lrocblas", "-o", tmp])
         if verbose:
             print(" ".join(link), flush=True)
         res = subprocess.run(link, capture_output=True, text=True)

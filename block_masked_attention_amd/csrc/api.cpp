@@ -221,6 +221,13 @@ std::shared_ptr<Entry> get_entry(const bdattn::Problem& P) {
   return e;
 }
 
+}  // namespace
+
+// The error channel of bdattn_last_error, for the library's other sources.
+int bdattn::record_error(int status, const std::string& msg) { return fail(status, msg); }
+
+namespace {
+
 int load(const bdattn_problem* p, bdattn::Problem* P) {
   std::string msg;
   int st = bdattn::load_problem(p, P, &msg);

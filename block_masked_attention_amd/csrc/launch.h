@@ -48,6 +48,10 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// Records `msg` as the calling thread's last error (bdattn_last_error) and
+// returns `status`.
+int record_error(int status, const std::string& msg);
+
 // True if this build has kernels for (dtype, d).
 bool have_kernels(int dtype, int d);
 

@@ -18,14 +18,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "bdattn.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(bdattn_\w+)\s*\(", src, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(bdattn_\w+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"bdattn_fwd", "bdattn_bwd", "bdattn_validate", "bdattn_workspace_size",
-            "bdattn_mask_render"} <= set(names)
+            "bdattn_mask_render", "bdattn_fwd_noalloc", "bdattn_lce_fwd", "bdattn_lce_bwd",
+            "bdattn_lce_fwd_bwd", "bdattn_lce_workspace_size"} <= set(names)
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -357,3 +362,25 @@ def test_gathered_buffer_mask_and_plan(case):
 def test_gathered_buffer_validation(kw, code):
     p = bd.problem(B=32, H=4, Hkv=2, d=128, dtype="bf16", n_clean_q=1024, **kw)
     assert bd.validate(p) == code
+
+
+def test_lce_host_validation_and_workspace():
+    """The linear cross-entropy's descriptor checks and workspace sizes, on
+    the host (nothing is enqueued for an invalid call)."""
+    ok = bd.lce_problem(1000, 256, 5000, chunk=256)
+    assert bd.lce_workspace_size(ok, 0) == 256 * 5000 * 4
+    assert bd.lce_workspace_size(ok, 1) == 256 * 5000 * 4 + 256 * 5000 * 2
+    small = bd.lce_problem(10, 256, 5000, chunk=256)  # the chunk is at most the tokens
+    assert bd.lce_workspace_size(small, 0) == (10 * 5000 * 4 + 255) // 256 * 256
+    n = ctypes.c_size_t(0)
+    for bad in (bd.lce_problem(10, 12, 5000), bd.lce_problem(10, 256, 5001),
+                bd.lce_problem(10, 256, 5000, chunk=0), bd.lce_problem(1 << 20, 256, 1 << 20, chunk=4096)):
+        assert bd.lib().bdattn_lce_workspace_size(ctypes.byref(bad), 0, ctypes.byref(n)) == -2
+    L = bd.lib()
+    vp = ctypes.c_void_p
+    good = vp(1 << 20)
+    # missing workspace, NULL targets, misaligned h: refused before any GPU work
+    assert L.bdattn_lce_fwd(ctypes.byref(ok), good, good, good, good, good, None, 0, None) == -5
+    assert L.bdattn_lce_fwd(ctypes.byref(ok), good, good, None, good, good, good, 1 << 30, None) == -1
+    assert L.bdattn_lce_fwd(ctypes.byref(ok), vp((1 << 20) + 8), good, good, good, good, good,
+                            1 << 30, None) == -1
