@@ -183,6 +183,164 @@ def time_split_forward(bd, spec, t, shards, reps):
     return {"shards": shards, "launches": len(parts), "ms": round((time.perf_counter() - t0) * 1e3 / reps, 3)}
 
 
+LCE_METRIC = "token-chunked linear CE fwd+bwd useful TFLOP/s (6*N*V*D); % of MI355X bf16 MFMA peak"
+
+
+def lce_cpu_baseline(spec, t, seconds: float):
+    """The float64 linear cross-entropy oracle, as it stands, on the first
+    tokens of the workload (full vocabulary), forward and backward, growing
+    the sample until about `seconds` of work; useful TFLOP/s over it."""
+    import numpy as np
+
+    from oracle import LinearCE
+
+    f64 = lambda x: x.float().cpu().numpy().astype(np.float64)
+    w = f64(t["w"])
+    n, spent, flops = 8, 0.0, 0.0
+    while spent < seconds and n <= spec.N:
+        h = f64(t["h"][:n])
+        tg = t["targets"][:n].cpu().numpy()
+        g = t["dloss"][:n].cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        o = LinearCE(h, w, tg)
+        _, lse = o.forward()
+        o.backward(g, lse)
+        spent = time.perf_counter() - t0
+        flops = 6.0 * n * spec.V * spec.D
+        if spent < seconds / 4:
+            n *= 2
+        else:
+            break
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or threads
+    except Exception:
+        pass
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the first {n} tokens, full vocabulary, float64 numpy forward + backward "
+                      f"(dW included), {spent:.1f} s", "seconds": round(spent, 2),
+            "cpu": platform.processor() or platform.machine(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def read_lce_profile(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary of
+    the linear cross-entropy workload, if it was taken on the current lce.hip
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_trace_hbm.md")
+    if not os.path.exists(path):
+        return None
+    m = {k: v for k, v in re.findall(r"^(\w+):\s*(\S+)\s*$", open(path).read(), re.M)}
+    from block_masked_attention_amd.rocprof import lce_source_hash
+    if m.get("kernel_source") != lce_source_hash() or m.get("kernel") != kernel:
+        return None
+    try:
+        return float(m["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def lce_main(args):
+    """The linear cross-entropy leg: one step = bdattn_lce_fwd_bwd over the
+    whole workload (every chunk: logits product, fused row kernel, dH and dW
+    products), inputs resident in device memory."""
+    import torch
+
+    import block_masked_attention_amd as bd
+    from workloads import LCE_CONFIGS, make_lce_inputs
+
+    spec = next((c for c in LCE_CONFIGS if c.name == args.workload), None)
+    if spec is None:
+        sys.exit(f"unknown workload {args.workload}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = make_lce_inputs(spec, device=dev)
+    p = bd.lce_problem(spec.N, spec.D, spec.V, chunk=spec.chunk)
+    N, D, V = spec.N, spec.D, spec.V
+    useful = 6.0 * N * V * D
+    log(f"[bench] workload {spec.name}: {spec.description}; useful flops/step {useful:.4e}")
+    out = (torch.empty(N, device=dev), torch.empty(N, device=dev),
+           torch.empty(N, D, dtype=torch.bfloat16, device=dev),
+           torch.empty(V, D, dtype=torch.float32, device=dev))
+    ws = torch.empty(bd.lce_workspace_size(p, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        bd.lce_fwd_bwd(p, t["h"], t["w"], t["targets"], t["dloss"], workspace=ws, out=out)
+
+    if args.copy_calibration:
+        src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] ran one plain device copy of 1 GiB (counter calibration)")
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    bd.profile_read_all()
+    bd.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        log(f"[bench] step {i + 1}/{args.steps} enqueued")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    bd.profile_enable(False)
+    prof = bd.profile_read_all()
+    ms_step = (t1 - t0) * 1e3 / max(1, args.steps)
+    value = useful / (ms_step * 1e-3) / 1e12
+    n_chunks = -(-N // spec.chunk)
+    kern = {}
+    for k in bd.LCE_PROFILED:
+        r = prof[k]
+        ms = r["ms"] / max(1, r["launches"])
+        kern[k] = dict(ms=round(ms, 4), launches_per_step=r["launches"] // max(1, args.steps))
+    # per launch (one chunk): each product 2*chunk*V*D flops; the row kernel's
+    # algorithmic bytes are one read of the chunk's fp32 logits and one write
+    # of its bf16 gradient (the kernel reads the logits a second time)
+    per_gemm = 2.0 * spec.chunk * V * D
+    for k in ("lce_logits", "lce_dh", "lce_dw"):
+        kern[k]["tflops"] = round(per_gemm / (kern[k]["ms"] * 1e-3) / 1e12, 1)
+    row_bytes = spec.chunk * V * (4 + 2)
+    kern["lce_rows"]["gb_per_s"] = round(row_bytes / (kern["lce_rows"]["ms"] * 1e-3) / 1e9, 1)
+    dom = max(("lce_logits", "lce_dh", "lce_dw"), key=lambda k: kern[k]["ms"])
+    traffic = read_lce_profile(spec.name, dom)
+    log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
+        f"({100 * value / PEAK_BF16_TFLOPS:.1f}% of peak); " +
+        ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in kern.items()))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = lce_cpu_baseline(spec, t, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+    res = {
+        "metric": LCE_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "description": spec.description, "tokens": N,
+                   "hidden": D, "vocab": V, "chunk": spec.chunk, "chunks": n_chunks,
+                   "useful_flops_per_step": useful, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kern,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": kern[dom]["tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern[dom]["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": per_gemm},
+        "row_kernel_roofline": {"bound": "hbm", "achieved": kern["lce_rows"]["gb_per_s"],
+                                "peak": 8000.0, "unit": "GB/s",
+                                "frac": round(kern["lce_rows"]["gb_per_s"] / 8000.0, 4),
+                                "bytes_per_launch": row_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -190,7 +348,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="256k",
-                    help="workload name (tiny, 8k, 64k, 256k, 512k_rank15)")
+                    help="workload name (tiny, 8k, 64k, 256k, 512k_rank15; lce_8k, lce_256k "
+                         "for the token-chunked linear cross-entropy)")
     ap.add_argument("--clean-mask", choices=("block", "token"), default="block",
                     help="what a clean query sees of its own block: all of it (block-causal, "
                          "the workloads' definition) or the keys up to its own position")
@@ -216,6 +375,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
               f"{world}); this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("lce"):
+        lce_main(args)
+        return
 
     import torch
 

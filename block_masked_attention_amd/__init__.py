@@ -203,12 +203,14 @@ def lib() -> ctypes.CDLL:
     L.bdattn_profile_enable.argtypes = [ctypes.c_int]
     L.bdattn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
+    L.bdattn_profile_read_n.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
     for name in ("bdattn_validate", "bdattn_workspace_size", "bdattn_mask_render",
                  "bdattn_visible_pairs", "bdattn_plan_stats", "bdattn_fwd", "bdattn_fwd_noalloc",
                  "bdattn_bwd",
                  "bdattn_merge", "bdattn_profile_enable", "bdattn_profile_read",
                  "bdattn_plan_cache_info", "bdattn_plan_cache_budget", "bdattn_lce_workspace_size",
-                 "bdattn_lce_fwd", "bdattn_lce_bwd", "bdattn_lce_fwd_bwd"):
+                 "bdattn_lce_fwd", "bdattn_lce_bwd", "bdattn_lce_fwd_bwd", "bdattn_profile_read_n"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L
@@ -280,6 +282,19 @@ def profile_enable(on: bool = True) -> None:
     """Record HIP events around the forward kernel and the backward's dQ and
     dK/dV kernels, on the stream each call is enqueued on."""
     _check(lib().bdattn_profile_enable(1 if on else 0), "profile_enable")
+
+
+LCE_PROFILED = ("lce_logits", "lce_rows", "lce_dh", "lce_dw")
+
+
+def profile_read_all() -> dict:
+    """profile_read for every slot: the attention kernels and the linear
+    cross-entropy's logits product, row kernel, dH and dW products."""
+    names = PROFILED_KERNELS + LCE_PROFILED
+    ms = (ctypes.c_double * len(names))()
+    n = (ctypes.c_int64 * len(names))()
+    _check(lib().bdattn_profile_read_n(len(names), ms, n), "profile_read_n")
+    return {k: dict(ms=ms[i], launches=n[i]) for i, k in enumerate(names)}
 
 
 def profile_read() -> dict:

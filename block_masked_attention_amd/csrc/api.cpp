@@ -281,7 +281,7 @@ int upload(Entry* e, int pass, const bdattn::WsLayout& w, char* ws, hipStream_t 
 // Benchmark instrumentation: per-thread list of (kernel index, events)
 // recorded by the launches while profiling is on. Kernel 0 = forward,
 // 1 = backward dQ, 2 = backward dK/dV.
-constexpr int kProfKernels = 3;
+constexpr int kProfKernels = bdattn::kProfiledKernels;
 struct Prof {
   bool on = false;
   std::vector<std::pair<int, bdattn::KernelEvents>> recs;
@@ -358,6 +358,10 @@ int upload_direct(const bdattn::Plan& plan, const bdattn::WsLayout& w, char* ws,
 
 }  // namespace
 
+const bdattn::KernelEvents* bdattn::profile_events(int first, int n, KernelEvents* ev) {
+  return prof_events(first, n, ev);
+}
+
 extern "C" {
 
 int bdattn_profile_enable(int on) {
@@ -366,8 +370,22 @@ int bdattn_profile_enable(int on) {
 }
 
 int bdattn_profile_read(double* ms, int64_t* launches) {
-  double t[kProfKernels] = {0, 0, 0};
-  int64_t n[kProfKernels] = {0, 0, 0};
+  double t[kProfKernels] = {};
+  int64_t n[kProfKernels] = {};
+  int st = BDATTN_OK;
+  if ((st = bdattn_profile_read_n(kProfKernels, t, n))) return st;
+  for (int k = 0; k < 3; ++k) {
+    if (ms) ms[k] = t[k];
+    if (launches) launches[k] = n[k];
+  }
+  return BDATTN_OK;
+}
+
+int bdattn_profile_read_n(int count, double* ms, int64_t* launches) {
+  if (count < 0 || count > kProfKernels)
+    return fail(BDATTN_ERR_INVALID_ARG, "count must lie in [0, " + std::to_string(kProfKernels) + "]");
+  double t[kProfKernels] = {};
+  int64_t n[kProfKernels] = {};
   int st = BDATTN_OK;
   for (auto& r : g_prof.recs) {
     float x = 0.f;
@@ -382,7 +400,7 @@ int bdattn_profile_read(double* ms, int64_t* launches) {
     (void)hipEventDestroy(r.second.stop);
   }
   g_prof.recs.clear();
-  for (int k = 0; k < kProfKernels; ++k) {
+  for (int k = 0; k < count; ++k) {
     if (ms) ms[k] = t[k];
     if (launches) launches[k] = n[k];
   }

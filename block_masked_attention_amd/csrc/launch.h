@@ -62,6 +62,14 @@ struct KernelEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// Benchmark instrumentation (bdattn_profile_enable): kernel slots 0 forward,
+// 1 backward dQ, 2 backward dK/dV, then the linear cross-entropy's 3 logits
+// product, 4 row kernel, 5 dH product, 6 dW product. profile_events fills
+// ev[0..n-1] with fresh events for slots first..first+n-1 and returns ev, or
+// returns nullptr when profiling is off; every returned pair must be recorded.
+constexpr int kProfiledKernels = 7;
+const KernelEvents* profile_events(int first, int n, KernelEvents* ev);
+
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int d, hipStream_t stream,
                       const KernelEvents* ev);
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t stream,

@@ -267,10 +267,19 @@ int run(Mode mode, const bdattn_lce_problem* p, const void* h_, const void* w_,
   uint16_t* grad = (uint16_t*)((char*)workspace + align_up(size_t(s.C) * s.V * sizeof(float)));
   for (int64_t r0 = 0; r0 < s.N; r0 += s.C) {
     const int cc = int(std::min<int64_t>(s.C, s.N - r0));
+    // benchmark events (slots 3..6: logits, row kernel, dH, dW), if profiling
+    KernelEvents evs[4];
+    const KernelEvents* ev = profile_events(3, mode == kFwd ? 2 : 4, evs);
+    auto mark = [&](int k, bool stop) {
+      if (ev) (void)hipEventRecord(stop ? ev[k].stop : ev[k].start, hs);
+    };
     // logits [cc, V] = h[r0:r0+cc] w^T   (column-major: [V, cc] = w^T' h')
+    mark(0, false);
     if ((st = gemm(bh, rocblas_operation_transpose, rocblas_operation_none, s.V, cc, s.D, w, s.D,
                    h + r0 * s.D, s.D, 0.f, logits, s.V, false, "logits")))
       return st;
+    mark(0, true);
+    mark(1, false);
     if (mode == kFwd)
       hipLaunchKernelGGL(lce_loss_kernel, dim3(cc), dim3(kRowThreads), 0, hs, logits, s.V,
                          targets + r0, s.ignore, loss + r0, lse + r0);
@@ -280,17 +289,22 @@ int run(Mode mode, const bdattn_lce_problem* p, const void* h_, const void* w_,
     else
       hipLaunchKernelGGL(lce_fused_kernel, dim3(cc), dim3(kRowThreads), 0, hs, logits, s.V,
                          targets + r0, s.ignore, dloss + r0, loss + r0, lse + r0, grad);
+    mark(1, true);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return record_error(BDATTN_ERR_HIP, std::string("row kernel: ") + hipGetErrorString(e));
     if (mode == kFwd) continue;
     // dh[r0:r0+cc] = G w   (column-major: [D, cc] = w' G')
+    mark(2, false);
     if ((st = gemm(bh, rocblas_operation_none, rocblas_operation_none, s.D, cc, s.V, w, s.D, grad,
                    s.V, 0.f, dh + r0 * s.D, s.D, true, "dh")))
       return st;
+    mark(2, true);
     // dw (+)= G^T h[r0:r0+cc]   (column-major: [D, V] (+)= h' G'^T)
+    mark(3, false);
     if ((st = gemm(bh, rocblas_operation_none, rocblas_operation_transpose, s.D, s.V, cc,
                    h + r0 * s.D, s.D, grad, s.V, r0 == 0 ? 0.f : 1.f, dw, s.D, false, "dw")))
       return st;
+    mark(3, true);
   }
   return BDATTN_OK;
 }

@@ -317,6 +317,121 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     log(f"[rocprof] wrote the four summaries under {dest}")
 
 
+# ------------------------------------------------ linear cross-entropy
+LCE_SOURCES = ("lce.hip",)
+# the three products of a chunk, told apart by the transposes in the library
+# kernels' names (Tensile naming: A "lik" = A transposed, B "jlk" = B transposed)
+LCE_GEMMS = (("lce_logits", "_Alik_Bljk"), ("lce_dh", "_Ailk_Bljk"), ("lce_dw", "_Ailk_Bjlk"))
+
+
+def lce_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in LCE_SOURCES:
+        with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def lce_role(name: str):
+    """lce_logits / lce_dh / lce_dw for the library products, lce_rows for the
+    fused row kernels, None for anything else."""
+    if "lce_fused_kernel" in name or "lce_loss_kernel" in name or "lce_grad_kernel" in name:
+        return "lce_rows"
+    for role, tag in LCE_GEMMS:
+        if name.startswith("Cijk") and tag in name:
+            return role
+    return None
+
+
+def lce_profile(args):
+    """Kernel trace and calibrated HBM traffic of one linear cross-entropy
+    step (bench.py --workload lce_*), per role."""
+    b = ["--workload", args.workload, "--no-cpu-baseline", "--steps", "1"]
+    d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", "1"], args.out,
+                       args.limit)
+    cal = b + ["--warmup", "0", "--copy-calibration"]
+    d_fetch = run_pass("fetch", ["--pmc", "FETCH_SIZE"], cal, args.out, args.limit)
+    d_write = run_pass("write", ["--pmc", "WRITE_SIZE"], cal, args.out, args.limit)
+    fetch_raw, write_raw = lce_counters(d_fetch), lce_counters(d_write)
+    cf = fetch_raw.pop(COPY_KERNEL, {}).get("FETCH_SIZE")
+    cw = write_raw.pop(COPY_KERNEL, {}).get("WRITE_SIZE")
+    fs = COPY_BYTES / (cf * 1024) if cf else None
+    ws = COPY_BYTES / (cw * 1024) if cw else None
+    rows = {}
+    for r in read_csv(d_trace, "kernel_stats"):
+        role = lce_role(r["Name"])
+        if role is None:
+            continue
+        x = rows.setdefault(role, dict(calls=0, ns=0.0, names=set()))
+        x["calls"] += int(r["Calls"])
+        x["ns"] += float(r["TotalDurationNs"])
+        x["names"].add(short_name(r["Name"])[:60])
+    for role, x in rows.items():
+        x["ms"] = x["ns"] / x["calls"] / 1e6
+        f, w = fetch_raw.get(role), write_raw.get(role)
+        if f and fs:
+            x["read_gb"] = f["FETCH_SIZE"] * 1024 * fs / 1e9
+        if w and ws:
+            x["write_gb"] = w["WRITE_SIZE"] * 1024 * ws / 1e9
+    sys.path.insert(0, ROOT)
+    from workloads import LCE_CONFIGS
+    spec = next(c for c in LCE_CONFIGS if c.name == args.workload)
+    cmd = f"python -m block_masked_attention_amd.rocprof --workload {args.workload} --out {args.out}"
+    if args.profiles:
+        cmd += f" --profiles {args.profiles}"
+    per_gemm = 2.0 * spec.chunk * spec.V * spec.D
+    out = [f"# linear cross-entropy, {args.workload} workload: rocprofv3 kernel trace and HBM traffic",
+           "", "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
+           f"Workload {args.workload}: {spec.description}; one forward + backward step "
+           f"(`bench.py --workload {args.workload} --no-cpu-baseline --steps 1`). Source hash of "
+           f"lce.hip {lce_source_hash()}. Per chunk: the logits product, the fused row kernel, the "
+           "dH product and the dW product; the products are rocBLAS kernels, told apart by the "
+           "transposes in their names. HBM bytes from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), "
+           f"scaled by a 1 GiB plain copy (factors {fs or 0:.3f} fetch, {ws or 0:.3f} write).", "",
+           "| role | kernel | launches | avg ms | TFLOP/s | HBM read GB | HBM write GB | HBM GB/s |",
+           "|---|---|---|---|---|---|---|---|"]
+    for role in ("lce_logits", "lce_rows", "lce_dh", "lce_dw"):
+        if role not in rows:
+            continue
+        x = rows[role]
+        tf = f"{per_gemm / (x['ms'] * 1e-3) / 1e12:.0f}" if role != "lce_rows" else ""
+        rd, wr = x.get("read_gb"), x.get("write_gb")
+        bw = f"{(rd + wr) / (x['ms'] * 1e-3):.0f}" if rd is not None and wr is not None else ""
+        out.append(f"| {role} | `{sorted(x['names'])[0]}` | {x['calls']} | {x['ms']:.3f} | {tf} | "
+                   f"{'' if rd is None else f'{rd:.2f}'} | {'' if wr is None else f'{wr:.2f}'} | {bw} |")
+    dom = max((k for k in rows if k != "lce_rows"), key=lambda k: rows[k]["ms"])
+    d = rows[dom]
+    nbytes = (d.get("read_gb", 0) + d.get("write_gb", 0)) * 1e9
+    out += ["", f"Dominant kernel (longest): {dom}.", "",
+            "Machine-readable lines for bench.py (valid only for the source hash below):", "",
+            f"kernel: {dom}", f"workload: {args.workload}", f"kernel_source: {lce_source_hash()}",
+            f"hbm_bytes_per_launch: {nbytes:.6e}"]
+    text = "\n".join(out) + "\n"
+    with open(os.path.join(args.out, "summary.md"), "w") as fh:
+        fh.write(text)
+    if args.profiles:
+        os.makedirs(args.profiles, exist_ok=True)
+        with open(os.path.join(args.profiles, f"{args.workload}_kernel_trace_hbm.md"), "w") as fh:
+            fh.write(text)
+    print(json.dumps({k: {kk: vv for kk, vv in v.items() if kk != "names"} for k, v in rows.items()}),
+          flush=True)
+
+
+def lce_counters(d):
+    """Counter totals per role (and the calibration copy), per dispatch."""
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in read_csv(d, "counter_collection"):
+        name = r["Kernel_Name"]
+        k = COPY_KERNEL if short_name(name) == COPY_KERNEL else lce_role(name)
+        if k is None:
+            continue
+        tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    return {k: dict({c: v / len(disp[k]) for c, v in cs.items()}) for k, cs in tot.items()}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -331,6 +446,9 @@ def main():
         sys.exit("rocprofv3 not found")
     os.makedirs(args.out, exist_ok=True)
     os.environ.setdefault("TMPDIR", "/tmp")
+    if args.workload.startswith("lce"):
+        lce_profile(args)
+        return
     b = ["--workload", args.workload, "--no-cpu-baseline", "--steps", "1"]
     if args.docs > 1:
         b += ["--docs", str(args.docs)]

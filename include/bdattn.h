@@ -276,6 +276,11 @@ int bdattn_merge(int64_t n_rows, int32_t H, int32_t d, int32_t dtype,
  * events; either pointer may be NULL. Off by default; costs nothing when off. */
 int bdattn_profile_enable(int on);
 int bdattn_profile_read(double* ms, int64_t* launches);
+/* The same for `count` kernel slots (at most 7): 0..2 as above, then the
+ * linear cross-entropy's (include/bdattn_lce.h) 3 logits product, 4 row
+ * kernel, 5 dH product, 6 dW product, each recorded once per chunk.
+ * BDATTN_ERR_INVALID_ARG for a count outside [0, 7]. */
+int bdattn_profile_read_n(int count, double* ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

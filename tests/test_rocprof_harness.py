@@ -107,3 +107,15 @@ def test_repository_summaries(tmp_path):
     assert float(m["clock_ghz"]) == pytest.approx(1e7 / 8 / 3e-3 / 1e9, abs=1e-3)
     sq = open(os.path.join(dest, "bdattn_8k_sq_counters.md")).read()
     assert "| derived: VALU instructions per MFMA | 3.00 |" in sq
+
+
+def test_lce_roles_follow_the_transposes_in_the_kernel_names():
+    """The linear cross-entropy's three library products are told apart by
+    the transposes Tensile writes into their names; the row kernels by name."""
+    from block_masked_attention_amd.rocprof import lce_role
+    assert lce_role("Cijk_Alik_Bljk_BBS_BH_Bias_HAS_MT256x256x64_MI16x16x1") == "lce_logits"
+    assert lce_role("Cijk_Ailk_Bljk_BBS_BH_MT256x256x64") == "lce_dh"
+    assert lce_role("Cijk_Ailk_Bjlk_BSS_BH_MT256x256x64") == "lce_dw"
+    assert lce_role("bdattn::(anonymous namespace)::lce_fused_kernel(float const*, int)") == "lce_rows"
+    assert lce_role("__amd_rocclr_copyBuffer") is None
+    assert lce_role("void at::native::vectorized_elementwise_kernel<4>") is None

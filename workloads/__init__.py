@@ -196,3 +196,54 @@ def small_spec(L=256, B=16, H=2, Hkv=2, d=32, dtype="f32", seed=7, std=1.0,
 
 
 __all__.append("small_spec")
+
+
+# ------------------------------------------------ linear cross-entropy
+@dataclass(frozen=True)
+class LceSpec:
+    """A token-chunked linear cross-entropy problem: N tokens with hidden
+    size D over a vocabulary of V entries, `chunk` tokens per chunk."""
+    name: str
+    N: int
+    D: int
+    V: int
+    chunk: int
+    seed: int = 0
+    logit_std: float = 2.0  # std of the logits h.w at initialisation
+    ignore_frac: float = 0.0  # fraction of targets set to ignore_index (-100)
+    description: str = ""
+
+
+# The loss of block-diffusion training is taken on the corrupted tokens: at
+# the 256K context that is 262,144 tokens per sequence. Vocabulary 131,072
+# and hidden size 4,096 (an 8B-class model of the family the pages train;
+# the pages state neither).
+LCE_CONFIGS: Tuple[LceSpec, ...] = (
+    LceSpec("lce_8k", 8192, 4096, 131072, 4096, seed=2001,
+            description="8192 tokens, hidden 4096, vocabulary 131072, chunks of 4096, bf16"),
+    LceSpec("lce_256k", 262144, 4096, 131072, 8192, seed=2002,
+            description="262144 tokens (the corrupted stream at 256K context), hidden 4096, "
+                        "vocabulary 131072, chunks of 8192, bf16"),
+)
+
+
+def make_lce_inputs(spec: LceSpec, device="cpu"):
+    """Seeded draws: h [N, D] ~ N(0, 1), w [V, D] ~ N(0, 1) * logit_std /
+    sqrt(D) (both rounded to bf16), targets uniform over [0, V) with
+    ignore_frac of them set to -100 (int32), and the upstream gradient of a
+    mean over the valid tokens (float32 [N])."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(spec.seed)
+    h = torch.randn(spec.N, spec.D, generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn(spec.V, spec.D, generator=g, device=dev) * (spec.logit_std / spec.D ** 0.5)
+         ).to(torch.bfloat16)
+    t = torch.randint(0, spec.V, (spec.N,), generator=g, device=dev, dtype=torch.int32)
+    if spec.ignore_frac > 0:
+        t[torch.rand(spec.N, generator=g, device=dev) < spec.ignore_frac] = -100
+    n_valid = int((t != -100).sum().item())
+    dloss = torch.full((spec.N,), 1.0 / max(1, n_valid), device=dev, dtype=torch.float32)
+    return dict(h=h, w=w, targets=t, dloss=dloss)
+
+
+__all__ += ["LceSpec", "LCE_CONFIGS", "make_lce_inputs"]
