@@ -254,6 +254,9 @@ def lce_main(args):
     spec = next((c for c in LCE_CONFIGS if c.name == args.workload), None)
     if spec is None:
         sys.exit(f"unknown workload {args.workload}")
+    if args.lce_chunk:
+        from dataclasses import replace
+        spec = replace(spec, chunk=args.lce_chunk)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t = make_lce_inputs(spec, device=dev)
@@ -365,6 +368,9 @@ def main():
                          "(2P chunks; rank r brings position chunks r and 2P-1-r), each key "
                          "masked by its original position; with --split-forward the clean part "
                          "is one launch over the whole gathered buffer")
+    ap.add_argument("--lce-chunk", type=int, default=0, metavar="C",
+                    help="linear cross-entropy workloads: tokens per chunk (default: the "
+                         "workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",

@@ -369,6 +369,32 @@ constexpr int kReadAhead = 3;
 // Left to itself, the compiler sinks each read next to its product when
 // registers are scarce, and every product then waits for a full LDS round
 // trip.
+// The same chain with hook(k) run right after product k, inside the fenced
+// slot: vector work placed there overlaps the products that follow it (a
+// wave issues independent vector instructions while its matrix products
+// run), instead of waiting for the whole chain.
+template <int N, int PF, class Frag, class Read, class Mma, class Hook>
+__device__ __forceinline__ void product_chain_hooked(Read read, Mma mma, Hook hook) {
+  Frag buf[PF];
+#pragma unroll
+  for (int k = 0; k < PF && k < N; ++k) buf[k] = read(k);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma(k, buf[k % PF]);
+    if (k + PF < N) buf[k % PF] = read(k + PF);
+    hook(k);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// max of x over lanes l and l ^ 32 (v_permlane32_swap: a register exchange
+// between the wave's halves, no LDS round trip)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int N, int PF, class Frag, class Read, class Mma>
 __device__ __forceinline__ void product_chain(Read read, Mma mma) {
   Frag buf[PF];

@@ -183,7 +183,7 @@ void fwd_kernel(FwdArgs a) {
         mx = fmaxf(mx, s[mb][i]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    mx = max_halves(mx) * a.scale_log2;
     if (__any(mx > m + kRescaleMargin)) {  // some row's maximum moved (wave-uniform)
       const float m_new = fmaxf(m, mx);
       const float alpha = m == kNegInf ? 0.f : fast_exp2(m - m_new);
@@ -201,25 +201,36 @@ void fwd_kernel(FwdArgs a) {
     // shifts LSE by up to 2^-9 and scales every recomputed P of the row)
     Frag pf[TK / 32][2];
     float rs = 0.f;
+    // weights of the 16-key slice mt (8 per lane), elements [i0, i1); packed
+    // to bf16 once complete
+    float pv[8];
+    auto weights = [&](int mt, int i0, int i1) __attribute__((always_inline)) {
+      const int mb = mt / 2, h = mt % 2;
 #pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(fmaf(s[mb][i], a.scale_log2, -m_use));
-        rs += p[i];
+      for (int i = i0; i < i1; ++i) {
+        pv[i] = fast_exp2(fmaf(s[mb][8 * h + i], a.scale_log2, -m_use));
+        rs += pv[i];
       }
-      pf[mb][0] = E::pack(p);
-      pf[mb][1] = E::pack(p + 8);
-    }
-    l += rs;
-    // O += V^T P over the tile's keys: product k = (16-key slice mt, column block db)
-    product_chain<TK / 32 * 2 * (D / 32), kReadAhead, Frag>(
-        [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<VT>(smem, 16 * (k / (D / 32)), k % (D / 32)); },
+      if (i1 == 8) pf[mb][h] = E::pack(pv);
+    };
+    // O += V^T P over the tile's keys: product k = (16-key slice mt, column
+    // block db). Slice 0's weights come first; slice mt + 1's are computed
+    // between the products of slice mt (same values and summation order as
+    // computing them all first).
+    constexpr int PS = D / 32;   // products per slice
+    constexpr int EPP = 8 / PS;  // weights computed after each product
+    weights(0, 0, 8);
+    product_chain_hooked<TK / 32 * 2 * PS, kReadAhead, Frag>(
+        [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<VT>(smem, 16 * (k / PS), k % PS); },
         [&](int k, const Frag& y) __attribute__((always_inline)) {
-          const int mt = k / (D / 32);
-          E::mma(o[k % (D / 32)], y, pf[mt / 2][mt % 2]);
+          const int mt = k / PS;
+          E::mma(o[k % PS], y, pf[mt / 2][mt % 2]);
+        },
+        [&](int k) __attribute__((always_inline)) {
+          const int mt = k / PS, db = k % PS;
+          if (mt + 1 < TK / 16) weights(mt + 1, db * EPP, (db + 1) * EPP);
         });
+    l += rs;
     lds_dma_wait();
     __syncthreads();
   };
