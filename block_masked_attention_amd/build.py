@@ -13,7 +13,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dkdv.hip", "lce.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dkdv.hip", "kernels_bwd_fused.hip", "lce.hip"]
 HEADERS = ["bdattn_mask.h", "plan.h", "launch.h", "device.h"]
 ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
 
@@ -24,9 +24,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
-# Per-file options: the key-tile backward is scheduled for instruction-level
-# parallelism (measured faster for that kernel, slower for the dQ kernel).
-FILE_FLAGS = {"kernels_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-file options: the key-tile backward kernels are scheduled for
+# instruction-level parallelism (measured faster for the dK/dV kernel, slower
+# for the dQ kernel).
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+FILE_FLAGS = {"kernels_dkdv.hip": _ILP, "kernels_bwd_fused.hip": _ILP}
 
 
 def hipcc() -> str:

@@ -30,6 +30,9 @@
 // Tile loops are double buffered with the buffer index a compile-time
 // constant of the loop body (two copies of each body), so every LDS operand
 // read carries its buffer in the instruction's immediate offset.
+#include <stdlib.h>
+#include <string.h>
+
 #include "device.h"
 
 namespace bdattn {
@@ -531,6 +534,16 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
                        st ? a.o_x : a.o_c, st ? a.do_x : a.do_c, st ? a.lse_x : a.lse_c,
                        st ? a.d_x : a.d_c, st ? a.l2_x : a.l2_c, n, n_pad, a.H);
   }
+  // BDATTN_BWD=fused10: the one-kernel backward (timed in the dK/dV slot)
+  const int dtype = BF16 ? BDATTN_BF16 : BDATTN_F32;
+  if (const char* e = getenv("BDATTN_BWD"); e && !strcmp(e, "fused10") && bwd_fused_supported(a, dtype, D)) {
+    if (ev) (void)hipEventRecord(ev[0].start, s);
+    if (ev) (void)hipEventRecord(ev[0].stop, s);
+    if (ev) (void)hipEventRecord(ev[1].start, s);
+    const hipError_t err = launch_bwd_fused(a, dtype, D, s);
+    if (ev) (void)hipEventRecord(ev[1].stop, s);
+    return err;
+  }
   if (ev) (void)hipEventRecord(ev[0].start, s);
   const dim3 grid(a.n_q_items), block(FWD_WAVES * 64);
   if (a.n_q_items > 0 && a.kv_map) {  // a gathered clean buffer
@@ -543,7 +556,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   if (ev) (void)hipEventRecord(ev[1].start, s);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess) e = launch_dkdv(a, BF16 ? BDATTN_BF16 : BDATTN_F32, D, s);
+  if (e == hipSuccess) e = launch_dkdv(a, dtype, D, s);
   if (ev) (void)hipEventRecord(ev[1].stop, s);
   return e;
 }

@@ -5,6 +5,9 @@
 // pass; visibility of §3.2 in bdattn_mask.h). Operand layouts and the LDS tile
 // format are described in device.h. This file is compiled on its own so that
 // its scheduling options apply to this kernel only.
+#include <stdlib.h>
+#include <string.h>
+
 #include "device.h"
 
 namespace bdattn {
@@ -232,7 +235,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     f32x16 sb[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) sb[mb] = zero16();
+    // S first: the raised priority gives the S chain the matrix core, so P's
+    // exponentials then overlap the dS wave's dP products
+    __builtin_amdgcn_s_setprio(2);
     scores(QT{}, sb);
+    __builtin_amdgcn_s_setprio(0);
     Frag pa[NMB][2];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -283,6 +290,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
     scores(GT{}, dp);
     __syncthreads();  // P handed over
+    // dS ahead of the P wave's dV products, so that the dK products start early
+    __builtin_amdgcn_s_setprio(2);
     Frag sa[NMB][2];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -298,6 +307,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       sa[mb][0] = E::pack(ds);
       sa[mb][1] = E::pack(ds + 8);
     }
+    __builtin_amdgcn_s_setprio(0);
     accumulate(QT{}, sa);
     pos = nxt;
     lds_dma_wait();
@@ -346,6 +356,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t s) {
   if (a.n_kv_items <= 0) return hipSuccess;
   const dim3 grid(a.n_kv_items), block(512);
+  if (const char* e = getenv("BDATTN_DKDV"); e && !strcmp(e, "fused")) return launch_dkdv_fused(a, dtype, d, s);
   if (dtype == BDATTN_BF16 && d == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128>), grid, block, 0, s, a);
   else if (dtype == BDATTN_BF16 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32>), grid, block, 0, s, a);
   else if (dtype == BDATTN_F32 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<false, 32>), grid, block, 0, s, a);

@@ -76,6 +76,12 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t stream,
                       const KernelEvents* ev);
 // The key-tile dK/dV kernel alone (called by launch_bwd after the dQ kernel).
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t stream);
+// Measured alternatives (kernels_bwd_fused.hip): dK/dV with one wave per 32
+// keys in both roles, and the whole backward in one kernel with dQ by float
+// atomics (bf16, d = 128, contiguous clean K/V: bwd_fused_supported).
+hipError_t launch_dkdv_fused(const BwdArgs& a, int dtype, int d, hipStream_t stream);
+bool bwd_fused_supported(const BwdArgs& a, int dtype, int d);
+hipError_t launch_bwd_fused(const BwdArgs& a, int dtype, int d, hipStream_t stream);
 // Merge of two partial results (bdattn_merge).
 hipError_t launch_merge(int64_t n_rows, int H, int d, int dtype, const void* o_a,
                         const float* lse_a, const void* o_b, const float* lse_b, void* o,
