@@ -30,6 +30,11 @@ bdattn_<workload>_{rocprof_summary,kernel_trace,hbm_traffic,sq_counters}.md.
 The HBM traffic file ends with machine-readable lines (dominant kernel,
 workload, kernel source hash, HBM bytes per launch, shader clock) that
 bench.py reports in its roofline while the kernel sources are unchanged.
+
+``--bwd fused10`` profiles the one-kernel backward (BDATTN_BWD=fused10, the
+measured alternative in kernels_bwd_fused.hip) instead of the split one; its
+write pass also counts TCC_EA0_ATOMIC (the float-atomic requests the L2
+passes on to memory), and its summaries are named <workload>_bwd_fused10.
 """
 from __future__ import annotations
 
@@ -45,9 +50,12 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ("kernels.hip", "kernels_dkdv.hip", "device.h", "bdattn_mask.h", "launch.h")
-BENCH_NAME = {"fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv"}
+# bench.py times the one-kernel backward in the dK/dV slot
+BENCH_NAME = {"fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv",
+              "bwd_fused_kernel": "bwd_dkdv"}
 MAIN_KERNELS = ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kernel",
-                "merge_kernel")
+                "merge_kernel", "bwd_fused_kernel", "fill_zero_f32", "store_dq")
+ATOMIC = "TCC_EA0_ATOMIC_sum"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
 SQ1 = ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
@@ -74,8 +82,13 @@ def kernel_source_hash() -> str:
 
 def short_name(kernel: str) -> str:
     """'void bdattn::(anonymous namespace)::bwd_dq_kernel<true, 128>(...)' ->
-    'bwd_dq_kernel<true, 128>'; other kernels keep their name up to '('."""
+    'bwd_dq_kernel<true, 128>'; 'void bdattn::(anonymous namespace)::store_dq(...)'
+    -> 'store_dq'; other kernels keep their name up to '('."""
     m = re.search(r"::(\w+<[^>]*>)\(", kernel)
+    if m:
+        return m.group(1)
+    # a library kernel that is not a template (rocprofv3 drops the "void ")
+    m = re.match(r"(?:void )?bdattn::(?:\(anonymous namespace\)::)?(\w+)\(", kernel)
     if m:
         return m.group(1)
     return kernel.split("(")[0].replace("void ", "").strip()
@@ -155,6 +168,8 @@ def summarise(dur, fetch, write, sq1, sq2, dev):
             r["hbm_write_gb"] = round(write[k]["WRITE_SIZE"] * 1024 * w_scale / 1e9, 3)
         if "hbm_read_gb" in r and "hbm_write_gb" in r:
             r["hbm_gbps"] = round((r["hbm_read_gb"] + r["hbm_write_gb"]) / s, 1)
+        if k in write and ATOMIC in write[k]:  # atomic requests beyond the L2, per launch
+            r["atomic_requests"] = write[k][ATOMIC]
         clocks = [c["GRBM_GUI_ACTIVE"] / dev["xcds"] / s / 1e9
                   for c in (sq1.get(k), sq2.get(k)) if c and "GRBM_GUI_ACTIVE" in c]
         if clocks:
@@ -182,6 +197,8 @@ def markdown(summary, workload, cmd):
             ("lds_busy", "LDS busy"), ("valu_per_mfma", "VALU/MFMA"),
             ("hbm_read_gb", "HBM read GB"), ("hbm_write_gb", "HBM write GB"),
             ("hbm_gbps", "HBM GB/s")]
+    if any("atomic_requests" in r for r in summary["kernels"].values()):
+        cols.append(("atomic_requests", "atomic requests"))
     out = [f"# bdattn kernels, {workload} workload: rocprofv3 summary", "",
            "Command (run from the repository root on one GPU):", "", "```", cmd, "```", "",
            f"Device {summary['device']['name']}: {summary['device']['cus']} CUs, "
@@ -212,13 +229,15 @@ def _main_rows(d_trace):
     return [r for r in read_csv(d_trace, "kernel_stats") if short_name(r["Name"]).startswith(MAIN_KERNELS)]
 
 
-def profile_key(workload, docs=1):
+def profile_key(workload, docs=1, bwd="split"):
     """Name of a profiled configuration: the workload, with the number of
-    packed documents when there are several."""
-    return workload + (f"_docs{docs}" if docs > 1 else "")
+    packed documents when there are several and the backward when it is not
+    the split one."""
+    return workload + (f"_docs{docs}" if docs > 1 else "") + ("" if bwd == "split" else f"_bwd_{bwd}")
 
 
-def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, summary, docs=1):
+def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, summary, docs=1,
+                   bwd="split"):
     """The four repository summaries of one harness run (tables only)."""
     sys.path.insert(0, ROOT)
     from workloads import config
@@ -228,7 +247,10 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     if docs > 1:
         desc += f"; {docs} packed documents (bench.py --docs {docs})"
     bench_extra = f" --docs {docs}" if docs > 1 else ""
-    workload = profile_key(workload, docs)
+    if bwd != "split":
+        desc += (f"; the one-kernel backward (environment BDATTN_BWD={bwd}, "
+                 "block_masked_attention_amd/csrc/kernels_bwd_fused.hip)")
+    workload = profile_key(workload, docs, bwd)
     head = ["Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
             f"Workload {workload}: {desc}. Kernel source hash {kernel_source_hash()}.", ""]
     os.makedirs(dest, exist_ok=True)
@@ -258,19 +280,22 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     cf, cw = fetch.get(COPY_KERNEL, {}), write.get(COPY_KERNEL, {})
     out = [f"# bdattn kernels, {workload} workload: HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE)",
            ""] + head + [
-        "The `fetch` and `write` passes: `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` over "
+        "The `fetch` and `write` passes: `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE"
+        + (f" {ATOMIC}" if bwd != "split" else "") + "` over "
         f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 0 "
         "--copy-calibration`. The calibration copy (`__amd_rocclr_copyBuffer`) reads and writes "
         f"exactly {COPY_BYTES // 1024} KiB; the counters read FETCH_SIZE = "
         f"{cf.get('FETCH_SIZE', 0):.0f} KiB and WRITE_SIZE = {cw.get('WRITE_SIZE', 0):.0f} KiB for "
         f"it, so the scale factors are {summary['fetch_scale']:.3f} (fetch) and "
         f"{summary['write_scale']:.3f} (write). Counts are per launch.", "",
-        "| kernel | launches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (GB, scaled) | write (GB, scaled) |",
-        "|---|---|---|---|---|---|"]
+        "| kernel | launches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (GB, scaled) | write (GB, scaled) |"
+        + (f" {ATOMIC} |" if bwd != "split" else ""),
+        "|---|---|---|---|---|---|" + ("---|" if bwd != "split" else "")]
     for k, r in summary["kernels"].items():
         f, w = fetch.get(k, {}), write.get(k, {})
         out.append(f"| `{k}` | {f.get('_dispatches', '')} | {f.get('FETCH_SIZE', 0):.0f} | "
-                   f"{w.get('WRITE_SIZE', 0):.0f} | {r.get('hbm_read_gb', '')} | {r.get('hbm_write_gb', '')} |")
+                   f"{w.get('WRITE_SIZE', 0):.0f} | {r.get('hbm_read_gb', '')} | {r.get('hbm_write_gb', '')} |"
+                   + (f" {w.get(ATOMIC, 0):.4g} |" if bwd != "split" else ""))
     main = {k: r for k, r in summary["kernels"].items() if _base(k) in BENCH_NAME}
     dom = max(main, key=lambda k: main[k]["ms"])
     r = main[dom]
@@ -441,6 +466,8 @@ def main():
     ap.add_argument("--docs", type=int, default=1, help="packed documents (bench.py --docs)")
     ap.add_argument("--profiles", default=None,
                     help="also write the repository summaries of this run into this directory")
+    ap.add_argument("--bwd", choices=("split", "fused10"), default="split",
+                    help="backward to profile (fused10: the one-kernel backward)")
     args = ap.parse_args()
     if shutil.which("rocprofv3") is None:
         sys.exit("rocprofv3 not found")
@@ -452,29 +479,34 @@ def main():
     b = ["--workload", args.workload, "--no-cpu-baseline", "--steps", "1"]
     if args.docs > 1:
         b += ["--docs", str(args.docs)]
+    if args.bwd != "split":  # read by the library at every backward call
+        os.environ["BDATTN_BWD"] = args.bwd
     d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", "1"], args.out,
                        args.limit)
     cal = b + ["--warmup", "0", "--copy-calibration"]
     d_fetch = run_pass("fetch", ["--pmc", "FETCH_SIZE"], cal, args.out, args.limit)
-    d_write = run_pass("write", ["--pmc", "WRITE_SIZE"], cal, args.out, args.limit)
+    d_write = run_pass("write", ["--pmc", "WRITE_SIZE"] + ([ATOMIC] if args.bwd != "split" else []),
+                       cal, args.out, args.limit)
     d_sq1 = run_pass("sq1", ["--pmc"] + SQ1, b + ["--warmup", "0"], args.out, args.limit)
     d_sq2 = run_pass("sq2", ["--pmc"] + SQ2, b + ["--warmup", "0"], args.out, args.limit)
     summary = summarise(durations(d_trace), counters(d_fetch), counters(d_write),
                         counters(d_sq1), counters(d_sq2), agent(d_trace))
-    summary["workload"] = profile_key(args.workload, args.docs)
+    summary["workload"] = profile_key(args.workload, args.docs, args.bwd)
     cmd = f"python -m block_masked_attention_amd.rocprof --workload {args.workload} --out {args.out}"
     if args.docs > 1:
         cmd += f" --docs {args.docs}"
+    if args.bwd != "split":
+        cmd += f" --bwd {args.bwd}"
     if args.profiles:
         cmd += f" --profiles {args.profiles}"
     with open(os.path.join(args.out, "summary.json"), "w") as fh:
         json.dump(summary, fh, indent=1)
     with open(os.path.join(args.out, "summary.md"), "w") as fh:
-        fh.write(markdown(summary, profile_key(args.workload, args.docs), cmd))
+        fh.write(markdown(summary, profile_key(args.workload, args.docs, args.bwd), cmd))
     if args.profiles:
         write_profiles(args.profiles, args.workload, cmd, d_trace, counters(d_fetch),
                        counters(d_write), counters(d_sq1), counters(d_sq2), agent(d_trace), summary,
-                       docs=args.docs)
+                       docs=args.docs, bwd=args.bwd)
     print(json.dumps(summary), flush=True)
 
 

@@ -32,6 +32,46 @@ def _counters(d, per_kernel):
 def test_short_names():
     assert rocprof.short_name(K) == "bwd_dq_kernel<true, 128>"
     assert rocprof.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+    assert rocprof.short_name("bdattn::(anonymous namespace)::store_dq(float const*, "
+                              "unsigned short*, unsigned short*, long, long, float)") == "store_dq"
+    assert rocprof.short_name("void bdattn::(anonymous namespace)::fill_zero_f32(float*, long)") \
+        == "fill_zero_f32"
+
+
+def test_one_kernel_backward_profile(tmp_path):
+    """--bwd fused10: the atomic requests of the write pass are reported per
+    launch, the summaries get their own name, and the dominant kernel is
+    reported in the dK/dV slot (where bench.py times it) under that name."""
+    assert rocprof.profile_key("64k") == "64k"
+    assert rocprof.profile_key("64k", 1, "fused10") == "64k_bwd_fused10"
+    assert rocprof.profile_key("256k", 16, "fused10") == "256k_docs16_bwd_fused10"
+    t = str(tmp_path)
+    kf = "void bdattn::(anonymous namespace)::bwd_fused_kernel<true, 128, true>(bdattn::BwdArgs, float*)"
+    kz = "bdattn::(anonymous namespace)::fill_zero_f32(float*, long)"
+    _write(t + "/trace", "kernel_stats", [
+        dict(Name=kf, Calls=1, AverageNs=4.0e8, MinNs=4.0e8, MaxNs=4.0e8, Percentage=90.0),
+        dict(Name=kz, Calls=1, AverageNs=1.0e5, MinNs=1.0e5, MaxNs=1.0e5, Percentage=0.1)])
+    _write(t + "/trace", "agent_info", [dict(Name="gfx950", Simd_Count=1024, Cu_Count=256,
+                                             Num_Xcc=8)])
+    _counters(t + "/fetch", [(rocprof.COPY_KERNEL, dict(FETCH_SIZE=524288)),
+                             (kf, dict(FETCH_SIZE=1000.0)), (kz, dict(FETCH_SIZE=1.0))])
+    _counters(t + "/write", [(rocprof.COPY_KERNEL, dict(WRITE_SIZE=1048576)),
+                             (kf, dict(WRITE_SIZE=64.0, TCC_EA0_ATOMIC_sum=1024.0, _dispatches=2)),
+                             (kz, dict(WRITE_SIZE=8.0, TCC_EA0_ATOMIC_sum=0.0))])
+    for p in ("sq1", "sq2"):
+        _counters(t + "/" + p, [(kf, dict(GRBM_GUI_ACTIVE=8 * 8.0e8))])
+    args = [rocprof.counters(t + "/" + p) for p in ("fetch", "write", "sq1", "sq2")]
+    s = rocprof.summarise(rocprof.durations(t + "/trace"), *args, rocprof.agent(t + "/trace"))
+    r = s["kernels"]["bwd_fused_kernel<true, 128, true>"]
+    assert r["atomic_requests"] == pytest.approx(1024.0)  # two dispatches of 1024: per launch
+    assert s["kernels"]["fill_zero_f32"]["atomic_requests"] == 0.0
+    assert "atomic requests" in rocprof.markdown(s, "64k_bwd_fused10", "cmd")
+    dest = str(tmp_path / "profiles")
+    rocprof.write_profiles(dest, "8k", "cmd", t + "/trace", *args, rocprof.agent(t + "/trace"), s,
+                           bwd="fused10")
+    txt = open(os.path.join(dest, "bdattn_8k_bwd_fused10_hbm_traffic.md")).read()
+    assert "TCC_EA0_ATOMIC_sum" in txt and "BDATTN_BWD=fused10" in txt
+    assert "kernel: bwd_dkdv" in txt and "workload: 8k_bwd_fused10" in txt
 
 
 def test_summary_arithmetic(tmp_path):
