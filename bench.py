@@ -196,8 +196,8 @@ def lce_cpu_baseline(spec, t, seconds: float):
 
     f64 = lambda x: x.float().cpu().numpy().astype(np.float64)
     w = f64(t["w"])
-    n, spent, flops = 8, 0.0, 0.0
-    while spent < seconds and n <= spec.N:
+
+    def run(n):
         h = f64(t["h"][:n])
         tg = t["targets"][:n].cpu().numpy()
         g = t["dloss"][:n].cpu().numpy().astype(np.float64)
@@ -205,12 +205,21 @@ def lce_cpu_baseline(spec, t, seconds: float):
         o = LinearCE(h, w, tg)
         _, lse = o.forward()
         o.backward(g, lse)
-        spent = time.perf_counter() - t0
-        flops = 6.0 * n * spec.V * spec.D
-        if spent < seconds / 4:
-            n *= 2
-        else:
+        return time.perf_counter() - t0
+
+    # grow the sample until it takes a tenth of the budget, then size the
+    # timed sample to the whole budget from that rate
+    n = 8
+    spent = run(n)
+    while spent < seconds / 10 and n < spec.N:
+        n = min(spec.N, 2 * n)
+        spent = run(n)
+    for _ in range(3):  # (the work has a fixed part: the dW product over the vocabulary)
+        if spent >= seconds / 2 or n >= spec.N:
             break
+        n = min(spec.N, max(n + 1, int(n * seconds / max(spent, 1e-3))))
+        spent = run(n)
+    flops = 6.0 * n * spec.V * spec.D
     threads = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
