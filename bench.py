@@ -362,6 +362,10 @@ def main():
     ap.add_argument("--workload", default="256k",
                     help="workload name (tiny, 8k, 64k, 256k, 512k_rank15; lce_8k, lce_256k "
                          "for the token-chunked linear cross-entropy)")
+    ap.add_argument("--precision", choices=("default", "f32-out", "split"), default="default",
+                    help="bf16 workloads: float32 outputs (f32-out), or float32 outputs with P "
+                         "and dS as two bf16 terms in their products (split); the useful-flop "
+                         "count stays 12d per pair and q head")
     ap.add_argument("--clean-mask", choices=("block", "token"), default="block",
                     help="what a clean query sees of its own block: all of it (block-causal, "
                          "the workloads' definition) or the keys up to its own position")
@@ -422,7 +426,11 @@ def main():
             c * C for r in range(P) for c in (r, 2 * P - 1 - r)))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    p = bd.from_spec(spec)
+    prec = {"default": bd.PRECISION_DEFAULT, "f32-out": bd.PRECISION_F32_OUT,
+            "split": bd.PRECISION_SPLIT}[args.precision]
+    if prec and (spec.dtype != "bf16" or args.split_forward):
+        sys.exit("--precision other than default: bf16 workloads, fused forward only")
+    p = bd.from_spec(spec, precision=prec)
     pairs = bd.visible_pairs(p)
     useful_step = 12.0 * spec.d * spec.H * pairs
     log(f"[bench] workload {spec.name}: {spec.description}; visible pairs/head {pairs}; "
@@ -433,8 +441,11 @@ def main():
     H, Hkv, d = spec.H, spec.Hkv, spec.d
     nc, nkv, nx = spec.n_clean_q, spec.n_clean_kv, spec.n_corr
     e = lambda *s, dtype=dt: torch.empty(s, dtype=dtype, device=dev)
-    fout = [e(nc, H, d), e(nx, H, d), e(H, nc, dtype=torch.float32), e(H, nx, dtype=torch.float32)]
-    bout = [e(nc, H, d), e(nx, H, d), e(nkv, Hkv, d), e(nkv, Hkv, d), e(nx, Hkv, d), e(nx, Hkv, d)]
+    ot = torch.float32 if prec else dt  # O, dQ, dK, dV
+    fout = [e(nc, H, d, dtype=ot), e(nx, H, d, dtype=ot), e(H, nc, dtype=torch.float32),
+            e(H, nx, dtype=torch.float32)]
+    bout = [e(nc, H, d, dtype=ot), e(nx, H, d, dtype=ot), e(nkv, Hkv, d, dtype=ot),
+            e(nkv, Hkv, d, dtype=ot), e(nx, Hkv, d, dtype=ot), e(nx, Hkv, d, dtype=ot)]
     ws_f = e(bd.workspace_size(p, 0), dtype=torch.uint8)
     ws_b = e(bd.workspace_size(p, 1), dtype=torch.uint8)
 
@@ -475,6 +486,8 @@ def main():
     # and the MFMA flops it executes (recomputed QK^T and dP included)
     useful_d = {"fwd": 4, "bwd_dq": 2, "bwd_dkdv": 6}
     executed_d = {"fwd": 4, "bwd_dq": 6, "bwd_dkdv": 8}
+    if prec == bd.PRECISION_SPLIT:  # the products with a split operand run twice
+        executed_d = {"fwd": 6, "bwd_dq": 8, "bwd_dkdv": 12}
     kern = {}
     for k, r in prof.items():
         ms = r["ms"] / max(1, r["launches"])
@@ -486,8 +499,8 @@ def main():
     from block_masked_attention_amd.rocprof import profile_key
     traffic, clock = read_profile(profile_key(spec.name, args.docs)
                                   + ("_token_causal" if spec.clean_mask else ""), dom)
-    if args.gathered:  # the committed profiles are of the position-ordered buffer
-        traffic, clock = None, None
+    if args.gathered or prec:  # the committed profiles are of the default kernels over
+        traffic, clock = None, None  # the position-ordered buffer
     log(f"[bench] {ms_step:.2f} ms/step, {value:.1f} useful TFLOP/s "
         f"({100 * value / peak:.1f}% of {peak} peak); " +
         ", ".join(f"{k} {v['ms']:.2f} ms ({v['useful_tflops']} useful, {v['executed_tflops']} "
@@ -521,6 +534,7 @@ def main():
         "config": {"workload": spec.name, "description": spec.description,
                    "clean_q": nc, "clean_kv": nkv, "corrupted": nx, "B": spec.B, "H": H,
                    "Hkv": Hkv, "d": d, "clean_mask": mask_name, "documents": args.docs,
+                   "precision": args.precision,
                    "clean_kv_order": (f"zigzag all-gather of {args.gathered} ranks"
                                       if args.gathered else "positions"),
                    "visible_pairs_per_head": pairs,

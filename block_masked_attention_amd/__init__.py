@@ -25,6 +25,10 @@ F32 = 0
 BF16 = 1
 CLEAN_BLOCK_CAUSAL = 0
 CLEAN_TOKEN_CAUSAL = 1
+# bdattn_precision (include/bdattn.h)
+PRECISION_DEFAULT = 0
+PRECISION_F32_OUT = 1
+PRECISION_SPLIT = 2
 STATUS = {0: "BDATTN_OK", -1: "BDATTN_ERR_INVALID_ARG", -2: "BDATTN_ERR_SHAPE",
           -3: "BDATTN_ERR_UNSUPPORTED", -4: "BDATTN_ERR_COVERAGE",
           -5: "BDATTN_ERR_WORKSPACE", -6: "BDATTN_ERR_HIP"}
@@ -60,6 +64,7 @@ class Problem(ctypes.Structure):
         ("doc_starts", ctypes.POINTER(ctypes.c_int32)),
         ("kv_chunk_len", ctypes.c_int32),
         ("kv_chunk_pos", ctypes.POINTER(ctypes.c_int32)),
+        ("precision", ctypes.c_int32),
     ]
 
     @property
@@ -73,7 +78,7 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
             scale: float = 0.0, clean_mask: int = CLEAN_BLOCK_CAUSAL, partial: bool = False,
             omit_corr_keys: bool = False,
             doc_starts: Optional[Sequence[int]] = None, kv_chunk_len: int = 0,
-            kv_chunk_pos: Optional[Sequence[int]] = None) -> Problem:
+            kv_chunk_pos: Optional[Sequence[int]] = None, precision: int = 0) -> Problem:
     """Problem descriptor. ``dtype`` is F32/BF16, "f32"/"bf16" or a torch dtype.
     Without ids the corrupted blocks are 0..n_corr_blocks-1 (default: as many
     as the clean query shard has blocks). ``clean_mask`` is CLEAN_BLOCK_CAUSAL
@@ -84,7 +89,11 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
     (the first 0, increasing, multiples of B); attention stays inside each.
     ``kv_chunk_len`` / ``kv_chunk_pos``: a gathered clean K/V buffer, chunks of
     ``kv_chunk_len`` keys whose global start positions are ``kv_chunk_pos``
-    (any order, together covering the buffer's position range)."""
+    (any order, together covering the buffer's position range).
+    ``precision`` (bf16 inputs): PRECISION_DEFAULT, PRECISION_F32_OUT (O, dQ,
+    dK, dV in float32; the backward then reads the float32 O) or
+    PRECISION_SPLIT (float32 outputs, and P and dS enter their products as two
+    bf16 terms); see include/bdattn.h."""
     dt = _dtype_code(dtype)
     if n_clean_kv is None:
         n_clean_kv = n_clean_q
@@ -112,6 +121,7 @@ def problem(B: int, H: int, Hkv: int, d: int, dtype, n_clean_q: int, clean_q_sta
         p.doc_starts = docs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     else:
         p.n_docs, p.doc_starts = 0, None
+    p.precision = int(precision)
     p.kv_chunk_len = int(kv_chunk_len)
     if kv_chunk_pos is not None and len(kv_chunk_pos) > 0:
         cpos = np.ascontiguousarray(np.asarray(kv_chunk_pos, dtype=np.int32))
@@ -138,7 +148,7 @@ def lce_problem(n_tokens: int, hidden: int, vocab: int, chunk: int = 4096,
     return p
 
 
-def from_spec(spec) -> Problem:
+def from_spec(spec, precision: int = 0) -> Problem:
     """Descriptor of a workload spec (any object with the descriptor's fields)."""
     return problem(spec.B, spec.H, spec.Hkv, spec.d, spec.dtype, spec.n_clean_q,
                    spec.clean_q_start, spec.n_clean_kv, spec.clean_kv_start,
@@ -148,7 +158,7 @@ def from_spec(spec) -> Problem:
                    omit_corr_keys=getattr(spec, "omit_corr_keys", False),
                    doc_starts=getattr(spec, "doc_starts", None),
                    kv_chunk_len=getattr(spec, "kv_chunk_len", 0),
-                   kv_chunk_pos=getattr(spec, "kv_chunk_pos", None))
+                   kv_chunk_pos=getattr(spec, "kv_chunk_pos", None), precision=precision)
 
 
 def _dtype_code(dtype) -> int:
@@ -317,6 +327,12 @@ def _tdtype(p: Problem):
     return torch.float32 if p.dtype == F32 else torch.bfloat16
 
 
+def _odtype(p: Problem):
+    """Element type of O, dQ, dK and dV."""
+    torch = _torch()
+    return torch.float32 if p.dtype == F32 or p.precision else torch.bfloat16
+
+
 def _expect(t, shape, dtype, name, device):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -374,14 +390,19 @@ def fwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, *, workspace=None, stream=None
                        (v_c, (nkv, Hkv, d), "v_c"), (q_x, (nx, H, d), "q_x"),
                        (k_x, (nx, Hkv, d), "k_x"), (v_x, (nx, Hkv, d), "v_x")):
         _expect(t, shp, dt, nm, dev)
+    odt = _odtype(p)
     with _on(stream):
         if out is None:
-            o_c = torch.empty((nc, H, d), dtype=dt, device=dev)
-            o_x = torch.empty((nx, H, d), dtype=dt, device=dev)
+            o_c = torch.empty((nc, H, d), dtype=odt, device=dev)
+            o_x = torch.empty((nx, H, d), dtype=odt, device=dev)
             lse_c = torch.empty((H, nc), dtype=torch.float32, device=dev)
             lse_x = torch.empty((H, nx), dtype=torch.float32, device=dev)
         else:
             o_c, o_x, lse_c, lse_x = out
+            for t, shp, tdt, nm in ((o_c, (nc, H, d), odt, "o_c"), (o_x, (nx, H, d), odt, "o_x"),
+                                    (lse_c, (H, nc), torch.float32, "lse_c"),
+                                    (lse_x, (H, nx), torch.float32, "lse_x")):
+                _expect(t, shp, tdt, nm, dev)
         ws = _workspace(p, 0, dev, workspace)
     st = lib().bdattn_fwd(ctypes.byref(p), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(q_x),
                           _ptr(k_x), _ptr(v_x), _ptr(o_c), _ptr(o_x), _ptr(lse_c), _ptr(lse_x),
@@ -397,29 +418,32 @@ def bwd(p: Problem, q_c, k_c, v_c, q_x, k_x, v_x, o_c, o_x, lse_c, lse_x, do_c, 
     dev = q_c.device if q_c.numel() else q_x.device
     if dev.type != "cuda":
         raise ValueError("bdattn runs on a GPU: inputs must be on a cuda (HIP) device")
-    dt = _tdtype(p)
+    dt, odt = _tdtype(p), _odtype(p)
     H, Hkv, d = int(p.H), int(p.Hkv), int(p.d)
     nc, nkv, nx = int(p.n_clean_q), int(p.n_clean_kv), p.n_corr
     for t, shp, tdt, nm in ((q_c, (nc, H, d), dt, "q_c"), (k_c, (nkv, Hkv, d), dt, "k_c"),
                             (v_c, (nkv, Hkv, d), dt, "v_c"), (q_x, (nx, H, d), dt, "q_x"),
                             (k_x, (nx, Hkv, d), dt, "k_x"), (v_x, (nx, Hkv, d), dt, "v_x"),
-                            (o_c, (nc, H, d), dt, "o_c"), (o_x, (nx, H, d), dt, "o_x"),
+                            (o_c, (nc, H, d), odt, "o_c"), (o_x, (nx, H, d), odt, "o_x"),
                             (lse_c, (H, nc), torch.float32, "lse_c"),
                             (lse_x, (H, nx), torch.float32, "lse_x"),
                             (do_c, (nc, H, d), dt, "do_c"), (do_x, (nx, H, d), dt, "do_x")):
         _expect(t, shp, tdt, nm, dev)
     with _on(stream):
         if out is None:
-            dq_c = torch.empty((nc, H, d), dtype=dt, device=dev)
-            dq_x = torch.empty((nx, H, d), dtype=dt, device=dev)
-            dk_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
-            dv_c = torch.empty((nkv, Hkv, d), dtype=dt, device=dev)
+            dq_c = torch.empty((nc, H, d), dtype=odt, device=dev)
+            dq_x = torch.empty((nx, H, d), dtype=odt, device=dev)
+            dk_c = torch.empty((nkv, Hkv, d), dtype=odt, device=dev)
+            dv_c = torch.empty((nkv, Hkv, d), dtype=odt, device=dev)
             # not written when the corrupted keys are omitted: returned as zeros
             alloc = torch.zeros if p.omit_corr_keys else torch.empty
-            dk_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
-            dv_x = alloc((nx, Hkv, d), dtype=dt, device=dev)
+            dk_x = alloc((nx, Hkv, d), dtype=odt, device=dev)
+            dv_x = alloc((nx, Hkv, d), dtype=odt, device=dev)
         else:
             dq_c, dq_x, dk_c, dv_c, dk_x, dv_x = out
+            for t, shp, nm in ((dq_c, (nc, H, d), "dq_c"), (dq_x, (nx, H, d), "dq_x"),
+                               (dk_c, (nkv, Hkv, d), "dk_c"), (dv_c, (nkv, Hkv, d), "dv_c")):
+                _expect(t, shp, odt, nm, dev)
         ws = _workspace(p, 1, dev, workspace)
     st = lib().bdattn_bwd(ctypes.byref(p), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(q_x),
                           _ptr(k_x), _ptr(v_x), _ptr(o_c), _ptr(o_x), _ptr(lse_c), _ptr(lse_x),

@@ -558,6 +558,7 @@ int fwd_impl(const bdattn_problem* p, const void* q_c, const void* k_c, const vo
   a.token_causal = P.token_causal;
   a.clean_kv_start = P.clean_kv_start;
   a.corr_keys = P.corr_keys;
+  a.precision = P.precision;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[1];
   hipError_t e = bdattn::launch_fwd(a, P.dtype, P.d, s, noalloc ? nullptr : prof_events(0, 1, ev));
@@ -636,6 +637,7 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.token_causal = P.token_causal;
   a.clean_kv_start = P.clean_kv_start;
   a.corr_keys = P.corr_keys;
+  a.precision = P.precision;
   a.scale = P.scale;
   a.scale_log2 = float(double(P.scale) * 1.4426950408889634);
   bdattn::KernelEvents ev[2];
@@ -649,7 +651,9 @@ int bdattn_merge(int64_t n_rows, int32_t H, int32_t d, int32_t dtype, const void
                  void* hip_stream) {
   if (dtype != BDATTN_F32 && dtype != BDATTN_BF16) return fail(BDATTN_ERR_INVALID_ARG, "unknown dtype");
   if (n_rows < 0 || H < 1) return fail(BDATTN_ERR_SHAPE, "n_rows must be >= 0 and H >= 1");
-  if (!bdattn::have_kernels(dtype, d))
+  // float32 results of bf16 problems (BDATTN_PRECISION_F32_OUT / SPLIT) merge
+  // as float32 at their head dim
+  if (!bdattn::have_kernels(dtype, d) && !(dtype == BDATTN_F32 && bdattn::have_kernels(BDATTN_BF16, d)))
     return fail(BDATTN_ERR_UNSUPPORTED, "no merge kernel for this head dim and dtype");
   if (n_rows > (int64_t(1) << 40) / (int64_t(H) * d))
     return fail(BDATTN_ERR_SHAPE, "merge problem too large");

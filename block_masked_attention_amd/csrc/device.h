@@ -360,6 +360,30 @@ struct TileCopy {
   }
 };
 
+// Eight floats as two bf16 fragments, x ~ hi + lo: hi = x rounded to bf16,
+// lo = the remainder x - hi rounded to bf16 (together about 16 bits of x).
+__device__ __forceinline__ void split_pack(const float* x, Elem<true>::Frag& hi,
+                                           Elem<true>::Frag& lo) {
+  hi = Elem<true>::pack(x);
+  const uint32_t h[4] = {hi.v.x, hi.v.y, hi.v.z, hi.v.w};
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[2 * j] = x[2 * j] - __uint_as_float(h[j] << 16);
+    r[2 * j + 1] = x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u);
+  }
+  lo = Elem<true>::pack(r);
+}
+
+// Four consecutive output values at element offset `off` of `out`: in the
+// element type of E, or as float32 when OF32 (float32 outputs for bf16
+// inputs; 16-byte aligned since off is a multiple of 4).
+template <class E, bool OF32>
+__device__ __forceinline__ void store_out(void* out, int64_t off, float a, float b, float c, float d) {
+  if constexpr (OF32) *(float4*)((float*)out + off) = make_float4(a, b, c, d);
+  else E::store4((typename E::T*)out + off, a, b, c, d);
+}
+
 // Operand reads kept in flight ahead of the matrix product that consumes them.
 constexpr int kReadAhead = 3;
 

@@ -87,9 +87,11 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
 // Forward. Per key tile: S^T = K Q^T (keys x queries, so each lane owns one
 // query row); mask only on tiles that need it; online softmax; O^T += V^T P^T.
 // ======================================================================
-template <bool BF16, int D, bool DOCS, bool MAPPED>
+template <bool BF16, int D, bool DOCS, bool MAPPED, int PREC>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
+  // bdattn_precision: float32 O (>= 1); P as two bf16 terms in P V (2)
+  constexpr bool OF32 = PREC >= 1, SPLIT = BF16 && PREC == 2;
   using E = Elem<BF16>;
   using T = typename E::T;
   using Frag = typename E::Frag;
@@ -202,7 +204,7 @@ void fwd_kernel(FwdArgs a) {
     // the row sum adds the fp32 weights: LSE must be exact, since the
     // backward rebuilds P from it (summing the bf16-rounded weights instead
     // shifts LSE by up to 2^-9 and scales every recomputed P of the row)
-    Frag pf[TK / 32][2];
+    Frag pf[TK / 32][2], pl[TK / 32][2];  // P (and its remainder when SPLIT)
     float rs = 0.f;
     // weights of the 16-key slice mt (8 per lane), elements [i0, i1); packed
     // to bf16 once complete
@@ -214,7 +216,10 @@ void fwd_kernel(FwdArgs a) {
         pv[i] = fast_exp2(fmaf(s[mb][8 * h + i], a.scale_log2, -m_use));
         rs += pv[i];
       }
-      if (i1 == 8) pf[mb][h] = E::pack(pv);
+      if (i1 == 8) {
+        if constexpr (SPLIT) split_pack(pv, pf[mb][h], pl[mb][h]);
+        else pf[mb][h] = E::pack(pv);
+      }
     };
     // O += V^T P over the tile's keys: product k = (16-key slice mt, column
     // block db). Slice 0's weights come first; slice mt + 1's are computed
@@ -228,6 +233,7 @@ void fwd_kernel(FwdArgs a) {
         [&](int k, const Frag& y) __attribute__((always_inline)) {
           const int mt = k / PS;
           E::mma(o[k % PS], y, pf[mt / 2][mt % 2]);
+          if constexpr (SPLIT) E::mma(o[k % PS], y, pl[mt / 2][mt % 2]);
         },
         [&](int k) __attribute__((always_inline)) {
           const int mt = k / PS, db = k % PS;
@@ -258,13 +264,14 @@ void fwd_kernel(FwdArgs a) {
   if (q.row_ok) {
     // a row that sees no key present (partial problems): O = 0, LSE = -inf
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    T* orow = (T*)(q.stream ? a.o_x : a.o_c) + ((int64_t)q.my_row * a.H + q.head) * D;
+    const int64_t orow = ((int64_t)q.my_row * a.H + q.head) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        E::store4(orow + 32 * db + 8 * g + 4 * hf, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
-                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        store_out<E, OF32>(q.stream ? a.o_x : a.o_c, orow + 32 * db + 8 * g + 4 * hf,
+                           o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                           o[db][4 * g + 3] * inv);
     }
     if (hf == 0) {
       float* lse = q.stream ? a.lse_x : a.lse_c;
@@ -279,7 +286,7 @@ void fwd_kernel(FwdArgs a) {
 // (query tiles past the end of a stream then contribute nothing). D is stored
 // negated so that the dK/dV kernel can start its dP accumulation from it.
 // ======================================================================
-template <bool BF16, int D>
+template <bool BF16, int D, bool OF32>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const void* do_,
                                                        const float* lse, float* Dout, float* L2out,
                                                        int32_t n_rows, int32_t n_pad, int32_t H) {
@@ -294,12 +301,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* o_, const voi
   const bool real = pair < npairs && row < n_rows;
   float acc = 0.f;
   if (real) {
-    typename E::Frag fo = E::load((const T*)o_ + pair * D + 8 * sub);
     typename E::Frag fg = E::load((const T*)do_ + pair * D + 8 * sub);
-    const T* po = (const T*)&fo;
     const T* pg = (const T*)&fg;
+    if constexpr (OF32 && BF16) {  // float32 O
+      const float4* po = (const float4*)((const float*)o_ + pair * D + 8 * sub);
+      const float4 x = po[0], y = po[1];
+      const float ov[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += E::to_f(po[e]) * E::to_f(pg[e]);
+      for (int e = 0; e < 8; ++e) acc += ov[e] * E::to_f(pg[e]);
+    } else {
+      typename E::Frag fo = E::load((const T*)o_ + pair * D + 8 * sub);
+      const T* po = (const T*)&fo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += E::to_f(po[e]) * E::to_f(pg[e]);
+    }
   }
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
@@ -360,9 +375,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* oa_, const float
 // D are scalars); P^T = exp2(S^T c - LSE2); dS^T = P^T (dP^T - D);
 // dQ^T += K^T dS^T with K^T read transposed from the K tile.
 // ======================================================================
-template <bool BF16, int D, bool DOCS, bool MAPPED>
+template <bool BF16, int D, bool DOCS, bool MAPPED, int PREC>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
+  // bdattn_precision: float32 dQ (>= 1); dS as two bf16 terms in dS K (2)
+  constexpr bool OF32 = PREC >= 1, SPLIT = BF16 && PREC == 2;
   using E = Elem<BF16>;
   using T = typename E::T;
   using Frag = typename E::Frag;
@@ -434,7 +451,7 @@ void bwd_dq_kernel(BwdArgs a) {
     if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
     const bool cl = j < q.n_ct;
     const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
-    Frag sf[TK / 32][2];
+    Frag sf[TK / 32][2], sl[TK / 32][2];  // dS (and its remainder when SPLIT)
 #pragma unroll
     for (int mb = 0; mb < TK / 32; ++mb) {
       // S and dP of key block mb, alternating: even k S (K rows), odd k dP (V rows)
@@ -463,8 +480,13 @@ void bwd_dq_kernel(BwdArgs a) {
         }
         ds[i] = p * (dp[i] + ndrow);
       }
-      sf[mb][0] = E::pack(ds);
-      sf[mb][1] = E::pack(ds + 8);
+      if constexpr (SPLIT) {
+        split_pack(ds, sf[mb][0], sl[mb][0]);
+        split_pack(ds + 8, sf[mb][1], sl[mb][1]);
+      } else {
+        sf[mb][0] = E::pack(ds);
+        sf[mb][1] = E::pack(ds + 8);
+      }
     }
     // dQ += K^T dS over the tile's keys: product k = (16-key slice mt, column block db)
     product_chain<TK / 32 * 2 * (D / 32), kReadAhead, Frag>(
@@ -472,6 +494,7 @@ void bwd_dq_kernel(BwdArgs a) {
         [&](int k, const Frag& y) __attribute__((always_inline)) {
           const int mt = k / (D / 32);
           E::mma(dq[k % (D / 32)], y, sf[mt / 2][mt % 2]);
+          if constexpr (SPLIT) E::mma(dq[k % (D / 32)], y, sl[mt / 2][mt % 2]);
         });
     lds_dma_wait();
     __syncthreads();
@@ -494,35 +517,46 @@ void bwd_dq_kernel(BwdArgs a) {
   sweep(std::true_type{}, q.jf1, n_tiles);
 
   if (q.row_ok) {
-    T* out = (T*)(q.stream ? a.dq_x : a.dq_c) + ((int64_t)q.my_row * a.H + q.head) * D;
+    const int64_t orow = ((int64_t)q.my_row * a.H + q.head) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        E::store4(out + 32 * db + 8 * g + 4 * hf, dq[db][4 * g] * a.scale,
-                  dq[db][4 * g + 1] * a.scale, dq[db][4 * g + 2] * a.scale,
-                  dq[db][4 * g + 3] * a.scale);
+        store_out<E, OF32>(q.stream ? a.dq_x : a.dq_c, orow + 32 * db + 8 * g + 4 * hf,
+                           dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
+                           dq[db][4 * g + 2] * a.scale, dq[db][4 * g + 3] * a.scale);
     }
   }
 }
 
-template <bool BF16, int D>
-hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
+template <bool BF16, int D, int PREC>
+hipError_t run_fwd_t(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
   const dim3 grid(a.n_items), block(FWD_WAVES * 64);
   if (a.n_items > 0 && a.kv_map) {  // a gathered clean buffer
-    if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, true>), grid, block, 0, s, a);
+    if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);
   } else if (a.n_items > 0) {
-    if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, false>), grid, block, 0, s, a);
+    if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, false, PREC>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, false, PREC>), grid, block, 0, s, a);
   }
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   return hipGetLastError();
 }
 
+// the precisions other than the default are separate instantiations for bf16
+// inputs only (float32 inputs have float32 outputs and operands already)
 template <bool BF16, int D>
-hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
+hipError_t run_fwd(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
+  if constexpr (BF16) {
+    if (a.precision == BDATTN_PRECISION_SPLIT) return run_fwd_t<BF16, D, 2>(a, s, ev);
+    if (a.precision == BDATTN_PRECISION_F32_OUT) return run_fwd_t<BF16, D, 1>(a, s, ev);
+  }
+  return run_fwd_t<BF16, D, 0>(a, s, ev);
+}
+
+template <bool BF16, int D, int PREC>
+hipError_t run_bwd_t(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   constexpr int LPR = D / 8;
   for (int st = 0; st < 2; ++st) {
     const int32_t n = st ? a.n_corr : a.n_clean_q;
@@ -530,7 +564,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
     const int32_t n_pad = row_pad(n);
     const int64_t threads = (int64_t)n_pad * a.H * LPR;
     const int blocks = int((threads + 255) / 256);
-    hipLaunchKernelGGL((bwd_prep_kernel<BF16, D>), dim3(blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwd_prep_kernel<BF16, D, (PREC >= 1)>), dim3(blocks), dim3(256), 0, s,
                        st ? a.o_x : a.o_c, st ? a.do_x : a.do_c, st ? a.lse_x : a.lse_c,
                        st ? a.d_x : a.d_c, st ? a.l2_x : a.l2_c, n, n_pad, a.H);
   }
@@ -547,11 +581,11 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
   const dim3 grid(a.n_q_items), block(FWD_WAVES * 64);
   if (a.n_q_items > 0 && a.kv_map) {  // a gathered clean buffer
-    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, true>), grid, block, 0, s, a);
+    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);
   } else if (a.n_q_items > 0) {
-    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false>), grid, block, 0, s, a);
+    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false, PREC>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false, PREC>), grid, block, 0, s, a);
   }
   if (ev) (void)hipEventRecord(ev[0].stop, s);
   if (ev) (void)hipEventRecord(ev[1].start, s);
@@ -559,6 +593,15 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (e == hipSuccess) e = launch_dkdv(a, dtype, D, s);
   if (ev) (void)hipEventRecord(ev[1].stop, s);
   return e;
+}
+
+template <bool BF16, int D>
+hipError_t run_bwd(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
+  if constexpr (BF16) {
+    if (a.precision == BDATTN_PRECISION_SPLIT) return run_bwd_t<BF16, D, 2>(a, s, ev);
+    if (a.precision == BDATTN_PRECISION_F32_OUT) return run_bwd_t<BF16, D, 1>(a, s, ev);
+  }
+  return run_bwd_t<BF16, D, 0>(a, s, ev);
 }
 
 }  // namespace
@@ -592,6 +635,7 @@ hipError_t launch_merge(int64_t n_rows, int H, int d, int dtype, const void* o_a
   if (dtype == BDATTN_BF16 && d == 128) return run_merge<true, 128>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
   if (dtype == BDATTN_BF16 && d == 32) return run_merge<true, 32>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
   if (dtype == BDATTN_F32 && d == 32) return run_merge<false, 32>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
+  if (dtype == BDATTN_F32 && d == 128) return run_merge<false, 128>(n_rows, H, o_a, lse_a, o_b, lse_b, o, lse, s);
   return hipErrorInvalidValue;
 }
 

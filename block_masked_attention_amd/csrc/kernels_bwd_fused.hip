@@ -370,6 +370,7 @@ __global__ void store_dq(const float* acc, uint16_t* dq_c, uint16_t* dq_x, int64
 }  // namespace
 
 hipError_t launch_dkdv_fused(const BwdArgs& a, int dtype, int d, hipStream_t s) {
+  if (a.precision) return hipErrorInvalidValue;  // the default precision only
   if (a.n_kv_items <= 0) return hipSuccess;
   const dim3 grid(a.n_kv_items), block(256);
   if (dtype == BDATTN_BF16 && d == 128) hipLaunchKernelGGL((bwd_fused_kernel<true, 128, false>), grid, block, 0, s, a, nullptr);
@@ -380,7 +381,7 @@ hipError_t launch_dkdv_fused(const BwdArgs& a, int dtype, int d, hipStream_t s) 
 }
 
 bool bwd_fused_supported(const BwdArgs& a, int dtype, int d) {
-  return dtype == BDATTN_BF16 && d == 128 && a.kv_map == nullptr;
+  return dtype == BDATTN_BF16 && d == 128 && a.kv_map == nullptr && !a.precision;
 }
 
 hipError_t launch_bwd_fused(const BwdArgs& a, int dtype, int d, hipStream_t s) {

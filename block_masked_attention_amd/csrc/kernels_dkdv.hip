@@ -30,9 +30,11 @@ using namespace dev;
 // current one is in use. Tiles whose rows all see every key of the workgroup
 // come first and skip the mask.
 // ======================================================================
-template <bool BF16, int D>
+template <bool BF16, int D, int PREC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a) {
+  // bdattn_precision: float32 dK, dV (>= 1); P and dS as two bf16 terms (2)
+  constexpr bool OF32 = PREC >= 1, SPLIT = BF16 && PREC == 2;
   using E = Elem<BF16>;
   using T = typename E::T;
   using Frag = typename E::Frag;
@@ -206,7 +208,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // acc += X^T Y over the TQ rows of tile TILE, X given as packed result-order
   // fragments [block][half], Y the rows read transposed: product k = (16-row
   // slice mt, column block db)
-  auto accumulate = [&](auto tile_tag, const Frag (*x)[2]) __attribute__((always_inline)) {
+  // (SPLIT: xl holds the remainders of x, a second product per fragment)
+  auto accumulate = [&](auto tile_tag, const Frag (*x)[2], const Frag (*xl)[2]) __attribute__((always_inline)) {
     constexpr uint32_t TILE = decltype(tile_tag)::value;
     product_chain<NMB * 2 * (D / 32), kReadAhead, Frag>(
         [&](int k) __attribute__((always_inline)) {
@@ -215,6 +218,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         [&](int k, const Frag& y) __attribute__((always_inline)) {
           const int mt = k / (D / 32);
           E::mma(acc[k % (D / 32)], x[mt / 2][mt % 2], y);
+          if constexpr (SPLIT) E::mma(acc[k % (D / 32)], xl[mt / 2][mt % 2], y);
         });
   };
 
@@ -240,7 +244,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __builtin_amdgcn_s_setprio(2);
     scores(QT{}, sb);
     __builtin_amdgcn_s_setprio(0);
-    Frag pa[NMB][2];
+    Frag pa[NMB][2], pl[NMB][2];  // P (and its remainder when SPLIT)
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       const f32x16& s = sb[mb];
@@ -258,11 +262,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
         p_hand[kg][mb][g][lane] = make_float4(p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]);
       }
-      pa[mb][0] = E::pack(p);
-      pa[mb][1] = E::pack(p + 8);
+      if constexpr (SPLIT) {
+        split_pack(p, pa[mb][0], pl[mb][0]);
+        split_pack(p + 8, pa[mb][1], pl[mb][1]);
+      } else {
+        pa[mb][0] = E::pack(p);
+        pa[mb][1] = E::pack(p + 8);
+      }
     }
     __syncthreads();  // P handed over
-    accumulate(GT{}, pa);
+    accumulate(GT{}, pa, pl);
     pos = nxt;
     lds_dma_wait();
     __syncthreads();
@@ -292,7 +301,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();  // P handed over
     // dS ahead of the P wave's dV products, so that the dK products start early
     __builtin_amdgcn_s_setprio(2);
-    Frag sa[NMB][2];
+    Frag sa[NMB][2], sl[NMB][2];  // dS (and its remainder when SPLIT)
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
       float ds[16];
@@ -304,11 +313,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
         ds[4 * g + 2] = p4.z * dp[mb][4 * g + 2];
         ds[4 * g + 3] = p4.w * dp[mb][4 * g + 3];
       }
-      sa[mb][0] = E::pack(ds);
-      sa[mb][1] = E::pack(ds + 8);
+      if constexpr (SPLIT) {
+        split_pack(ds, sa[mb][0], sl[mb][0]);
+        split_pack(ds + 8, sa[mb][1], sl[mb][1]);
+      } else {
+        sa[mb][0] = E::pack(ds);
+        sa[mb][1] = E::pack(ds + 8);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
-    accumulate(QT{}, sa);
+    accumulate(QT{}, sa, sl);
     pos = nxt;
     lds_dma_wait();
     __syncthreads();
@@ -339,14 +353,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // write dV (P wave) or dK times the scale (dS wave) for this pair's 32 keys
-  T* out = (T*)(p_role ? (kstream ? a.dv_x : a.dv_c) : (kstream ? a.dk_x : a.dk_c));
+  void* out = p_role ? (kstream ? a.dv_x : a.dv_c) : (kstream ? a.dk_x : a.dk_c);
   const float osc = p_role ? 1.f : a.scale;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key0 + 32 * kg + 8 * (i >> 2) + 4 * hf + (i & 3);
-      if (key < n_keys) out[((int64_t)(key + kv_off) * a.Hkv + kvh) * D + 32 * db + lk] = E::from_f(acc[db][i] * osc);
+      const int64_t o = ((int64_t)(key + kv_off) * a.Hkv + kvh) * D + 32 * db + lk;
+      if (key < n_keys) {
+        if constexpr (OF32) ((float*)out)[o] = acc[db][i] * osc;
+        else ((T*)out)[o] = E::from_f(acc[db][i] * osc);
+      }
     }
   }
 }
@@ -356,10 +374,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t s) {
   if (a.n_kv_items <= 0) return hipSuccess;
   const dim3 grid(a.n_kv_items), block(512);
-  if (const char* e = getenv("BDATTN_DKDV"); e && !strcmp(e, "fused")) return launch_dkdv_fused(a, dtype, d, s);
-  if (dtype == BDATTN_BF16 && d == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128>), grid, block, 0, s, a);
-  else if (dtype == BDATTN_BF16 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32>), grid, block, 0, s, a);
-  else if (dtype == BDATTN_F32 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<false, 32>), grid, block, 0, s, a);
+  if (const char* e = getenv("BDATTN_DKDV"); e && !strcmp(e, "fused") && !a.precision)
+    return launch_dkdv_fused(a, dtype, d, s);
+  const int pr = dtype == BDATTN_BF16 ? a.precision : 0;  // bdattn_precision (bf16 inputs)
+  if (dtype == BDATTN_BF16 && d == 128 && pr == 2) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128, 2>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_BF16 && d == 128 && pr == 1) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128, 1>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_BF16 && d == 128) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128, 0>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_BF16 && d == 32 && pr == 2) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32, 2>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_BF16 && d == 32 && pr == 1) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32, 1>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_BF16 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 32, 0>), grid, block, 0, s, a);
+  else if (dtype == BDATTN_F32 && d == 32) hipLaunchKernelGGL((bwd_dkdv_kernel<false, 32, 0>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

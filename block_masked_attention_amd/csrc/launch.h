@@ -22,6 +22,7 @@ struct FwdArgs {
   int32_t token_causal;    // clean rows see their own block up to their position only
   int32_t clean_kv_start;  // global position of clean buffer row 0
   int32_t corr_keys;       // the local corrupted keys are present
+  int32_t precision;       // bdattn_precision: float32 O (>= 1), split P (2)
   float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -45,6 +46,7 @@ struct BwdArgs {
   int32_t token_causal;    // clean rows see their own block up to their position only
   int32_t clean_kv_start;  // global position of clean buffer row 0
   int32_t corr_keys;       // the local corrupted keys are present
+  int32_t precision;       // bdattn_precision: float32 O (read), dQ, dK, dV (>= 1), split P, dS (2)
   float scale, scale_log2;
 };
 

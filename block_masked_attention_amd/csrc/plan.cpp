@@ -94,6 +94,10 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
     *msg = "only a partial problem may omit the corrupted keys";
     return BDATTN_ERR_INVALID_ARG;
   }
+  if (p->precision < BDATTN_PRECISION_DEFAULT || p->precision > BDATTN_PRECISION_SPLIT) {
+    *msg = "unknown precision";
+    return BDATTN_ERR_INVALID_ARG;
+  }
   if (p->B < 1 || p->H < 1 || p->Hkv < 1) {
     *msg = "B, H and Hkv must be >= 1";
     return BDATTN_ERR_SHAPE;
@@ -134,6 +138,7 @@ int load_problem(const bdattn_problem* p, Problem* out, std::string* msg) {
   P.token_causal = p->clean_mask == BDATTN_CLEAN_TOKEN_CAUSAL ? 1 : 0;
   P.clean_kv_start = int32_t(p->clean_kv_start);
   P.partial = p->partial;
+  P.precision = p->dtype == BDATTN_BF16 ? p->precision : BDATTN_PRECISION_DEFAULT;
   P.corr_keys = p->omit_corr_keys ? 0 : 1;
   P.scale = p->scale > 0.f ? p->scale : float(1.0 / sqrt(double(p->d)));
   P.n_clean_q = int32_t(p->n_clean_q);

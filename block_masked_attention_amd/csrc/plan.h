@@ -60,6 +60,7 @@ struct Problem {
   int32_t clean_kv_start = 0;  // global position of clean buffer row 0 (partial problems)
   int32_t partial = 0;         // attention over the keys present only
   int32_t corr_keys = 1;       // the local corrupted keys are present
+  int32_t precision = 0;       // bdattn_precision (bf16 inputs; not part of the plan)
   float scale;  // resolved (> 0)
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr_blocks;
   std::vector<int32_t> ids;  // always materialised (0..n-1 when NULL)

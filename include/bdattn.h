@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BDATTN_VERSION 4
+#define BDATTN_VERSION 5
 
 typedef enum {
   BDATTN_OK = 0,
@@ -79,6 +79,12 @@ typedef enum {
 } bdattn_status;
 
 typedef enum { BDATTN_F32 = 0, BDATTN_BF16 = 1 } bdattn_dtype;
+/* Output precision of a bf16 problem (bdattn_problem.precision). */
+typedef enum {
+  BDATTN_PRECISION_DEFAULT = 0,
+  BDATTN_PRECISION_F32_OUT = 1,
+  BDATTN_PRECISION_SPLIT = 2
+} bdattn_precision;
 
 /* What a clean query sees of its own clean block (§3.2): all of it, or the
  * keys at positions up to its own. Corrupted queries are not affected. */
@@ -94,7 +100,7 @@ typedef struct {
   int32_t H;       /* query heads */
   int32_t Hkv;     /* key/value heads; H % Hkv == 0 (q head h reads KV head h/(H/Hkv)) */
   int32_t d;       /* head dim: 32 or 128 */
-  int32_t dtype;   /* bdattn_dtype of every Q/K/V/O/dO/dQ/dK/dV tensor */
+  int32_t dtype;   /* bdattn_dtype of every Q/K/V/O/dO/dQ/dK/dV tensor (but see precision) */
   float scale;     /* softmax scale; <= 0 selects 1/sqrt(d) */
   int64_t n_clean_q;      /* local clean queries ...                         */
   int64_t clean_q_start;  /* ... at global clean positions [start, start+n)  */
@@ -146,6 +152,19 @@ typedef struct {
    * not such a multiple). dk_c/dv_c rows follow the buffer's order. */
   int32_t kv_chunk_len;
   const int32_t* kv_chunk_pos;
+  /* bdattn_precision (bf16 inputs; ignored for float32 inputs). DEFAULT:
+   * every tensor is of `dtype`. F32_OUT: O, dQ, dK and dV are float32 tensors
+   * (the backward reads the forward's float32 O; dO stays bf16); the kernels
+   * accumulate in float32 either way, so only the final stores change and the
+   * float32 O rounds to the default one bit for bit. SPLIT: F32_OUT, and the
+   * softmax weights P and the score gradients dS enter their matrix products
+   * (P V, dV = P^T dO, dK = dS^T Q, dQ = dS K) as two bf16 terms, a rounded
+   * value and its rounded remainder, so those products see them to about 16
+   * bits instead of 8; the products with a split operand run twice (26d
+   * instead of 18d matrix flops per pair and q head). The measured
+   * alternatives selected by BDATTN_DKDV / BDATTN_BWD support DEFAULT only
+   * and are not used otherwise. */
+  int32_t precision;
 } bdattn_problem;
 
 /* BDATTN_VERSION of the loaded library. */
@@ -258,7 +277,8 @@ int bdattn_bwd(const bdattn_problem* p,
  *   lse[h,i] = ln(exp(lse_a[h,i]) + exp(lse_b[h,i])),
  *   o[i,h,:] = (exp(lse_a - lse) o_a[i,h,:] + exp(lse_b - lse) o_b[i,h,:]).
  * A part with LSE = -inf has weight 0; a row with -inf in both gets o = 0,
- * lse = -inf. o_a/o_b/o are [n_rows, H, d] of `dtype` (32 or 128 for d), LSE
+ * lse = -inf. o_a/o_b/o are [n_rows, H, d] of `dtype` (32 or 128 for d; float32
+ * at d = 128 too, for the float32 outputs of bf16 problems), LSE
  * [H, n_rows] float32; o may alias o_a or o_b and lse lse_a or lse_b (each
  * element is read before it is written by the same thread). Device pointers,
  * 16-byte aligned; enqueued on hip_stream. */

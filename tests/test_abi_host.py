@@ -12,7 +12,7 @@ import block_masked_attention_amd as bd
 from oracle import (corrupted_copies, documents, key_positions, key_tokens, layout, query_positions,
                     query_tokens, visible)
 from tests.test_oracle import read_golden
-from workloads import CONFIGS
+from workloads import CONFIGS, small_spec
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert bd.version() == 4
+    assert bd.version() == 5
 
 
 def test_status_strings():
@@ -384,3 +384,18 @@ def test_lce_host_validation_and_workspace():
     assert L.bdattn_lce_fwd(ctypes.byref(ok), good, good, None, good, good, good, 1 << 30, None) == -1
     assert L.bdattn_lce_fwd(ctypes.byref(ok), vp((1 << 20) + 8), good, good, good, good, good,
                             1 << 30, None) == -1
+
+
+def test_precision_is_validated():
+    """bdattn_problem.precision is a bdattn_precision (0 default, 1 float32
+    outputs, 2 float32 outputs with split operands); anything else is refused
+    on the host."""
+    spec = small_spec(L=64, B=16, H=2, Hkv=2, d=32, dtype="bf16")
+    for v, ok in ((0, True), (1, True), (2, True), (3, False), (-1, False)):
+        p = bd.from_spec(spec)
+        p.precision = v
+        if ok:
+            assert bd.workspace_size(p, 0) > 0
+        else:
+            with pytest.raises(bd.BdattnError):
+                bd.workspace_size(p, 0)
