@@ -26,7 +26,8 @@ import torch
 import block_masked_attention_amd as bd
 from tests._helpers import f64, rms_err
 from tests.gpu_util import OUT_NAMES, oracle_full, say
-from tests.test_gpu_parity import SMALL, _sampled, long_key_blocks
+from tests.test_gpu_gathered import SMALL as GATHERED
+from tests.test_gpu_parity import DOCS, SMALL, _sampled, long_key_blocks
 from tests.test_gpu_partial import part_inputs, part_problem, pieces
 from workloads import CONFIGS, INPUT_NAMES, make_inputs, small_spec
 
@@ -60,6 +61,10 @@ def literal(got, want, names=OUT_NAMES):
 
 
 BF16_SMALL = [(label, kw) for label, kw in SMALL if kw["dtype"] == "bf16"]
+# the descriptor options the small list leaves out: packed documents and a
+# gathered clean buffer (the chunks in zigzag all-gather order)
+BF16_MORE = [(label, kw, {}) for label, kw in DOCS if kw["dtype"] == "bf16"] + [
+    (label, kw, g) for label, kw, g in GATHERED if kw["dtype"] == "bf16"]
 
 
 @pytest.mark.parametrize("label,kw", BF16_SMALL, ids=[c[0] for c in BF16_SMALL])
@@ -75,10 +80,13 @@ def test_f32_forward_rounds_to_the_bf16_forward(label, kw):
     assert torch.equal(f32[2], f16[2]) and torch.equal(f32[3], f16[3])
 
 
-@pytest.mark.parametrize("label,kw", BF16_SMALL, ids=[c[0] for c in BF16_SMALL])
-def test_small_problems_meet_the_stated_bound(label, kw):
+CASES = [(label, kw, {}) for label, kw in BF16_SMALL] + BF16_MORE
+
+
+@pytest.mark.parametrize("label,kw,g", CASES, ids=[c[0] for c in CASES])
+def test_small_problems_meet_the_stated_bound(label, kw, g):
     _need_gpu()
-    spec = small_spec(name=label, **kw)
+    spec = small_spec(name=label, **kw).with_(**g)
     t = make_inputs(spec, device="cuda")
     want = oracle_full(spec, t)
     errs = literal(run_prec(spec, t), want)
