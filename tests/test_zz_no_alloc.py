@@ -1,7 +1,8 @@
 """The allocation-free forward (bdattn_fwd_noalloc) against bdattn_fwd,
 called through the C ABI: two calls in a row, the second on a smaller
-problem, each bitwise equal to the forward with a workspace; a problem whose
-scratch exceeds the library's array is refused before any GPU work."""
+problem, each bitwise equal to the forward with a workspace (also with
+float32 outputs); a problem whose scratch exceeds the library's array is
+refused before any GPU work."""
 import ctypes
 
 import pytest
@@ -14,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _noalloc(p, t):
-    dt = torch.float32 if p.dtype == bd.F32 else torch.bfloat16
+    dt = torch.float32 if p.dtype == bd.F32 or p.precision else torch.bfloat16
     nc, nx, H, d = int(p.n_clean_q), p.n_corr, int(p.H), int(p.d)
     o_c = torch.full((nc, H, d), float("nan"), dtype=dt, device="cuda")
     o_x = torch.full((nx, H, d), float("nan"), dtype=dt, device="cuda")
@@ -44,6 +45,25 @@ def test_noalloc_forward_equals_the_workspace_forward_twice_in_a_row():
         assert st == 0, bd.lib().bdattn_last_error().decode()
         want = bd.fwd(p, *[t[k] for k in INPUT_NAMES])
         torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)
+
+
+def test_noalloc_forward_with_float32_outputs():
+    """The precision modes reach the allocation-free forward too: float32
+    outputs (and split operands), bitwise those of bdattn_fwd."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    spec = small_spec(L=1024, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=33)
+    t = make_inputs(spec, device="cuda")
+    for prec in (bd.PRECISION_F32_OUT, bd.PRECISION_SPLIT):
+        print(f"[gpu] no-alloc forward, precision {prec}", flush=True)
+        p = bd.from_spec(spec, precision=prec)
+        st, got = _noalloc(p, t)
+        assert st == 0, bd.lib().bdattn_last_error().decode()
+        want = bd.fwd(p, *[t[k] for k in INPUT_NAMES])
+        torch.cuda.synchronize()
+        assert got[0].dtype == torch.float32
         for a, b in zip(got, want):
             assert torch.equal(a, b)
 
