@@ -27,7 +27,7 @@ import block_masked_attention_amd as bd
 from tests._helpers import f64, rms_err
 from tests.gpu_util import OUT_NAMES, oracle_full, say
 from tests.test_gpu_gathered import SMALL as GATHERED
-from tests.test_gpu_parity import DOCS, SMALL, _sampled, long_key_blocks
+from tests.test_gpu_parity import DOCS, RANDOM, RANDOM_DOCS, SMALL, _sampled, long_key_blocks
 from tests.test_gpu_partial import part_inputs, part_problem, pieces
 from workloads import CONFIGS, INPUT_NAMES, make_inputs, small_spec
 
@@ -80,7 +80,9 @@ def test_f32_forward_rounds_to_the_bf16_forward(label, kw):
     assert torch.equal(f32[2], f16[2]) and torch.equal(f32[3], f16[3])
 
 
-CASES = [(label, kw, {}) for label, kw in BF16_SMALL] + BF16_MORE
+# the parity suite's seeded random problems (every descriptor option mixed in)
+BF16_RANDOM = [(label, kw, {}) for label, kw in RANDOM + RANDOM_DOCS if kw["dtype"] == "bf16"]
+CASES = [(label, kw, {}) for label, kw in BF16_SMALL] + BF16_MORE + BF16_RANDOM
 
 
 @pytest.mark.parametrize("label,kw,g", CASES, ids=[c[0] for c in CASES])
