@@ -2,8 +2,9 @@
 (MFMA) utilisation, LDS utilisation and HBM traffic per kernel, for one
 workload of ``bench.py``.
 
-Each measurement is its own rocprofv3 run of ``bench.py`` (one step), started
-as a child process with a time limit:
+Each measurement is its own rocprofv3 run of ``bench.py`` (one warm-up step
+and one timed step, so that every pass averages the same two launches of each
+kernel), started as a child process with a time limit:
 
   trace   --kernel-trace --stats                     kernel durations
   fetch   --pmc FETCH_SIZE, with a 1 GiB plain copy  HBM reads
@@ -58,6 +59,8 @@ MAIN_KERNELS = ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_prep_kern
 ATOMIC = "TCC_EA0_ATOMIC_sum"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
+MIN_CLOCK_MS = 0.1  # shorter kernels get no clock-derived figures
+WARMUP = 1  # bench.py warm-up steps in every pass (durations and counters average all launches)
 SQ1 = ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
        "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
        "GRBM_GUI_ACTIVE"]
@@ -131,11 +134,23 @@ def durations(d):
     return out
 
 
+def counter_rows(d):
+    """The counter rows of a pass. Of the runtime's copy kernel only the
+    calibration copy is kept: the dispatch with the largest grid (the runtime
+    also runs small copies of the same kernel, e.g. for host uploads, which
+    would otherwise dilute the per-dispatch average)."""
+    rows = read_csv(d, "counter_collection")
+    copies = [r for r in rows if short_name(r["Kernel_Name"]) == COPY_KERNEL]
+    keep = max(copies, key=lambda r: int(r["Grid_Size"]))["Dispatch_Id"] if copies else None
+    return [r for r in rows
+            if short_name(r["Kernel_Name"]) != COPY_KERNEL or r["Dispatch_Id"] == keep]
+
+
 def counters(d):
     """Counter totals per kernel, divided by the kernel's dispatch count."""
     tot = collections.defaultdict(lambda: collections.defaultdict(float))
     disp = collections.defaultdict(set)
-    for r in read_csv(d, "counter_collection"):
+    for r in counter_rows(d):
         k = short_name(r["Kernel_Name"])
         tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
         disp[k].add(r["Dispatch_Id"])
@@ -170,8 +185,11 @@ def summarise(dur, fetch, write, sq1, sq2, dev):
             r["hbm_gbps"] = round((r["hbm_read_gb"] + r["hbm_write_gb"]) / s, 1)
         if k in write and ATOMIC in write[k]:  # atomic requests beyond the L2, per launch
             r["atomic_requests"] = write[k][ATOMIC]
+        # (GRBM_GUI_ACTIVE also counts the launch around a kernel, so the
+        # clock and the figures per cycle mean nothing for very short ones)
         clocks = [c["GRBM_GUI_ACTIVE"] / dev["xcds"] / s / 1e9
-                  for c in (sq1.get(k), sq2.get(k)) if c and "GRBM_GUI_ACTIVE" in c]
+                  for c in (sq1.get(k), sq2.get(k)) if c and "GRBM_GUI_ACTIVE" in c
+                  and t["ms"] >= MIN_CLOCK_MS]
         if clocks:
             ghz = sum(clocks) / len(clocks)
             cycles = ghz * 1e9 * s
@@ -268,7 +286,7 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     rows = _main_rows(d_trace)
     out = [f"# bdattn kernels, {workload} workload: rocprofv3 kernel trace", ""] + head + [
         "The `trace` pass: `rocprofv3 --kernel-trace --stats` over `bench.py --workload "
-        f"{spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 1`.", "",
+        f"{spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup {WARMUP}`.", "",
         "| kernel | calls | avg ms | min ms | max ms | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
@@ -282,7 +300,7 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
            ""] + head + [
         "The `fetch` and `write` passes: `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE"
         + (f" {ATOMIC}" if bwd != "split" else "") + "` over "
-        f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 0 "
+        f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup {WARMUP} "
         "--copy-calibration`. The calibration copy (`__amd_rocclr_copyBuffer`) reads and writes "
         f"exactly {COPY_BYTES // 1024} KiB; the counters read FETCH_SIZE = "
         f"{cf.get('FETCH_SIZE', 0):.0f} KiB and WRITE_SIZE = {cw.get('WRITE_SIZE', 0):.0f} KiB for "
@@ -315,12 +333,12 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
     ks = [k for k in summary["kernels"] if _base(k) in BENCH_NAME]
     out = [f"# bdattn kernels, {workload} workload: SQ counters (rocprofv3 --pmc)", ""] + head + [
         "The `sq1` and `sq2` passes run `rocprofv3 --pmc` with these counter sets over "
-        f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup 0`: sq1 = "
+        f"`bench.py --workload {spec.name}{bench_extra} --no-cpu-baseline --steps 1 --warmup {WARMUP}`: sq1 = "
         f"{' '.join(SQ1)}; sq2 = {' '.join(SQ2)}. Clock = GRBM_GUI_ACTIVE / {dev['xcds']} XCDs / "
         f"duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({dev['simds']} SIMDs x cycles); LDS "
         f"busy = SQ_LDS_IDX_ACTIVE / ({dev['cus']} CUs x cycles).", "",
         "| counter | " + " | ".join(f"`{k}`" for k in ks) + " |", "|---|" + "---|" * len(ks),
-        "| duration (ms, kernel trace) | " + " | ".join(f"{summary['kernels'][k]['ms']:.0f}" for k in ks) + " |"]
+        "| duration (ms, kernel trace) | " + " | ".join(f"{summary['kernels'][k]['ms']:.4g}" for k in ks) + " |"]
     for c in dict.fromkeys(SQ1 + SQ2):
         vals = []
         for k in ks:
@@ -373,9 +391,9 @@ def lce_profile(args):
     """Kernel trace and calibrated HBM traffic of one linear cross-entropy
     step (bench.py --workload lce_*), per role."""
     b = ["--workload", args.workload, "--no-cpu-baseline", "--steps", "1"]
-    d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", "1"], args.out,
+    d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", str(WARMUP)], args.out,
                        args.limit)
-    cal = b + ["--warmup", "0", "--copy-calibration"]
+    cal = b + ["--warmup", str(WARMUP), "--copy-calibration"]
     d_fetch = run_pass("fetch", ["--pmc", "FETCH_SIZE"], cal, args.out, args.limit)
     d_write = run_pass("write", ["--pmc", "WRITE_SIZE"], cal, args.out, args.limit)
     fetch_raw, write_raw = lce_counters(d_fetch), lce_counters(d_write)
@@ -447,7 +465,7 @@ def lce_counters(d):
     """Counter totals per role (and the calibration copy), per dispatch."""
     tot = collections.defaultdict(lambda: collections.defaultdict(float))
     disp = collections.defaultdict(set)
-    for r in read_csv(d, "counter_collection"):
+    for r in counter_rows(d):
         name = r["Kernel_Name"]
         k = COPY_KERNEL if short_name(name) == COPY_KERNEL else lce_role(name)
         if k is None:
@@ -481,14 +499,14 @@ def main():
         b += ["--docs", str(args.docs)]
     if args.bwd != "split":  # read by the library at every backward call
         os.environ["BDATTN_BWD"] = args.bwd
-    d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", "1"], args.out,
+    d_trace = run_pass("trace", ["--kernel-trace", "--stats"], b + ["--warmup", str(WARMUP)], args.out,
                        args.limit)
-    cal = b + ["--warmup", "0", "--copy-calibration"]
+    cal = b + ["--warmup", str(WARMUP), "--copy-calibration"]
     d_fetch = run_pass("fetch", ["--pmc", "FETCH_SIZE"], cal, args.out, args.limit)
     d_write = run_pass("write", ["--pmc", "WRITE_SIZE"] + ([ATOMIC] if args.bwd != "split" else []),
                        cal, args.out, args.limit)
-    d_sq1 = run_pass("sq1", ["--pmc"] + SQ1, b + ["--warmup", "0"], args.out, args.limit)
-    d_sq2 = run_pass("sq2", ["--pmc"] + SQ2, b + ["--warmup", "0"], args.out, args.limit)
+    d_sq1 = run_pass("sq1", ["--pmc"] + SQ1, b + ["--warmup", str(WARMUP)], args.out, args.limit)
+    d_sq2 = run_pass("sq2", ["--pmc"] + SQ2, b + ["--warmup", str(WARMUP)], args.out, args.limit)
     summary = summarise(durations(d_trace), counters(d_fetch), counters(d_write),
                         counters(d_sq1), counters(d_sq2), agent(d_trace))
     summary["workload"] = profile_key(args.workload, args.docs, args.bwd)

@@ -22,10 +22,11 @@ def _write(d, name, rows):
 def _counters(d, per_kernel):
     rows = []
     for i, (k, cs) in enumerate(per_kernel):
+        grid = cs.pop("_grid", 131072)
         for disp in range(cs.pop("_dispatches", 1)):
             for c, v in cs.items():
-                rows.append(dict(Dispatch_Id=f"{i}.{disp}", Kernel_Name=k, Counter_Name=c,
-                                 Counter_Value=v))
+                rows.append(dict(Dispatch_Id=f"{i}.{disp}", Kernel_Name=k, Grid_Size=grid,
+                                 Counter_Name=c, Counter_Value=v))
     _write(d, "counter_collection", rows)
 
 
@@ -107,6 +108,20 @@ def test_summary_arithmetic(tmp_path):
     assert r["valu_per_mfma"] == pytest.approx(3.0) and r["lds_per_mfma"] == pytest.approx(1.5)
     md = rocprof.markdown(s, "256k", "python -m block_masked_attention_amd.rocprof")
     assert "| `bwd_dq_kernel<true, 128>` | 2 | 2 | 50% | 25% |" in md
+
+
+def test_calibration_uses_the_large_copy_only(tmp_path):
+    """The runtime also dispatches its copy kernel for small uploads; only
+    the 1 GiB calibration copy (the largest grid) may set the scale factors."""
+    t = str(tmp_path)
+    _counters(t + "/fetch", [(rocprof.COPY_KERNEL, dict(FETCH_SIZE=8.0, _grid=1024, _dispatches=2)),
+                             (rocprof.COPY_KERNEL, dict(FETCH_SIZE=524288.0)),
+                             (K, dict(FETCH_SIZE=1000.0))])
+    c = rocprof.counters(t + "/fetch")
+    assert c[rocprof.COPY_KERNEL]["FETCH_SIZE"] == pytest.approx(524288.0)
+    assert c[rocprof.COPY_KERNEL]["_dispatches"] == 1
+    assert rocprof.lce_counters(t + "/fetch")[rocprof.COPY_KERNEL]["FETCH_SIZE"] == \
+        pytest.approx(524288.0)
 
 
 def test_repository_summaries(tmp_path):
