@@ -280,7 +280,8 @@ def write_profiles(dest, workload, cmd, d_trace, fetch, write, sq1, sq2, dev, su
                  "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles); LDS busy = "
                  "SQ_LDS_IDX_ACTIVE / (CUs x cycles); HBM bytes per launch from FETCH_SIZE and "
                  "WRITE_SIZE, scaled by the plain copy. Each figure comes from its own rocprofv3 "
-                 "run of one bench step (block_masked_attention_amd/rocprof.py lists the "
+                 "run of one warm-up and one timed bench step, averaged per launch "
+                 "(block_masked_attention_amd/rocprof.py lists the "
                  "passes); durations come from the kernel-trace pass.\n")
     # 2. kernel trace
     rows = _main_rows(d_trace)
