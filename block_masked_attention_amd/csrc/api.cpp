@@ -2,6 +2,7 @@
 // and kernel launches.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -343,8 +344,10 @@ int scratch_address(void** out) {
 // vectors (pageable memory, consumed before each copy call returns), so no
 // pinned staging buffer is taken.
 int upload_direct(const bdattn::Plan& plan, const bdattn::WsLayout& w, char* ws, hipStream_t s) {
+  static const int32_t zeros[bdattn::kClaimCounters] = {};  // the work-claim counters
   struct Part { size_t off; const void* src; size_t bytes; };
-  const Part parts[] = {{w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t)},
+  const Part parts[] = {{w.claim, zeros, sizeof(zeros)},
+                        {w.ids, plan.P.ids.data(), plan.P.ids.size() * sizeof(int32_t)},
                         {w.spans, plan.P.spans.data(), plan.P.spans.size() * sizeof(BdDocSpan)},
                         {w.kv_map, plan.P.kv_map.data(), plan.P.kv_map.size() * sizeof(int32_t)},
                         {w.q_items, plan.fwd.data(), w.q_items_bytes}};
@@ -354,6 +357,13 @@ int upload_direct(const bdattn::Plan& plan, const bdattn::WsLayout& w, char* ws,
     if (er != hipSuccess) return fail(BDATTN_ERR_HIP, std::string("scratch upload: ") + hipGetErrorString(er));
   }
   return BDATTN_OK;
+}
+
+// Work claiming across the XCDs' queues (kClaimQueues in plan.h) unless
+// BDATTN_CLAIM=0, which runs item i on workgroup i (the static deal).
+bool claim_on() {
+  const char* e = getenv("BDATTN_CLAIM");
+  return !(e && !strcmp(e, "0"));
 }
 
 }  // namespace
@@ -552,6 +562,7 @@ int fwd_impl(const bdattn_problem* p, const void* q_c, const void* k_c, const vo
   a.n_kv_map = int32_t(P.kv_map.size());
   a.items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_items = int32_t(plan->fwd.size());
+  a.claim = claim_on() ? (int32_t*)(ws + w.claim) : nullptr;
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
@@ -627,6 +638,8 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.n_q_items = int32_t(plan->fwd.size());
   a.kv_items = (const bdattn::BwdItem*)(ws + w.kv_items);
   a.n_kv_items = int32_t(plan->bwd.size());
+  a.claim_q = claim_on() ? (int32_t*)(ws + w.claim) : nullptr;
+  a.claim_kv = a.claim_q ? a.claim_q + bdattn::kClaimQueues : nullptr;
   a.d_c = (float*)(ws + w.d_c);
   a.d_x = (float*)(ws + w.d_x);
   a.l2_c = (float*)(ws + w.l2_c);

@@ -55,6 +55,33 @@ constexpr float kLn2 = 0.6931471805599453f;
 // of strongly peaked rows amplify.)
 constexpr float kRescaleMargin = 0.f;
 
+// The work item of this workgroup (the protocol is described with
+// kClaimQueues in plan.h): with ctr == nullptr item blockIdx.x of a grid of n;
+// else thread 0 claims one from the counters ctr[0..kClaimQueues) of a grid
+// of n + claim_extra(n) and the workgroup reads it from LDS; -1 when every
+// queue is empty (the workgroup then ends). Each item is claimed exactly once:
+// a claim is one atomic add, counters only grow, and a workgroup gives up
+// only after it has seen every queue empty.
+__device__ __forceinline__ int claim_item(int32_t* ctr, int n) {
+  __shared__ int s_item;
+  if (ctr == nullptr) return blockIdx.x;
+  if (threadIdx.x == 0) {
+    int item = -1;
+    const int home = blockIdx.x % kClaimQueues;
+    for (int v = 0; v < kClaimQueues && item < 0; ++v) {
+      const int y = (home + v) % kClaimQueues;
+      const int len = n > y ? (n - y + kClaimQueues - 1) / kClaimQueues : 0;
+      if (v && __hip_atomic_load(ctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len)
+        continue;
+      const int c = __hip_atomic_fetch_add(ctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c < len) item = y + kClaimQueues * c;
+    }
+    s_item = item;
+  }
+  __syncthreads();
+  return s_item;
+}
+
 // 2^x with one v_exp_f32 (results below 2^-126 flush to zero, which is
 // harmless for softmax weights; exp2(-inf) = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -106,7 +106,9 @@ void fwd_kernel(FwdArgs a) {
   const int lq = lane & 31, hf = lane >> 5;
   const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
                     a.n_clean_kv, a.corr_keys != 0, DOCS ? a.docs : nullptr};
-  const QTile q = q_tile<TK, DOCS>(a.items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
+  const int wi = claim_item(a.claim, a.n_items);
+  if (wi < 0) return;  // every item taken (the whole workgroup)
+  const QTile q = q_tile<TK, DOCS>(a.items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
                              a.n_clean_q, a.n_corr, rs, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
@@ -394,7 +396,9 @@ void bwd_dq_kernel(BwdArgs a) {
   const int lq = lane & 31, hf = lane >> 5;
   const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
                     a.n_clean_kv, a.corr_keys != 0, DOCS ? a.docs : nullptr};
-  const QTile q = q_tile<TK, DOCS>(a.q_items[blockIdx.x], a.rows_per_item, a.Gw, a.H, a.Hkv,
+  const int wi = claim_item(a.claim_q, a.n_q_items);
+  if (wi < 0) return;  // every item taken (the whole workgroup)
+  const QTile q = q_tile<TK, DOCS>(a.q_items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
                              a.n_clean_q, a.n_corr, rs, wave, lq);
   const int n_tiles = q.n_ct + q.n_xt;
   const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
@@ -532,7 +536,7 @@ void bwd_dq_kernel(BwdArgs a) {
 template <bool BF16, int D, int PREC>
 hipError_t run_fwd_t(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  const dim3 grid(a.n_items), block(FWD_WAVES * 64);
+  const dim3 grid(a.n_items + (a.claim ? claim_extra(a.n_items) : 0)), block(FWD_WAVES * 64);
   if (a.n_items > 0 && a.kv_map) {  // a gathered clean buffer
     if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);
@@ -579,7 +583,7 @@ hipError_t run_bwd_t(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
     return err;
   }
   if (ev) (void)hipEventRecord(ev[0].start, s);
-  const dim3 grid(a.n_q_items), block(FWD_WAVES * 64);
+  const dim3 grid(a.n_q_items + (a.claim_q ? claim_extra(a.n_q_items) : 0)), block(FWD_WAVES * 64);
   if (a.n_q_items > 0 && a.kv_map) {  // a gathered clean buffer
     if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);

@@ -48,7 +48,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(sizeof(smem) + sizeof(r_row) + sizeof(p_hand) <= 160 * 1024, "LDS");
   constexpr uint32_t TB = TSZ * sizeof(T);  // bytes per tile
 
-  const BwdItem item = a.kv_items[blockIdx.x];
+  const int wi = claim_item(a.claim_kv, a.n_kv_items);
+  if (wi < 0) return;  // every item taken (the whole workgroup)
+  const BwdItem item = a.kv_items[wi];
   const int it_x0 = item.x0, it_x1 = item.x1, it_c0 = item.c0, it_c1 = item.c1;
   const int it_xf = item.xf, it_cf = item.cf, it_xfe = item.xfe, it_cfe = item.cfe;
   const int kstream = item.hs & 1, kvh = item.hs >> 1;
@@ -373,9 +375,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 hipError_t launch_dkdv(const BwdArgs& a, int dtype, int d, hipStream_t s) {
   if (a.n_kv_items <= 0) return hipSuccess;
-  const dim3 grid(a.n_kv_items), block(512);
   if (const char* e = getenv("BDATTN_DKDV"); e && !strcmp(e, "fused") && !a.precision)
     return launch_dkdv_fused(a, dtype, d, s);
+  const dim3 grid(a.n_kv_items + (a.claim_kv ? claim_extra(a.n_kv_items) : 0)), block(512);
   const int pr = dtype == BDATTN_BF16 ? a.precision : 0;  // bdattn_precision (bf16 inputs)
   if (dtype == BDATTN_BF16 && d == 128 && pr == 2) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128, 2>), grid, block, 0, s, a);
   else if (dtype == BDATTN_BF16 && d == 128 && pr == 1) hipLaunchKernelGGL((bwd_dkdv_kernel<true, 128, 1>), grid, block, 0, s, a);

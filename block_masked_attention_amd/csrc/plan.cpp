@@ -259,6 +259,8 @@ size_t n_kv_items(const Problem& P) {
 WsLayout workspace_layout(const Problem& P, int pass) {
   WsLayout w;
   size_t off = 0;
+  w.claim = off;
+  off = align_up(off + sizeof(int32_t) * kClaimCounters, WS_ALIGN);
   w.ids = off;
   off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, P.ids.size()), WS_ALIGN);
   w.spans = off;

@@ -33,6 +33,19 @@ constexpr int BWD_TQ = BDATTN_BWD_TQ;
 
 constexpr size_t WS_ALIGN = 256;
 
+// Work claiming (the forward, dQ and dK/dV kernels). A work list, sorted
+// longest first, is dealt over kClaimQueues queues: queue x holds items x,
+// x + 8, x + 16, ... The hardware places workgroup i on XCD i mod 8, and that
+// workgroup first claims from queue i mod 8, so while every XCD keeps pace
+// each runs the items of the static deal. XCDs do not run at one speed, so
+// the grid has claim_extra(n) workgroups beyond the n items: an XCD that has
+// emptied its queue takes the next items of another, and workgroups that
+// find every queue empty end at once. The counters (one per queue) sit in
+// the workspace's uploaded head and so restart at zero with every launch.
+constexpr int kClaimQueues = 8;
+constexpr int kClaimCounters = 3 * kClaimQueues;  // forward or dQ, dK/dV, spare
+BD_HD int32_t claim_extra(int32_t n) { return kClaimQueues * ((n + 31) / 32); }  // n / 4, rounded up
+
 // One forward work item: `tile` of `rows` query rows (stream bit 0 of hs),
 // head group hs >> 1 (Gw consecutive q heads).
 struct FwdItem {
@@ -100,6 +113,7 @@ void build_plan(const Problem& P, Plan* plan);
 // LSE * log2(e), are float [H][round_up(n, BWD_TQ)]: every query tile's
 // values are one contiguous run, and rows past n hold -D = 0, LSE = +inf.
 struct WsLayout {
+  size_t claim = 0;  // kClaimCounters int32 work-claim counters (zero when uploaded)
   size_t ids = 0, spans = 0, kv_map = 0, q_items = 0, q_items_bytes = 0, kv_items = 0,
          kv_items_bytes = 0;
   size_t d_c = 0, d_x = 0, l2_c = 0, l2_x = 0;  // bwd row data
