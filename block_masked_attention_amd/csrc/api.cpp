@@ -359,11 +359,18 @@ int upload_direct(const bdattn::Plan& plan, const bdattn::WsLayout& w, char* ws,
   return BDATTN_OK;
 }
 
-// Work claiming across the XCDs' queues (kClaimQueues in plan.h) unless
-// BDATTN_CLAIM=0, which runs item i on workgroup i (the static deal).
-bool claim_on() {
+// Work claiming across the XCDs' queues (kClaimQueues in plan.h) for a list
+// of n_items items that sweep `steps` tiles in all. It pays when the list is
+// long (16 or more items per CU of the 256, so an XCD's last items can go to
+// another) and its items are long enough (32 tiles or more on average) to
+// hide the claim's atomic round trip, about 1.5 us; else workgroup i runs
+// item i (the static deal). BDATTN_CLAIM=0 forces the static deal and
+// BDATTN_CLAIM=1 forces claiming.
+bool claim_on(size_t n_items, int64_t steps) {
   const char* e = getenv("BDATTN_CLAIM");
-  return !(e && !strcmp(e, "0"));
+  if (e && !strcmp(e, "0")) return false;
+  if (e && !strcmp(e, "1")) return true;
+  return n_items >= 4096 && steps >= 32 * int64_t(n_items);
 }
 
 }  // namespace
@@ -562,7 +569,7 @@ int fwd_impl(const bdattn_problem* p, const void* q_c, const void* k_c, const vo
   a.n_kv_map = int32_t(P.kv_map.size());
   a.items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_items = int32_t(plan->fwd.size());
-  a.claim = claim_on() ? (int32_t*)(ws + w.claim) : nullptr;
+  a.claim = claim_on(plan->fwd.size(), plan->fwd_tiles) ? (int32_t*)(ws + w.claim) : nullptr;
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
@@ -638,8 +645,9 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   a.n_q_items = int32_t(plan->fwd.size());
   a.kv_items = (const bdattn::BwdItem*)(ws + w.kv_items);
   a.n_kv_items = int32_t(plan->bwd.size());
-  a.claim_q = claim_on() ? (int32_t*)(ws + w.claim) : nullptr;
-  a.claim_kv = a.claim_q ? a.claim_q + bdattn::kClaimQueues : nullptr;
+  int32_t* const ctr = (int32_t*)(ws + w.claim);
+  a.claim_q = claim_on(plan->fwd.size(), plan->fwd_tiles) ? ctr : nullptr;
+  a.claim_kv = claim_on(plan->bwd.size(), plan->bwd_qtiles) ? ctr + bdattn::kClaimQueues : nullptr;
   a.d_c = (float*)(ws + w.d_c);
   a.d_x = (float*)(ws + w.d_x);
   a.l2_c = (float*)(ws + w.l2_c);

@@ -1,6 +1,7 @@
 """Work claiming on the GPU: the forward, dQ and dK/dV kernels take their work
-items from per-XCD queues with stealing (the default), or workgroup i runs
-item i (BDATTN_CLAIM=0). Every item computes the same values whichever
+items from per-XCD queues with stealing (BDATTN_CLAIM=1; by default the host
+claims only for long lists of long items), or workgroup i runs item i
+(BDATTN_CLAIM=0). Every item computes the same values whichever
 workgroup runs it, so both schedules must give bitwise equal outputs; the
 outputs start as NaN, so an item that no workgroup ran would show. The
 claimed schedule runs three times per case (the steals differ from run to
@@ -66,7 +67,7 @@ def _check(spec, monkeypatch):
     want = _run(spec, t)
     # a row with no visible key gets LSE = -inf and O = 0 (never NaN)
     assert not any(torch.isnan(x).any().item() for x in want), "static schedule left an output unwritten"
-    monkeypatch.delenv("BDATTN_CLAIM", raising=False)
+    monkeypatch.setenv("BDATTN_CLAIM", "1")
     for rep in range(3):
         got = _run(spec, t)
         holes = [torch.isnan(x).any().item() for x in got]
