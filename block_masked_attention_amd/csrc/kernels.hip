@@ -19,7 +19,8 @@
 //                    every query tile (and q head of the KV group) that sees
 //                    the keys, written once (kernels_dkdv.hip)
 //   merge_kernel     two partial results over disjoint key sets -> one
-// No kernel uses atomics, so every output is bitwise reproducible.
+// No output is accumulated with atomics (the only atomics are the work-claim
+// counters, claim_item in device.h), so every output is bitwise reproducible.
 //
 // Matrix products use the CDNA4 32x32x16 bf16 MFMA (fp32 accumulate), or, for
 // fp32 problems, eight 32x32x2 fp32 MFMAs per 16-deep step. The softmax is the

@@ -42,8 +42,10 @@
  * Ownership and execution: every tensor pointer is a DEVICE pointer owned by
  * the caller. bdattn_fwd / bdattn_bwd enqueue work on `hip_stream` (a
  * hipStream_t; NULL = the default stream) and return without waiting; they
- * never allocate device memory. They use no atomics: results are bitwise
- * reproducible for a given problem and inputs. Scratch space is the caller's `workspace`
+ * never allocate device memory. No result is accumulated with atomics (the
+ * only atomics are integer counters that hand work items to workgroups, and
+ * an item computes the same values whichever workgroup runs it): results are
+ * bitwise reproducible for a given problem and inputs. Scratch space is the caller's `workspace`
  * (device memory of at least bdattn_workspace_size bytes, 256-byte aligned),
  * which must not be used by anything else until the enqueued work is done.
  * Outputs are overwritten, never accumulated into. Tensor pointers must be

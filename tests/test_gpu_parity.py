@@ -115,8 +115,9 @@ def test_tiny_workload_full_parity():
 
 
 def test_repeat_calls_and_determinism():
-    """No kernel uses atomics and every output element is written by one
-    thread, so repeated calls are bitwise identical."""
+    """No output is accumulated with atomics (the work-claim counters only
+    choose which workgroup runs an item) and every output element is written
+    by one thread, so repeated calls are bitwise identical."""
     _need_gpu()
     spec = small_spec(L=512, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=3)
     t = make_inputs(spec, device="cuda")
