@@ -73,13 +73,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources whose counters a profile describes."""
+def code_lines(text: str):
+    """The lines of a C++ source without // comments, trailing blanks and empty
+    lines (a "//" inside a string literal is kept)."""
+    out = []
+    for line in text.splitlines():
+        cut, quoted = len(line), False
+        for i, ch in enumerate(line):
+            if ch == '"' and (i == 0 or line[i - 1] != "\\"):
+                quoted = not quoted
+            elif not quoted and line.startswith("//", i):
+                cut = i
+                break
+        line = line[:cut].rstrip()
+        if line:
+            out.append(line)
+    return out
+
+
+def kernel_source_hash(csrc: str = None) -> str:
+    """Hash of the code of the kernel sources whose counters a profile
+    describes (comments do not count)."""
     import hashlib
+    csrc = csrc or os.path.join(ROOT, "block_masked_attention_amd", "csrc")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_masked_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update("\n".join(code_lines(fh.read())).encode() + b"\n")
     return h.hexdigest()[:16]
 
 

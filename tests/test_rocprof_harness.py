@@ -174,3 +174,20 @@ def test_lce_roles_follow_the_transposes_in_the_kernel_names():
     assert lce_role("bdattn::(anonymous namespace)::lce_fused_kernel(float const*, int)") == "lce_rows"
     assert lce_role("__amd_rocclr_copyBuffer") is None
     assert lce_role("void at::native::vectorized_elementwise_kernel<4>") is None
+
+
+def test_kernel_source_hash_ignores_comments(tmp_path):
+    """A committed profile stays valid across comment edits of the kernel
+    sources, not across code edits."""
+    import shutil
+    src = os.path.join(rocprof.ROOT, "block_masked_attention_amd", "csrc")
+    for f in rocprof.KERNEL_SOURCES:
+        shutil.copy(os.path.join(src, f), tmp_path / f)
+    base = rocprof.kernel_source_hash(str(tmp_path))
+    assert base == rocprof.kernel_source_hash()
+    k = tmp_path / "kernels.hip"
+    text = k.read_text()
+    k.write_text("// a new comment line\n" + text.replace("\n", "  // trailing note\n", 1))
+    assert rocprof.kernel_source_hash(str(tmp_path)) == base
+    k.write_text(text.replace("kNegInf", "kNegInf ", 1) + "\nint unused_symbol;\n")
+    assert rocprof.kernel_source_hash(str(tmp_path)) != base
