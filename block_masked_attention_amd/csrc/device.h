@@ -74,7 +74,7 @@ __device__ __forceinline__ int claim_item(int32_t* ctr, int n) {
       if (v && __hip_atomic_load(ctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len)
         continue;
       const int c = __hip_atomic_fetch_add(ctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (c < len) item = y + kClaimQueues * c;
+      if (c >= 0 && c < len) item = y + kClaimQueues * c;  // (c < 0: a clobbered counter)
     }
     s_item = item;
   }

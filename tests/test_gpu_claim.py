@@ -5,7 +5,7 @@ claims only for long lists of long items), or workgroup i runs item i
 workgroup runs it, so both schedules must give bitwise equal outputs; the
 outputs start as NaN, so an item that no workgroup ran would show. The
 claimed schedule runs three times per case (the steals differ from run to
-run). Cases: small problems with every descriptor option (packed documents,
+run) on the same workspaces, whose claim counters every call restarts. Cases: small problems with every descriptor option (packed documents,
 a share's rows, a gathered buffer, GQA, fp32) and the 8K workload, whose
 1,024 query-tile and 2,048 key-tile items span all 256 CUs.
 
@@ -44,8 +44,9 @@ def _nan_like(*shape, dtype):
     return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
 
 
-def _run(spec, t):
-    """fwd + bwd into NaN-filled outputs; returns the ten outputs."""
+def _run(spec, t, ws):
+    """fwd + bwd into NaN-filled outputs with the workspaces ws; returns the
+    ten outputs."""
     p = bd.from_spec(spec)
     dt = t["q_c"].dtype
     H, Hkv, d = spec.H, spec.Hkv, spec.d
@@ -55,21 +56,25 @@ def _run(spec, t):
     g = [_nan_like(nc, H, d, dtype=dt), _nan_like(nx, H, d, dtype=dt), _nan_like(nkv, Hkv, d, dtype=dt),
          _nan_like(nkv, Hkv, d, dtype=dt), _nan_like(nx, Hkv, d, dtype=dt), _nan_like(nx, Hkv, d, dtype=dt)]
     ins = [t[k] for k in INPUT_NAMES]
-    bd.fwd(p, *ins, out=f)
-    bd.bwd(p, *ins, *f, t["do_c"], t["do_x"], out=g)
+    bd.fwd(p, *ins, out=f, workspace=ws[0])
+    bd.bwd(p, *ins, *f, t["do_c"], t["do_x"], out=g, workspace=ws[1])
     torch.cuda.synchronize()
     return f + g
 
 
 def _check(spec, monkeypatch):
     t = make_inputs(spec, device="cuda")
+    # one pair of workspaces for every run: each call must restart the claim
+    # counters the previous one left at the end of their queues
+    p = bd.from_spec(spec)
+    ws = [torch.zeros(bd.workspace_size(p, k), dtype=torch.uint8, device="cuda") for k in (0, 1)]
     monkeypatch.setenv("BDATTN_CLAIM", "0")
-    want = _run(spec, t)
+    want = _run(spec, t, ws)
     # a row with no visible key gets LSE = -inf and O = 0 (never NaN)
     assert not any(torch.isnan(x).any().item() for x in want), "static schedule left an output unwritten"
     monkeypatch.setenv("BDATTN_CLAIM", "1")
     for rep in range(3):
-        got = _run(spec, t)
+        got = _run(spec, t, ws)
         holes = [torch.isnan(x).any().item() for x in got]
         same = [torch.equal(a, b) for a, b in zip(got, want)]
         say(f"  {spec.name}: claimed schedule run {rep}: no NaN left {not any(holes)}, bitwise {same}")

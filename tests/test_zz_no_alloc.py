@@ -2,7 +2,8 @@
 called through the C ABI: two calls in a row, the second on a smaller
 problem, each bitwise equal to the forward with a workspace (also with
 float32 outputs); a problem whose scratch exceeds the library's array is
-refused before any GPU work."""
+refused before any GPU work; with work claiming forced on, the claim
+counters in the scratch array restart at zero with every call."""
 import ctypes
 
 import pytest
@@ -46,6 +47,29 @@ def test_noalloc_forward_equals_the_workspace_forward_twice_in_a_row():
         want = bd.fwd(p, *[t[k] for k in INPUT_NAMES])
         torch.cuda.synchronize()
         for a, b in zip(got, want):
+            assert torch.equal(a, b)
+
+
+def test_noalloc_forward_with_claimed_work(monkeypatch):
+    """Work claimed from the queue counters (forced on: these problems are
+    small) in the scratch array: every call starts them at zero, so three
+    calls in a row (large, small, large) each equal bdattn_fwd bitwise, with
+    no output left unwritten."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    monkeypatch.setenv("BDATTN_CLAIM", "1")
+    big = small_spec(L=4096, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=34)
+    small = small_spec(L=1024, B=16, H=4, Hkv=2, d=128, dtype="bf16", std=0.5, seed=35)
+    for spec in (big, small, big):
+        print(f"[gpu] no-alloc forward, claimed work: {spec.name} L={spec.n_clean_q}", flush=True)
+        t = make_inputs(spec, device="cuda")
+        p = bd.from_spec(spec)
+        st, got = _noalloc(p, t)
+        assert st == 0, bd.lib().bdattn_last_error().decode()
+        want = bd.fwd(p, *[t[k] for k in INPUT_NAMES])
+        torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert not torch.isnan(a).any().item()
             assert torch.equal(a, b)
 
 
