@@ -57,27 +57,18 @@ constexpr float kRescaleMargin = 0.f;
 
 // The work item of this workgroup (the protocol is described with
 // kClaimQueues in plan.h): with ctr == nullptr item blockIdx.x of a grid of n;
-// else thread 0 claims one from the counters ctr[0..kClaimQueues) of a grid
-// of n + claim_extra(n) and the workgroup reads it from LDS; -1 when every
-// queue is empty (the workgroup then ends). Each item is claimed exactly once:
-// a claim is one atomic add, counters only grow, and a workgroup gives up
-// only after it has seen every queue empty.
+// else thread 0 claims one (claim_next) from the counters
+// ctr[0..kClaimQueues) of a grid of n + claim_extra(n), starting with queue
+// blockIdx.x mod 8, and the workgroup reads it from LDS; -1 when every queue
+// is empty (the workgroup then ends).
 __device__ __forceinline__ int claim_item(int32_t* ctr, int n) {
   __shared__ int s_item;
   if (ctr == nullptr) return blockIdx.x;
-  if (threadIdx.x == 0) {
-    int item = -1;
-    const int home = blockIdx.x % kClaimQueues;
-    for (int v = 0; v < kClaimQueues && item < 0; ++v) {
-      const int y = (home + v) % kClaimQueues;
-      const int len = n > y ? (n - y + kClaimQueues - 1) / kClaimQueues : 0;
-      if (v && __hip_atomic_load(ctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len)
-        continue;
-      const int c = __hip_atomic_fetch_add(ctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (c >= 0 && c < len) item = y + kClaimQueues * c;  // (c < 0: a clobbered counter)
-    }
-    s_item = item;
-  }
+  if (threadIdx.x == 0)
+    s_item = claim_next(
+        blockIdx.x % kClaimQueues, n,
+        [&](int y) { return __hip_atomic_load(ctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+        [&](int y) { return __hip_atomic_fetch_add(ctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); });
   __syncthreads();
   return s_item;
 }

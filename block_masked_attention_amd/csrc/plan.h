@@ -46,6 +46,26 @@ constexpr int kClaimQueues = 8;
 constexpr int kClaimCounters = 3 * kClaimQueues;  // forward or dQ, dK/dV, spare
 BD_HD int32_t claim_extra(int32_t n) { return kClaimQueues * ((n + 31) / 32); }  // n / 4, rounded up
 
+// One claim: the next item of the first queue, from `home` on, that still
+// holds one, or -1 when every queue is empty. load(y) reads counter y (an
+// older value is harmless: the counters only grow, so it can only cost an
+// extra fetch_add); fetch_add(y) adds 1 to counter y and returns its old
+// value. Each item is returned exactly once over all claims: queue y's items
+// go to the fetch_adds that return 0 .. len - 1, and a claim gives up only
+// after seeing every queue at or past its length. (A negative counter, which
+// only a clobbered workspace can hold, yields no item.)
+template <class Load, class FetchAdd>
+BD_HD int32_t claim_next(int home, int32_t n, Load load, FetchAdd fetch_add) {
+  for (int v = 0; v < kClaimQueues; ++v) {
+    const int y = (home + v) % kClaimQueues;
+    const int32_t len = n > y ? (n - y + kClaimQueues - 1) / kClaimQueues : 0;
+    if (v && load(y) >= len) continue;
+    const int32_t c = fetch_add(y);
+    if (c >= 0 && c < len) return y + kClaimQueues * c;
+  }
+  return -1;
+}
+
 // One forward work item: `tile` of `rows` query rows (stream bit 0 of hs),
 // head group hs >> 1 (Gw consecutive q heads).
 struct FwdItem {
