@@ -70,7 +70,9 @@ __device__ __forceinline__ int claim_item(int32_t* ctr, int n) {
         [&](int y) { return __hip_atomic_load(ctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
         [&](int y) { return __hip_atomic_fetch_add(ctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); });
   __syncthreads();
-  return s_item;
+  // (the same in every lane: as a scalar, the work item's fields load into
+  // scalar registers and the code that decodes them stays scalar)
+  return __builtin_amdgcn_readfirstlane(s_item);
 }
 
 // 2^x with one v_exp_f32 (results below 2^-126 flush to zero, which is
@@ -237,8 +239,9 @@ struct OperandReads {
   }
 };
 
-// Row bounds of local row `row` of a query stream (0 clean, 1 corrupted), in
-// terms of the keys present: clean buffer indices and local corrupted keys.
+// Row bounds of local rows of a query stream (0 clean, 1 corrupted), in
+// terms of the keys present (clean buffer indices and local corrupted keys),
+// from this description of the problem.
 struct RowSpace {
   int32_t clean_q_start, B;
   const int32_t* ids;
@@ -247,12 +250,28 @@ struct RowSpace {
   bool corr_keys;    // the local corrupted keys are present
   const BdDocSpan* docs;  // document of each global block (nullptr: one document)
 };
-__device__ __forceinline__ BdRowBounds row_bounds(int stream, int32_t row, const RowSpace& rs) {
-  BdRowBounds r = stream == 0 ? bd_clean_row(rs.clean_q_start + row, rs.B, rs.token_causal)
-                              : bd_corr_row(row, rs.ids[row / rs.B], rs.B);
-  if (rs.docs)  // the document of the row's block (a corrupted row's: its id's)
-    r = bd_in_document(r, rs.docs[stream == 0 ? (rs.clean_q_start + row) / rs.B : rs.ids[row / rs.B]]);
-  return bd_in_buffer(r, rs.kv0, rs.nkv, rs.corr_keys);
+// Bounds of three rows of one stream at once. Every table load (block ids,
+// then documents) is issued before any is used, so their round trips overlap
+// (a work item's start waits on them).
+__device__ __forceinline__ void row_bounds3(int stream, const int32_t (&row)[3], const RowSpace& rs,
+                                            BdRowBounds (&out)[3]) {
+  int32_t id[3] = {0, 0, 0};
+  if (stream) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) id[i] = rs.ids[row[i] / rs.B];
+  }
+  BdDocSpan sp[3];
+  if (rs.docs) {  // the document of the row's block (a corrupted row's: its id's)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) sp[i] = rs.docs[stream == 0 ? (rs.clean_q_start + row[i]) / rs.B : id[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    BdRowBounds r = stream == 0 ? bd_clean_row(rs.clean_q_start + row[i], rs.B, rs.token_causal)
+                                : bd_corr_row(row[i], id[i], rs.B);
+    if (rs.docs) r = bd_in_document(r, sp[i]);
+    out[i] = bd_in_buffer(r, rs.kv0, rs.nkv, rs.corr_keys);
+  }
 }
 
 // Buffer rows of the clean key tiles of a gathered buffer: map[j] is the

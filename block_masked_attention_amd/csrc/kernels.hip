@@ -71,9 +71,10 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
   q.my_row = q.row0 + (wave / Gw) * 32 + lq;
   q.row_ok = q.my_row < q.n_rows;
   q.crow = min(q.my_row, q.n_rows - 1);
-  q.rb = row_bounds(q.stream, q.crow, rs);
-  const BdRowBounds first = row_bounds(q.stream, q.row0, rs);
-  const BdRowBounds last = row_bounds(q.stream, row_end - 1, rs);
+  BdRowBounds b[3];  // this lane's row, the item's first and last rows
+  row_bounds3(q.stream, {q.crow, q.row0, row_end - 1}, rs, b);
+  q.rb = b[0];
+  const BdRowBounds first = b[1], last = b[2];
   q.j0 = DOCS ? first.clo / TK : 0;
   // (with documents, rows that see no clean key at all sweep none)
   q.n_ct = DOCS && last.cb <= first.clo ? q.j0 : (last.cb + TK - 1) / TK;
