@@ -22,12 +22,12 @@ namespace bdattn {
 constexpr int FWD_WAVES = BDATTN_FWD_WAVES;
 constexpr int FWD_ROWS_PER_WAVE = 32;
 constexpr int FWD_TK = 64;
-// Backward dK/dV: a workgroup of 4 waves owns BWD_TK keys of one KV head (32
-// per wave) and sweeps the query rows that see them in tiles of BWD_TQ.
+// Backward dK/dV: a workgroup owns BWD_TK keys of one KV head, 32 per SIMD
+// (two waves of 64 lanes each in the split kernel), and sweeps the query rows
+// that see them in tiles of BWD_TQ.
 #ifndef BDATTN_BWD_TQ
 #define BDATTN_BWD_TQ 64
 #endif
-constexpr int BWD_WAVES = 4;
 constexpr int BWD_TK = 128;
 constexpr int BWD_TQ = BDATTN_BWD_TQ;
 
