@@ -373,6 +373,41 @@ bool claim_on(size_t n_items, int64_t steps) {
   return n_items >= 4096 && steps >= 32 * int64_t(n_items);
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+  static std::mutex mu;
+  static int count[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!count[dev] &&
+      hipDeviceGetAttribute(&count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    count[dev] = 0;
+  return count[dev];
+}
+
+// Persistent grid for a query-tile list of n_items items that sweep `steps`
+// tiles in all, when not claiming one item per workgroup: one workgroup per
+// CU, each claiming item after item from the queues, pays when items are
+// short (under 128 tiles on average, so that an item's start-up and the
+// latency of its stores weigh) and there are more items than CUs. Returns
+// the grid size, or 0. BDATTN_PERSIST=0 / 1 forces it off / on (on: whenever
+// there are more items than CUs).
+// The persistent query-tile kernels are built for bf16 at head dim 128, the
+// default precision and a clean K/V buffer in position order.
+bool persist_kernels(const bdattn::Problem& P) {
+  return P.dtype == BDATTN_BF16 && P.d == 128 && P.precision == 0 && P.kv_map.empty();
+}
+
+int32_t persist_grid(size_t n_items, int64_t steps, bool claiming) {
+  const char* e = getenv("BDATTN_PERSIST");
+  if (claiming || (e && !strcmp(e, "0"))) return 0;
+  const int cus = cu_count();
+  if (cus <= 0 || n_items <= size_t(cus)) return 0;
+  if (e && !strcmp(e, "1")) return cus;
+  return steps < 128 * int64_t(n_items) ? cus : 0;
+}
+
 }  // namespace
 
 const bdattn::KernelEvents* bdattn::profile_events(int first, int n, KernelEvents* ev) {
@@ -570,6 +605,8 @@ int fwd_impl(const bdattn_problem* p, const void* q_c, const void* k_c, const vo
   a.items = (const bdattn::FwdItem*)(ws + w.q_items);
   a.n_items = int32_t(plan->fwd.size());
   a.claim = claim_on(plan->fwd.size(), plan->fwd_tiles) ? (int32_t*)(ws + w.claim) : nullptr;
+  a.persist = persist_kernels(P) ? persist_grid(plan->fwd.size(), plan->fwd_tiles, a.claim != nullptr) : 0;
+  if (a.persist) a.claim = (int32_t*)(ws + w.claim);  // the persistent grid claims its items
   a.B = P.B; a.H = P.H; a.Hkv = P.Hkv; a.Gw = plan->Gw; a.rows_per_item = plan->fwd_rows;
   a.n_clean_q = P.n_clean_q; a.clean_q_start = P.clean_q_start; a.n_clean_kv = P.n_clean_kv;
   a.n_corr = P.n_corr();
@@ -648,6 +685,8 @@ int bdattn_bwd(const bdattn_problem* p, const void* q_c, const void* k_c, const 
   int32_t* const ctr = (int32_t*)(ws + w.claim);
   a.claim_q = claim_on(plan->fwd.size(), plan->fwd_tiles) ? ctr : nullptr;
   a.claim_kv = claim_on(plan->bwd.size(), plan->bwd_qtiles) ? ctr + bdattn::kClaimQueues : nullptr;
+  a.persist = persist_kernels(P) ? persist_grid(plan->fwd.size(), plan->fwd_tiles, a.claim_q != nullptr) : 0;
+  if (a.persist) a.claim_q = ctr;  // the persistent grid claims its items
   a.d_c = (float*)(ws + w.d_c);
   a.d_x = (float*)(ws + w.d_x);
   a.l2_c = (float*)(ws + w.l2_c);

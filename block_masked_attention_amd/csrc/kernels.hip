@@ -89,7 +89,7 @@ __device__ __forceinline__ QTile q_tile(const FwdItem& it, int rows_per_item, in
 // Forward. Per key tile: S^T = K Q^T (keys x queries, so each lane owns one
 // query row); mask only on tiles that need it; online softmax; O^T += V^T P^T.
 // ======================================================================
-template <bool BF16, int D, bool DOCS, bool MAPPED, int PREC>
+template <bool BF16, int D, bool DOCS, bool MAPPED, int PREC, bool PERSIST = false>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   // bdattn_precision: float32 O (>= 1); P as two bf16 terms in P V (2)
@@ -108,178 +108,183 @@ void fwd_kernel(FwdArgs a) {
   const int lq = lane & 31, hf = lane >> 5;
   const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
                     a.n_clean_kv, a.corr_keys != 0, DOCS ? a.docs : nullptr};
-  const int wi = claim_item(a.claim, a.n_items);
-  if (wi < 0) return;  // every item taken (the whole workgroup)
-  const QTile q = q_tile<TK, DOCS>(a.items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
-                             a.n_clean_q, a.n_corr, rs, wave, lq);
-  const int n_tiles = q.n_ct + q.n_xt;
-  const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
+  // The workgroup's items: the one claim_item gives it, or, when PERSIST, one
+  // claim after another until every queue is empty (a short work list on a
+  // grid of one workgroup per CU: each next item starts while the previous
+  // one's stores are in flight, with no workgroup launch in between).
+  for (int wi = claim_item(a.claim, a.n_items); wi >= 0 && wi < a.n_items;
+       wi = PERSIST ? claim_item(a.claim, a.n_items) : -1) {
+    const QTile q = q_tile<TK, DOCS>(a.items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
+                               a.n_clean_q, a.n_corr, rs, wave, lq);
+    const int n_tiles = q.n_ct + q.n_xt;
+    const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
 
-  // Q as the B operand of S^T = K Q^T: column = this lane's row, natural over d
-  Frag qf[D / 16];
-  {
-    const T* qrow = qsrc + ((int64_t)q.crow * a.H + q.head) * D;
+    // Q as the B operand of S^T = K Q^T: column = this lane's row, natural over d
+    Frag qf[D / 16];
+    {
+      const T* qrow = qsrc + ((int64_t)q.crow * a.H + q.head) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = q.row_ok ? E::load(qrow + 16 * ks + 8 * hf) : E::zero();
-  }
-
-  TileCopy<T, TK, D, FWD_WAVES> cp;
-  cp.init(wave, lane, (int64_t)a.Hkv * D);
-  const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
-  const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
-  const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
-  const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
-  // gathered buffer (MAPPED): clean key tile j (position order) sits at
-  // buffer tile kv_map[j]; the masks keep working in position order
-  KeyTileMap<TK> km;
-  if constexpr (MAPPED) {
-    if (q.n_ct > q.j0) km.init(a.kv_map, a.n_kv_map, q.j0, lane);
-  }
-  // stage key tile j (K then V) into LDS buffer `buf`
-  auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
-    const bool cl = j < q.n_ct;
-    int k0;
-    if constexpr (MAPPED) k0 = cl ? km.row(j, lane) : q.xlo + (j - q.n_ct) * TK;
-    else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
-    const int nk = cl ? a.n_clean_kv : a.n_corr;
-    T* dst = smem + buf * 2 * TSZ;
-    cp.issue(dst, cl ? kc : kx, k0, nk);
-    cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
-  };
-
-  OperandReads<BF16, D> rd;
-  rd.init(lane);
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) o[i] = zero16();
-  float m = kNegInf, l = 0.f;  // running reference maximum (log2 units), row sum
-
-  // one key tile in LDS buffer BUF (the next one is copied into the other)
-  auto body = [&](auto mask_tag, auto buf_tag, int j) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int BUF = decltype(buf_tag)::value;
-    constexpr uint32_t KT = BUF * 2 * TB, VT = KT + TB;
-    if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
-    const bool cl = j < q.n_ct;
-    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
-
-    // S of both key blocks, alternating blocks: product k = (ks, mb)
-    f32x16 s[TK / 32];
-#pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) s[mb] = zero16();
-    product_chain<TK / 32 * D / 16, kReadAhead, Frag>(
-        [&](int k) __attribute__((always_inline)) { return rd.template row_frag<KT>(smem, k % (TK / 32), k / (TK / 32)); },
-        [&](int k, const Frag& f) __attribute__((always_inline)) { E::mma(s[k % (TK / 32)], f, qf[k / (TK / 32)]); });
-    // online softmax; the row max is taken on raw scores (the scale is > 0)
-    // and the scale folded into the exponent's multiply-add
-    float mx = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (MASK) {
-          const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          // (documents: clo <= key < cb as one unsigned compare; a test of the
-          // same form as the corrupted one lets the compiler pick the bound
-          // fields by address, which moves the bounds to scratch memory)
-          const bool vis = cl ? (DOCS ? uint32_t(key - q.rb.clo) < uint32_t(q.rb.cb - q.rb.clo)
-                                      : key < q.rb.cb)
-                              : bd_sees_corr(q.rb, key);
-          s[mb][i] = vis ? s[mb][i] : kNegInf;
-        }
-        mx = fmaxf(mx, s[mb][i]);
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = q.row_ok ? E::load(qrow + 16 * ks + 8 * hf) : E::zero();
     }
-    mx = max_halves(mx) * a.scale_log2;
-    if (__any(mx > m + kRescaleMargin)) {  // some row's maximum moved (wave-uniform)
-      const float m_new = fmaxf(m, mx);
-      const float alpha = m == kNegInf ? 0.f : fast_exp2(m - m_new);
-      l *= alpha;
+
+    TileCopy<T, TK, D, FWD_WAVES> cp;
+    cp.init(wave, lane, (int64_t)a.Hkv * D);
+    const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
+    const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
+    const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
+    const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
+    // gathered buffer (MAPPED): clean key tile j (position order) sits at
+    // buffer tile kv_map[j]; the masks keep working in position order
+    KeyTileMap<TK> km;
+    if constexpr (MAPPED) {
+      if (q.n_ct > q.j0) km.init(a.kv_map, a.n_kv_map, q.j0, lane);
+    }
+    // stage key tile j (K then V) into LDS buffer `buf`
+    auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
+      const bool cl = j < q.n_ct;
+      int k0;
+      if constexpr (MAPPED) k0 = cl ? km.row(j, lane) : q.xlo + (j - q.n_ct) * TK;
+      else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+      const int nk = cl ? a.n_clean_kv : a.n_corr;
+      T* dst = smem + buf * 2 * TSZ;
+      cp.issue(dst, cl ? kc : kx, k0, nk);
+      cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
+    };
+
+    OperandReads<BF16, D> rd;
+    rd.init(lane);
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = zero16();
+    float m = kNegInf, l = 0.f;  // running reference maximum (log2 units), row sum
+
+    // one key tile in LDS buffer BUF (the next one is copied into the other)
+    auto body = [&](auto mask_tag, auto buf_tag, int j) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr int BUF = decltype(buf_tag)::value;
+      constexpr uint32_t KT = BUF * 2 * TB, VT = KT + TB;
+      if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
+      const bool cl = j < q.n_ct;
+      const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+
+      // S of both key blocks, alternating blocks: product k = (ks, mb)
+      f32x16 s[TK / 32];
+#pragma unroll
+      for (int mb = 0; mb < TK / 32; ++mb) s[mb] = zero16();
+      product_chain<TK / 32 * D / 16, kReadAhead, Frag>(
+          [&](int k) __attribute__((always_inline)) { return rd.template row_frag<KT>(smem, k % (TK / 32), k / (TK / 32)); },
+          [&](int k, const Frag& f) __attribute__((always_inline)) { E::mma(s[k % (TK / 32)], f, qf[k / (TK / 32)]); });
+      // online softmax; the row max is taken on raw scores (the scale is > 0)
+      // and the scale folded into the exponent's multiply-add
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < TK / 32; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (MASK) {
+            const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            // (documents: clo <= key < cb as one unsigned compare; a test of the
+            // same form as the corrupted one lets the compiler pick the bound
+            // fields by address, which moves the bounds to scratch memory)
+            const bool vis = cl ? (DOCS ? uint32_t(key - q.rb.clo) < uint32_t(q.rb.cb - q.rb.clo)
+                                        : key < q.rb.cb)
+                                : bd_sees_corr(q.rb, key);
+            s[mb][i] = vis ? s[mb][i] : kNegInf;
+          }
+          mx = fmaxf(mx, s[mb][i]);
+        }
+      }
+      mx = max_halves(mx) * a.scale_log2;
+      if (__any(mx > m + kRescaleMargin)) {  // some row's maximum moved (wave-uniform)
+        const float m_new = fmaxf(m, mx);
+        const float alpha = m == kNegInf ? 0.f : fast_exp2(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+        m = m_new;
+      }
+      const float m_use = m == kNegInf ? 0.f : m;
+      // the row sum adds the fp32 weights: LSE must be exact, since the
+      // backward rebuilds P from it (summing the bf16-rounded weights instead
+      // shifts LSE by up to 2^-9 and scales every recomputed P of the row)
+      Frag pf[TK / 32][2], pl[TK / 32][2];  // P (and its remainder when SPLIT)
+      float rs = 0.f;
+      // weights of the 16-key slice mt (8 per lane), elements [i0, i1); packed
+      // to bf16 once complete
+      float pv[8];
+      auto weights = [&](int mt, int i0, int i1) __attribute__((always_inline)) {
+        const int mb = mt / 2, h = mt % 2;
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+          pv[i] = fast_exp2(fmaf(s[mb][8 * h + i], a.scale_log2, -m_use));
+          rs += pv[i];
+        }
+        if (i1 == 8) {
+          if constexpr (SPLIT) split_pack(pv, pf[mb][h], pl[mb][h]);
+          else pf[mb][h] = E::pack(pv);
+        }
+      };
+      // O += V^T P over the tile's keys: product k = (16-key slice mt, column
+      // block db). Slice 0's weights come first; slice mt + 1's are computed
+      // between the products of slice mt (same values and summation order as
+      // computing them all first).
+      constexpr int PS = D / 32;   // products per slice
+      constexpr int EPP = 8 / PS;  // weights computed after each product
+      weights(0, 0, 8);
+      product_chain_hooked<TK / 32 * 2 * PS, kReadAhead, Frag>(
+          [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<VT>(smem, 16 * (k / PS), k % PS); },
+          [&](int k, const Frag& y) __attribute__((always_inline)) {
+            const int mt = k / PS;
+            E::mma(o[k % PS], y, pf[mt / 2][mt % 2]);
+            if constexpr (SPLIT) E::mma(o[k % PS], y, pl[mt / 2][mt % 2]);
+          },
+          [&](int k) __attribute__((always_inline)) {
+            const int mt = k / PS, db = k % PS;
+            if (mt + 1 < TK / 16) weights(mt + 1, db * EPP, (db + 1) * EPP);
+          });
+      l += rs;
+      lds_dma_wait();
+      __syncthreads();
+    };
+    auto sweep = [&](auto mask_tag, int j0, int j1) __attribute__((always_inline)) {
+      int j = j0;
+      if (j < j1 && (j & 1)) body(mask_tag, Int<1>{}, j++);
+      for (; j + 1 < j1; j += 2) {
+        body(mask_tag, Int<0>{}, j);
+        body(mask_tag, Int<1>{}, j + 1);
+      }
+      if (j < j1) body(mask_tag, Int<0>{}, j);
+    };
+    if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
+    vm_drain();
+    __syncthreads();
+    // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
+    if constexpr (DOCS) sweep(std::true_type{}, q.j0, q.jf0);
+    sweep(std::false_type{}, q.jf0, q.jf1);
+    sweep(std::true_type{}, q.jf1, n_tiles);
+
+    const float lt = l + __shfl_xor(l, 32);
+    if (q.row_ok) {
+      // a row that sees no key present (partial problems): O = 0, LSE = -inf
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int64_t orow = ((int64_t)q.my_row * a.H + q.head) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        for (int g = 0; g < 4; ++g)
+          store_out<E, OF32>(q.stream ? a.o_x : a.o_c, orow + 32 * db + 8 * g + 4 * hf,
+                             o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                             o[db][4 * g + 3] * inv);
       }
-      m = m_new;
-    }
-    const float m_use = m == kNegInf ? 0.f : m;
-    // the row sum adds the fp32 weights: LSE must be exact, since the
-    // backward rebuilds P from it (summing the bf16-rounded weights instead
-    // shifts LSE by up to 2^-9 and scales every recomputed P of the row)
-    Frag pf[TK / 32][2], pl[TK / 32][2];  // P (and its remainder when SPLIT)
-    float rs = 0.f;
-    // weights of the 16-key slice mt (8 per lane), elements [i0, i1); packed
-    // to bf16 once complete
-    float pv[8];
-    auto weights = [&](int mt, int i0, int i1) __attribute__((always_inline)) {
-      const int mb = mt / 2, h = mt % 2;
-#pragma unroll
-      for (int i = i0; i < i1; ++i) {
-        pv[i] = fast_exp2(fmaf(s[mb][8 * h + i], a.scale_log2, -m_use));
-        rs += pv[i];
+      if (hf == 0) {
+        float* lse = q.stream ? a.lse_x : a.lse_c;
+        lse[(int64_t)q.head * q.n_rows + q.my_row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : kNegInf;
       }
-      if (i1 == 8) {
-        if constexpr (SPLIT) split_pack(pv, pf[mb][h], pl[mb][h]);
-        else pf[mb][h] = E::pack(pv);
-      }
-    };
-    // O += V^T P over the tile's keys: product k = (16-key slice mt, column
-    // block db). Slice 0's weights come first; slice mt + 1's are computed
-    // between the products of slice mt (same values and summation order as
-    // computing them all first).
-    constexpr int PS = D / 32;   // products per slice
-    constexpr int EPP = 8 / PS;  // weights computed after each product
-    weights(0, 0, 8);
-    product_chain_hooked<TK / 32 * 2 * PS, kReadAhead, Frag>(
-        [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<VT>(smem, 16 * (k / PS), k % PS); },
-        [&](int k, const Frag& y) __attribute__((always_inline)) {
-          const int mt = k / PS;
-          E::mma(o[k % PS], y, pf[mt / 2][mt % 2]);
-          if constexpr (SPLIT) E::mma(o[k % PS], y, pl[mt / 2][mt % 2]);
-        },
-        [&](int k) __attribute__((always_inline)) {
-          const int mt = k / PS, db = k % PS;
-          if (mt + 1 < TK / 16) weights(mt + 1, db * EPP, (db + 1) * EPP);
-        });
-    l += rs;
-    lds_dma_wait();
-    __syncthreads();
-  };
-  auto sweep = [&](auto mask_tag, int j0, int j1) __attribute__((always_inline)) {
-    int j = j0;
-    if (j < j1 && (j & 1)) body(mask_tag, Int<1>{}, j++);
-    for (; j + 1 < j1; j += 2) {
-      body(mask_tag, Int<0>{}, j);
-      body(mask_tag, Int<1>{}, j + 1);
-    }
-    if (j < j1) body(mask_tag, Int<0>{}, j);
-  };
-  if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
-  vm_drain();
-  __syncthreads();
-  // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
-  if constexpr (DOCS) sweep(std::true_type{}, q.j0, q.jf0);
-  sweep(std::false_type{}, q.jf0, q.jf1);
-  sweep(std::true_type{}, q.jf1, n_tiles);
-
-  const float lt = l + __shfl_xor(l, 32);
-  if (q.row_ok) {
-    // a row that sees no key present (partial problems): O = 0, LSE = -inf
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int64_t orow = ((int64_t)q.my_row * a.H + q.head) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store_out<E, OF32>(q.stream ? a.o_x : a.o_c, orow + 32 * db + 8 * g + 4 * hf,
-                           o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
-                           o[db][4 * g + 3] * inv);
-    }
-    if (hf == 0) {
-      float* lse = q.stream ? a.lse_x : a.lse_c;
-      lse[(int64_t)q.head * q.n_rows + q.my_row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : kNegInf;
     }
   }
 }
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* oa_, const float
 // D are scalars); P^T = exp2(S^T c - LSE2); dS^T = P^T (dP^T - D);
 // dQ^T += K^T dS^T with K^T read transposed from the K tile.
 // ======================================================================
-template <bool BF16, int D, bool DOCS, bool MAPPED, int PREC>
+template <bool BF16, int D, bool DOCS, bool MAPPED, int PREC, bool PERSIST = false>
 __global__ __launch_bounds__(FWD_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   // bdattn_precision: float32 dQ (>= 1); dS as two bf16 terms in dS K (2)
@@ -398,139 +403,144 @@ void bwd_dq_kernel(BwdArgs a) {
   const int lq = lane & 31, hf = lane >> 5;
   const RowSpace rs{a.clean_q_start, a.B, a.ids, a.token_causal != 0, a.clean_kv_start,
                     a.n_clean_kv, a.corr_keys != 0, DOCS ? a.docs : nullptr};
-  const int wi = claim_item(a.claim_q, a.n_q_items);
-  if (wi < 0) return;  // every item taken (the whole workgroup)
-  const QTile q = q_tile<TK, DOCS>(a.q_items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
-                             a.n_clean_q, a.n_corr, rs, wave, lq);
-  const int n_tiles = q.n_ct + q.n_xt;
-  const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
-  const T* gsrc = (const T*)(q.stream ? a.do_x : a.do_c);
+  // The workgroup's items: the one claim_item gives it, or, when PERSIST, one
+  // claim after another until every queue is empty (a short work list on a
+  // grid of one workgroup per CU: each next item starts while the previous
+  // one's stores are in flight, with no workgroup launch in between).
+  for (int wi = claim_item(a.claim_q, a.n_q_items); wi >= 0 && wi < a.n_q_items;
+       wi = PERSIST ? claim_item(a.claim_q, a.n_q_items) : -1) {
+    const QTile q = q_tile<TK, DOCS>(a.q_items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
+                               a.n_clean_q, a.n_corr, rs, wave, lq);
+    const int n_tiles = q.n_ct + q.n_xt;
+    const T* qsrc = (const T*)(q.stream ? a.q_x : a.q_c);
+    const T* gsrc = (const T*)(q.stream ? a.do_x : a.do_c);
 
-  Frag qf[D / 16], gf[D / 16];
-  {
-    const int64_t off = ((int64_t)q.crow * a.H + q.head) * D;
+    Frag qf[D / 16], gf[D / 16];
+    {
+      const int64_t off = ((int64_t)q.crow * a.H + q.head) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = q.row_ok ? E::load(qsrc + off + 16 * ks + 8 * hf) : E::zero();
-      gf[ks] = q.row_ok ? E::load(gsrc + off + 16 * ks + 8 * hf) : E::zero();
+      for (int ks = 0; ks < D / 16; ++ks) {
+        qf[ks] = q.row_ok ? E::load(qsrc + off + 16 * ks + 8 * hf) : E::zero();
+        gf[ks] = q.row_ok ? E::load(gsrc + off + 16 * ks + 8 * hf) : E::zero();
+      }
     }
-  }
-  const int64_t ri = (int64_t)q.head * row_pad(q.n_rows) + q.crow;
-  const float lse2 = q.row_ok ? (q.stream ? a.l2_x : a.l2_c)[ri] : __builtin_inff();
-  const float ndrow = q.row_ok ? (q.stream ? a.d_x : a.d_c)[ri] : 0.f;  // -D
+    const int64_t ri = (int64_t)q.head * row_pad(q.n_rows) + q.crow;
+    const float lse2 = q.row_ok ? (q.stream ? a.l2_x : a.l2_c)[ri] : __builtin_inff();
+    const float ndrow = q.row_ok ? (q.stream ? a.d_x : a.d_c)[ri] : 0.f;  // -D
 
-  TileCopy<T, TK, D, FWD_WAVES> cp;
-  cp.init(wave, lane, (int64_t)a.Hkv * D);
-  const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
-  const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
-  const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
-  const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
-  // gathered buffer (MAPPED): clean key tile j (position order) sits at
-  // buffer tile kv_map[j]; the masks keep working in position order
-  KeyTileMap<TK> km;
-  if constexpr (MAPPED) {
-    if (q.n_ct > q.j0) km.init(a.kv_map, a.n_kv_map, q.j0, lane);
-  }
-  // stage key tile j (K then V) into LDS buffer `buf`
-  auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
-    const bool cl = j < q.n_ct;
-    int k0;
-    if constexpr (MAPPED) k0 = cl ? km.row(j, lane) : q.xlo + (j - q.n_ct) * TK;
-    else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
-    const int nk = cl ? a.n_clean_kv : a.n_corr;
-    T* dst = smem + buf * 2 * TSZ;
-    cp.issue(dst, cl ? kc : kx, k0, nk);
-    cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
-  };
+    TileCopy<T, TK, D, FWD_WAVES> cp;
+    cp.init(wave, lane, (int64_t)a.Hkv * D);
+    const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
+    const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
+    const T* const vc = (const T*)a.v_c + (int64_t)q.kvh * D;
+    const T* const vx = (const T*)a.v_x + (int64_t)q.kvh * D;
+    // gathered buffer (MAPPED): clean key tile j (position order) sits at
+    // buffer tile kv_map[j]; the masks keep working in position order
+    KeyTileMap<TK> km;
+    if constexpr (MAPPED) {
+      if (q.n_ct > q.j0) km.init(a.kv_map, a.n_kv_map, q.j0, lane);
+    }
+    // stage key tile j (K then V) into LDS buffer `buf`
+    auto fetch = [&](int j, int buf) __attribute__((always_inline)) {
+      const bool cl = j < q.n_ct;
+      int k0;
+      if constexpr (MAPPED) k0 = cl ? km.row(j, lane) : q.xlo + (j - q.n_ct) * TK;
+      else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+      const int nk = cl ? a.n_clean_kv : a.n_corr;
+      T* dst = smem + buf * 2 * TSZ;
+      cp.issue(dst, cl ? kc : kx, k0, nk);
+      cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
+    };
 
-  OperandReads<BF16, D> rd;
-  rd.init(lane);
+    OperandReads<BF16, D> rd;
+    rd.init(lane);
 
-  f32x16 dq[D / 32];
+    f32x16 dq[D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
+    for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
 
-  auto body = [&](auto mask_tag, auto buf_tag, int j) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int BUF = decltype(buf_tag)::value;
-    constexpr uint32_t KT = BUF * 2 * TB, VT = KT + TB;
-    if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
-    const bool cl = j < q.n_ct;
-    const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
-    Frag sf[TK / 32][2], sl[TK / 32][2];  // dS (and its remainder when SPLIT)
+    auto body = [&](auto mask_tag, auto buf_tag, int j) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr int BUF = decltype(buf_tag)::value;
+      constexpr uint32_t KT = BUF * 2 * TB, VT = KT + TB;
+      if (j + 1 < n_tiles) fetch(j + 1, BUF ^ 1);
+      const bool cl = j < q.n_ct;
+      const int k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
+      Frag sf[TK / 32][2], sl[TK / 32][2];  // dS (and its remainder when SPLIT)
 #pragma unroll
-    for (int mb = 0; mb < TK / 32; ++mb) {
-      // S and dP of key block mb, alternating: even k S (K rows), odd k dP (V rows)
-      f32x16 s = zero16(), dp = zero16();
-      product_chain<2 * D / 16, kReadAhead, Frag>(
-          [&](int k) __attribute__((always_inline)) {
-            return (k & 1) ? rd.template row_frag<VT>(smem, mb, k / 2) : rd.template row_frag<KT>(smem, mb, k / 2);
-          },
-          [&](int k, const Frag& f) __attribute__((always_inline)) {
-            if (k & 1) E::mma(dp, f, gf[k / 2]);
-            else E::mma(s, f, qf[k / 2]);
-          });
-      float ds[16];
+      for (int mb = 0; mb < TK / 32; ++mb) {
+        // S and dP of key block mb, alternating: even k S (K rows), odd k dP (V rows)
+        f32x16 s = zero16(), dp = zero16();
+        product_chain<2 * D / 16, kReadAhead, Frag>(
+            [&](int k) __attribute__((always_inline)) {
+              return (k & 1) ? rd.template row_frag<VT>(smem, mb, k / 2) : rd.template row_frag<KT>(smem, mb, k / 2);
+            },
+            [&](int k, const Frag& f) __attribute__((always_inline)) {
+              if (k & 1) E::mma(dp, f, gf[k / 2]);
+              else E::mma(s, f, qf[k / 2]);
+            });
+        float ds[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
-        if (MASK) {
-          const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
-          // (documents: clo <= key < cb as one unsigned compare; a test of the
-          // same form as the corrupted one lets the compiler pick the bound
-          // fields by address, which moves the bounds to scratch memory)
-          const bool vis = cl ? (DOCS ? uint32_t(key - q.rb.clo) < uint32_t(q.rb.cb - q.rb.clo)
-                                      : key < q.rb.cb)
-                              : bd_sees_corr(q.rb, key);
-          p = vis ? p : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(s[i], a.scale_log2, -lse2));
+          if (MASK) {
+            const int key = k0 + 32 * mb + 8 * (i >> 2) + 4 * hf + (i & 3);
+            // (documents: clo <= key < cb as one unsigned compare; a test of the
+            // same form as the corrupted one lets the compiler pick the bound
+            // fields by address, which moves the bounds to scratch memory)
+            const bool vis = cl ? (DOCS ? uint32_t(key - q.rb.clo) < uint32_t(q.rb.cb - q.rb.clo)
+                                        : key < q.rb.cb)
+                                : bd_sees_corr(q.rb, key);
+            p = vis ? p : 0.f;
+          }
+          ds[i] = p * (dp[i] + ndrow);
         }
-        ds[i] = p * (dp[i] + ndrow);
+        if constexpr (SPLIT) {
+          split_pack(ds, sf[mb][0], sl[mb][0]);
+          split_pack(ds + 8, sf[mb][1], sl[mb][1]);
+        } else {
+          sf[mb][0] = E::pack(ds);
+          sf[mb][1] = E::pack(ds + 8);
+        }
       }
-      if constexpr (SPLIT) {
-        split_pack(ds, sf[mb][0], sl[mb][0]);
-        split_pack(ds + 8, sf[mb][1], sl[mb][1]);
-      } else {
-        sf[mb][0] = E::pack(ds);
-        sf[mb][1] = E::pack(ds + 8);
+      // dQ += K^T dS over the tile's keys: product k = (16-key slice mt, column block db)
+      product_chain<TK / 32 * 2 * (D / 32), kReadAhead, Frag>(
+          [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<KT>(smem, 16 * (k / (D / 32)), k % (D / 32)); },
+          [&](int k, const Frag& y) __attribute__((always_inline)) {
+            const int mt = k / (D / 32);
+            E::mma(dq[k % (D / 32)], y, sf[mt / 2][mt % 2]);
+            if constexpr (SPLIT) E::mma(dq[k % (D / 32)], y, sl[mt / 2][mt % 2]);
+          });
+      lds_dma_wait();
+      __syncthreads();
+    };
+    auto sweep = [&](auto mask_tag, int j0, int j1) __attribute__((always_inline)) {
+      int j = j0;
+      if (j < j1 && (j & 1)) body(mask_tag, Int<1>{}, j++);
+      for (; j + 1 < j1; j += 2) {
+        body(mask_tag, Int<0>{}, j);
+        body(mask_tag, Int<1>{}, j + 1);
       }
-    }
-    // dQ += K^T dS over the tile's keys: product k = (16-key slice mt, column block db)
-    product_chain<TK / 32 * 2 * (D / 32), kReadAhead, Frag>(
-        [&](int k) __attribute__((always_inline)) { return rd.template tr_frag<KT>(smem, 16 * (k / (D / 32)), k % (D / 32)); },
-        [&](int k, const Frag& y) __attribute__((always_inline)) {
-          const int mt = k / (D / 32);
-          E::mma(dq[k % (D / 32)], y, sf[mt / 2][mt % 2]);
-          if constexpr (SPLIT) E::mma(dq[k % (D / 32)], y, sl[mt / 2][mt % 2]);
-        });
-    lds_dma_wait();
+      if (j < j1) body(mask_tag, Int<0>{}, j);
+    };
+    if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
+    vm_drain();
     __syncthreads();
-  };
-  auto sweep = [&](auto mask_tag, int j0, int j1) __attribute__((always_inline)) {
-    int j = j0;
-    if (j < j1 && (j & 1)) body(mask_tag, Int<1>{}, j++);
-    for (; j + 1 < j1; j += 2) {
-      body(mask_tag, Int<0>{}, j);
-      body(mask_tag, Int<1>{}, j + 1);
-    }
-    if (j < j1) body(mask_tag, Int<0>{}, j);
-  };
-  if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
-  vm_drain();
-  __syncthreads();
-  // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
-  if constexpr (DOCS) sweep(std::true_type{}, q.j0, q.jf0);
-  sweep(std::false_type{}, q.jf0, q.jf1);
-  sweep(std::true_type{}, q.jf1, n_tiles);
+    // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
+    if constexpr (DOCS) sweep(std::true_type{}, q.j0, q.jf0);
+    sweep(std::false_type{}, q.jf0, q.jf1);
+    sweep(std::true_type{}, q.jf1, n_tiles);
 
-  if (q.row_ok) {
-    const int64_t orow = ((int64_t)q.my_row * a.H + q.head) * D;
+    if (q.row_ok) {
+      const int64_t orow = ((int64_t)q.my_row * a.H + q.head) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store_out<E, OF32>(q.stream ? a.dq_x : a.dq_c, orow + 32 * db + 8 * g + 4 * hf,
-                           dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
-                           dq[db][4 * g + 2] * a.scale, dq[db][4 * g + 3] * a.scale);
+        for (int g = 0; g < 4; ++g)
+          store_out<E, OF32>(q.stream ? a.dq_x : a.dq_c, orow + 32 * db + 8 * g + 4 * hf,
+                             dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
+                             dq[db][4 * g + 2] * a.scale, dq[db][4 * g + 3] * a.scale);
+      }
     }
   }
 }
@@ -539,6 +549,14 @@ template <bool BF16, int D, int PREC>
 hipError_t run_fwd_t(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
   const dim3 grid(a.n_items + (a.claim ? claim_extra(a.n_items) : 0)), block(FWD_WAVES * 64);
+  if constexpr (BF16 && D == 128 && PREC == 0) {
+    if (a.n_items > 0 && a.persist > 0) {  // (the host sets persist only without kv_map)
+      if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, false, PREC, true>), dim3(a.persist), block, 0, s, a);
+      else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, false, PREC, true>), dim3(a.persist), block, 0, s, a);
+      if (ev) (void)hipEventRecord(ev[0].stop, s);
+      return hipGetLastError();
+    }
+  }
   if (a.n_items > 0 && a.kv_map) {  // a gathered clean buffer
     if (a.docs) hipLaunchKernelGGL((fwd_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fwd_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);
@@ -586,10 +604,19 @@ hipError_t run_bwd_t(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   }
   if (ev) (void)hipEventRecord(ev[0].start, s);
   const dim3 grid(a.n_q_items + (a.claim_q ? claim_extra(a.n_q_items) : 0)), block(FWD_WAVES * 64);
-  if (a.n_q_items > 0 && a.kv_map) {  // a gathered clean buffer
+  bool launched = false;
+  if constexpr (BF16 && D == 128 && PREC == 0) {
+    if (a.n_q_items > 0 && a.persist > 0) {  // (the host sets persist only without kv_map)
+      if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false, PREC, true>), dim3(a.persist), block, 0, s, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false, PREC, true>), dim3(a.persist), block, 0, s, a);
+      launched = true;
+    }
+  }
+  if (launched || a.n_q_items <= 0) {
+  } else if (a.kv_map) {  // a gathered clean buffer
     if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);
-  } else if (a.n_q_items > 0) {
+  } else {
     if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false, PREC>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false, PREC>), grid, block, 0, s, a);
   }

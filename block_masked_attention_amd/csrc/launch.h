@@ -18,6 +18,7 @@ struct FwdArgs {
   const FwdItem* items;    // device work list
   int32_t n_items;
   int32_t* claim;          // kClaimQueues work-claim counters, or nullptr: workgroup i runs item i
+  int32_t persist;         // > 0: a grid of `persist` workgroups that claim items until none is left
   int32_t B, H, Hkv, Gw, rows_per_item;
   int32_t n_clean_q, clean_q_start, n_clean_kv, n_corr;
   int32_t token_causal;    // clean rows see their own block up to their position only
@@ -41,6 +42,7 @@ struct BwdArgs {
   const BwdItem* kv_items;  // dK/dV kernel: key-tile work list
   int32_t n_kv_items;
   int32_t *claim_q, *claim_kv;  // work-claim counters of the two lists, or nullptr (static)
+  int32_t persist;         // dQ kernel: > 0, a grid of `persist` workgroups that claim items until none is left
   float *d_c, *d_x;        // workspace: -D = -rowsum(dO * O)    [H][row_pad(n)]
   float *l2_c, *l2_x;      // workspace: LSE * log2(e), +inf pad [H][row_pad(n)]
   int32_t B, H, Hkv, Gw, rows_per_item;

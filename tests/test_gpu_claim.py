@@ -1,11 +1,13 @@
 """Work claiming on the GPU: the forward, dQ and dK/dV kernels take their work
 items from per-XCD queues with stealing (BDATTN_CLAIM=1; by default the host
 claims only for long lists of long items), or workgroup i runs item i
-(BDATTN_CLAIM=0). Every item computes the same values whichever
+(BDATTN_CLAIM=0); for short lists the forward and dQ kernels can also run on a
+persistent grid of one workgroup per CU that claims item after item
+(BDATTN_PERSIST=1). Every item computes the same values whichever
 workgroup runs it, so both schedules must give bitwise equal outputs; the
 outputs start as NaN, so an item that no workgroup ran would show. The
-claimed schedule runs three times per case (the steals differ from run to
-run) on the same workspaces, whose claim counters every call restarts. Cases: small problems with every descriptor option (packed documents,
+claimed schedules run three times each per case (the steals differ from run
+to run) on the same workspaces, whose claim counters every call restarts. Cases: small problems with every descriptor option (packed documents,
 a share's rows, a gathered buffer, GQA, fp32) and the 8K workload, whose
 1,024 query-tile and 2,048 key-tile items span all 256 CUs.
 
@@ -69,16 +71,22 @@ def _check(spec, monkeypatch):
     p = bd.from_spec(spec)
     ws = [torch.zeros(bd.workspace_size(p, k), dtype=torch.uint8, device="cuda") for k in (0, 1)]
     monkeypatch.setenv("BDATTN_CLAIM", "0")
+    monkeypatch.setenv("BDATTN_PERSIST", "0")
     want = _run(spec, t, ws)
     # a row with no visible key gets LSE = -inf and O = 0 (never NaN)
     assert not any(torch.isnan(x).any().item() for x in want), "static schedule left an output unwritten"
-    monkeypatch.setenv("BDATTN_CLAIM", "1")
-    for rep in range(3):
-        got = _run(spec, t, ws)
-        holes = [torch.isnan(x).any().item() for x in got]
-        same = [torch.equal(a, b) for a, b in zip(got, want)]
-        say(f"  {spec.name}: claimed schedule run {rep}: no NaN left {not any(holes)}, bitwise {same}")
-        assert not any(holes) and all(same)
+    # one item per workgroup, claimed; then a persistent grid claiming item
+    # after item (it applies to lists with more items than CUs)
+    for claim, persist in (("1", "0"), ("0", "1")):
+        monkeypatch.setenv("BDATTN_CLAIM", claim)
+        monkeypatch.setenv("BDATTN_PERSIST", persist)
+        for rep in range(3):
+            got = _run(spec, t, ws)
+            holes = [torch.isnan(x).any().item() for x in got]
+            same = [torch.equal(a, b) for a, b in zip(got, want)]
+            say(f"  {spec.name}: claim {claim} persist {persist} run {rep}: no NaN left "
+                f"{not any(holes)}, bitwise {same}")
+            assert not any(holes) and all(same)
 
 
 @pytest.mark.parametrize("spec", CASES, ids=lambda s: s.name)
@@ -90,3 +98,12 @@ def test_claimed_schedule_is_bitwise_the_static_one(spec, monkeypatch):
 def test_claimed_schedule_8k_workload(monkeypatch):
     _need_gpu()
     _check(config("8k"), monkeypatch)
+
+
+def test_persistent_grid_with_many_short_documents(monkeypatch):
+    """1,024 query-tile items of 64 documents: the host's choice for such a
+    list is the persistent grid, forced here against the static deal."""
+    _need_gpu()
+    starts = [0] + [256 * k + 32 * (k % 5) for k in range(1, 64)]
+    _check(small_spec(L=16384, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=12,
+                      doc_starts=starts, name="bf16 d128 64 documents"), monkeypatch)
