@@ -7,9 +7,11 @@ persistent grid of one workgroup per CU that claims item after item
 workgroup runs it, so both schedules must give bitwise equal outputs; the
 outputs start as NaN, so an item that no workgroup ran would show. The
 claimed schedules run three times each per case (the steals differ from run
-to run) on the same workspaces, whose claim counters every call restarts. Cases: small problems with every descriptor option (packed documents,
-a share's rows, a gathered buffer, GQA, fp32) and the 8K workload, whose
-1,024 query-tile and 2,048 key-tile items span all 256 CUs.
+to run) on the same workspaces, whose claim counters every call restarts.
+Cases: small problems with every descriptor option (packed documents, a
+share's rows, a gathered buffer, GQA, fp32), the 8K workload, whose 1,024
+query-tile and 2,048 key-tile items span all 256 CUs, and 64 short documents
+(1,024 short query-tile items: the persistent grid's case).
 
 The library reads the switch at every call.
 """
