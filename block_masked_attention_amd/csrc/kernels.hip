@@ -111,9 +111,12 @@ void fwd_kernel(FwdArgs a) {
   // The workgroup's items: the one claim_item gives it, or, when PERSIST, one
   // claim after another until every queue is empty (a short work list on a
   // grid of one workgroup per CU: each next item starts while the previous
-  // one's stores are in flight, with no workgroup launch in between).
-  for (int wi = claim_item(a.claim, a.n_items); wi >= 0 && wi < a.n_items;
-       wi = PERSIST ? claim_item(a.claim, a.n_items) : -1) {
+  // one's stores are in flight, with no workgroup launch in between; on long
+  // lists it is claimed during the previous item's start, beside its loads).
+  // (claimed ahead only on long lists: with few items per workgroup, a late
+  // claim balances the end of the list better)
+  const bool ahead = PERSIST && a.n_items >= 16 * a.persist;
+  for (int wi = claim_item(a.claim, a.n_items), next = -1; wi >= 0 && wi < a.n_items; wi = next) {
     const QTile q = q_tile<TK, DOCS>(a.items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
                                a.n_clean_q, a.n_corr, rs, wave, lq);
     const int n_tiles = q.n_ct + q.n_xt;
@@ -261,6 +264,9 @@ void fwd_kernel(FwdArgs a) {
       if (j < j1) body(mask_tag, Int<0>{}, j);
     };
     if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
+    if constexpr (PERSIST) {
+      if (ahead) next = claim_item(a.claim, a.n_items);
+    }
     vm_drain();
     __syncthreads();
     // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
@@ -285,6 +291,9 @@ void fwd_kernel(FwdArgs a) {
         float* lse = q.stream ? a.lse_x : a.lse_c;
         lse[(int64_t)q.head * q.n_rows + q.my_row] = lt > 0.f ? (m + log2f(lt)) * kLn2 : kNegInf;
       }
+    }
+    if constexpr (PERSIST) {
+      if (!ahead) next = claim_item(a.claim, a.n_items);
     }
   }
 }
@@ -406,9 +415,12 @@ void bwd_dq_kernel(BwdArgs a) {
   // The workgroup's items: the one claim_item gives it, or, when PERSIST, one
   // claim after another until every queue is empty (a short work list on a
   // grid of one workgroup per CU: each next item starts while the previous
-  // one's stores are in flight, with no workgroup launch in between).
-  for (int wi = claim_item(a.claim_q, a.n_q_items); wi >= 0 && wi < a.n_q_items;
-       wi = PERSIST ? claim_item(a.claim_q, a.n_q_items) : -1) {
+  // one's stores are in flight, with no workgroup launch in between; on long
+  // lists it is claimed during the previous item's start, beside its loads).
+  // (claimed ahead only on long lists: with few items per workgroup, a late
+  // claim balances the end of the list better)
+  const bool ahead = PERSIST && a.n_q_items >= 16 * a.persist;
+  for (int wi = claim_item(a.claim_q, a.n_q_items), next = -1; wi >= 0 && wi < a.n_q_items; wi = next) {
     const QTile q = q_tile<TK, DOCS>(a.q_items[wi], a.rows_per_item, a.Gw, a.H, a.Hkv,
                                a.n_clean_q, a.n_corr, rs, wave, lq);
     const int n_tiles = q.n_ct + q.n_xt;
@@ -524,6 +536,9 @@ void bwd_dq_kernel(BwdArgs a) {
       if (j < j1) body(mask_tag, Int<0>{}, j);
     };
     if (n_tiles > q.j0) fetch(q.j0, q.j0 & 1);
+    if constexpr (PERSIST) {
+      if (ahead) next = claim_item(a.claim_q, a.n_q_items);
+    }
     vm_drain();
     __syncthreads();
     // tiles [jf0, jf1) lie inside every row's clean interval and skip the mask
@@ -541,6 +556,9 @@ void bwd_dq_kernel(BwdArgs a) {
                              dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
                              dq[db][4 * g + 2] * a.scale, dq[db][4 * g + 3] * a.scale);
       }
+    }
+    if constexpr (PERSIST) {
+      if (!ahead) next = claim_item(a.claim_q, a.n_q_items);
     }
   }
 }
