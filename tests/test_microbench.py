@@ -33,3 +33,30 @@ def test_block_contents(op, v, l):
 def test_builds(tmp_path):
     exe = mfma_mix.build(str(tmp_path))
     assert (tmp_path / "mfma_mix").exists() and exe.endswith("mfma_mix")
+
+
+def test_power_block_contents():
+    """The power microbenchmark's loop block: four products over the two A and
+    two B operand sets (every pairing once), v vector instructions after each,
+    writing only v80..v95."""
+    from block_masked_attention_amd.microbench import mfma_power
+    for v in mfma_power.VALU_COUNTS:
+        lines = mfma_power.block(v).split("\\n\\t")
+        mf = [x for x in lines if x.startswith("v_mfma_f32_32x32x16_bf16")]
+        assert len(mf) == 4 and len(lines) == 4 + 4 * v
+        pairs = {tuple(x.replace(",", "").split()[2:4]) for x in mf}
+        assert pairs == {("v[64:67]", "v[68:71]"), ("v[72:75]", "v[76:79]"),
+                         ("v[64:67]", "v[76:79]"), ("v[72:75]", "v[68:71]")}
+        accs = [x.replace(",", "").split()[1] for x in mf]
+        assert accs == [f"v[{16 * m}:{16 * m + 15}]" for m in range(4)]
+        for x in lines:
+            if x.startswith("v_fma_f32"):
+                assert 80 <= int(x.split()[1].rstrip(",")[1:]) < 96
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not __import__("os").path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not installed")
+def test_power_builds(tmp_path):
+    from block_masked_attention_amd.microbench import mfma_power
+    exe = mfma_power.build(str(tmp_path))
+    assert (tmp_path / "mfma_power").exists() and exe.endswith("mfma_power")
