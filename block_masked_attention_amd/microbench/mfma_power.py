@@ -6,7 +6,7 @@ One workgroup of 8 waves per CU (two per SIMD; it holds 100 KiB of LDS, so no
 second one fits). Each wave repeats one inline-assembly block of four
 independent `v_mfma_f32_32x32x16_bf16`, which alternate between two A and two
 B operand sets (A0 B0, A1 B1, A0 B1, A1 B0), each product followed by V
-`v_fma_f32` on independent registers. The operands come from a buffer filled
+`v_fma_f32` on independent registers and L `ds_read_b128` (1 KiB per wave). The operands come from a buffer filled
 on the host, either with zeros or with bf16 values drawn from N(0, 0.25) (the
 attention inputs' distribution), distinct per wave and lane; the accumulators
 start at zero. One launch runs for about half a second; the wall time of the
@@ -19,8 +19,8 @@ Usage (on the GPU machine, from the repository root):
 
     python -m block_masked_attention_amd.microbench.mfma_power [--out DIR]
 
-prints one line per (data, vector instructions per product) and a markdown
-table.
+prints one line per (data, vector instructions and LDS reads per product)
+and a markdown table.
 """
 from __future__ import annotations
 
@@ -31,7 +31,8 @@ import subprocess
 import sys
 import tempfile
 
-VALU_COUNTS = (0, 4)
+# (vector instructions, LDS reads) after each product
+MIXES = ((0, 0), (4, 0), (0, 1), (4, 1))
 DATA = ("zeros", "normal")
 ITERS = 3_000_000
 FLOP_PER_MFMA = 2 * 32 * 32 * 16
@@ -40,10 +41,12 @@ CLOBBER = ",".join(f'"v{i}"' for i in range(128))
 PAIRS = (("v[64:67]", "v[68:71]"), ("v[72:75]", "v[76:79]"), ("v[64:67]", "v[76:79]"), ("v[72:75]", "v[68:71]"))
 
 
-def block(v):
+def block(v, l=0):
     """The assembly of one loop iteration: 4 MFMAs over alternating operand
-    sets, each followed by v vector instructions."""
-    lines, vi = [], 0
+    sets, each followed by v vector instructions and l `ds_read_b128` (1 KiB
+    per wave, the lanes' 16 bytes side by side), the reads waited for at the
+    end of the block."""
+    lines, vi, li = [], 0, 0
     for m, (a, b) in enumerate(PAIRS):
         acc = f"v[{16 * m}:{16 * m + 15}]"
         lines.append(f"v_mfma_f32_32x32x16_bf16 {acc}, {a}, {b}, {acc}")
@@ -51,6 +54,12 @@ def block(v):
             r = 80 + vi % 16
             lines.append(f"v_fma_f32 v{r}, v{r}, v96, v97")
             vi += 1
+        for _ in range(l):
+            d = 100 + 4 * (li % 4)
+            lines.append(f"ds_read_b128 v[{d}:{d + 3}], v98")
+            li += 1
+    if l:
+        lines.append("s_waitcnt lgkmcnt(0)")  # the reads complete inside the block
     return "\\n\\t".join(lines)
 
 
@@ -59,8 +68,8 @@ def source():
     moves = "\\n\\t".join(f"v_mov_b32 v{64 + i}, %{i}" for i in range(16))
     ins = ", ".join(f'"v"(r[{i}])' for i in range(16))
     zero_acc = "\\n\\t".join(f"v_mov_b32 v{i}, 0" for i in range(64))
-    for v in VALU_COUNTS:
-        name = f"power_{v}"
+    for v, l in MIXES:
+        name = f"power_{v}_{l}"
         ks.append(f'''
 __global__ __launch_bounds__(512) void {name}(const unsigned* ops, unsigned long long* clk, int iters) {{
   // this lane's 16 operand dwords (8 waves per workgroup, 64 lanes per wave)
@@ -69,10 +78,13 @@ __global__ __launch_bounds__(512) void {name}(const unsigned* ops, unsigned long
 #pragma unroll
   for (int i = 0; i < 16; ++i) r[i] = o[i];
   asm volatile("{moves}" :: {ins} : {CLOBBER});
-  asm volatile("{zero_acc}\\n\\tv_mov_b32 v96, 0x3f7ff000\\n\\tv_mov_b32 v97, 0x3a000000" ::: {CLOBBER});
+  // v96, v97: fma operands; v98: this lane's LDS byte offset (16 * lane, < 1 KiB)
+  asm volatile("{zero_acc}\\n\\tv_mov_b32 v96, 0x3f7ff000\\n\\tv_mov_b32 v97, 0x3a000000\\n\\t"
+               "v_mbcnt_lo_u32_b32 v99, -1, 0\\n\\tv_mbcnt_hi_u32_b32 v99, -1, v99\\n\\t"
+               "v_lshlrev_b32 v98, 4, v99\\n\\tv_and_b32 v98, 0x3f0, v98" ::: {CLOBBER});
   const unsigned long long c0 = __builtin_amdgcn_s_memtime();
   const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-  for (int i = 0; i < iters; ++i) asm volatile("{block(v)}" ::: {CLOBBER}, "memory");
+  for (int i = 0; i < iters; ++i) asm volatile("{block(v, l)}" ::: {CLOBBER}, "memory");
   asm volatile("s_nop 7\\n\\ts_nop 7" ::: "memory");  // the last products drain
   const unsigned long long c1 = __builtin_amdgcn_s_memtime();
   const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(512) void {name}(const unsigned* ops, unsigned long
   }}
 }}''')
         for d in DATA:
-            calls.append(f'  run({name}, "{d}", {v}, cus);')
+            calls.append(f'  run({name}, "{d}", {v}, {l}, cus);')
     main = f'''
 #define CHECK(x) do {{ if ((x) != hipSuccess) {{ printf("HIP error at line %d\\n", __LINE__); exit(1); }} }} while (0)
 static unsigned* d_ops;
@@ -109,7 +121,7 @@ static void fill(const char* data) {{
 }}
 
 template <class K>
-static void run(K k, const char* data, int v, int cus) {{
+static void run(K k, const char* data, int v, int l, int cus) {{
   fill(data);
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
@@ -143,7 +155,7 @@ static void run(K k, const char* data, int v, int cus) {{
   const double mfma = double(cus) * 8.0 * 4.0 * {ITERS};
   // cycles per product per SIMD: the loops' span at that clock over the
   // 2 waves x 4 x iters products of a SIMD
-  printf("%s %d %.1f %.3f %.2f %.1f %.1f %.2f %.2f %d\\n", data, v, mfma * {FLOP_PER_MFMA} / (ms * 1e-3) / 1e12, ghz,
+  printf("%s %d %d %.1f %.3f %.2f %.1f %.1f %.2f %.2f %d\\n", data, v, l, mfma * {FLOP_PER_MFMA} / (ms * 1e-3) / 1e12, ghz,
          ghz * 1e9 * span_ms * 1e-3 / (2.0 * 4.0 * {ITERS}), ms, span_ms, (s1 - s0) * 1e-5, (f1 - f0) * 1e-5, cus);
   fflush(stdout);
   CHECK(hipEventDestroy(e0));
@@ -157,7 +169,7 @@ int main() {{
   n_ops = (size_t)cus * 8 * 64 * 16;
   CHECK(hipMalloc(&d_ops, n_ops * 4));
   CHECK(hipMalloc(&d_clk, sizeof(unsigned long long) * 4 * 8 * cus));
-  printf("data valu_per_mfma tflops shader_ghz cycles_per_mfma ms loop_span_ms start_spread_ms end_spread_ms cus\\n");
+  printf("data valu_per_mfma lds_per_mfma tflops shader_ghz cycles_per_mfma ms loop_span_ms start_spread_ms end_spread_ms cus\\n");
 {chr(10).join(calls)}
   CHECK(hipFree(d_ops));
   CHECK(hipFree(d_clk));
@@ -195,10 +207,10 @@ def main():
     res = subprocess.run([exe], check=True, stdout=subprocess.PIPE, text=True, timeout=120)
     print(res.stdout, end="", flush=True)
     rows = [l.split() for l in res.stdout.splitlines()[1:] if l.strip()]
-    print("\n| operands | vector instructions per product | TFLOP/s (wall) | shader clock (GHz) "
-          "| cycles per product per SIMD |\n|---|---|---|---|---|")
-    for data, v, tf, ghz, cyc, *_ in rows:
-        print(f"| {data} | {v} | {float(tf):.0f} | {float(ghz):.2f} | {float(cyc):.1f} |")
+    print("\n| operands | vector instructions per product | LDS reads (1 KiB) per product | TFLOP/s (wall) "
+          "| shader clock (GHz) | cycles per product per SIMD |\n|---|---|---|---|---|---|")
+    for data, v, l, tf, ghz, cyc, *_ in rows:
+        print(f"| {data} | {v} | {l} | {float(tf):.0f} | {float(ghz):.2f} | {float(cyc):.1f} |")
 
 
 if __name__ == "__main__":

@@ -37,21 +37,29 @@ def test_builds(tmp_path):
 
 def test_power_block_contents():
     """The power microbenchmark's loop block: four products over the two A and
-    two B operand sets (every pairing once), v vector instructions after each,
-    writing only v80..v95."""
+    two B operand sets (every pairing once), v vector instructions and l LDS
+    reads after each, the reads waited for inside the block; the vector
+    instructions write only v80..v95 and the reads only v100..v115."""
     from block_masked_attention_amd.microbench import mfma_power
-    for v in mfma_power.VALU_COUNTS:
-        lines = mfma_power.block(v).split("\\n\\t")
+    for v, l in mfma_power.MIXES:
+        lines = mfma_power.block(v, l).split("\\n\\t")
         mf = [x for x in lines if x.startswith("v_mfma_f32_32x32x16_bf16")]
-        assert len(mf) == 4 and len(lines) == 4 + 4 * v
+        assert len(mf) == 4 and len(lines) == 4 + 4 * v + 4 * l + (1 if l else 0)
         pairs = {tuple(x.replace(",", "").split()[2:4]) for x in mf}
         assert pairs == {("v[64:67]", "v[68:71]"), ("v[72:75]", "v[76:79]"),
                          ("v[64:67]", "v[76:79]"), ("v[72:75]", "v[68:71]")}
         accs = [x.replace(",", "").split()[1] for x in mf]
         assert accs == [f"v[{16 * m}:{16 * m + 15}]" for m in range(4)]
+        reads = [i for i, x in enumerate(lines) if x.startswith("ds_read_b128")]
+        assert len(reads) == 4 * l
+        if l:
+            assert lines[-1] == "s_waitcnt lgkmcnt(0)" and max(reads) < len(lines) - 1
         for x in lines:
             if x.startswith("v_fma_f32"):
                 assert 80 <= int(x.split()[1].rstrip(",")[1:]) < 96
+            if x.startswith("ds_read_b128"):
+                lo, hi = x.split()[1].strip("v[],").split(":")
+                assert 100 <= int(lo) and int(hi) < 116
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not __import__("os").path.exists("/opt/rocm/bin/hipcc"),
