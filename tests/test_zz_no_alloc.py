@@ -2,8 +2,9 @@
 called through the C ABI: two calls in a row, the second on a smaller
 problem, each bitwise equal to the forward with a workspace (also with
 float32 outputs); a problem whose scratch exceeds the library's array is
-refused before any GPU work; with work claiming forced on, the claim
-counters in the scratch array restart at zero with every call."""
+refused before any GPU work; with work claiming or the persistent grid
+forced on, the claim counters in the scratch array restart at zero with
+every call."""
 import ctypes
 
 import pytest
@@ -62,6 +63,32 @@ def test_noalloc_forward_with_claimed_work(monkeypatch):
     small = small_spec(L=1024, B=16, H=4, Hkv=2, d=128, dtype="bf16", std=0.5, seed=35)
     for spec in (big, small, big):
         print(f"[gpu] no-alloc forward, claimed work: {spec.name} L={spec.n_clean_q}", flush=True)
+        t = make_inputs(spec, device="cuda")
+        p = bd.from_spec(spec)
+        st, got = _noalloc(p, t)
+        assert st == 0, bd.lib().bdattn_last_error().decode()
+        want = bd.fwd(p, *[t[k] for k in INPUT_NAMES])
+        torch.cuda.synchronize()
+        for a, b in zip(got, want):
+            assert not torch.isnan(a).any().item()
+            assert torch.equal(a, b)
+
+
+def test_noalloc_forward_on_the_persistent_grid(monkeypatch):
+    """Many short documents (lists of more items than CUs) on the persistent
+    grid, forced on: its workgroups claim item after item from the counters
+    in the scratch array, and three calls in a row (large, smaller, large)
+    each equal bdattn_fwd bitwise, with no output left unwritten."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    monkeypatch.setenv("BDATTN_CLAIM", "0")
+    monkeypatch.setenv("BDATTN_PERSIST", "1")
+    big = small_spec(L=16384, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=36,
+                     doc_starts=[0] + [256 * k + 32 * (k % 5) for k in range(1, 64)])
+    small = small_spec(L=8192, B=32, H=8, Hkv=2, d=128, dtype="bf16", std=0.5, seed=37,
+                       doc_starts=[0] + [256 * k + 64 * (k % 3) for k in range(1, 32)])
+    for spec in (big, small, big):
+        print(f"[gpu] no-alloc forward, persistent grid: {spec.name} L={spec.n_clean_q}", flush=True)
         t = make_inputs(spec, device="cuda")
         p = bd.from_spec(spec)
         st, got = _noalloc(p, t)
