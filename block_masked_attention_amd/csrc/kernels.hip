@@ -131,7 +131,13 @@ void fwd_kernel(FwdArgs a) {
         qf[ks] = q.row_ok ? E::load(qrow + 16 * ks + 8 * hf) : E::zero();
     }
 
-    TileCopy<T, TK, D, FWD_WAVES> cp;
+    // the first CW waves copy the key tiles. A tile's copies pass the CU's
+    // memory pipeline at about 64 bytes a cycle, and a wave waits at each of
+    // its copies until the pipeline takes it; the older wave of each SIMD,
+    // which runs ahead of its partner, absorbs that wait, and the younger one
+    // starts its products at once.
+    constexpr int CW = FWD_COPY_WAVES;
+    TileCopy<T, TK, D, CW> cp;
     cp.init(wave, lane, (int64_t)a.Hkv * D);
     const T* const kc = (const T*)a.k_c + (int64_t)q.kvh * D;
     const T* const kx = (const T*)a.k_x + (int64_t)q.kvh * D;
@@ -151,8 +157,10 @@ void fwd_kernel(FwdArgs a) {
       else k0 = cl ? j * TK : q.xlo + (j - q.n_ct) * TK;
       const int nk = cl ? a.n_clean_kv : a.n_corr;
       T* dst = smem + buf * 2 * TSZ;
-      cp.issue(dst, cl ? kc : kx, k0, nk);
-      cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
+      if (CW == FWD_WAVES || wave < CW) {
+        cp.issue(dst, cl ? kc : kx, k0, nk);
+        cp.issue(dst + TSZ, cl ? vc : vx, k0, nk);
+      }
     };
 
     OperandReads<BF16, D> rd;

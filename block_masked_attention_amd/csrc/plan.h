@@ -20,6 +20,12 @@ namespace bdattn {
 #define BDATTN_FWD_WAVES 8
 #endif
 constexpr int FWD_WAVES = BDATTN_FWD_WAVES;
+// Waves of the forward that copy its key tiles: the older wave of each SIMD
+// (waves w and w + 4 share one), which runs ahead of its partner
+#ifndef BDATTN_FWD_COPY_WAVES
+#define BDATTN_FWD_COPY_WAVES (BDATTN_FWD_WAVES / 2)
+#endif
+constexpr int FWD_COPY_WAVES = BDATTN_FWD_COPY_WAVES;
 constexpr int FWD_ROWS_PER_WAVE = 32;
 constexpr int FWD_TK = 64;
 // Backward dK/dV: a workgroup owns BWD_TK keys of one KV head, 32 per SIMD
