@@ -20,10 +20,11 @@ namespace bdattn {
 #define BDATTN_FWD_WAVES 8
 #endif
 constexpr int FWD_WAVES = BDATTN_FWD_WAVES;
-// Waves of the forward that copy its key tiles: the older wave of each SIMD
-// (waves w and w + 4 share one), which runs ahead of its partner
+// Waves of the forward that copy its key tiles: with 8 waves, the older wave
+// of each SIMD (waves w and w + 4 share one), which runs ahead of its partner;
+// with 4 (one per SIMD), all of them
 #ifndef BDATTN_FWD_COPY_WAVES
-#define BDATTN_FWD_COPY_WAVES (BDATTN_FWD_WAVES / 2)
+#define BDATTN_FWD_COPY_WAVES (BDATTN_FWD_WAVES == 8 ? 4 : BDATTN_FWD_WAVES)
 #endif
 constexpr int FWD_COPY_WAVES = BDATTN_FWD_COPY_WAVES;
 constexpr int FWD_ROWS_PER_WAVE = 32;
