@@ -97,13 +97,16 @@ def code_lines(text: str):
 
 def kernel_source_hash(csrc: str = None) -> str:
     """Hash of the code of the kernel sources whose counters a profile
-    describes (comments do not count)."""
+    describes (comments do not count) and of their compiler options."""
     import hashlib
     csrc = csrc or os.path.join(ROOT, "block_masked_attention_amd", "csrc")
+    from block_masked_attention_amd import build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(csrc, f)) as fh:
             h.update("\n".join(code_lines(fh.read())).encode() + b"\n")
+    # and the compiler options they are built with
+    h.update(repr((build.HIP_FLAGS, sorted(build.FILE_FLAGS.items()))).encode())
     return h.hexdigest()[:16]
 
 
