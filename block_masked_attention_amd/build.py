@@ -13,7 +13,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbdattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dkdv.hip", "kernels_bwd_fused.hip", "lce.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "kernels.hip", "kernels_dq_docs.hip", "kernels_dkdv.hip",
+           "kernels_bwd_fused.hip", "lce.hip"]
 HEADERS = ["bdattn_mask.h", "plan.h", "launch.h", "device.h"]
 ROCM_LIB = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
 
@@ -24,11 +25,15 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
-# Per-file options: the attention kernels are scheduled for instruction-level
-# parallelism (measured faster for the dK/dV kernel, and by 0.4-0.8% for the
-# forward and dQ kernels).
+# Per-file machine-scheduler strategies, the fastest measured for each file's
+# kernels: instruction-level parallelism for the key-tile backward kernels and
+# the dQ kernel's packed-document variants (which the register-minimising
+# schedule makes spill), the iterative register-minimising schedule for the
+# other forward and dQ kernels (dQ 2.4% faster than with max-ilp at 256K).
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
-FILE_FLAGS = {"kernels.hip": _ILP, "kernels_dkdv.hip": _ILP, "kernels_bwd_fused.hip": _ILP}
+_MINREG = ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"]
+FILE_FLAGS = {"kernels.hip": _MINREG, "kernels_dq_docs.hip": _ILP, "kernels_dkdv.hip": _ILP,
+              "kernels_bwd_fused.hip": _ILP}
 
 
 def hipcc() -> str:

@@ -37,6 +37,15 @@
 #include "device.h"
 
 namespace bdattn {
+
+// dQ launches for problems with packed documents. They live in a translation
+// unit of their own (kernels_dq_docs.hip, which compiles this file's kernels
+// with BDATTN_DQ_DOCS_UNIT defined) so that they can be built with another
+// machine scheduler than the rest of this file: the register-minimising
+// schedule that suits the other query-tile kernels makes this variant spill.
+template <bool BF16, int D, int PREC, bool MAPPED, bool PERSIST>
+void launch_dq_docs(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s);
+
 namespace {
 
 using namespace dev;
@@ -571,6 +580,7 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+#ifndef BDATTN_DQ_DOCS_UNIT
 template <bool BF16, int D, int PREC>
 hipError_t run_fwd_t(const FwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   if (ev) (void)hipEventRecord(ev[0].start, s);
@@ -633,17 +643,17 @@ hipError_t run_bwd_t(const BwdArgs& a, hipStream_t s, const KernelEvents* ev) {
   bool launched = false;
   if constexpr (BF16 && D == 128 && PREC == 0) {
     if (a.n_q_items > 0 && a.persist > 0) {  // (the host sets persist only without kv_map)
-      if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false, PREC, true>), dim3(a.persist), block, 0, s, a);
+      if (a.docs) launch_dq_docs<BF16, D, PREC, false, true>(a, dim3(a.persist), block, s);
       else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false, PREC, true>), dim3(a.persist), block, 0, s, a);
       launched = true;
     }
   }
   if (launched || a.n_q_items <= 0) {
   } else if (a.kv_map) {  // a gathered clean buffer
-    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, true, PREC>), grid, block, 0, s, a);
+    if (a.docs) launch_dq_docs<BF16, D, PREC, true, false>(a, grid, block, s);
     else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, true, PREC>), grid, block, 0, s, a);
   } else {
-    if (a.docs) hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, false, PREC>), grid, block, 0, s, a);
+    if (a.docs) launch_dq_docs<BF16, D, PREC, false, false>(a, grid, block, s);
     else hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, false, false, PREC>), grid, block, 0, s, a);
   }
   if (ev) (void)hipEventRecord(ev[0].stop, s);
@@ -704,5 +714,28 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int d, hipStream_t s, const K
   if (dtype == BDATTN_F32 && d == 32) return run_bwd<false, 32>(a, s, ev);
   return hipErrorInvalidValue;
 }
+#else  // BDATTN_DQ_DOCS_UNIT
+}  // namespace
+
+template <bool BF16, int D, int PREC, bool MAPPED, bool PERSIST>
+void launch_dq_docs(const BwdArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, true, MAPPED, PREC, PERSIST>), grid, block, 0, s, a);
+}
+
+// the variants run_bwd_t launches: every (dtype, d, precision) with and
+// without a gathered buffer, and the persistent grid of bf16, d = 128
+#define BDATTN_DQ_DOCS(BF16, D, PREC)                                                         \
+  template void launch_dq_docs<BF16, D, PREC, false, false>(const BwdArgs&, dim3, dim3, hipStream_t); \
+  template void launch_dq_docs<BF16, D, PREC, true, false>(const BwdArgs&, dim3, dim3, hipStream_t);
+BDATTN_DQ_DOCS(true, 128, 0)
+BDATTN_DQ_DOCS(true, 128, 1)
+BDATTN_DQ_DOCS(true, 128, 2)
+BDATTN_DQ_DOCS(true, 32, 0)
+BDATTN_DQ_DOCS(true, 32, 1)
+BDATTN_DQ_DOCS(true, 32, 2)
+BDATTN_DQ_DOCS(false, 32, 0)
+#undef BDATTN_DQ_DOCS
+template void launch_dq_docs<true, 128, 0, false, true>(const BwdArgs&, dim3, dim3, hipStream_t);
+#endif  // BDATTN_DQ_DOCS_UNIT
 
 }  // namespace bdattn

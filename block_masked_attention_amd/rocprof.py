@@ -53,8 +53,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # the kernels, their shared device code and tile constants (plan.h), and the
 # host code that orders their work and picks their launch shapes (plan.cpp,
 # api.cpp)
-KERNEL_SOURCES = ("kernels.hip", "kernels_dkdv.hip", "device.h", "bdattn_mask.h", "launch.h",
-                  "plan.h", "plan.cpp", "api.cpp")
+KERNEL_SOURCES = ("kernels.hip", "kernels_dq_docs.hip", "kernels_dkdv.hip", "device.h", "bdattn_mask.h",
+                  "launch.h", "plan.h", "plan.cpp", "api.cpp")
 # bench.py times the one-kernel backward in the dK/dV slot
 BENCH_NAME = {"fwd_kernel": "fwd", "bwd_dq_kernel": "bwd_dq", "bwd_dkdv_kernel": "bwd_dkdv",
               "bwd_fused_kernel": "bwd_dkdv"}
